@@ -1,0 +1,166 @@
+"""Pins of the oracle's weight decoders and block dot (CPU only).
+
+Pins:
+  * hand-derived golden blocks, one per format (tests/golden/decode_blocks.json) -- they fix the
+    layout readings (nibble order, group/sign/sub-scale positions, the CB3 high-bit plane);
+  * an independent vectorised numpy decoder written here (reshape / unpackbits / fancy
+    indexing, nothing shared with the C loops), over exhaustive code enumerations;
+  * dense equivalence: sum_b c_b equals a float64 numpy matmul of the dequantized weight matrix
+    with the dequantized q8_1 activations (a textbook mat-vec identity);
+  * a planted mistake (one flipped weight byte) changes the result.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from moe_routed_expert_route_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+Q8_0, NL4, CB2, CB3 = 1, 2, 3, 4
+BB = {Q8_0: 34, NL4: 18, CB2: 70, CB3: 110}
+BW = {Q8_0: 32, NL4: 32, CB2: 256, CB3: 256}
+
+
+def np_dequant(fmt, mat, rows, cols, nl4, cb2, cb3):
+    """Independent numpy decoder: float64 [rows, cols]."""
+    nb = cols // BW[fmt]
+    b = np.asarray(mat, np.uint8).reshape(rows, nb, BB[fmt])
+    d = b[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64)
+    if fmt == Q8_0:
+        return (d[..., None] * b[..., 2:].view(np.int8)).reshape(rows, cols)
+    if fmt == NL4:
+        nib = b[..., 2:18]
+        codes = np.concatenate([nib & 15, nib >> 4], axis=-1)
+        return (d[..., None] * np.asarray(nl4, np.int64)[codes]).reshape(rows, cols)
+    if fmt == CB2:
+        grid = np.asarray(cb2, np.int64).reshape(256, 8)
+        mags = grid[b[..., 2:34]].reshape(rows, nb, 256)
+        neg = np.unpackbits(b[..., 34:66], axis=-1, bitorder="little").astype(np.int64)
+        sc = b[..., 66:70]
+    else:
+        grid = np.asarray(cb3, np.int64).reshape(512, 4)
+        hi = np.unpackbits(b[..., 66:74], axis=-1, bitorder="little").astype(np.int64)
+        idx = b[..., 2:66].astype(np.int64) | (hi << 8)
+        mags = grid[idx].reshape(rows, nb, 256)
+        neg = np.unpackbits(b[..., 74:106], axis=-1, bitorder="little").astype(np.int64)
+        sc = b[..., 106:110]
+    codes = mags * (1 - 2 * neg)
+    sub = np.stack([sc & 15, sc >> 4], axis=-1).reshape(rows, nb, 8).astype(np.float64)
+    scale = d[..., None] * (2 * sub + 1)
+    return (np.repeat(scale, 32, axis=-1) * codes).reshape(rows, cols)
+
+
+def np_dequant_q8_1(xq, n):
+    b = np.asarray(xq, np.uint8).reshape(n // 32, 36)
+    d = b[:, 0:2].copy().view(np.float16)[:, 0].astype(np.float64)
+    return (d[:, None] * b[:, 4:].view(np.int8)).reshape(n)
+
+
+def _tables(key=0):
+    import oracle
+    return oracle.Tables(synth.nl4_table(key), synth.cb2_grid(key), synth.cb3_grid(key))
+
+
+def _from_hex(s):
+    return np.frombuffer(bytes.fromhex(s), np.uint8)
+
+
+def test_golden_q8_0(orc):
+    g = json.load(open(os.path.join(GOLD, "decode_blocks.json")))["q8_0"]
+    blk = np.concatenate([_from_hex(g["bytes_hex"]), np.array(g["q"], np.int8).view(np.uint8)])
+    codes, scales = orc.decode_row(Q8_0, blk, 32, orc.Tables())
+    assert codes.tolist() == g["q"] and scales.tolist() == [g["scale"]]
+    assert (codes[:8] * scales[0]).tolist() == g["values_first8"]
+
+
+def test_golden_nl4(orc):
+    g = json.load(open(os.path.join(GOLD, "decode_blocks.json")))["nl4"]
+    blk = np.concatenate([_from_hex("003c"), np.array([i | (15 - i) << 4 for i in range(16)], np.uint8)])
+    codes, scales = orc.decode_row(NL4, blk, 32, orc.Tables(nl4=np.array(g["table"], np.int8)))
+    assert codes.tolist() == g["codes"] and scales.tolist() == [g["scale"]]
+
+
+def test_golden_cb2(orc):
+    g = json.load(open(os.path.join(GOLD, "decode_blocks.json")))["cb2"]
+    grid = np.array([[2 * ((r + j) % 4) + 1 for j in range(8)] for r in range(256)], np.uint8)
+    blk = np.zeros(70, np.uint8)
+    blk[0:2] = _from_hex("003c")
+    blk[2:34] = np.arange(32)
+    blk[34:66] = [1 << (gg % 8) for gg in range(32)]
+    blk[66:70] = _from_hex("10325476")
+    codes, scales = orc.decode_row(CB2, blk, 256, orc.Tables(cb2=grid.reshape(-1)))
+    assert codes[:16].tolist() == g["codes_0_16"]
+    assert codes[248:].tolist() == g["codes_248_256"]
+    assert scales.tolist() == g["scales"]
+
+
+def test_golden_cb3(orc):
+    g = json.load(open(os.path.join(GOLD, "decode_blocks.json")))["cb3"]
+    grid = np.array([[2 * ((r + 3 * j) % 8) + 1 for j in range(4)] for r in range(512)], np.uint8)
+    blk = np.zeros(110, np.uint8)
+    blk[0:2] = _from_hex("0040")
+    blk[2:66] = np.arange(64)
+    blk[66] = 0x02
+    blk[74] = 0x01
+    blk[75] = 0x80
+    blk[106:110] = _from_hex("210000f0")
+    codes, scales = orc.decode_row(CB3, blk, 256, orc.Tables(cb3=grid.reshape(-1)))
+    assert codes[:16].tolist() == g["codes_0_16"]
+    assert scales.tolist() == g["scales"]
+
+
+def _enumerating_matrix(fmt, rows, cols, key):
+    """Random matrix whose code fields run through every value the format has."""
+    m = synth.weight_matrix(fmt, rows, cols, key).reshape(-1, BB[fmt]).copy()
+    n = m.shape[0]
+    if fmt == NL4:
+        m[:, 2:18] = (np.arange(n * 16) % 256).reshape(n, 16)          # every nibble pair
+    elif fmt == CB2:
+        m[:, 2:34] = (np.arange(n * 32) % 256).reshape(n, 32)          # every grid row
+        m[:, 66:70] = (np.arange(n * 4) * 0x11 % 256).reshape(n, 4)     # every sub-scale
+    elif fmt == CB3:
+        m[:, 2:66] = (np.arange(n * 64) % 256).reshape(n, 64)
+        m[:, 66:74] = (np.arange(n * 8) * 37 % 256).reshape(n, 8)      # both hi-bit values
+        m[:, 106:110] = (np.arange(n * 4) * 0x11 % 256).reshape(n, 4)
+    return m.reshape(-1)
+
+
+@pytest.mark.parametrize("fmt", [Q8_0, NL4, CB2, CB3])
+def test_decoder_matches_numpy(orc, fmt):
+    rows, cols = 24, 512
+    tb = _tables(1)
+    mat = _enumerating_matrix(fmt, rows, cols, 5)
+    ref = np_dequant(fmt, mat, rows, cols, tb.nl4, tb.cb2, tb.cb3)
+    got = orc.dequantize(fmt, mat, rows, cols, tb)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("fmt", [Q8_0, NL4, CB2, CB3])
+def test_matvec_dense_equivalence(orc, fmt):
+    rows, cols = 40, 768
+    tb = _tables(2)
+    mat = synth.weight_matrix(fmt, rows, cols, 9)
+    x = synth.activations(1, cols, 3)[0]
+    xq = orc.quantize_q8_1(x)
+    W = np_dequant(fmt, mat, rows, cols, tb.nl4, tb.cb2, tb.cb3)
+    xd = np_dequant_q8_1(xq, cols)
+    ref = W @ xd
+    out, S = orc.matvec(fmt, mat, rows, cols, xq, tb)
+    assert np.all(np.abs(out - ref) <= 1e-12 * S)
+    # S is the sum of |block contributions|: never below |out|, equal for one-signed blocks
+    assert np.all(S >= np.abs(out))
+    Sref = np.abs((W * xd[None, :]).reshape(rows, cols // 32, 32).sum(-1)).sum(-1)
+    assert np.allclose(S, Sref, rtol=1e-12, atol=0)
+
+
+def test_planted_weight_corruption_detected(orc):
+    tb = _tables(3)
+    mat = synth.weight_matrix(NL4, 8, 256, 4)
+    xq = orc.quantize_q8_1(synth.activations(1, 256, 4)[0])
+    out, S = orc.matvec(NL4, mat, 8, 256, xq, tb)
+    bad = mat.copy()
+    bad[18 * 3 + 7] ^= 0x11        # row 0, block 3: flip two codes
+    out2, _ = orc.matvec(NL4, bad, 8, 256, xq, tb)
+    assert np.any(np.abs(out2 - out) > 2e-5 * S)
