@@ -1,0 +1,179 @@
+/*
+ * moe_route.h -- grouped routed-expert MoE decode for one MI355X (gfx950), C ABI.
+ *
+ * The operation (from the pages this method is described on):
+ *   "#363 experts: smaller and fewer launches for the verify window's PCIe call", opening
+ *   paragraph: a verify window of T tokens with top-k routing has up to cap_groups = T x k
+ *   (expert) groups; the grouped gate/up and down kernels run one group per block row, with
+ *   n_groups read on the device. "What changes": group g runs in block row g % gridDim.y and the
+ *   results do not depend on the grid; SwiGLU and the q8_1 quantization run in one kernel over the
+ *   call's own entries [grp_start[0], grp_start[n_groups]), the SwiGLU product rounded on its own
+ *   before the q8_1 block sums. "Exactness": entries may start past index 0, destinations may be
+ *   scattered, stale scratch must not matter, rows a call must not write keep their contents.
+ *   "#2058 Verify window: the routed experts' gate/up with the group's q8_1 rows in shared
+ *   memory", "Why": each expert's weights are decoded once per group and applied to the group's
+ *   1-4 entries, whose 36-byte q8_1 activation rows are staged on chip.
+ *
+ * Conventions for every entry point:
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only enqueues work on it:
+ *    no call allocates, frees, synchronises or reads device memory from the host, so every call
+ *    can be captured into a HIP graph.
+ *  - Pointers are device pointers unless a comment says "host". The caller owns all memory.
+ *  - Return value: MOE_OK (0) or a negative moe_status for a problem the host can see (null
+ *    pointer, bad shape or format, a HIP launch error). Problems only the device can see (an
+ *    expert id, token or destination out of range, n_groups above cap_groups, a bounded wait that
+ *    ran out) make the device skip that group or entry and OR a bit into *plan->err
+ *    (MOE_ERR_* below); nothing traps or prints.
+ *  - Results are bit-identical for every grid_limit (0 = automatic) and between
+ *    moe_layer_decode and the composed calls quantize -> gate_up -> swiglu -> down_scatter.
+ *
+ * Weight formats (the pages name the formats but print no layout; these are the layouts this
+ * library reads, all little-endian, blocks packed with no padding, fp16 scale first):
+ *   Q8_0  34 B / 32 w : [0:2] fp16 d, [2:34] int8 q[32]; w_j = d * q_j.
+ *   NL4   18 B / 32 w : [0:2] fp16 d, [2:18] b[16]; code of w_i = T[b[i] & 15], of w_(i+16) =
+ *                       T[b[i] >> 4]; T = 16-entry int8 table (nl4_table); w = d * code.
+ *   CB2   70 B / 256 w: [0:2] fp16 D, [2:34] idx[32] (8-weight groups), [34:66] sign bytes (bit j
+ *                       of byte g set = weight 8g+j negative), [66:70] eight 4-bit sub-scales s_b
+ *                       (sub-block b = weights 32b..32b+31, low nibble first); code =
+ *                       +-G2[idx][j], G2 = 256 x 8 uint8 grid (cb2_grid); w = D (2 s_b + 1) code.
+ *   CB3  110 B / 256 w: [0:2] fp16 D, [2:66] low index bytes (4-weight groups), [66:74] high index
+ *                       bits (group g: bit g%8 of byte g/8), [74:106] sign bits (weight i: bit i%8
+ *                       of byte i/8), [106:110] sub-scales as CB2; code = +-G3[idx][j], G3 = 512 x 4
+ *                       uint8 grid (cb3_grid); w = D (2 s_b + 1) code.
+ *   q8_1  36 B / 32 values (activations): [0:2] fp16 d, [2:4] fp16 s, [4:36] int8 q[32], with
+ *         amax = max|x|, d = amax / 127 (float32), q = clamp(round-half-away(x / d), +-127)
+ *         (0 if amax == 0), d16 = fp16(d), s16 = fp16(f(d16) * sum q), all IEEE float32.
+ * A matrix of R rows x C columns is R consecutive rows of C / block_weights blocks.
+ * Shapes: C must be a multiple of 64 for Q8_0 / NL4 and of 256 for CB2 / CB3; n_embd and n_ff
+ * at most MOE_MAX_DIM.
+ * Block contribution: c_b = scale_w * f(d_x) * sum_j code_j q_j (exact int32 sum); a row's dot
+ * product is the sum of its c_b.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MAX_DIM 8192          /* max n_embd / n_ff */
+#define MOE_MAX_CALL_ENTRIES 64   /* max cap_entries (T x k) of one call */
+#define MOE_MAX_GROUPS 64         /* max cap_groups of one call */
+
+typedef enum { MOE_FMT_Q8_0 = 1, MOE_FMT_NL4 = 2, MOE_FMT_CB2 = 3, MOE_FMT_CB3 = 4 } moe_fmt;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_ARG = -1,    /* null pointer or bad scalar argument */
+  MOE_E_FMT = -2,    /* unknown weight format */
+  MOE_E_SHAPE = -3,  /* dimension not supported (see "Shapes") */
+  MOE_E_HIP = -4,    /* a HIP call failed; moe_last_error() has its text */
+  MOE_E_WS = -5      /* workspace missing or too small */
+} moe_status;
+
+/* Device error bits OR-ed into *plan->err (sticky until the caller clears them). */
+#define MOE_ERR_NGROUPS 1u   /* *n_groups < 0 or > cap_groups: the call did nothing */
+#define MOE_ERR_ENTRIES 2u   /* grp_start not ascending or more than cap_entries entries */
+#define MOE_ERR_EXPERT 4u    /* grp_expert out of [0, n_experts): that group skipped */
+#define MOE_ERR_SRC 8u       /* ent_src out of [0, n_tokens): that entry skipped */
+#define MOE_ERR_DST 16u      /* ent_dst out of [0, n_rows): that entry skipped */
+#define MOE_ERR_ALIGN 32u    /* a weight pointer not 2-byte aligned: that group skipped */
+#define MOE_ERR_WAIT 64u     /* a bounded on-device wait ran out (results of the call invalid) */
+
+/* One MoE layer's experts. Host struct, read during the call only. */
+typedef struct moe_layer {
+  int32_t n_embd, n_ff, n_experts;
+  int32_t fmt_gate_up;           /* format of gate and up (moe_fmt) */
+  int32_t fmt_down;              /* format of down */
+  const void* const* gate;       /* device array [n_experts] of device pointers: n_ff x n_embd */
+  const void* const* up;         /* same */
+  const void* const* down;       /* device array [n_experts]: n_embd x n_ff */
+  const int8_t* nl4_table;       /* 16 B, needed if a format is NL4 (else may be NULL) */
+  const uint8_t* cb2_grid;       /* 256 x 8 B, needed if a format is CB2 */
+  const uint8_t* cb3_grid;       /* 512 x 4 B, needed if a format is CB3 */
+} moe_layer;
+
+/* The entries of one call grouped by expert. Host struct holding device pointers. */
+typedef struct moe_plan {
+  int32_t cap_groups;            /* host: most groups a call may have (grid sizing), >= 1 */
+  int32_t cap_entries;           /* host: most entries a call may have, >= 1 */
+  int32_t* n_groups;             /* device scalar 0..cap_groups, read on the device */
+  int32_t* grp_expert;           /* [cap_groups] expert of each group */
+  int32_t* grp_start;            /* [cap_groups + 1] absolute first entry of each group */
+  int32_t* ent_src;              /* token row of x / xq of each entry (absolute index) */
+  int32_t* ent_dst;              /* output row of Y of each entry */
+  float* ent_w;                  /* router weight of each entry */
+  uint32_t* err;                 /* device sticky error bits (MOE_ERR_*) */
+} moe_plan;
+
+/* Router ("#363 ...": the window's tokens each pick top-k experts). For each of T tokens:
+ * softmax over E float32 logits [T][E], the k largest by (logit descending, expert id
+ * ascending), weights renormalised over those k. Outputs ids int32 [T][k] and w float32 [T][k],
+ * in rank order. 1 <= k <= min(E, 32), E <= 1024. */
+int moe_route_topk(void* stream, const float* logits, int T, int E, int k, int32_t* ids,
+                   float* w);
+
+/* Group the T*k entries by expert ("#2058 ...", "Why"): groups ascending by expert id, entries
+ * in a group ascending by token; entry indices are absolute, starting at entry_base >= 0.
+ * Writes *n_groups, grp_expert, grp_start[0..n_groups], ent_src (= token), ent_dst
+ * (= dst_of_token[token], or the token if dst_of_token is NULL), ent_w (= w[token][rank]).
+ * Requires T*k <= plan->cap_entries and T*k <= plan->cap_groups (host-checked). Ids out of
+ * [0, E) set MOE_ERR_EXPERT and their entries are dropped. One workgroup; tiny. */
+int moe_build_plan(void* stream, const int32_t* ids, const float* w, const int32_t* dst_of_token,
+                   int T, int k, int E, int entry_base, const moe_plan* plan);
+
+/* q8_1 quantization of `rows` rows of n float32 values (n % 32 == 0) into rows * n/32 blocks of
+ * 36 B (layout above), bit-exact IEEE float32 ("#363 ...", "What changes": the quantizer). */
+int moe_quantize_q8_1(void* stream, const float* x, int rows, int n, void* q);
+
+/* Grouped gate/up: for each entry a of the call (group g, expert e) and row r < n_ff,
+ * g[a][r] = sum_b c_b(gate_e row r, xq row ent_src[a]) and the same for u with up_e.
+ * xq: n_tokens rows of n_embd/32 q8_1 blocks. g, u: float32 rows of stride ld >= n_ff, indexed by
+ * absolute entry; only the call's entries' rows are written. */
+int moe_gate_up(void* stream, const moe_layer* L, const moe_plan* P, const void* xq, int n_tokens,
+                float* g, float* u, int ld, int grid_limit);
+
+/* Fused SwiGLU + q8_1 over the call's entries: h = (g / (1 + exp(-g))) * u, each operation a
+ * float32 rounding, then hq = q8_1(h). h may be NULL. hq rows: n_ff/32 blocks per absolute entry;
+ * h rows: stride ld. Only the call's entries are read or written. */
+int moe_swiglu_q8_1(void* stream, const moe_plan* P, const float* g, const float* u, int n_ff,
+                    int ld, float* h, void* hq);
+
+/* Grouped down + weighted scatter: o_a[m] = sum_b c_b(down_e row m, hq row a) for m < n_embd, then
+ * Y[ent_dst[a]][m] = Y + sum over the call's entries with that destination, in ascending entry
+ * order, of ent_w[a] * o_a[m] (float32). Y: n_rows rows of stride ldy; rows no entry names are
+ * neither read nor written. Uses the workspace (see moe_workspace_bytes / moe_workspace_init). */
+int moe_down_scatter(void* stream, const moe_layer* L, const moe_plan* P, const void* hq,
+                     float* Y, int n_rows, int ldy, void* workspace, size_t ws_bytes,
+                     int grid_limit);
+
+/* Host: bytes of workspace the down/scatter and layer calls need for this layer and plan. */
+size_t moe_workspace_bytes(const moe_layer* L, const moe_plan* P);
+
+/* Clear the workspace's synchronisation counters (enqueued fill kernel). Call once after
+ * allocating a workspace; every call leaves the counters cleared again. */
+int moe_workspace_init(void* stream, void* workspace, size_t ws_bytes);
+
+/* The whole step in one launch: q8_1(x rows) -> grouped gate/up -> SwiGLU + q8_1 -> grouped down
+ * -> weighted scatter into Y, for the call's entries. x: n_tokens float32 rows of n_embd.
+ * Bit-identical to the composed calls. The workspace also holds the intermediates (layout:
+ * moe_workspace_layout). Calls that overlap on one workspace race; calls in one stream do not. */
+int moe_layer_decode(void* stream, const moe_layer* L, const moe_plan* P, const float* x,
+                     int n_tokens, float* Y, int n_rows, int ldy, void* workspace,
+                     size_t ws_bytes, int grid_limit);
+
+/* Host: byte offsets inside the workspace of the intermediates of the last moe_layer_decode:
+ * off[0] g float32 [cap_entries][n_ff], off[1] u (same), off[2] hq [cap_entries][n_ff/32 * 36 B],
+ * off[3] o float32 [cap_entries][n_embd]; rows indexed by (entry - grp_start[0]). */
+int moe_workspace_layout(const moe_layer* L, const moe_plan* P, size_t off[4]);
+
+const char* moe_status_string(int status);   /* host, static string */
+const char* moe_last_error(void);            /* host, text of the last MOE_E_HIP on this thread */
+
+#ifdef __cplusplus
+}
+#endif
+#endif

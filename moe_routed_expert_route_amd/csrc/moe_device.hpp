@@ -1,0 +1,239 @@
+// Device building blocks for the grouped routed-expert decode kernels (gfx950, wave64).
+//
+// * binary16 helpers and the q8_1 block quantizer (bit-exact IEEE float32: d = amax / 127,
+//   q = round half away from zero of x / d, clamped to +-127; s = fp16(f(d16) * sum q)). The
+//   36-byte q8_1 block is the activation format of "#2058 Verify window: the routed experts'
+//   gate/up with the group's q8_1 rows in shared memory", section "Why"; the rounding rule is the
+//   library's reading of a quantizer the pages leave unstated.
+// * SwiGLU rounded op by op in float32 ("#363 experts: smaller and fewer launches for the verify
+//   window's PCIe call", "What changes": the product is rounded on its own before the q8_1 sums).
+// * Weight decoders that read a weight unit (32 weights) out of a byte image staged in LDS, at any
+//   byte alignment, and return eight dwords of int8 codes plus the unit's float scale.
+// * Fixed-order cross-lane sums (DPP), so every kernel variant reduces a row in the same order.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_LDS __attribute__((address_space(3)))
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace moe {
+
+constexpr int kThreads = 256;          // every kernel runs 4 waves of 64
+constexpr int kMaxSlots = 4;           // entries staged at once (a group's rows of the window)
+
+enum Fmt : int { Q8_0 = 1, NL4 = 2, CB2 = 3, CB3 = 4 };
+
+// ------------------------------------------------------------------ binary16 ----------------
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+__device__ __forceinline__ uint32_t f2h(float f) {   // round to nearest even, subnormals kept
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// ------------------------------------------------------------------ q8_1 ---------------------
+
+__device__ __forceinline__ float round_half_away(float v) {
+  float t = __builtin_truncf(v);
+  if (__builtin_fabsf(v - t) >= 0.5f) t += __builtin_copysignf(1.0f, v);  // v - t is exact
+  return t;
+}
+
+// s16 = fp16(f(d16) * isum). The product is exact in float32 (11 x 12 bits), so rounding it once
+// to fp16 is the whole story except for the sign of a zero product: IEEE gives -0 when d16 is
+// +0 and isum < 0. That case is set explicitly, whatever instruction the compiler picks for the
+// multiply + convert.
+__device__ __forceinline__ uint32_t sum_field(uint32_t d16, int isum) {
+  uint32_t s = f2h(h2f(d16) * (float)isum);
+  if (d16 == 0 && isum < 0) s = 0x8000u;
+  return s;
+}
+
+// One 32-value block: q[0..7] = the 32 int8 codes packed little-endian, d = f(d16) as float,
+// d16 / s16 = the stored fp16 fields.
+struct QBlock {
+  uint32_t q[8];
+  float d;
+  uint32_t d16, s16;
+};
+
+__device__ __forceinline__ QBlock quant_block(const float v[32]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float a = __builtin_fabsf(v[i]);
+    amax = a > amax ? a : amax;
+  }
+  const float d = amax / 127.0f;
+  QBlock b;
+  int isum = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int q = 0;
+      if (amax != 0.0f) {
+        float r = round_half_away(v[4 * w + j] / d);
+        r = r > 127.0f ? 127.0f : r;
+        r = r < -127.0f ? -127.0f : r;
+        q = (int)r;
+      }
+      isum += q;
+      packed |= ((uint32_t)q & 0xFFu) << (8 * j);
+    }
+    b.q[w] = packed;
+  }
+  b.d16 = f2h(d);
+  b.d = h2f(b.d16);
+  b.s16 = sum_field(b.d16, isum);
+  return b;
+}
+
+// h = silu(g) * u with every operation a float32 rounding, in this order.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  float den = 1.0f + expf(-g);
+  float s = g / den;
+  return s * u;
+}
+
+// ------------------------------------------------------------------ cross-lane sums ---------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+
+// Sum over aligned groups of L lanes (L a power of two, 1..64); every lane of a group ends with
+// the same value (each step adds two equal partial sums in either order, which is exact-
+// commutative), so the result is a fixed function of the L inputs.
+__device__ __forceinline__ float group_sum(float v, int L) {
+  if (L >= 2) v = v + dpp<0xB1>(v);    // quad_perm [1,0,3,2]  (xor 1)
+  if (L >= 4) v = v + dpp<0x4E>(v);    // quad_perm [2,3,0,1]  (xor 2)
+  if (L >= 8) v = v + dpp<0x141>(v);   // row_half_mirror      (quad <-> quad)
+  if (L >= 16) v = v + dpp<0x140>(v);  // row_mirror           (half-row <-> half-row)
+  if (L >= 32) v = v + __shfl_xor(v, 16);
+  if (L >= 64) v = v + __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max32(float v) {   // max over aligned groups of 32 lanes
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) {
+    float o = __shfl_xor(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ int wave_sum32(int v) {
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// ------------------------------------------------------------------ LDS byte images ---------
+
+// Little-endian dword starting at any byte offset of an LDS image (reads two aligned dwords; the
+// image keeps 16 bytes of slack after its end for this).
+__device__ __forceinline__ uint32_t ldw(const MOE_LDS uint32_t* W, uint32_t off) {
+  const uint32_t i = off >> 2;
+  return __builtin_amdgcn_alignbyte(W[i + 1], W[i], off & 3u);
+}
+
+// 16-entry int8 lookup of four 4-bit codes (one per byte) with v_perm: entries 0-7 and 8-15 are
+// looked up separately and merged by the code's bit 3.
+__device__ __forceinline__ uint32_t lut16(uint32_t c, const uint32_t t[4]) {
+  const uint32_t s = c & 0x07070707u;
+  const uint32_t lo = __builtin_amdgcn_perm(t[1], t[0], s);
+  const uint32_t hi = __builtin_amdgcn_perm(t[3], t[2], s);
+  // selector 4 picks byte 0 of the first operand (0xFF), selector 12 yields 0x00
+  const uint32_t m = __builtin_amdgcn_perm(0xFFFFFFFFu, 0u, (c & 0x08080808u) | 0x04040404u);
+  return (lo & m) | (hi & ~m);
+}
+
+// Negate the bytes of `mag` (each 1..15) selected by the low 4 bits of `nib` (bit j -> byte j).
+__device__ __forceinline__ uint32_t apply_sign(uint32_t mag, uint32_t nib) {
+  const uint32_t t = (nib * 0x00204081u) & 0x01010101u;   // bit j -> bit 0 of byte j
+  const uint32_t m = (t << 8) - t;                          // 0xFF in selected bytes
+  return (mag ^ m) + t;                                     // ~mag + 1 per selected byte
+}
+
+struct Tables {
+  uint32_t nl4[4];                       // NL4 table in registers
+  const MOE_LDS uint32_t* cb2;           // 256 x 8 B grid in LDS (2 dwords per row)
+  const MOE_LDS uint32_t* cb3;           // 512 x 4 B grid in LDS (1 dword per row)
+};
+
+// Decode weight unit u (32 weights, u = 32-weight index inside the row) of a row whose first byte
+// sits at LDS byte offset `row`. c[k] holds the codes of weights 4k..4k+3 of the unit.
+template <int FMT>
+__device__ __forceinline__ void decode_unit(const MOE_LDS uint32_t* W, uint32_t row, int u,
+                                            const Tables& tb, uint32_t c[8], float& sc) {
+  if constexpr (FMT == Q8_0) {
+    const uint32_t o = row + 34u * (uint32_t)u;
+    sc = h2f(ldw(W, o) & 0xFFFFu);
+    const uint32_t b = (o + 2) >> 2, sh = (o + 2) & 3u;
+    uint32_t w[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) w[i] = W[b + i];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_alignbyte(w[k + 1], w[k], sh);
+  } else if constexpr (FMT == NL4) {
+    const uint32_t o = row + 18u * (uint32_t)u;
+    sc = h2f(ldw(W, o) & 0xFFFFu);
+    const uint32_t b = (o + 2) >> 2, sh = (o + 2) & 3u;
+    uint32_t w[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) w[i] = W[b + i];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t n = __builtin_amdgcn_alignbyte(w[k + 1], w[k], sh);
+      c[k] = lut16(n & 0x0F0F0F0Fu, tb.nl4);            // weights 4k..4k+3
+      c[k + 4] = lut16((n >> 4) & 0x0F0F0F0Fu, tb.nl4);  // weights 16+4k..16+4k+3
+    }
+  } else if constexpr (FMT == CB2) {
+    const uint32_t so = row + 70u * (uint32_t)(u >> 3);
+    const uint32_t su = (uint32_t)u & 7u;
+    const float D = h2f(ldw(W, so) & 0xFFFFu);
+    const uint32_t idx4 = ldw(W, so + 2 + 4 * su);
+    const uint32_t sg4 = ldw(W, so + 34 + 4 * su);
+    const uint32_t s = (ldw(W, so + 66) >> (4 * su)) & 15u;
+    sc = D * (float)(2 * s + 1);
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const uint32_t idx = (idx4 >> (8 * gq)) & 0xFFu;
+      const uint32_t sg = (sg4 >> (8 * gq)) & 0xFFu;
+      c[2 * gq] = apply_sign(tb.cb2[2 * idx], sg & 15u);
+      c[2 * gq + 1] = apply_sign(tb.cb2[2 * idx + 1], sg >> 4);
+    }
+  } else {  // CB3
+    const uint32_t so = row + 110u * (uint32_t)(u >> 3);
+    const uint32_t su = (uint32_t)u & 7u;
+    const float D = h2f(ldw(W, so) & 0xFFFFu);
+    const uint32_t lo0 = ldw(W, so + 2 + 8 * su);
+    const uint32_t lo1 = ldw(W, so + 6 + 8 * su);
+    const uint32_t hib = ldw(W, so + 66 + su);
+    const uint32_t sg4 = ldw(W, so + 74 + 4 * su);
+    const uint32_t s = (ldw(W, so + 106) >> (4 * su)) & 15u;
+    sc = D * (float)(2 * s + 1);
+#pragma unroll
+    for (int gq = 0; gq < 8; ++gq) {
+      const uint32_t lo = ((gq < 4 ? lo0 : lo1) >> (8 * (gq & 3))) & 0xFFu;
+      const uint32_t idx = lo | (((hib >> gq) & 1u) << 8);
+      c[gq] = apply_sign(tb.cb3[idx], (sg4 >> (4 * gq)) & 15u);
+    }
+  }
+}
+
+__host__ __device__ constexpr int block_bytes(int fmt) {
+  return fmt == Q8_0 ? 34 : fmt == NL4 ? 18 : fmt == CB2 ? 70 : fmt == CB3 ? 110 : 0;
+}
+__host__ __device__ constexpr int block_weights(int fmt) {
+  return (fmt == CB2 || fmt == CB3) ? 256 : 32;
+}
+
+}  // namespace moe

@@ -1,0 +1,230 @@
+"""GPU parity of the HIP path (through the C-ABI) against the CPU oracle, stage by stage.
+
+Workloads (seeded, synthetic; shapes from the pages): the small 8-expert Q8_0 layer; the
+2560 x 768 NL4 layer with 128 experts, top-8, T = 1; 2560 x 768 CB2 gate/up + NL4 down with a
+T = 4 Zipf window; 2560 x 640 CB3 gate/up + Q8_0 down with 256 experts at T = 1..4 and a window
+whose tokens share their experts; 4096 x 1536 Q8_0 plans built directly with 0 / 1 / 2 / 4 / 32
+groups, entries from index 7, destinations scattered over 64 NaN-filled rows ("#363 experts:
+smaller and fewer launches for the verify window's PCIe call", "Exactness").
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_routed_expert_route_amd import binding as B
+from moe_routed_expert_route_amd import synth
+
+from . import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+Q8_0, NL4, CB2, CB3 = 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    B.lib()
+
+
+# ------------------------------------------------------------------ quantizer -----------------
+
+def test_quantize_bitexact():
+    g = np.random.default_rng(5)
+    rows = [g.standard_normal(2560) * s for s in (1.0, 1e-3, 37.0, 2e-7)]
+    tie = np.zeros(2560)
+    tie[0::32] = 127.0
+    tie[1::32] = np.arange(80) - 39.5          # exact k + 1/2 quotients
+    rows += [tie, np.zeros(2560)]
+    x = np.stack(rows).astype(np.float32)
+    q = B.moe_quantize_q8_1(torch.from_numpy(x).to(U.dev()))
+    torch.cuda.synchronize()
+    U.assert_q81_equal(q.cpu().numpy(), oracle.quantize_q8_1(x), x)
+
+
+def test_quantize_golden():
+    import json
+    import os
+    doc = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "q8_1_blocks.json")))
+    x = np.stack([np.array(b["x"], np.float32) for b in doc["blocks"]])
+    q = B.moe_quantize_q8_1(torch.from_numpy(x).to(U.dev())).cpu().numpy()
+    for b, row in zip(doc["blocks"], q):
+        assert int(row[0]) | int(row[1]) << 8 == int(b["d16"], 16)
+        assert int(row[2]) | int(row[3]) << 8 == int(b["s16"], 16)
+        assert row[4:].view(np.int8).tolist() == b["q"]
+
+
+# ------------------------------------------------------------------ route and plan ------------
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (1, 128, 8), (4, 128, 8), (4, 256, 8), (3, 1000, 32)])
+def test_route_topk(T, E, k):
+    lg = synth.router_logits(T, E, T, E, k, 1)
+    lg[0, 3] = lg[0, 5] = lg[0].max() + 1.0          # a tie at the top: lower id first
+    ids, w = B.moe_route_topk(torch.from_numpy(lg).to(U.dev()), k)
+    oids, ow = oracle.route_topk(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    wg = w.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(wg - ow) <= 4 * np.spacing(ow.astype(np.float32)).astype(np.float64))
+
+
+@pytest.mark.parametrize("T,E,k,base", [(1, 8, 2, 0), (1, 128, 8, 0), (4, 128, 8, 7), (4, 256, 8, 3)])
+def test_build_plan(T, E, k, base):
+    ids = synth.zipf_ids(T, E, k, 1.1, T, E, base)
+    w = synth.rng(31, T).uniform(0.01, 1, (T, k)).astype(np.float32)
+    dst = synth.rng(32, T).choice(64, T, replace=False).astype(np.int32)
+    plan = B.Plan(T * k, T * k, entry_capacity=base + T * k, device=U.dev())
+    d = U.dev()
+    B.moe_build_plan(torch.from_numpy(ids).to(d), torch.from_numpy(w).to(d), plan, E,
+                     dst_of_token=torch.from_numpy(dst).to(d), entry_base=base)
+    got = plan.get()
+    ref = oracle.build_plan(ids, w, dst, E, base)
+    for key in ("grp_expert", "grp_start", "ent_src", "ent_dst"):
+        assert np.array_equal(got[key], ref[key]), key
+    assert np.array_equal(U.bits(got["ent_w"]), U.bits(ref["ent_w"]))
+    assert got["n_groups"] == ref["n_groups"] and plan.errors() == 0
+
+
+# ------------------------------------------------------------------ whole step, stage-wise ----
+
+ROUTED = {
+    "small_q8": dict(n_embd=256, n_ff=128, E=8, k=2, T=1, fg=Q8_0, fd=Q8_0),
+    "nl4_t1": dict(n_embd=2560, n_ff=768, E=128, k=8, T=1, fg=NL4, fd=NL4),
+    "cb2_nl4_t4_zipf": dict(n_embd=2560, n_ff=768, E=128, k=8, T=4, fg=CB2, fd=NL4, ids="zipf"),
+    "cb3_q8_t2": dict(n_embd=2560, n_ff=640, E=256, k=8, T=2, fg=CB3, fd=Q8_0, ids="uniform"),
+    "cb3_q8_t4_shared": dict(n_embd=2560, n_ff=640, E=256, k=8, T=4, fg=CB3, fd=Q8_0, ids="shared"),
+    "q8_nl4_t3": dict(n_embd=512, n_ff=256, E=16, k=4, T=3, fg=Q8_0, fd=NL4),
+    "nl4_cb2_t2": dict(n_embd=768, n_ff=512, E=16, k=4, T=2, fg=NL4, fd=CB2),
+    "cb2_cb3_t4": dict(n_embd=512, n_ff=512, E=12, k=3, T=4, fg=CB2, fd=CB3),
+    # groups of 4 entries on rows split over fewer lanes than entries (down: 2 lanes per row)
+    "q8_t4_shared_small": dict(n_embd=256, n_ff=128, E=8, k=2, T=4, fg=Q8_0, fd=Q8_0, ids="shared"),
+    # 2 units per row: one or two lanes per row
+    "nl4_t4_shared_tiny": dict(n_embd=64, n_ff=64, E=4, k=2, T=4, fg=NL4, fd=Q8_0, ids="shared"),
+}
+
+
+def _routed(name, key=0):
+    p = ROUTED[name]
+    ids = None
+    if p.get("ids") == "zipf":
+        ids = synth.zipf_ids(p["T"], p["E"], p["k"], 1.1, key)
+    elif p.get("ids") == "uniform":
+        ids = synth.uniform_ids(p["T"], p["E"], p["k"], key)
+    elif p.get("ids") == "shared":
+        ids = synth.shared_ids(p["T"], p["E"], p["k"], key)
+    return U.routed_case(name, p["n_embd"], p["n_ff"], p["E"], p["k"], p["T"], p["fg"], p["fd"], key,
+                         ids=ids)
+
+
+@pytest.mark.parametrize("name", list(ROUTED))
+def test_layer_stages(name):
+    c = _routed(name)
+    T, k = c.T, c.k
+    base = 5
+    n_rows = 16
+    dst = synth.rng(40, T).choice(n_rows, T, replace=False).astype(np.int32)
+    plan, ids, w = U.gpu_route_and_plan(c, T * k, T * k, entry_base=base, dst_of_token=dst)
+    ph = plan.get()
+    assert np.array_equal(ids.cpu().numpy(), oracle.route_topk(c.logits, k)[0])
+    Y0 = U.y0_for(n_rows, c.n_embd, dst, 1)
+    comp = U.run_composed(c, plan, c.x, Y0, n_rows)
+    assert comp["err"] == 0
+    worst = U.check_stages(c, ph, comp, Y0)
+    print(f"{name}: worst err/S {worst:.3g}")
+    # the single-launch path gives the same bits, and so do its intermediates
+    fused = U.run_fused(c, plan, c.x, Y0)
+    assert fused["err"] == 0
+    assert np.array_equal(U.bits(fused["Y"]), U.bits(comp["Y"]))
+    ws, off = fused["ws"].cpu().numpy(), fused["off"]
+    ne = int(ph["grp_start"][-1] - base)
+    gw = ws[off[0]:off[0] + ne * c.n_ff * 4].view(np.float32).reshape(ne, c.n_ff)
+    hqw = ws[off[2]:off[2] + ne * (c.n_ff // 32) * 36].reshape(ne, -1)
+    assert np.array_equal(U.bits(gw), U.bits(comp["g"][base:base + ne]))
+    assert np.array_equal(hqw, comp["hq"][base:base + ne])
+
+
+@pytest.mark.parametrize("name", ["nl4_t1", "cb2_nl4_t4_zipf"])
+def test_grid_invariance(name):
+    c = _routed(name, key=2)
+    T, k = c.T, c.k
+    plan, _, _ = U.gpu_route_and_plan(c, T * k, T * k)
+    Y0 = U.y0_for(T, c.n_embd, range(T), 3)
+    ref = U.run_fused(c, plan, c.x, Y0)["Y"]
+    comp = U.run_composed(c, plan, c.x, Y0, T)["Y"]
+    assert np.array_equal(U.bits(ref), U.bits(comp))
+    for gl in (1, 2, 3, 4, T * k, 5000):
+        y = U.run_fused(c, plan, c.x, Y0, grid_limit=gl)["Y"]
+        assert np.array_equal(U.bits(y), U.bits(ref)), gl
+        y2 = U.run_composed(c, plan, c.x, Y0, T, grid_limit=gl)["Y"]
+        assert np.array_equal(U.bits(y2), U.bits(ref)), gl
+
+
+# ------------------------------------------------------------------ edge matrix ---------------
+
+_C5 = {}
+
+
+def _c5_case(ng):
+    if ng not in _C5:
+        p = synth.direct_plan(ng, 256, 4, 64, 7, 5, max_entries=32)
+        c = U.Case(f"c5_{ng}", 4096, 1536, 256, Q8_0, Q8_0, 5, p["grp_expert"])
+        c.x = synth.activations(4, 4096, 5, ng)
+        _C5[ng] = (c, p)
+    return _C5[ng]
+
+
+@pytest.mark.parametrize("ng", [0, 1, 2, 4, 32])
+def test_edges_q8_4096(ng):
+    c, p = _c5_case(ng)
+    plan = B.Plan(32, 32, entry_capacity=7 + 32, device=U.dev())
+    plan.set(p)
+    Y0 = U.y0_for(64, 4096, p["ent_dst"], 9)
+    comp = U.run_composed(c, plan, c.x, Y0, 64)
+    assert comp["err"] == 0
+    if ng == 0:
+        assert np.array_equal(U.bits(comp["Y"]), U.bits(Y0))
+    else:
+        U.check_stages(c, p, comp, Y0)
+    # entries past index 0: rows 0..6 of g / u / hq are never written
+    assert np.array_equal(U.bits(comp["g"][:7]), np.full((7, 1536), U.NAN_BITS, np.uint32))
+    assert np.all(comp["hq"][:7] == 0xA5)
+    fused = U.run_fused(c, plan, c.x, Y0, stale=True)
+    assert np.array_equal(U.bits(fused["Y"]), U.bits(comp["Y"]))
+    for gl in (1, 3, 4, 33):
+        assert np.array_equal(U.bits(U.run_fused(c, plan, c.x, Y0, grid_limit=gl)["Y"]),
+                              U.bits(comp["Y"])), gl
+
+
+def test_negative_corrupted_weight_is_caught():
+    """A byte flipped in the oracle's copy of one expert must fail the parity check."""
+    c = _routed("small_q8", key=3)
+    plan, _, _ = U.gpu_route_and_plan(c, 2, 2)
+    ph = plan.get()
+    Y0 = U.y0_for(1, c.n_embd, [0], 4)
+    comp = U.run_composed(c, plan, c.x, Y0, 1)
+    U.check_stages(c, ph, comp, Y0)
+    e = int(ph["grp_expert"][0])
+    bad = c.gate[e].copy()
+    bad[2 + 34 * 3] ^= 0x40           # row 0, block 3, one quant
+    c.gate[e] = bad
+    with pytest.raises(AssertionError):
+        U.check_stages(c, ph, comp, Y0)
+
+
+def test_device_errors_reported():
+    c = _routed("small_q8", key=4)
+    plan, _, _ = U.gpu_route_and_plan(c, 2, 2)
+    Y0 = U.y0_for(1, c.n_embd, [0], 5)
+    plan.n_groups.fill_(3)                       # above cap_groups
+    r = U.run_fused(c, plan, c.x, Y0)
+    assert r["err"] & 1 and np.array_equal(U.bits(r["Y"]), U.bits(Y0))
+    plan.err.zero_()
+    plan.n_groups.fill_(2)
+    plan.grp_expert[1] = 99                      # expert out of range: that group skipped
+    r = U.run_fused(c, plan, c.x, Y0)
+    assert r["err"] & 4
+    plan.err.zero_()
+    plan.grp_expert[1] = int(plan.get()["grp_expert"][0]) + 1
+    plan.ent_dst[0] = 50                          # destination out of range: entry skipped
+    r = U.run_fused(c, plan, c.x, Y0)
+    assert r["err"] & 16

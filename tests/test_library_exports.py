@@ -1,0 +1,50 @@
+"""The C-ABI library loads (no GPU needed) and exports every function include/moe_route.h
+declares; the binding's ctypes structs match the header's field order. No compute call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_route.h")
+LIB = os.path.join(ROOT, "moe_routed_expert_route_amd", "libmoe_route.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_entry_points():
+    names = _declared()
+    for n in ("moe_route_topk", "moe_build_plan", "moe_quantize_q8_1", "moe_gate_up",
+              "moe_swiglu_q8_1", "moe_down_scatter", "moe_layer_decode"):
+        assert n in names
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built (run __graft_entry__.build())")
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    lib.moe_status_string.restype = ctypes.c_char_p
+    assert lib.moe_status_string(0) == b"ok"
+
+
+def test_binding_structs_follow_header():
+    from moe_routed_expert_route_amd import binding
+    src = open(HEADER).read()
+    for cname, py in (("moe_layer", binding.MoeLayer), ("moe_plan", binding.MoePlan)):
+        body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (cname, cname), src, re.S).group(1)
+        body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+        fields = []
+        for decl in body.split(";"):
+            decl = decl.strip()
+            if not decl:
+                continue
+            names = [re.sub(r"[\*\s]", "", n.split()[-1]) for n in decl.split(",")]
+            first = decl.split(",")[0].split()[-1].lstrip("*")
+            fields += [first] + [n.strip().lstrip("*") for n in decl.split(",")[1:]]
+        assert [f[0] for f in py._fields_] == fields, (cname, fields)
