@@ -81,7 +81,6 @@ typedef enum {
 #define MOE_ERR_SRC 8u       /* ent_src out of [0, n_tokens): that entry skipped */
 #define MOE_ERR_DST 16u      /* ent_dst out of [0, n_rows): that entry skipped */
 #define MOE_ERR_ALIGN 32u    /* a weight pointer not 2-byte aligned: that group skipped */
-#define MOE_ERR_WAIT 64u     /* a bounded on-device wait ran out (results of the call invalid) */
 
 /* One MoE layer's experts. Host struct, read during the call only. */
 typedef struct moe_layer {
@@ -144,31 +143,38 @@ int moe_swiglu_q8_1(void* stream, const moe_plan* P, const float* g, const float
 
 /* Grouped down + weighted scatter: o_a[m] = sum_b c_b(down_e row m, hq row a) for m < n_embd, then
  * Y[ent_dst[a]][m] = Y + sum over the call's entries with that destination, in ascending entry
- * order, of ent_w[a] * o_a[m] (float32). Y: n_rows rows of stride ldy; rows no entry names are
- * neither read nor written. Uses the workspace (see moe_workspace_bytes / moe_workspace_init). */
+ * order, of ent_w[a] * o_a[m] (float32, each product and sum rounded). Y: n_rows rows of stride
+ * ldy; rows no entry names are neither read nor written. hq: q8_1 rows by absolute entry. */
 int moe_down_scatter(void* stream, const moe_layer* L, const moe_plan* P, const void* hq,
-                     float* Y, int n_rows, int ldy, void* workspace, size_t ws_bytes,
-                     int grid_limit);
+                     float* Y, int n_rows, int ldy, int grid_limit);
 
-/* Host: bytes of workspace the down/scatter and layer calls need for this layer and plan. */
+/* Host: bytes of workspace the single-call paths need for this layer and plan capacity (the
+ * intermediates of the call: g, u and the q8_1 rows of h). The workspace is 256-byte aligned and
+ * needs no clearing: a call reads only bytes it wrote itself. */
 size_t moe_workspace_bytes(const moe_layer* L, const moe_plan* P);
 
-/* Clear the workspace's synchronisation counters (enqueued fill kernel). Call once after
- * allocating a workspace; every call leaves the counters cleared again. */
-int moe_workspace_init(void* stream, void* workspace, size_t ws_bytes);
-
-/* The whole step in one launch: q8_1(x rows) -> grouped gate/up -> SwiGLU + q8_1 -> grouped down
- * -> weighted scatter into Y, for the call's entries. x: n_tokens float32 rows of n_embd.
- * Bit-identical to the composed calls. The workspace also holds the intermediates (layout:
- * moe_workspace_layout). Calls that overlap on one workspace race; calls in one stream do not. */
+/* The whole step for the call's entries in two launches: q8_1(x rows) -> grouped gate/up ->
+ * SwiGLU + q8_1 -> grouped down -> weighted scatter into Y. x: n_tokens float32 rows of n_embd
+ * (16-byte aligned). Bit-identical to the composed calls quantize -> gate_up -> swiglu ->
+ * down_scatter. Calls that overlap on one workspace race; calls in one stream do not. */
 int moe_layer_decode(void* stream, const moe_layer* L, const moe_plan* P, const float* x,
                      int n_tokens, float* Y, int n_rows, int ldy, void* workspace,
                      size_t ws_bytes, int grid_limit);
 
-/* Host: byte offsets inside the workspace of the intermediates of the last moe_layer_decode:
- * off[0] g float32 [cap_entries][n_ff], off[1] u (same), off[2] hq [cap_entries][n_ff/32 * 36 B],
- * off[3] o float32 [cap_entries][n_embd]; rows indexed by (entry - grp_start[0]). */
-int moe_workspace_layout(const moe_layer* L, const moe_plan* P, size_t off[4]);
+/* Same step starting from the router logits [T][n_experts] (float32): every gate/up workgroup
+ * routes the T tokens (top-k, as moe_route_topk) and groups the entries (as moe_build_plan with
+ * entry_base and dst_of_token) itself, and workgroup 0 writes that plan into P for the down
+ * launch and for the caller. Bit-identical to route_topk -> build_plan -> moe_layer_decode.
+ * Requires T*k <= cap_entries, T*k <= cap_groups, k <= 32, n_experts <= 1024. */
+int moe_layer_decode_routed(void* stream, const moe_layer* L, const moe_plan* P,
+                            const float* logits, int T, int k, const int32_t* dst_of_token,
+                            int entry_base, const float* x, float* Y, int n_rows, int ldy,
+                            void* workspace, size_t ws_bytes, int grid_limit);
+
+/* Host: byte offsets inside the workspace of the intermediates of the last single-call step:
+ * off[0] g float32 [cap_entries][n_ff], off[1] u (same), off[2] hq [cap_entries][n_ff/32 * 36 B];
+ * rows indexed by (entry - grp_start[0]). */
+int moe_workspace_layout(const moe_layer* L, const moe_plan* P, size_t off[3]);
 
 const char* moe_status_string(int status);   /* host, static string */
 const char* moe_last_error(void);            /* host, text of the last MOE_E_HIP on this thread */

@@ -18,11 +18,12 @@ Q8_0, NL4, CB2, CB3 = 1, 2, 3, 4
 BLOCK_BYTES = {Q8_0: 34, NL4: 18, CB2: 70, CB3: 110}
 BLOCK_WEIGHTS = {Q8_0: 32, NL4: 32, CB2: 256, CB3: 256}
 
-ERR_BITS = {1: "NGROUPS", 2: "ENTRIES", 4: "EXPERT", 8: "SRC", 16: "DST", 32: "ALIGN", 64: "WAIT"}
+ERR_BITS = {1: "NGROUPS", 2: "ENTRIES", 4: "EXPERT", 8: "SRC", 16: "DST", 32: "ALIGN"}
 
 EXPORTS = ("moe_route_topk", "moe_build_plan", "moe_quantize_q8_1", "moe_gate_up",
-           "moe_swiglu_q8_1", "moe_down_scatter", "moe_workspace_bytes", "moe_workspace_init",
-           "moe_layer_decode", "moe_workspace_layout", "moe_status_string", "moe_last_error")
+           "moe_swiglu_q8_1", "moe_down_scatter", "moe_workspace_bytes",
+           "moe_layer_decode", "moe_layer_decode_routed", "moe_workspace_layout",
+           "moe_status_string", "moe_last_error")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -55,12 +56,14 @@ def lib():
                                   _P, _I, _I]
         L.moe_swiglu_q8_1.argtypes = [_P, ctypes.POINTER(MoePlan), _P, _P, _I, _I, _P, _P]
         L.moe_down_scatter.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan), _P, _P,
-                                       _I, _I, _P, ctypes.c_size_t, _I]
+                                       _I, _I, _I]
         L.moe_workspace_bytes.argtypes = [ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan)]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
-        L.moe_workspace_init.argtypes = [_P, _P, ctypes.c_size_t]
         L.moe_layer_decode.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan), _P, _I,
                                        _P, _I, _I, _P, ctypes.c_size_t, _I]
+        L.moe_layer_decode_routed.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan),
+                                              _P, _I, _I, _P, _I, _P, _P, _I, _I, _P,
+                                              ctypes.c_size_t, _I]
         L.moe_workspace_layout.argtypes = [ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan),
                                            ctypes.POINTER(ctypes.c_size_t)]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -225,34 +228,42 @@ def moe_workspace_bytes(layer: Layer, plan: Plan) -> int:
     return int(lib().moe_workspace_bytes(ctypes.byref(layer.struct), ctypes.byref(plan.struct)))
 
 
-def moe_workspace_init(ws, stream=None):
-    _check(lib().moe_workspace_init(_stream(stream), _ptr(ws), ws.numel()), "moe_workspace_init")
-
-
 def workspace(layer: Layer, plan: Plan, device="cuda"):
-    """Allocate and clear a workspace for this layer geometry and plan capacity."""
+    """Allocate a workspace for this layer geometry and plan capacity (no clearing needed: a
+    call reads only bytes it wrote itself)."""
     nb = moe_workspace_bytes(layer, plan)
     if nb == 0:
         raise RuntimeError("moe_workspace_bytes: bad layer or plan")
     ws = torch.empty(nb, dtype=torch.uint8, device=device)
-    moe_workspace_init(ws)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("workspace not 256-byte aligned")
     return ws
 
 
 def moe_workspace_layout(layer: Layer, plan: Plan):
-    off = (ctypes.c_size_t * 4)()
+    off = (ctypes.c_size_t * 3)()
     _check(lib().moe_workspace_layout(ctypes.byref(layer.struct), ctypes.byref(plan.struct), off),
            "moe_workspace_layout")
     return [int(v) for v in off]
 
 
-def moe_down_scatter(layer: Layer, plan: Plan, hq, Y, ws, grid_limit=0, stream=None):
+def moe_down_scatter(layer: Layer, plan: Plan, hq, Y, grid_limit=0, stream=None):
     _check(lib().moe_down_scatter(_stream(stream), ctypes.byref(layer.struct), ctypes.byref(plan.struct),
-                                  _ptr(hq), _ptr(Y), Y.shape[0], Y.stride(0), _ptr(ws), ws.numel(),
-                                  grid_limit), "moe_down_scatter")
+                                  _ptr(hq), _ptr(Y), Y.shape[0], Y.stride(0), grid_limit),
+           "moe_down_scatter")
 
 
 def moe_layer_decode(layer: Layer, plan: Plan, x, Y, ws, grid_limit=0, stream=None):
     _check(lib().moe_layer_decode(_stream(stream), ctypes.byref(layer.struct), ctypes.byref(plan.struct),
                                   _ptr(x), x.shape[0], _ptr(Y), Y.shape[0], Y.stride(0), _ptr(ws),
                                   ws.numel(), grid_limit), "moe_layer_decode")
+
+
+def moe_layer_decode_routed(layer: Layer, plan: Plan, logits, k, x, Y, ws, dst_of_token=None,
+                            entry_base=0, grid_limit=0, stream=None):
+    T = logits.shape[0]
+    _check(lib().moe_layer_decode_routed(_stream(stream), ctypes.byref(layer.struct),
+                                         ctypes.byref(plan.struct), _ptr(logits), T, k,
+                                         _ptr(dst_of_token), entry_base, _ptr(x), _ptr(Y), Y.shape[0],
+                                         Y.stride(0), _ptr(ws), ws.numel(), grid_limit),
+           "moe_layer_decode_routed")

@@ -118,8 +118,19 @@ class Workload:
         B.moe_layer_decode(self.layers[l], self.plans[l], self.d_x[l], self.Y[l], self.ws[l],
                            grid_limit=grid_limit, stream=stream)
 
+    def decode_routed(self, l, stream=None, grid_limit=0):
+        B.moe_layer_decode_routed(self.layers[l], self.plans[l], self.d_logits[l], self.k,
+                                  self.d_x[l], self.Y[l], self.ws[l], grid_limit=grid_limit,
+                                  stream=stream)
+
     def step(self, stream=None):
-        """One pass of the whole hot path over every layer: route, group, decode."""
+        """One pass of the whole hot path over every layer: route, group, decode (two launches
+        per layer: routing and grouping run inside the gate/up launch)."""
+        for l in range(self.L):
+            self.decode_routed(l, stream)
+
+    def step_separate(self, stream=None):
+        """The same pass with routing and grouping as launches of their own."""
         for l in range(self.L):
             self.route_plan(l, stream)
             self.decode(l, stream)

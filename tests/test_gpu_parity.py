@@ -141,6 +141,13 @@ def test_layer_stages(name):
     hqw = ws[off[2]:off[2] + ne * (c.n_ff // 32) * 36].reshape(ne, -1)
     assert np.array_equal(U.bits(gw), U.bits(comp["g"][base:base + ne]))
     assert np.array_equal(hqw, comp["hq"][base:base + ne])
+    # routing + grouping inside the gate/up launch: same plan, same bits
+    r = U.run_routed(c, c.x, Y0, entry_base=base, dst_of_token=dst)
+    assert r["err"] == 0
+    for key in ("n_groups", "grp_expert", "grp_start", "ent_src", "ent_dst"):
+        assert np.array_equal(np.asarray(r["plan"][key]), np.asarray(ph[key])), key
+    assert np.array_equal(U.bits(r["plan"]["ent_w"]), U.bits(ph["ent_w"]))
+    assert np.array_equal(U.bits(r["Y"]), U.bits(comp["Y"]))
 
 
 @pytest.mark.parametrize("name", ["nl4_t1", "cb2_nl4_t4_zipf"])
@@ -157,6 +164,8 @@ def test_grid_invariance(name):
         assert np.array_equal(U.bits(y), U.bits(ref)), gl
         y2 = U.run_composed(c, plan, c.x, Y0, T, grid_limit=gl)["Y"]
         assert np.array_equal(U.bits(y2), U.bits(ref)), gl
+        y3 = U.run_routed(c, c.x, Y0, grid_limit=gl)["Y"]
+        assert np.array_equal(U.bits(y3), U.bits(ref)), gl
 
 
 # ------------------------------------------------------------------ edge matrix ---------------
