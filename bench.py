@@ -1,21 +1,26 @@
 """Benchmark: grouped routed-expert MoE decode on one MI355X.
 
-Workload (seeded, synthetic, shaped like the pages' measurements): 48 MoE layers, each with its own
-128 experts in a 4-bit nonlinear format (NL4: 32 weights per 18-byte block), n_embd 2560, n_ff 768,
-top-8 routing of one token (T = 1). All 48 x 128 experts are resident (20.4 GB pool), so each
-pass reads its routed experts cold (1.27 GB per pass, far above the 256 MB Infinity Cache).
+Headline workload (seeded, synthetic, shaped like the pages' measurements): 48 MoE layers, each
+with its own 128 experts in the 4-bit nonlinear format (NL4: 32 weights per 18-byte block),
+n_embd 2560, n_ff 768, top-8 routing of one token (T = 1). All 48 x 128 experts are resident
+(20.4 GB pool), so a pass reads its routed experts cold (1.27 GB per pass, far above the 256 MB
+last-level cache).
 
-A step is one pass of the whole path over the 48 layers: top-k routing of the layer's logits,
-grouping of the entries by expert, and the single-launch layer decode (q8_1 of x, grouped gate/up,
-SwiGLU + q8_1, grouped down, weighted scatter). Steps are replayed from a HIP graph.
+A step is one pass of the whole path over the 48 layers, two launches per layer: (1) top-k
+routing of the layer's logits, grouping of the entries by expert, q8_1 of x, grouped gate/up,
+SwiGLU + q8_1 of h; (2) grouped down + weighted scatter into Y. Steps are replayed from a HIP
+graph.
 
 Printed: one JSON line. value = expert-weight GB/s (distinct routed experts' bytes per pass / time
-per pass); us_per_layer_call = time per layer; roofline = the layer-decode kernel alone, timed
-with HIP events around each launch; cpu_baseline = the CPU oracle on a sample of layers.
+per pass); us_per_layer_call = time per layer; roofline = the dominant kernel alone, timed with
+HIP events around each of its launches on the stream it runs on; t_sweep = the same measurement
+at T = 1..4 (shared experts: the per-extra-row cost; the 256-expert CB3/Q8_0 geometry with
+uniform routing); cpu_baseline = the CPU oracle on a sample of layer calls.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,16 +30,34 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("moe_routed_expert_route_amd/csrc/moe_route.hip",
+                  "moe_routed_expert_route_amd/csrc/moe_device.hpp")
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def source_digest():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def barrier():
+    import torch.distributed as dist
+    if dist.is_available() and dist.is_initialized():
+        dist.barrier()
+
+
 def time_graph(graph, n):
+    """ms per replay of `graph` over n replays (HIP events on the replay stream), bracketed by a
+    barrier and a device synchronize on both sides."""
     import torch
+    barrier()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record()
@@ -42,26 +65,89 @@ def time_graph(graph, n):
         graph.replay()
     ev1.record()
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / n, (time.perf_counter() - t0) * 1e3 / n
+    barrier()
+    return ev0.elapsed_time(ev1) / n
 
 
-def decode_kernel_us(wl, reps):
-    """Average duration of the layer-decode launch, HIP events around each launch on its stream."""
+def kernel_us(wl, reps):
+    """Average duration of each launch kind (gate/up, down), HIP events around every launch on
+    the stream the launch runs on (the current stream), eager, cycling over the layers."""
     import torch
     s = torch.cuda.current_stream()
-    evs = []
+    evs = {"gate_up": [], "down": []}
     for _ in range(reps):
         for l in range(wl.L):
-            wl.route_plan(l)
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(s)
-            wl.decode(l)
-            b.record(s)
-            evs.append((a, b))
+            for kind, fn in (("gate_up", wl.gate_up), ("down", wl.down)):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(s)
+                fn(l)
+                b.record(s)
+                evs[kind].append((a, b))
     torch.cuda.synchronize()
-    ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-    return sum(ts) / len(ts), ts[len(ts) // 2]
+    out = {}
+    for kind, lst in evs.items():
+        ts = sorted(a.elapsed_time(b) * 1e3 for a, b in lst)
+        out[kind] = (sum(ts) / len(ts), ts[len(ts) // 2])
+    return out
+
+
+def measure(wl, steps, warmup, reps=2):
+    """Graph-replayed step time, plain-stream step time and per-kernel launch times."""
+    import torch
+    wl.step()
+    torch.cuda.synchronize()
+    errs = [p.errors() for p in wl.plans]
+    assert not any(errs), errs
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        wl.step()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ms_step = time_graph(g, steps)
+    t0 = time.perf_counter()
+    for _ in range(3):
+        wl.step()
+    torch.cuda.synchronize()
+    ms_plain = (time.perf_counter() - t0) * 1e3 / 3
+    ks = kernel_us(wl, reps)
+    del g
+    return ms_step, ms_plain, ks
+
+
+def traffic_for(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary of `workload`, or None
+    when there is none or the kernel sources changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        doc = json.load(f)
+    if doc.get("source_sha256") != source_digest():
+        return None
+    k = doc.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def sweep_line(name, T, routing, steps, warmup):
+    import torch
+
+    from moe_routed_expert_route_amd.workloads import Workload
+    wl = Workload(name, device="cuda", T=T, routing=routing)
+    ms_step, _, ks = measure(wl, steps, warmup, reps=1)
+    bytes_pass = float(sum(wl.weight_bytes_per_layer()))
+    us = ms_step * 1e3 / wl.L
+    line = {"T": T, "routing": routing, "us_per_layer_call": round(us, 3),
+            "gbs": round(bytes_pass / (ms_step * 1e-3) / 1e9, 1),
+            "distinct_experts_per_layer": round(sum(wl.distinct_experts(l) for l in range(wl.L)) / wl.L, 2),
+            "gate_up_us": round(ks["gate_up"][0], 3), "down_us": round(ks["down"][0], 3)}
+    del wl
+    torch.cuda.empty_cache()
+    return line
 
 
 def main():
@@ -72,13 +158,14 @@ def main():
     ap.add_argument("--workload", default="nl4_2560x768_t1")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time to measure")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the T = 1..4 lines")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path would shard by expert groups; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this build "
+              "runs on a single GPU (the path would shard by expert ownership, one rank per GPU)",
+              file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from moe_routed_expert_route_amd import binding as B
@@ -86,53 +173,32 @@ def main():
 
     B.lib()
     torch.cuda.set_device(0)
-    log("building workload")
+    log(f"building workload {args.workload}")
     wl = Workload(args.workload, device="cuda", log=log)
     per_layer = wl.weight_bytes_per_layer()
     bytes_pass = float(sum(per_layer))
     log(f"pool {wl.pool_bytes / 1e9:.2f} GB, routed bytes per pass {bytes_pass / 1e9:.3f} GB")
-
-    # eager warm-up (also checks the plans)
-    wl.step()
-    torch.cuda.synchronize()
-    errs = [p.errors() for p in wl.plans]
-    assert not any(errs), errs
-
-    # graph of one step (48 x [route, plan, decode])
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s):
-        wl.step()
-    torch.cuda.synchronize()
-    # decode-only graph (48 x decode), plans already built
-    g2 = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g2, stream=s):
-        for l in range(wl.L):
-            wl.decode(l)
-    torch.cuda.synchronize()
-
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    ms_step, wall_ms = time_graph(g, args.steps)
-    ms_dec, _ = time_graph(g2, args.steps)
-    # plain stream, no graph
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(3):
-        wl.step()
-    torch.cuda.synchronize()
-    ms_plain = (time.perf_counter() - t0) * 1e3 / 3
-    log("per-launch kernel timing")
-    k_avg_us, k_med_us = decode_kernel_us(wl, 2)
+    log(f"warmup {args.warmup}, timing {args.steps} steps")
+    ms_step, ms_plain, ks = measure(wl, args.steps, args.warmup)
+    log("step timed")
 
     us_layer = ms_step * 1e3 / wl.L
     gbs = bytes_pass / (ms_step * 1e-3) / 1e9
-    bytes_layer = bytes_pass / wl.L
-    achieved = bytes_layer / (k_avg_us * 1e-6) / 1e9
+    lb = [wl.launch_bytes(l) for l in range(wl.L)]
+    kb = {"gate_up": sum(b[0] for b in lb) / wl.L, "down": sum(b[1] for b in lb) / wl.L}
+    fmt_names = {1: "Q8_0", 2: "NL4", 3: "CB2", 4: "CB3"}
+    kname = {"gate_up": f"k_gate_up<{fmt_names[wl.fg]}, GU_ROUTED>",
+             "down": f"k_down<{fmt_names[wl.fd]}>"}
+    kernels = {}
+    for kind in ("gate_up", "down"):
+        avg, med = ks[kind]
+        ach = kb[kind] / (avg * 1e-6) / 1e9
+        kernels[kind] = {"kernel": kname[kind], "avg_launch_us": round(avg, 3),
+                         "median_launch_us": round(med, 3), "bytes_per_launch": int(kb[kind]),
+                         "achieved_gbs": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4)}
+    dom = max(kernels, key=lambda k: ks[k][0])
+    dk = kernels[dom]
+    traffic = traffic_for(args.workload, dom)
     res = {
         "metric": "us per MoE-layer decode call at T=1..4; expert-weight GB/s (frac of HBM peak)",
         "value": round(gbs, 1),
@@ -153,16 +219,31 @@ def main():
                    "top_k": wl.k, "T": wl.T, "parallelism": "single GPU"},
         "us_per_layer_call": round(us_layer, 3),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-        "us_per_layer_decode_only": round(ms_dec * 1e3 / wl.L, 3),
         "us_per_layer_plain_stream": round(ms_plain * 1e3 / wl.L, 3),
-        "roofline": {"bound": "hbm", "kernel": "moe_layer_decode (k_layer)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": int(bytes_layer), "avg_launch_us": round(k_avg_us, 3),
-                     "median_launch_us": round(k_med_us, 3)},
+        "roofline": {"bound": "hbm", "kernel": dk["kernel"], "achieved": dk["achieved_gbs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["frac"],
+                     "traffic": traffic, "bytes_per_launch": dk["bytes_per_launch"],
+                     "avg_launch_us": dk["avg_launch_us"]},
+        "kernels": kernels,
     }
     if not args.no_cpu:
         res["cpu_baseline"] = run_cpu_baseline(wl, args.cpu_seconds)
+    del wl
+    torch.cuda.empty_cache()
+    if not args.no_sweep:
+        sweep = {"nl4_2560x768_shared": [], "cb3q8_2560x640_uniform": []}
+        for T in (1, 2, 3, 4):
+            log(f"sweep nl4 2560x768 shared experts T={T}")
+            sweep["nl4_2560x768_shared"].append(sweep_line("nl4_2560x768_t1", T, "shared", 10, 3))
+        t1 = sweep["nl4_2560x768_shared"][0]["us_per_layer_call"]
+        for ln in sweep["nl4_2560x768_shared"][1:]:
+            ln["per_extra_row_frac_of_t1"] = round((ln["us_per_layer_call"] - t1) / (ln["T"] - 1) / t1, 4)
+        for T in (1, 2, 3, 4):
+            log(f"sweep cb3/q8 2560x640 uniform T={T}")
+            sweep["cb3q8_2560x640_uniform"].append(sweep_line("cb3q8_2560x640", T, "uniform", 10, 3))
+        log("cb2/nl4 T=4 zipf")
+        sweep["cb2nl4_2560x768_t4_zipf"] = [sweep_line("cb2nl4_2560x768_t4_zipf", 4, "zipf", 10, 3)]
+        res["t_sweep"] = sweep
     print(json.dumps(res), flush=True)
 
 

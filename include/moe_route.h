@@ -171,6 +171,19 @@ int moe_layer_decode_routed(void* stream, const moe_layer* L, const moe_plan* P,
                             int entry_base, const float* x, float* Y, int n_rows, int ldy,
                             void* workspace, size_t ws_bytes, int grid_limit);
 
+/* The first of the two launches of moe_layer_decode (logits == NULL: the plan in P as built) or
+ * of moe_layer_decode_routed (logits != NULL: route and group here, publish the plan into P;
+ * then n_tokens must equal T). Leaves g, u and the q8_1 rows of h in the workspace
+ * (moe_workspace_layout). For callers that put other work between the halves or time them. */
+int moe_layer_gate_up(void* stream, const moe_layer* L, const moe_plan* P, const float* logits,
+                      int T, int k, const int32_t* dst_of_token, int entry_base, const float* x,
+                      int n_tokens, void* workspace, size_t ws_bytes, int grid_limit);
+
+/* The second launch: grouped down over the workspace's q8_1 rows of h + weighted scatter into Y,
+ * as moe_down_scatter; entries whose token is not below n_tokens are skipped. */
+int moe_layer_down(void* stream, const moe_layer* L, const moe_plan* P, const void* workspace,
+                   size_t ws_bytes, int n_tokens, float* Y, int n_rows, int ldy, int grid_limit);
+
 /* Host: byte offsets inside the workspace of the intermediates of the last single-call step:
  * off[0] g float32 [cap_entries][n_ff], off[1] u (same), off[2] hq [cap_entries][n_ff/32 * 36 B];
  * rows indexed by (entry - grp_start[0]). */

@@ -22,7 +22,8 @@ ERR_BITS = {1: "NGROUPS", 2: "ENTRIES", 4: "EXPERT", 8: "SRC", 16: "DST", 32: "A
 
 EXPORTS = ("moe_route_topk", "moe_build_plan", "moe_quantize_q8_1", "moe_gate_up",
            "moe_swiglu_q8_1", "moe_down_scatter", "moe_workspace_bytes",
-           "moe_layer_decode", "moe_layer_decode_routed", "moe_workspace_layout",
+           "moe_layer_decode", "moe_layer_decode_routed", "moe_layer_gate_up", "moe_layer_down",
+           "moe_workspace_layout",
            "moe_status_string", "moe_last_error")
 
 _lib = None
@@ -64,6 +65,10 @@ def lib():
         L.moe_layer_decode_routed.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan),
                                               _P, _I, _I, _P, _I, _P, _P, _I, _I, _P,
                                               ctypes.c_size_t, _I]
+        L.moe_layer_gate_up.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan), _P, _I,
+                                        _I, _P, _I, _P, _I, _P, ctypes.c_size_t, _I]
+        L.moe_layer_down.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan), _P,
+                                     ctypes.c_size_t, _I, _P, _I, _I, _I]
         L.moe_workspace_layout.argtypes = [ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan),
                                            ctypes.POINTER(ctypes.c_size_t)]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -267,3 +272,19 @@ def moe_layer_decode_routed(layer: Layer, plan: Plan, logits, k, x, Y, ws, dst_o
                                          _ptr(dst_of_token), entry_base, _ptr(x), _ptr(Y), Y.shape[0],
                                          Y.stride(0), _ptr(ws), ws.numel(), grid_limit),
            "moe_layer_decode_routed")
+
+
+def moe_layer_gate_up(layer: Layer, plan: Plan, x, ws, logits=None, k=0, dst_of_token=None,
+                      entry_base=0, grid_limit=0, stream=None):
+    """First launch of the layer step (routing and grouping too when logits are given)."""
+    T = logits.shape[0] if logits is not None else 0
+    _check(lib().moe_layer_gate_up(_stream(stream), ctypes.byref(layer.struct), ctypes.byref(plan.struct),
+                                   _ptr(logits), T, k, _ptr(dst_of_token), entry_base, _ptr(x),
+                                   x.shape[0], _ptr(ws), ws.numel(), grid_limit), "moe_layer_gate_up")
+
+
+def moe_layer_down(layer: Layer, plan: Plan, ws, n_tokens, Y, grid_limit=0, stream=None):
+    """Second launch of the layer step: down over the workspace's h rows + scatter into Y."""
+    _check(lib().moe_layer_down(_stream(stream), ctypes.byref(layer.struct), ctypes.byref(plan.struct),
+                                _ptr(ws), ws.numel(), n_tokens, _ptr(Y), Y.shape[0], Y.stride(0),
+                                grid_limit), "moe_layer_down")

@@ -4,25 +4,31 @@
 // paragraph and "What changes"; "#2058 Verify window: the routed experts' gate/up with the group's
 // q8_1 rows in shared memory", "Why"): token-expert entries grouped by expert; each expert's
 // gate/up weights streamed once per group and dotted with the group's q8_1 activation rows;
-// SwiGLU + q8_1 fused; the down projection grouped the same way; its rows scatter-added into the
+// SwiGLU fused; the down projection grouped the same way; its rows scatter-added into the
 // destination rows with the router weights.
 //
 // Design for gfx950 (the pages' CUDA kernels are prior art, not the blueprint):
-//  * Two launches per layer, no cross-workgroup synchronisation inside a kernel (a grid-wide
-//    release/acquire costs tens of microseconds on this part; the kernel boundary is cheaper):
-//      gate/up kernel: one work item = one 32-row h block of one group (rows of gate and up), so
-//        SwiGLU and the q8_1 quantization of that h block finish in the same workgroup;
-//      down kernel: one work item = a tile of rows of Y across every group of the call, so each
-//        output element is summed by one workgroup in ascending entry order (deterministic, no
-//        atomics, no partial buffers).
-//  * Each wave streams its own weight rows HBM -> LDS with direct-to-LDS 16-byte loads
-//    (global_load_lds_dwordx4, fully coalesced whatever the block size: 18/34/70/110-byte blocks
-//    do not align to 16 bytes) through a private ring of slots. Every chunk costs exactly M load
-//    instructions per wave, so "chunk k has landed" is a vmcnt wait with a known count: loads of
-//    later chunks stay in flight while the wave computes, with no workgroup barrier in the loop.
+//  * Two launches per layer and no cross-workgroup synchronisation inside a kernel (a grid-wide
+//    release/acquire costs more than the kernel boundary on this part):
+//      gate/up kernel: one work item = 2 rp consecutive h rows of one group (rp = weight rows per
+//        wave pass); wave w streams the gate and up rows of its rp / 2 h rows, dots them with the
+//        group's entries and writes SwiGLU(g, u) straight out, so items need no workgroup barrier;
+//      down kernel: one work item = rp rows of Y across every group of the call, so each output
+//        element is summed by one workgroup in ascending entry order (deterministic, no atomics);
+//        its prologue quantizes the call's h rows to q8_1 in LDS.
+//  * Latency first: a layer call moves tens of MB, so every dependent round trip to memory shows.
+//    Each kernel issues all independent loads of its prologue at once (logits, x, tables, plan or
+//    descriptor, expert pointers), routes with one wave per token (a ballot radix select) and
+//    groups with one wave; the gate/up launch leaves a one-read descriptor of the call (groups,
+//    entries, down pointers) for the down launch.
+//  * Each wave streams its weight rows HBM -> LDS with direct-to-LDS 16-byte loads
+//    (global_load_lds_dwordx4, fully coalesced for 18/34/70/110-byte blocks that do not align to
+//    16 bytes) through a private ring of slots. Every chunk costs exactly M load instructions, and
+//    loads complete in issue order, so "chunk k has landed" is a vmcnt wait on the number of
+//    loads issued after it: later chunks stay in flight while the wave computes. Stores issued
+//    between two waits only raise the count, so they can make a wait longer, never too short.
 //  * Weight units are decoded out of LDS at any byte alignment (v_alignbyte); activations sit in
-//    LDS as q8_1 (split 16-byte halves + float scale for the gate/up kernel, raw 36-byte blocks
-//    next to the weights for the down kernel).
+//    LDS as q8_1 split into 16-byte halves plus the float scale.
 //  * A row is split over L lanes (a power of two chosen from the shape only); lane l takes units
 //    l, l+L, ...; per unit v_dot4 (int8) per 4 weights, then scale * d_x * isum in float32; the L
 //    partial sums meet in a fixed DPP tree. The lane map depends only on the shape, so every
@@ -32,7 +38,6 @@
 #include <string.h>
 
 #include <algorithm>
-#include <mutex>
 #include <string>
 
 #include "../../include/moe_route.h"
@@ -40,9 +45,17 @@
 
 namespace moe {
 
-constexpr int kWaves = 4;                      // every heavy kernel runs 4 waves (256 threads)
-constexpr int kMaxEnt = MOE_MAX_CALL_ENTRIES;  // 64
-constexpr int kChunkCap = 8192;                // weight bytes per streamed chunk (target)
+constexpr int kGuWaves = 16, kGuThreads = 64 * kGuWaves;  // gate/up workgroup (one per CU)
+constexpr int kDnWaves = 8, kDnThreads = 64 * kDnWaves;   // down workgroup
+constexpr int kSlots = kMaxSlots;                         // entries per dot pass (4)
+constexpr int kMaxEnt = MOE_MAX_CALL_ENTRIES;             // 64
+constexpr int kMaxGrp = MOE_MAX_GROUPS;                   // 64
+constexpr int kChunkCap = 8192;          // weight bytes per streamed chunk (target)
+constexpr int kGuActMax = 48 * 1024;     // LDS for the call's token activations (q8_1)
+constexpr int kDnActMax = 64 * 1024;     // LDS for the call's h rows (q8_1)
+constexpr int kLdsMax = 160 * 1024;      // LDS per workgroup on gfx950
+constexpr int kMaxE = 1024;              // most experts a routed call handles
+constexpr int kRouteWaves = 4;           // tokens routed at once (their logits staged in LDS)
 
 // ------------------------------------------------------------------ argument blocks ---------
 
@@ -83,21 +96,40 @@ struct Stream {
   int M, NS;
 };
 
+// The call as the gate/up launch leaves it for the down launch (device memory, at the start of
+// the workspace): int words, then the down pointers.
+constexpr int kDescNg = 0, kDescE0 = 1, kDescN = 2;
+constexpr int kDescGs = 4;                    // [kMaxGrp + 1] group starts, relative to e0
+constexpr int kDescDst = kDescGs + 68;        // [kMaxEnt] destination row
+constexpr int kDescW = kDescDst + kMaxEnt;    // [kMaxEnt] router weight (float)
+constexpr int kDescLive = kDescW + kMaxEnt;   // [kMaxEnt] 1 = compute and scatter this entry
+constexpr int kDescPtrByte = 4 * (kDescLive + kMaxEnt);   // [kMaxGrp] down pointers (u64)
+constexpr int kDescBytes = kDescPtrByte + 8 * kMaxGrp;
+constexpr int kDescReserve = 2048;            // workspace bytes reserved for it
+static_assert(kDescPtrByte % 16 == 0 && kDescBytes % 16 == 0 && kDescBytes <= kDescReserve, "desc");
+
 // ------------------------------------------------------------------ small helpers -----------
 
 // Values broadcast through LDS are the same in every lane; readfirstlane puts them in scalar
 // registers, so branches and loop bounds built from them are whole-wave (scalar) branches and
 // every barrier stays in control flow the compiler sees as uniform.
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ const uint8_t* uni_ptr(const uint8_t* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
+__device__ __forceinline__ uint64_t uni64(uint64_t v) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-  return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ void set_err(uint32_t* err, uint32_t bit) {
   if (err) atomicOr(err, bit);
+}
+
+// LDS written by some lanes of a wave, then read by other lanes of the same wave: a wave's LDS
+// operations execute in order; this keeps the compiler from moving them across each other.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // s_waitcnt vmcnt(n) for n = 0..63, leaving expcnt and lgkmcnt alone (gfx9 encoding: vmcnt low
@@ -139,67 +171,234 @@ __device__ __forceinline__ void issue_chunk(MOE_LDS uint8_t* slot, int M, const 
   }
 }
 
-__device__ void load_tables(const LayerArgs& A, bool need2, bool need3, MOE_LDS uint32_t* g2,
-                            MOE_LDS uint32_t* g3, Tables& tb) {
-  if (A.nl4) {
-    const uint32_t* t = (const uint32_t*)A.nl4;
-    tb.nl4[0] = t[0];
-    tb.nl4[1] = t[1];
-    tb.nl4[2] = t[2];
-    tb.nl4[3] = t[3];
-  } else {
-    tb.nl4[0] = tb.nl4[1] = tb.nl4[2] = tb.nl4[3] = 0;
+// 16-byte chunk index where span b of a two-span chunk starts: after span a, one chunk of gap.
+__device__ __forceinline__ uint32_t span_b_chunk(uint64_t a, uint32_t na) {
+  return (((uint32_t)(a & 15) + na + 15) >> 4) + 1;
+}
+
+// ------------------------------------------------------------------ activations in LDS ------
+
+// q8_1 activations in split form: 16-byte halves of the quants and the float scale per 32-value
+// block; act row r (a token or an entry), unit u at slot r * U + u.
+struct ActSplit {
+  MOE_LDS u32x4* lo;
+  MOE_LDS u32x4* hi;
+  MOE_LDS float* d;
+  int U;
+  __device__ __forceinline__ void get(int r, int u, uint32_t q[8], float& dx) const {
+    const u32x4 a = lo[r * U + u], b = hi[r * U + u];
+    q[0] = a.x; q[1] = a.y; q[2] = a.z; q[3] = a.w;
+    q[4] = b.x; q[5] = b.y; q[6] = b.z; q[7] = b.w;
+    dx = d[r * U + u];
   }
-  if (need2)
-    for (int i = threadIdx.x; i < 512; i += kThreads) g2[i] = ((const uint32_t*)A.cb2)[i];
-  if (need3)
-    for (int i = threadIdx.x; i < 512; i += kThreads) g3[i] = ((const uint32_t*)A.cb3)[i];
-  tb.cb2 = g2;
-  tb.cb3 = g3;
+};
+
+__device__ __forceinline__ ActSplit act_layout(MOE_LDS uint8_t* p, int rows, int U) {
+  ActSplit a;
+  a.lo = (MOE_LDS u32x4*)p;
+  a.hi = a.lo + rows * U;
+  a.d = (MOE_LDS float*)(a.hi + rows * U);
+  a.U = U;
+  return a;
+}
+__host__ __device__ inline int act_bytes(int rows, int U) { return (rows * U * 36 + 15) & ~15; }
+
+// Activation rows are staged in a fixed unrolled shape (constant register indices, no scratch):
+// float rows as one float4 per lane and pass (8 lanes per 32-value block, quantized with an
+// 8-lane DPP max), q8_1 rows as one dword per lane and pass (9 per 36-byte block).
+// Loads are branch-free (an index past the data reloads element 0, whose value is never used),
+// so they all issue back to back and the register arrays stay plain registers.
+template <int NT, int NP>
+__device__ __forceinline__ void act_issue_f(const float* base, long stride, int nblk, int U,
+                                            float4 (&xr)[NP]) {
+  if (nblk <= 0) return;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    int f = (int)threadIdx.x + p * NT;   // float4 f % 8 of block f / 8
+    f = f < nblk * 8 ? f : 0;
+    const int b = f >> 3, r = b / U, u = b - r * U;
+    xr[p] = ((const float4*)(base + (long)r * stride + 32 * u))[f & 7];
+  }
+}
+
+template <int NT, int NP>
+__device__ __forceinline__ void act_store_f(const float4 (&xr)[NP], int nblk, const ActSplit& act) {
+  if (nblk <= 0) return;
+  MOE_LDS uint32_t* lo32 = (MOE_LDS uint32_t*)act.lo;
+  MOE_LDS uint32_t* hi32 = (MOE_LDS uint32_t*)act.hi;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    // every lane of the wave takes part in the 8-lane max (full-wave DPP)
+    const int f = (int)threadIdx.x + p * NT;
+    const float4 v = xr[p];
+    float m = fmaxf(fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
+                    fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w)));
+    m = fmaxf(m, dpp<0xB1>(m));    // xor 1
+    m = fmaxf(m, dpp<0x4E>(m));    // xor 2
+    m = fmaxf(m, dpp<0x141>(m));   // the other quad of the 8
+    if (p * NT < nblk * 8 && f < nblk * 8) {
+      const int b = f >> 3, part = f & 7;
+      const float d = m / 127.0f;
+      uint32_t packed = 0;
+      if (m != 0.0f) {
+        const float xs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float r = round_half_away(xs[j] / d);
+          r = r > 127.0f ? 127.0f : r;
+          r = r < -127.0f ? -127.0f : r;
+          packed |= ((uint32_t)(int)r & 0xFFu) << (8 * j);
+        }
+      }
+      if (part < 4)
+        lo32[b * 4 + part] = packed;
+      else
+        hi32[b * 4 + part - 4] = packed;
+      if (part == 0) act.d[b] = h2f(f2h(d));
+    }
+  }
+}
+
+// The blocks past what the registers held: plain loads and the scalar quantizer.
+template <int NT>
+__device__ void act_rest_f(const float* base, long stride, int b0, int nblk, int U, ActSplit act) {
+  for (int b = b0 + (int)threadIdx.x; b < nblk; b += NT) {
+    const int r = b / U, u = b - r * U;
+    const float4* pp = (const float4*)(base + (long)r * stride + 32 * u);
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 ff = pp[q];
+      v[4 * q] = ff.x;
+      v[4 * q + 1] = ff.y;
+      v[4 * q + 2] = ff.z;
+      v[4 * q + 3] = ff.w;
+    }
+    const QBlock bq = quant_block(v);
+    act.lo[b] = u32x4{bq.q[0], bq.q[1], bq.q[2], bq.q[3]};
+    act.hi[b] = u32x4{bq.q[4], bq.q[5], bq.q[6], bq.q[7]};
+    act.d[b] = bq.d;
+  }
+}
+
+// q8_1 rows: block b (= row * U + unit) at base + b * 36.
+template <int NT, int NP>
+__device__ __forceinline__ void act_issue_q(const uint8_t* base, int nblk, uint32_t (&qr)[NP]) {
+  if (nblk <= 0) return;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int f = (int)threadIdx.x + p * NT;   // dword f % 9 of block f / 9
+    qr[p] = ((const uint32_t*)base)[f < nblk * 9 ? f : 0];
+  }
+}
+
+template <int NT, int NP>
+__device__ __forceinline__ void act_store_q(const uint32_t (&qr)[NP], int nblk, const ActSplit& act) {
+  if (nblk <= 0) return;
+  MOE_LDS uint32_t* lo32 = (MOE_LDS uint32_t*)act.lo;
+  MOE_LDS uint32_t* hi32 = (MOE_LDS uint32_t*)act.hi;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int f = (int)threadIdx.x + p * NT;
+    if (f < nblk * 9) {
+      const int b = f / 9, k = f - b * 9;
+      if (k == 0)
+        act.d[b] = h2f(qr[p] & 0xFFFFu);
+      else if (k <= 4)
+        lo32[b * 4 + k - 1] = qr[p];
+      else
+        hi32[b * 4 + k - 5] = qr[p];
+    }
+  }
+}
+
+template <int NT>
+__device__ void act_rest_q(const uint8_t* base, int b0, int nblk, ActSplit act) {
+  for (int b = b0 + (int)threadIdx.x; b < nblk; b += NT) {
+    const uint32_t* pp = (const uint32_t*)(base + (size_t)b * 36);
+    uint32_t qq[9];
+#pragma unroll
+    for (int q = 0; q < 9; ++q) qq[q] = pp[q];
+    act.lo[b] = u32x4{qq[1], qq[2], qq[3], qq[4]};
+    act.hi[b] = u32x4{qq[5], qq[6], qq[7], qq[8]};
+    act.d[b] = h2f(qq[0] & 0xFFFFu);
+  }
+}
+
+// Stage nblk activation blocks into `act`: the register loads of the first blocks (up to
+// NT * NPMAX / 8 float rows, NT * NPMAX / 9 q8_1 rows) go out at once in a pass count rounded up to
+// a power of two (straight-line code, no register array merges), then mid() runs (work that must
+// not wait for those loads), then the blocks are quantized or split into LDS; blocks past the
+// register passes follow with plain loads.
+template <int NT, int NP, class Mid>
+__device__ __forceinline__ void act_stage_f_np(const float* base, long stride, int nreg, int U,
+                                               const ActSplit& act, Mid& mid) {
+  float4 xr[NP];
+  act_issue_f<NT, NP>(base, stride, nreg, U, xr);
+  mid(NP);
+  act_store_f<NT, NP>(xr, nreg, act);
+}
+template <int NT, int NPMAX, class Mid>
+__device__ __forceinline__ void act_stage_f(const float* base, long stride, int nblk, int U,
+                                            const ActSplit& act, Mid mid) {
+  const int nreg = min(nblk, NT * NPMAX / 8);
+  const int np = (nreg * 8 + NT - 1) / NT;
+  if (np == 0)
+    mid(0);
+  else if (np == 1)
+    act_stage_f_np<NT, 1>(base, stride, nreg, U, act, mid);
+  else if (np == 2)
+    act_stage_f_np<NT, 2>(base, stride, nreg, U, act, mid);
+  else if (np <= 4 || NPMAX < 8)
+    act_stage_f_np<NT, (NPMAX < 4 ? NPMAX : 4)>(base, stride, nreg, U, act, mid);
+  else if (np <= 8 || NPMAX < 16)
+    act_stage_f_np<NT, (NPMAX < 8 ? NPMAX : 8)>(base, stride, nreg, U, act, mid);
+  else
+    act_stage_f_np<NT, NPMAX>(base, stride, nreg, U, act, mid);
+  if (nblk > nreg) act_rest_f<NT>(base, stride, nreg, nblk, U, act);
+}
+
+template <int NT, int NP, class Mid>
+__device__ __forceinline__ void act_stage_q_np(const uint8_t* base, int nreg, const ActSplit& act, Mid& mid) {
+  uint32_t qr[NP];
+  act_issue_q<NT, NP>(base, nreg, qr);
+  mid(NP);
+  act_store_q<NT, NP>(qr, nreg, act);
+}
+template <int NT, int NPMAX, class Mid>
+__device__ __forceinline__ void act_stage_q(const uint8_t* base, int nblk, const ActSplit& act, Mid mid) {
+  const int nreg = min(nblk, NT * NPMAX / 9);
+  const int np = (nreg * 9 + NT - 1) / NT;
+  if (np == 0)
+    mid(0);
+  else if (np == 1)
+    act_stage_q_np<NT, 1>(base, nreg, act, mid);
+  else if (np == 2)
+    act_stage_q_np<NT, 2>(base, nreg, act, mid);
+  else if (np <= 4 || NPMAX < 8)
+    act_stage_q_np<NT, (NPMAX < 4 ? NPMAX : 4)>(base, nreg, act, mid);
+  else if (np <= 8 || NPMAX < 16)
+    act_stage_q_np<NT, (NPMAX < 8 ? NPMAX : 8)>(base, nreg, act, mid);
+  else
+    act_stage_q_np<NT, NPMAX>(base, nreg, act, mid);
+  if (nblk > nreg) act_rest_q<NT>(base, nreg, nblk, act);
 }
 
 // ------------------------------------------------------------------ one row-pass of dots ----
 
-// Activation slots in split form (gate/up kernel): 16-byte halves of the quants and the float
-// scale per 32-value block, entry slot stride `umax`.
-struct ActSplit {
-  const MOE_LDS u32x4* lo;
-  const MOE_LDS u32x4* hi;
-  const MOE_LDS float* d;
-  int umax;
-  __device__ __forceinline__ void get(int e, int u, uint32_t q[8], float& dx) const {
-    const u32x4 a = lo[e * umax + u], b = hi[e * umax + u];
-    q[0] = a.x; q[1] = a.y; q[2] = a.z; q[3] = a.w;
-    q[4] = b.x; q[5] = b.y; q[6] = b.z; q[7] = b.w;
-    dx = d[e * umax + u];
-  }
-};
-
-// Activation rows as raw 36-byte q8_1 blocks in LDS (down kernel): entry e's row at byte offset
-// base + e * rowb, 4-byte aligned.
-struct ActRaw {
-  const MOE_LDS uint32_t* W;
-  uint32_t base, rowb;
-  __device__ __forceinline__ void get(int e, int u, uint32_t q[8], float& dx) const {
-    const uint32_t o = (base + (uint32_t)e * rowb + 36u * (uint32_t)u) >> 2;
-    dx = h2f(W[o] & 0xFFFFu);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = W[o + 1 + i];
-  }
-};
-
-// Dot the rows of one wave pass with ne (<= 4) activation entries. The wave's lanes cover rp rows
-// (row i = lane >> lgL, i < nrows) of L lanes; row i's bytes start at LDS byte `row0 + i * rb`.
-// out(i, e, value) is called by one lane per (row, entry) after the fixed-order lane reduction.
-template <int FMT, class Act, class Out>
-__device__ __forceinline__ void dot_pass(const MOE_LDS uint32_t* W, uint32_t row0, int nrows,
-                                         const Geom& G, const Tables& tb, const Act& act, int ne,
-                                         Out out) {
+// Dot the rows of one wave pass with ne (<= 4) activation rows sidx[0..ne). The wave's lanes
+// cover nrows rows (row i = lane >> lgL) of L lanes; rows i < half start at LDS byte ra + i rb,
+// the others at rb0 + (i - half) rb. out(i, e, value) is called by one lane per (row, entry)
+// after the fixed-order lane reduction.
+template <int FMT, class Out>
+__device__ __forceinline__ void dot_pass(const MOE_LDS uint32_t* W, uint32_t ra, uint32_t rb0, int half,
+                                         int nrows, const Geom& G, const Tables& tb, const ActSplit& act,
+                                         const int (&sidx)[kSlots], int ne, Out out) {
   const int lane = threadIdx.x & 63;
   const int i = lane >> G.lgL, li = lane & (G.L - 1);
-  float acc[kMaxSlots] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[kSlots] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (i < nrows) {
-    const uint32_t row = row0 + (uint32_t)(i * G.rb);
+    const uint32_t row = i < half ? ra + (uint32_t)(i * G.rb) : rb0 + (uint32_t)((i - half) * G.rb);
     for (int k = 0; k < G.upl; ++k) {
       const int u = li + (k << G.lgL);
       if (u < G.U) {
@@ -207,11 +406,11 @@ __device__ __forceinline__ void dot_pass(const MOE_LDS uint32_t* W, uint32_t row
         float sc;
         decode_unit<FMT>(W, row, u, tb, c, sc);
 #pragma unroll
-        for (int e = 0; e < kMaxSlots; ++e) {
+        for (int e = 0; e < kSlots; ++e) {
           if (e < ne) {
             uint32_t q[8];
             float dx;
-            act.get(e, u, q, dx);
+            act.get(sidx[e], u, q, dx);
             int s = __builtin_amdgcn_sdot4((int)c[0], (int)q[0], 0, false);
             s = __builtin_amdgcn_sdot4((int)c[1], (int)q[1], s, false);
             s = __builtin_amdgcn_sdot4((int)c[2], (int)q[2], s, false);
@@ -227,12 +426,12 @@ __device__ __forceinline__ void dot_pass(const MOE_LDS uint32_t* W, uint32_t row
     }
   }
 #pragma unroll
-  for (int e = 0; e < kMaxSlots; ++e)
+  for (int e = 0; e < kSlots; ++e)
     if (e < ne) acc[e] = group_sum(acc[e], G.L);
   // every lane of the row holds every sum; lane li stores the entries e = li (mod L)
   if (i < nrows) {
 #pragma unroll
-    for (int e = 0; e < kMaxSlots; ++e)
+    for (int e = 0; e < kSlots; ++e)
       if (e < ne && (e & (G.L - 1)) == li) out(i, e, acc[e]);
   }
 }
@@ -264,151 +463,251 @@ __device__ __forceinline__ void swiglu_q81_lanes(float gv, float uv, int l32, bo
   }
 }
 
-// ------------------------------------------------------------------ routing (workgroup) -----
+// ------------------------------------------------------------------ routing (one wave) ------
 
-// Top-k of one token's E logits by (logit descending, expert id ascending) with the whole
-// workgroup: each expert's rank is the number of experts that beat it; ranks < k are selected.
-// Weights: ex_j = exp(l_j - l_top) in rank order, w_j = ex_j / (((ex_0 + ex_1) + ex_2) + ...).
-// lg: the token's logits staged in LDS. Writes ids/w (LDS) in rank order.
-__device__ void route_token_wg(const MOE_LDS float* lg, int E, int k, MOE_LDS int* ids, MOE_LDS float* w,
-                               MOE_LDS float* ex) {
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    const float v = lg[e];
-    int rank = 0;
-    for (int o = 0; o < E; ++o) {
-      const float lo = lg[o];
-      rank += (lo > v) | ((lo == v) & (o < e));
+// Unsigned key with the order of the float (-0 and +0 share a key).
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t b = __float_as_uint(f + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float unkey(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// One token's E (<= 1024) logits into LDS (dst[e], e < 64 ceil(E / 64)) with direct-to-LDS 4-byte
+// loads of one wave; past E a lane reloads row[0], which route_wave ignores.
+__device__ __forceinline__ void issue_logits(const float* row, int E, MOE_LDS float* dst) {
+  const int lane = threadIdx.x & 63;
+  for (int j = 0; 64 * j < E; ++j) {
+    const int e = 64 * j + lane;
+    __builtin_amdgcn_global_load_lds((const void*)(row + (e < E ? e : 0)), (MOE_LDS void*)(dst + 64 * j), 4,
+                                     0, 0);
+  }
+}
+__host__ __device__ inline int logits_pad(int E) { return (E + 63) & ~63; }
+
+// Top-k (k <= min(E, 32)) of the logits one wave holds, by (logit descending, expert id
+// ascending): a radix select over ballots finds the k-th largest key (bit by bit, the largest
+// prefix that at least k keys reach), ties at that key go to the lowest ids, and the k chosen get
+// their exact ranks by comparison. Weights: ex_j = exp(l_j - l_0) in rank order,
+// w_j = ex_j / (((ex_0 + ex_1) + ex_2) + ...). Writes ids/w[0..k) (LDS) in rank order.
+// lg_in: the token's logits in LDS (issue_logits); V = logits per lane (E <= 64 V); scr: 96 words
+// of LDS for this wave.
+template <int V>
+__device__ __forceinline__ void route_wave_v(const MOE_LDS float* lg_in, int E, int k, MOE_LDS int* ids, MOE_LDS float* w,
+                             MOE_LDS uint32_t* scr) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  uint32_t key[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) key[j] = (64 * j + lane < E) ? fkey(lg_in[64 * j + lane]) : 0u;   // 0: no expert
+  uint32_t tau = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = tau | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j) cnt += __popcll(__ballot(key[j] >= c));
+    tau = cnt >= k ? c : tau;
+  }
+  int ngt = 0;
+#pragma unroll
+  for (int j = 0; j < V; ++j) ngt += __popcll(__ballot(key[j] > tau));
+  const int need = k - ngt;   // keys equal to tau to take, lowest ids first
+  int eqb = 0, selb = 0;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const uint64_t eqm = __ballot(key[j] == tau);
+    const bool sel = key[j] > tau || (key[j] == tau && eqb + __popcll(eqm & lt) < need);
+    const uint64_t sm = __ballot(sel);
+    if (sel) {
+      const int pos = selb + __popcll(sm & lt);
+      scr[pos] = key[j];
+      scr[32 + pos] = (uint32_t)(64 * j + lane);
     }
-    if (rank < k) ids[rank] = e;
+    eqb += __popcll(eqm);
+    selb += __popcll(sm);
   }
-  __syncthreads();
-  if ((int)threadIdx.x < k) ex[threadIdx.x] = expf(lg[ids[threadIdx.x]] - lg[ids[0]]);
-  __syncthreads();
-  if (threadIdx.x == 0) {
+  wave_lds_sync();
+  MOE_LDS float* lg = (MOE_LDS float*)(scr + 64);
+  if (lane < k) {
+    const uint32_t mk = scr[lane];
+    const uint32_t mid = scr[32 + lane];
+    int r = 0;
+    for (int o = 0; o < k; ++o) {
+      const uint32_t ok = scr[o], oid = scr[32 + o];
+      r += (ok > mk) | ((ok == mk) & (oid < mid));
+    }
+    ids[r] = (int)mid;
+    lg[r] = unkey(mk);
+  }
+  wave_lds_sync();
+  float ex = 0.0f;
+  if (lane < k) ex = expf(lg[lane] - lg[0]);
+  wave_lds_sync();
+  if (lane < k) lg[lane] = ex;
+  wave_lds_sync();
+  MOE_LDS float* sum = (MOE_LDS float*)scr;   // the keys are no longer needed
+  if (lane == 0) {
     float s = 0.0f;
-    for (int j = 0; j < k; ++j) s = s + ex[j];
-    ex[32] = s;
+    for (int j = 0; j < k; ++j) s = s + lg[j];
+    sum[0] = s;
   }
-  __syncthreads();
-  if ((int)threadIdx.x < k) w[threadIdx.x] = ex[threadIdx.x] / ex[32];
-  __syncthreads();
+  wave_lds_sync();
+  if (lane < k) w[lane] = ex / sum[0];
+  wave_lds_sync();
 }
 
-// Group n = T * k entries (ids/w in LDS, token-major) by expert into plan arrays in LDS: groups
-// ascending by expert id, entries ascending by token inside a group; absolute entry indices start
-// at entry_base. Invalid ids (out of [0, E)) are dropped and reported.
-struct PlanLds {
-  MOE_LDS int* ids;     // [64] in: entry expert (token-major)
-  MOE_LDS float* w;     // [64] in: entry weight
-  MOE_LDS int* first;   // [64] scratch
-  MOE_LDS int* gexp;    // [64] out: group expert
-  MOE_LDS int* gstart;  // [65] out: group start (absolute)
-  MOE_LDS int* esrc;    // [64] out (relative to entry_base)
-  MOE_LDS int* edst;
-  MOE_LDS float* ew;
-  MOE_LDS int* ng;      // [1]
+__device__ __forceinline__ void route_wave(const MOE_LDS float* lg, int E, int k, MOE_LDS int* ids,
+                                           MOE_LDS float* w, MOE_LDS uint32_t* scr) {
+  if (E <= 64)
+    route_wave_v<1>(lg, E, k, ids, w, scr);
+  else if (E <= 128)
+    route_wave_v<2>(lg, E, k, ids, w, scr);
+  else if (E <= 256)
+    route_wave_v<4>(lg, E, k, ids, w, scr);
+  else if (E <= 512)
+    route_wave_v<8>(lg, E, k, ids, w, scr);
+  else
+    route_wave_v<16>(lg, E, k, ids, w, scr);
+}
+
+// ------------------------------------------------------------------ plan in LDS -------------
+
+struct PlanL {
+  MOE_LDS int* rid;        // [64] routed expert of entry i (token-major: token i / k)
+  MOE_LDS float* rw;       // [64] its router weight
+  MOE_LDS uint32_t* skey;  // [64] grouping scratch
+  MOE_LDS int* sidx;       // [64]
+  MOE_LDS int* sexp;       // [64]
+  MOE_LDS int* gexp;       // [64] group expert
+  MOE_LDS int* gstart;     // [65] group start (absolute entry)
+  MOE_LDS int* esrc;       // [64] entry (relative to e0): token
+  MOE_LDS int* edst;       // [64] destination row
+  MOE_LDS float* ew;       // [64] router weight
+  MOE_LDS int* elive;      // [64] entry computed (source in range)
+  MOE_LDS int* dtok;       // [64] destination of each token (routing)
+  MOE_LDS int* misc;       // [16] 0: n_groups, 1: e0 (absolute), 2: e1, 3: raw n_groups
+  MOE_LDS uint32_t* rscr;  // [4 waves][96] routing scratch
+  MOE_LDS int* emap;       // [kMaxE] expert -> group (routing with prefetched pointers)
 };
-constexpr int kPlanLdsInts = 64 * 8 + 2;
+constexpr int kPlanLInts = 64 * 5 + 64 + 68 + 64 * 5 + 16 + 4 * 96 + kMaxE;
+constexpr int kPlanLBytes = (4 * kPlanLInts + 15) & ~15;
 
-__device__ inline PlanLds plan_lds(MOE_LDS int* base) {
-  return PlanLds{base, (MOE_LDS float*)(base + 64), base + 128, base + 192, base + 256, base + 321,
-                 base + 385, (MOE_LDS float*)(base + 449), base + 513};
+__device__ inline PlanL plan_l(MOE_LDS int* b) {
+  PlanL p;
+  p.rid = b;
+  p.rw = (MOE_LDS float*)(b + 64);
+  p.skey = (MOE_LDS uint32_t*)(b + 128);
+  p.sidx = b + 192;
+  p.sexp = b + 256;
+  p.gexp = b + 320;
+  p.gstart = b + 384;
+  p.esrc = b + 452;
+  p.edst = b + 516;
+  p.ew = (MOE_LDS float*)(b + 580);
+  p.elive = b + 644;
+  p.dtok = b + 708;
+  p.misc = b + 772;
+  p.rscr = (MOE_LDS uint32_t*)(b + 788);
+  p.emap = b + 788 + 4 * 96;
+  return p;
 }
+static_assert(788 + 4 * 96 + kMaxE == kPlanLInts, "plan layout");
 
-__device__ void group_entries_wg(const PlanLds& p, int T, int k, int E, const int32_t* dst_of_token,
-                                 int entry_base, uint32_t* err) {
-  const int n = T * k;
-  const int i = threadIdx.x;
+// Group n (<= 64) entries (rid/rw, token-major with k per token) by expert with one wave: each
+// entry's key (expert, entry index) gets its rank among all keys, the entries land in key order
+// (groups ascending by expert, entries ascending by token inside a group), and a group starts
+// where the expert changes. Ids out of [0, E) are dropped and reported. Entry indices are
+// absolute from entry_base; esrc/edst/ew are relative to it.
+__device__ __forceinline__ void group_wave(const PlanL& p, int n, int k, int E, int entry_base, uint32_t* err) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt = (1ull << lane) - 1ull;
   int e = -1;
-  if (i < n) {
-    e = p.ids[i];
-    if (e < 0 || e >= E) {
+  uint32_t key = 0xFFFFFFFFu;
+  if (lane < n) {
+    e = p.rid[lane];
+    if (e >= 0 && e < E) {
+      key = ((uint32_t)e << 6) | (uint32_t)lane;
+    } else {
       set_err(err, MOE_ERR_EXPERT);
       e = -1;
     }
   }
-  if (i < 64) p.first[i] = 0;
-  __syncthreads();
-  if (i < n) {
-    int first = e >= 0;
-    for (int q = 0; q < i && first; ++q) first = p.ids[q] != e;
-    p.first[i] = first;
+  p.skey[lane] = key;
+  wave_lds_sync();
+  int r = 0;
+  for (int o = 0; o < n; ++o) r += p.skey[o] < key;
+  const bool valid = e >= 0;
+  const int nv = __popcll(__ballot(valid));
+  if (valid) {
+    p.sexp[r] = e;
+    p.sidx[r] = lane;
   }
-  __syncthreads();
-  if (i < n) {
-    int grp = 0, before = 0, pos = 0, nvalid = 0, ngroups = 0;
-    for (int m = 0; m < n; ++m) {
-      const int em = p.ids[m];
-      if (em < 0 || em >= E) continue;
-      ++nvalid;
-      ngroups += p.first[m];
-      if (e < 0) continue;
-      if (m < i && em == e) ++pos;
-      if (em < e) {
-        ++before;
-        grp += p.first[m];
-      }
-    }
-    if (e >= 0) {
-      const int t = i / k;
-      const int slot = before + pos;
-      p.esrc[slot] = t;
-      p.edst[slot] = dst_of_token ? dst_of_token[t] : t;
-      p.ew[slot] = p.w[i];
-      if (p.first[i]) {
-        p.gexp[grp] = e;
-        p.gstart[grp] = entry_base + before;
-      }
-    }
-    if (i == 0) {
-      p.gstart[ngroups] = entry_base + nvalid;
-      *p.ng = ngroups;
-    }
+  wave_lds_sync();
+  // lane = position in key order
+  const bool live = lane < nv;
+  const int se = live ? p.sexp[lane] : -1;
+  const int prev = (live && lane > 0) ? p.sexp[lane - 1] : -2;
+  const bool first = live && se != prev;
+  const uint64_t fm = __ballot(first);
+  const int ng = __popcll(fm);
+  if (first) {
+    const int g = __popcll(fm & lt);
+    p.gexp[g] = se;
+    p.gstart[g] = entry_base + lane;
   }
-  __syncthreads();
+  if (live) {
+    const int i = p.sidx[lane];
+    const int t = i / k;
+    p.esrc[lane] = t;
+    p.edst[lane] = p.dtok[t];
+    p.ew[lane] = p.rw[i];
+    p.elive[lane] = 1;
+  }
+  if (lane == 0) {
+    p.gstart[ng] = entry_base + nv;
+    p.misc[0] = ng;
+    p.misc[1] = entry_base;
+    p.misc[2] = entry_base + nv;
+  }
+  wave_lds_sync();
 }
 
-// Copy a plan built in LDS out to the caller's plan arrays.
-__device__ void publish_plan(const PlanLds& p, const PlanArgs& P, int entry_base) {
-  const int ng = uni(*p.ng);
-  const int nv = uni(p.gstart[ng]) - entry_base;
-  const int i = threadIdx.x;
-  if (i < ng) {
+// Copy the plan built in LDS out to the caller's plan arrays (NT threads).
+template <int NT>
+__device__ __forceinline__ void publish_plan(const PlanL& p, const PlanArgs& P) {
+  const int ng = uni(p.misc[0]), e0 = uni(p.misc[1]), n = uni(p.misc[2]) - e0;
+  for (int i = threadIdx.x; i < ng; i += NT) {
     P.grp_expert[i] = p.gexp[i];
     P.grp_start[i] = p.gstart[i];
   }
-  if (i == 0) {
+  if (threadIdx.x == 0) {
     P.grp_start[ng] = p.gstart[ng];
     *P.n_groups = ng;
   }
-  if (i < nv) {
-    P.ent_src[entry_base + i] = p.esrc[i];
-    P.ent_dst[entry_base + i] = p.edst[i];
-    P.ent_w[entry_base + i] = p.ew[i];
+  for (int i = threadIdx.x; i < n; i += NT) {
+    P.ent_src[e0 + i] = p.esrc[i];
+    P.ent_dst[e0 + i] = p.edst[i];
+    P.ent_w[e0 + i] = p.ew[i];
   }
 }
 
-// ------------------------------------------------------------------ call validation ---------
-
-struct Call {
-  int ng, e0, e1;
-};
-
-// Validate the call's group table (thread 0) and broadcast it. Bad tables make the call empty.
-__device__ Call read_call(const PlanArgs& P, MOE_LDS int* misc) {
+// A plan the caller built: validate the group table (thread 0; raw values in gs[0..cap] and
+// raw_ng) and write n_groups, e0, e1 to out[0..2]. A bad table makes the call empty.
+__device__ __forceinline__ void validate_groups(const MOE_LDS int* gs, int raw_ng, const PlanArgs& P, MOE_LDS int* out) {
   if (threadIdx.x == 0) {
-    int ng = *P.n_groups;
+    int ng = raw_ng;
     int e0 = 0, e1 = 0;
     if (ng < 0 || ng > P.cap_groups) {
       set_err(P.err, MOE_ERR_NGROUPS);
       ng = 0;
     }
     if (ng > 0) {
-      e0 = P.grp_start[0];
+      e0 = gs[0];
       bool ok = e0 >= 0;
       int prev = e0;
       for (int g = 1; g <= ng; ++g) {
-        const int s = P.grp_start[g];
+        const int s = gs[g];
         ok = ok && s >= prev;
         prev = s;
       }
@@ -419,14 +718,18 @@ __device__ Call read_call(const PlanArgs& P, MOE_LDS int* misc) {
         e0 = e1 = 0;
       }
     }
-    misc[0] = ng;
-    misc[1] = e0;
-    misc[2] = e1;
+    out[0] = ng;
+    out[1] = e0;
+    out[2] = e1;
   }
-  __syncthreads();
-  const Call c{uni(misc[0]), uni(misc[1]), uni(misc[2])};
-  __syncthreads();
-  return c;
+}
+
+__device__ __forceinline__ bool ptr_ok(uint64_t v, uint32_t* err) {
+  if (v & 1) {
+    set_err(err, MOE_ERR_ALIGN);
+    return false;
+  }
+  return true;
 }
 
 // ------------------------------------------------------------------ gate/up kernel ----------
@@ -438,510 +741,484 @@ struct GuArgs {
   PlanArgs P;
   Geom G;
   Stream S;
-  int umax;             // activation slot stride (units)
-  int n_tokens;
+  int n_tokens;         // act rows (tokens)
   const uint8_t* xq;    // composed: q8_1 rows per token
   const float* x;       // fused / routed: float rows per token
   float* g;             // composed: g rows (absolute entry, stride ld); fused: workspace rows
   float* u;
   int ld;
-  uint8_t* hq;          // fused / routed: workspace q8_1 rows (relative entry)
-  const float* logits;  // routed mode: [T][E] router logits
+  float* h;             // fused / routed: workspace h rows (relative entry, stride n_ff)
+  uint8_t* desc;        // fused / routed: the call's descriptor for the down launch
+  const float* logits;  // routed: [T][E] router logits
   int T, E, k;
   const int32_t* dst_of_token;
   int entry_base;
+  int lds_ring, lds_act;
+  int sw;               // waves that stream items (the ring holds sw waves' slots)
 };
 
-struct GuSmem {
-  MOE_LDS uint8_t* ring;     // kWaves * NS * M KB
-  MOE_LDS u32x4* qlo;        // [kMaxSlots][umax]
-  MOE_LDS u32x4* qhi;
-  MOE_LDS float* xd;
-  MOE_LDS float* gu;         // [kMaxSlots][64]: g rows 0..31, u rows 32..63 of the h block
-  MOE_LDS uint32_t* g2;      // 512 dwords
-  MOE_LDS uint32_t* g3;      // 512 dwords
-  MOE_LDS int* misc;         // [64]
-  MOE_LDS int* plan;         // routed mode: kPlanLdsInts
-  MOE_LDS float* lg;         // routed mode: logits [E] + ex [64]
-};
+constexpr int kGuStage = 64;   // floats of per-wave output staging (kSlots x 16 rows)
+constexpr int kGuFixed = 4096 + kPlanLBytes + 8 * 3 * kMaxGrp + 4 * kGuStage * kGuWaves;
+constexpr int kGuXPass = 8;    // float4 (or q8_1 dword) register passes: 1024 float blocks, 910 q8_1
 
-__host__ __device__ inline int gu_smem_bytes(const Stream& S, int umax, int E) {
-  return kWaves * S.NS * S.M * 1024 + kMaxSlots * umax * 36 + kMaxSlots * 64 * 4 + 4096 + 256 +
-         (E > 0 ? kPlanLdsInts * 4 + (E + 64) * 4 : 0);
+__host__ __device__ inline int gu_smem_bytes(int lds_ring, int lds_act) {
+  return lds_ring + lds_act + kGuFixed;
 }
 
-__device__ GuSmem gu_layout(const Stream& S, int umax) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  GuSmem s;
-  MOE_LDS uint8_t* p = (MOE_LDS uint8_t*)smem;
-  s.ring = p;
-  p += kWaves * S.NS * S.M * 1024;
-  s.qlo = (MOE_LDS u32x4*)p;
-  p += kMaxSlots * umax * 16;
-  s.qhi = (MOE_LDS u32x4*)p;
-  p += kMaxSlots * umax * 16;
-  s.xd = (MOE_LDS float*)p;
-  p += kMaxSlots * umax * 4;
-  s.gu = (MOE_LDS float*)p;
-  p += kMaxSlots * 64 * 4;
-  s.g2 = (MOE_LDS uint32_t*)p;
-  p += 2048;
-  s.g3 = (MOE_LDS uint32_t*)p;
-  p += 2048;
-  s.misc = (MOE_LDS int*)p;
-  p += 256;
-  s.plan = (MOE_LDS int*)p;
-  p += kPlanLdsInts * 4;
-  s.lg = (MOE_LDS float*)p;
-  return s;
-}
-
-// This h block's activations are loaded into registers before the weight stream is issued, so
-// "they landed" is a vmcnt wait that leaves the stream in flight; they are then quantized (fused)
-// or split (composed) into LDS.
-constexpr int kActBlocks = 512;                          // ne * U handled in registers
-constexpr int kXPass = kActBlocks * 8 / kThreads;        // float4 per lane (fused)
-constexpr int kQPass = kActBlocks * 9 / kThreads;        // dwords per lane (composed)
-
+// One workgroup per CU; the work items are per wave: item (group g, j) = h rows
+// [j rp / 2, (j + 1) rp / 2) of group g, spread over the streaming waves of the grid (the first
+// sw waves of each workgroup; wave-granular balance). A wave streams its item's gate and up rows
+// as one two-span chunk.
 template <int FMT, int MODE>
-__global__ __launch_bounds__(kThreads) void k_gate_up(GuArgs a) {
-  const GuSmem sm = gu_layout(a.S, a.umax);
-  Tables tb;
-  load_tables(a.A, FMT == CB2, FMT == CB3, sm.g2, sm.g3, tb);
+__global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
   const Geom& G = a.G;
-  const int nb = a.A.n_ff / 32;   // h blocks per group
-  const int wave = threadIdx.x >> 6;
-  const PlanLds pl = plan_lds(sm.plan);
-  Call call;
-  if constexpr (MODE == GU_ROUTED) {
-    // route every token and group the entries here (every workgroup derives the same plan from
-    // the same logits); workgroup 0 publishes it for the down kernel and the caller
-    for (int t = 0; t < a.T; ++t) {
-      for (int e = threadIdx.x; e < a.E; e += kThreads) sm.lg[e] = a.logits[(size_t)t * a.E + e];
-      __syncthreads();
-      route_token_wg(sm.lg, a.E, a.k, pl.ids + t * a.k, pl.w + t * a.k, sm.lg + a.E);
-    }
-    group_entries_wg(pl, a.T, a.k, a.E, a.dst_of_token, a.entry_base, a.P.err);
-    if (blockIdx.x == 0) publish_plan(pl, a.P, a.entry_base);
-    const int ng = uni(*pl.ng);
-    call = Call{ng, a.entry_base, uni(pl.gstart[ng])};
-  } else {
-    call = read_call(a.P, sm.misc);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  MOE_LDS uint8_t* ring = (MOE_LDS uint8_t*)smem;
+  const ActSplit act = act_layout(ring + a.lds_ring, a.n_tokens, G.U);
+  MOE_LDS uint8_t* p8 = ring + a.lds_ring + a.lds_act;
+  MOE_LDS uint32_t* g2 = (MOE_LDS uint32_t*)p8;
+  MOE_LDS uint32_t* g3 = g2 + 512;
+  const PlanL pl = plan_l((MOE_LDS int*)(p8 + 4096));
+  MOE_LDS uint64_t* gptr = (MOE_LDS uint64_t*)(p8 + 4096 + kPlanLBytes);   // [group][gate, up, down]
+  MOE_LDS float* stage = (MOE_LDS float*)(p8 + 4096 + kPlanLBytes + 8 * 3 * kMaxGrp) + wave * kGuStage;
+  MOE_LDS float* lgs = (MOE_LDS float*)ring;   // routed: staged logits (prologue only)
+  const int Epad = logits_pad(a.E);
+
+  // ---- 1. every load that depends on nothing, at once
+  uint32_t t_nl4[4] = {0u, 0u, 0u, 0u};
+  if (a.A.nl4) {
+    const uint32_t* t = (const uint32_t*)a.A.nl4;
+    t_nl4[0] = t[0];
+    t_nl4[1] = t[1];
+    t_nl4[2] = t[2];
+    t_nl4[3] = t[3];
   }
-  const int items = call.ng * nb;
-  MOE_LDS uint8_t* myring = sm.ring + wave * a.S.NS * a.S.M * 1024;
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int g = it / nb, j = it - g * nb;
-    // group info (thread 0), broadcast
-    if (threadIdx.x == 0) {
-      int e, a0, a1;
-      if constexpr (MODE == GU_ROUTED) {
-        e = pl.gexp[g];
-        a0 = pl.gstart[g];
-        a1 = pl.gstart[g + 1];
-      } else {
-        e = a.P.grp_expert[g];
-        a0 = a.P.grp_start[g];
-        a1 = a.P.grp_start[g + 1];
+  uint32_t t_cb = 0;
+  if constexpr (FMT == CB2 || FMT == CB3) {
+    const uint32_t* src = (const uint32_t*)(FMT == CB2 ? a.A.cb2 : a.A.cb3);
+    if (tid < 512) t_cb = src[tid];
+  }
+  int r_dt = 0, r_gs = 0, r_ge = 0, r_ng = 0;
+  uint64_t pg = 0, pu = 0, pd = 0;
+  if constexpr (MODE == GU_ROUTED) {
+    if (tid < a.T) r_dt = a.dst_of_token ? a.dst_of_token[tid] : tid;
+    if (tid < a.E) {
+      pg = (uint64_t)(uintptr_t)a.A.gate[tid];
+      pu = (uint64_t)(uintptr_t)a.A.up[tid];
+      pd = (uint64_t)(uintptr_t)a.A.down[tid];
+    }
+    if (wave < kRouteWaves && wave < a.T) issue_logits(a.logits + (size_t)wave * a.E, a.E, lgs + wave * Epad);
+  } else {
+    if (tid == 0) r_ng = *a.P.n_groups;
+    if (tid <= a.P.cap_groups) r_gs = a.P.grp_start[tid];
+    if (tid < a.P.cap_groups) r_ge = a.P.grp_expert[tid];
+  }
+
+  // ---- 2. activations of every token; while their loads fly, waves route their token
+  Tables tb;
+  tb.nl4[0] = t_nl4[0];
+  tb.nl4[1] = t_nl4[1];
+  tb.nl4[2] = t_nl4[2];
+  tb.nl4[3] = t_nl4[3];
+  tb.cb2 = g2;
+  tb.cb3 = g3;
+  const int rT = a.T, rE = a.E, rk = a.k;
+  auto mid = [=](int pending) {
+    if constexpr (MODE == GU_ROUTED) {
+      if (wave < kRouteWaves && wave < rT) {
+        wait_vm(pending);   // every load before this thread's activation loads, the logits too
+        route_wave(lgs + wave * Epad, rE, rk, pl.rid + wave * rk, pl.rw + wave * rk, pl.rscr + wave * 96);
       }
-      int ok = 1;
-      const uint8_t* w0 = nullptr;
-      const uint8_t* w1 = nullptr;
-      if (e < 0 || e >= a.A.n_experts) {
-        set_err(a.P.err, MOE_ERR_EXPERT);
-        ok = 0;
-      } else {
-        w0 = (const uint8_t*)a.A.gate[e];
-        w1 = (const uint8_t*)a.A.up[e];
-        if ((((uintptr_t)w0) | ((uintptr_t)w1)) & 1) {
-          set_err(a.P.err, MOE_ERR_ALIGN);
-          ok = 0;
-        }
+    }
+  };
+  if constexpr (MODE == GU_COMPOSED)
+    act_stage_q<kGuThreads, kGuXPass>(a.xq, a.n_tokens * G.U, act, mid);
+  else
+    act_stage_f<kGuThreads, kGuXPass>(a.x, a.A.n_embd, a.n_tokens * G.U, G.U, act, mid);
+  if constexpr (FMT == CB2 || FMT == CB3)
+    if (tid < 512) (FMT == CB2 ? g2 : g3)[tid] = t_cb;
+  if constexpr (MODE == GU_ROUTED) {
+    if (tid < a.T) pl.dtok[tid] = r_dt;
+    if (tid < a.E) pl.emap[tid] = -1;
+    // tokens past the first kRouteWaves: one more round per kRouteWaves tokens
+    if (wave < kRouteWaves) {
+      for (int t = wave + kRouteWaves; t < a.T; t += kRouteWaves) {
+        issue_logits(a.logits + (size_t)t * a.E, a.E, lgs + wave * Epad);
+        __builtin_amdgcn_s_waitcnt(MOE_VM(0));
+        route_wave(lgs + wave * Epad, a.E, a.k, pl.rid + t * a.k, pl.rw + t * a.k, pl.rscr + wave * 96);
       }
-      sm.misc[4] = ok;
-      sm.misc[5] = a0;
-      sm.misc[6] = a1;
-      *(MOE_LDS uint64_t*)(sm.misc + 8) = (uint64_t)(uintptr_t)w0;
-      *(MOE_LDS uint64_t*)(sm.misc + 10) = (uint64_t)(uintptr_t)w1;
+    }
+  } else {
+    if (tid == 0) pl.misc[3] = r_ng;
+    if (tid <= a.P.cap_groups) pl.gstart[tid] = r_gs;
+    if (tid < a.P.cap_groups) pl.gexp[tid] = r_ge;
+  }
+  __syncthreads();
+
+  // ---- 3. the plan: grouped here, or the caller's, validated
+  if constexpr (MODE == GU_ROUTED) {
+    if (wave == 0) group_wave(pl, a.T * a.k, a.k, a.E, a.entry_base, a.P.err);
+    __syncthreads();
+    const int ng = uni(pl.misc[0]);
+    if (tid < ng) pl.emap[pl.gexp[tid]] = tid;
+    __syncthreads();
+    if (tid < a.E) {
+      const int g = pl.emap[tid];
+      if (g >= 0) {
+        gptr[3 * g] = ptr_ok(pg | pu, a.P.err) ? pg : 0;
+        gptr[3 * g + 1] = pu;
+        gptr[3 * g + 2] = ptr_ok(pd, a.P.err) ? pd : 0;
+      }
     }
     __syncthreads();
-    const int ok = uni(sm.misc[4]);
-    const int a0 = uni(sm.misc[5]), a1 = uni(sm.misc[6]);
-    const uint8_t* wg = uni_ptr((const uint8_t*)(uintptr_t)(*(const MOE_LDS uint64_t*)(sm.misc + 8)));
-    const uint8_t* wu = uni_ptr((const uint8_t*)(uintptr_t)(*(const MOE_LDS uint64_t*)(sm.misc + 10)));
+  } else {
+    validate_groups(pl.gstart, pl.misc[3], a.P, pl.misc);
     __syncthreads();
-    if (!ok) continue;
-    for (int c0 = a0; c0 < a1; c0 += kMaxSlots) {
-      const int ne = min(kMaxSlots, a1 - c0);
-      // entry sources (invalid -> no activation, nothing written)
-      if (threadIdx.x < kMaxSlots) {
-        int src = -1;
-        if ((int)threadIdx.x < ne) {
-          if constexpr (MODE == GU_ROUTED)
-            src = pl.esrc[c0 + threadIdx.x - a.entry_base];
-          else
-            src = a.P.ent_src[c0 + threadIdx.x];
-          if (src < 0 || src >= a.n_tokens) {
-            set_err(a.P.err, MOE_ERR_SRC);
-            src = -1;
-          }
-        }
-        sm.misc[12 + threadIdx.x] = src;
+    const int ng = uni(pl.misc[0]), e0 = uni(pl.misc[1]), n = uni(pl.misc[2]) - e0;
+    int r_src = 0, r_dst = 0;
+    float r_w = 0.0f;
+    uint64_t vg = 0, vu = 0, vd = 0;
+    int e = -1;
+    if (tid < n) {
+      r_src = a.P.ent_src[e0 + tid];
+      r_dst = a.P.ent_dst[e0 + tid];
+      r_w = a.P.ent_w[e0 + tid];
+    }
+    if (tid < ng) {
+      e = pl.gexp[tid];
+      if (e >= 0 && e < a.A.n_experts) {
+        vg = (uint64_t)(uintptr_t)a.A.gate[e];
+        vu = (uint64_t)(uintptr_t)a.A.up[e];
+        if (MODE == GU_FUSED) vd = (uint64_t)(uintptr_t)a.A.down[e];
       }
-      __syncthreads();
-      int srcs[kMaxSlots];
+    }
+    if (tid < n) {
+      const bool src_ok = r_src >= 0 && r_src < a.n_tokens;
+      if (!src_ok) set_err(a.P.err, MOE_ERR_SRC);
+      pl.esrc[tid] = src_ok ? r_src : 0;
+      pl.edst[tid] = r_dst;
+      pl.ew[tid] = r_w;
+      pl.elive[tid] = src_ok;
+    }
+    if (tid < ng) {
+      const bool e_ok = e >= 0 && e < a.A.n_experts;
+      if (!e_ok) set_err(a.P.err, MOE_ERR_EXPERT);
+      gptr[3 * tid] = (e_ok && ptr_ok(vg | vu, a.P.err)) ? vg : 0;
+      gptr[3 * tid + 1] = vu;
+      gptr[3 * tid + 2] = (e_ok && MODE == GU_FUSED && ptr_ok(vd, a.P.err)) ? vd : 0;
+    }
+    __syncthreads();
+  }
+  const int ng = uni(pl.misc[0]), e0 = uni(pl.misc[1]), n = uni(pl.misc[2]) - e0;
+
+  // ---- 4. workgroup 0 leaves the plan (routed) and the call's descriptor (fused / routed)
+  if (MODE != GU_COMPOSED && blockIdx.x == 0) {
+    if constexpr (MODE == GU_ROUTED) publish_plan<kGuThreads>(pl, a.P);
+    int* dw = (int*)a.desc;
+    uint64_t* dp = (uint64_t*)(a.desc + kDescPtrByte);
+    if (tid == 0) {
+      dw[kDescNg] = ng;
+      dw[kDescE0] = e0;
+      dw[kDescN] = n;
+    }
+    if (tid <= ng) dw[kDescGs + tid] = pl.gstart[tid] - e0;
+    if (tid < ng) dp[tid] = gptr[3 * tid] ? gptr[3 * tid + 2] : 0;
+    if (tid < n) {
+      int g = 0;
+      while (g + 1 < ng && pl.gstart[g + 1] - e0 <= tid) ++g;
+      dw[kDescDst + tid] = pl.edst[tid];
+      ((float*)dw)[kDescW + tid] = pl.ew[tid];
+      dw[kDescLive + tid] = pl.elive[tid] && gptr[3 * g] != 0;
+    }
+  }
+
+  // ---- 5. this wave's items, streamed through its ring
+  const int half = G.rp >> 1;
+  const int nbw = a.A.n_ff / half;   // items per group
+  const int items = ng * nbw;
+  const int gw = (int)blockIdx.x * a.sw + wave, TW = (int)gridDim.x * a.sw;
+  const int nit = (wave < a.sw && gw < items) ? (items - gw + TW - 1) / TW : 0;
+  const int M = a.S.M, NS = a.S.NS;
+  MOE_LDS uint8_t* myring = ring + wave * NS * M * 1024;
+  const uint32_t nspan = (uint32_t)(half * G.rb);
+  auto issue_item = [&](int kk, MOE_LDS uint8_t* slot) {
+    const int it = gw + kk * TW;
+    const int g = it / nbw, j = it - g * nbw;
+    const uint64_t wg = uni64(gptr[3 * g]);
+    if (wg) {
+      const uint64_t wu = uni64(gptr[3 * g + 1]);
+      const uint64_t off = (uint64_t)(j * half) * (uint64_t)G.rb;
+      issue_chunk(slot, M, (const uint8_t*)(uintptr_t)(wg + off), nspan,
+                  (const uint8_t*)(uintptr_t)(wu + off), nspan, span_b_chunk(wg + off, nspan));
+    } else {   // a skipped group keeps the count of loads: one 16-byte chunk every lane reloads
+      issue_chunk(slot, M, (const uint8_t*)a.P.grp_start, 1, nullptr, 0, 0);
+    }
+  };
+  __builtin_amdgcn_s_waitcnt(MOE_VM(0));   // nothing of ours in flight before the stream
+  const int pre = min(NS, nit);
+  for (int kk = 0; kk < pre; ++kk) issue_item(kk, myring + kk * M * 1024);
+  int issued = pre;
+  for (int kk = 0; kk < nit; ++kk) {
+    wait_vm((issued - 1 - kk) * M);
+    MOE_LDS uint8_t* slot = myring + (kk % NS) * M * 1024;
+    const int it = gw + kk * TW;
+    const int g = it / nbw, j = it - g * nbw;
+    const uint64_t wgv = uni64(gptr[3 * g]);
+    if (wgv) {
+      const uint64_t off = (uint64_t)(j * half) * (uint64_t)G.rb;
+      const uint32_t sb = (uint32_t)(slot - ring);
+      const uint32_t ra = sb + (uint32_t)((wgv + off) & 15);
+      const uint32_t rb0 = sb + 16 * span_b_chunk(wgv + off, nspan) +
+                           (uint32_t)((uni64(gptr[3 * g + 1]) + off) & 15);
+      const int a0 = uni(pl.gstart[g]) - e0, a1 = uni(pl.gstart[g + 1]) - e0;
+      const int hr0 = j * half;
+      for (int c0 = a0; c0 < a1; c0 += kSlots) {
+        const int ne = min(kSlots, a1 - c0);
+        int sidx[kSlots];
+        int live[kSlots];
 #pragma unroll
-      for (int e = 0; e < kMaxSlots; ++e) srcs[e] = uni(sm.misc[12 + e]);
-      __builtin_amdgcn_s_waitcnt(MOE_VM(0));   // nothing of ours in flight before the stream
-      // 1. activation loads into registers, older than every weight load issued below, with a
-      //    fixed unrolled shape (constant register indices): fused, one float4 of x per lane and
-      //    pass (8 lanes per 32-value block); composed, one dword of a q8_1 block per lane and pass
-      const int nblk = ne * G.U;
-      const bool in_regs = nblk <= kActBlocks;
-      float4 xr[kXPass];
-      uint32_t qr[kQPass];
-      if (in_regs) {
-        if constexpr (MODE == GU_COMPOSED) {
-#pragma unroll
-          for (int p = 0; p < kQPass; ++p) {
-            const int f = threadIdx.x + p * kThreads;   // dword f % 9 of block f / 9
-            qr[p] = 0;
-            if (f < nblk * 9) {
-              const int b = f / 9, e = b / G.U, u = b - e * G.U;
-              if (srcs[e] >= 0)
-                qr[p] = ((const uint32_t*)(a.xq + ((size_t)srcs[e] * G.U + u) * 36))[f - b * 9];
-            }
-          }
-        } else {
-#pragma unroll
-          for (int p = 0; p < kXPass; ++p) {
-            const int f = threadIdx.x + p * kThreads;   // float4 f % 8 of block f / 8
-            xr[p] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (f < nblk * 8) {
-              const int b = f >> 3, e = b / G.U, u = b - e * G.U;
-              if (srcs[e] >= 0)
-                xr[p] = ((const float4*)(a.x + (size_t)srcs[e] * a.A.n_embd + 32 * u))[f & 7];
-            }
-          }
+        for (int e = 0; e < kSlots; ++e) {
+          sidx[e] = e < ne ? uni(pl.esrc[c0 + e]) : 0;
+          live[e] = e < ne ? uni(pl.elive[c0 + e]) : 0;
         }
-      }
-      // 2. this wave's rows of the h block: gate rows [32 j + 8 wave, +8) then the same up rows,
-      //    in chunks of up to rp rows, streamed through the wave's ring
-      const int cpm = (8 + G.rp - 1) / G.rp;   // chunks per matrix
-      const int nch = 2 * cpm;
-      const int r_base = 32 * j + 8 * wave;
-      const int pre = min(a.S.NS, nch);
-      for (int kc = 0; kc < pre; ++kc) {
-        const int m = kc / cpm, r0 = r_base + (kc - m * cpm) * G.rp;
-        const int rows = min(G.rp, r_base + 8 - r0);
-        issue_chunk(myring + kc * a.S.M * 1024, a.S.M, (m == 0 ? wg : wu) + (size_t)r0 * G.rb,
-                    (uint32_t)(rows * G.rb), nullptr, 0, 0);
-      }
-      // 3. activations -> LDS split form once they have landed
-      MOE_LDS uint32_t* qlo32 = (MOE_LDS uint32_t*)sm.qlo;
-      MOE_LDS uint32_t* qhi32 = (MOE_LDS uint32_t*)sm.qhi;
-      if (in_regs) {
-        wait_vm(pre * a.S.M);
-        if constexpr (MODE == GU_COMPOSED) {
+        dot_pass<FMT>((const MOE_LDS uint32_t*)ring, ra, rb0, half, G.rp, G, tb, act, sidx, ne,
+                      [&](int i, int e, float v) { stage[e * 16 + i] = v; });
+        wave_lds_sync();
+        if (lane < ne * half) {
+          const int e = lane / half, r = lane - e * half;
+          const float gv = stage[e * 16 + r], uv = stage[e * 16 + half + r];
+          bool is_live = false;
 #pragma unroll
-          for (int p = 0; p < kQPass; ++p) {
-            const int f = threadIdx.x + p * kThreads;
-            if (f < nblk * 9) {
-              const int b = f / 9, k = f - b * 9, e = b / G.U, u = b - e * G.U;
-              const int slotw = e * a.umax + u;
-              if (k == 0)
-                sm.xd[slotw] = srcs[e] >= 0 ? h2f(qr[p] & 0xFFFFu) : 0.0f;
-              else if (k <= 4)
-                qlo32[slotw * 4 + k - 1] = qr[p];
-              else
-                qhi32[slotw * 4 + k - 5] = qr[p];
-            }
-          }
-        } else {
-#pragma unroll
-          for (int p = 0; p < kXPass; ++p) {
-            // every lane of the wave takes part in the 8-lane max (full-wave DPP)
-            const int f = threadIdx.x + p * kThreads;
-            const float4 v = xr[p];
-            float m = fmaxf(fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
-                            fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w)));
-            m = fmaxf(m, dpp<0xB1>(m));    // xor 1
-            m = fmaxf(m, dpp<0x4E>(m));    // xor 2
-            m = fmaxf(m, dpp<0x141>(m));   // the other quad of the 8
-            if (p * kThreads < nblk * 8 && f < nblk * 8) {
-              const int b = f >> 3, part = f & 7, e = b / G.U, u = b - e * G.U;
-              const int slotw = e * a.umax + u;
-              const float d = m / 127.0f;
-              uint32_t packed = 0;
-              if (m != 0.0f) {
-                const float xs[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                  float r = round_half_away(xs[jj] / d);
-                  r = r > 127.0f ? 127.0f : r;
-                  r = r < -127.0f ? -127.0f : r;
-                  packed |= ((uint32_t)(int)r & 0xFFu) << (8 * jj);
-                }
-              }
-              if (part < 4)
-                qlo32[slotw * 4 + part] = packed;
-              else
-                qhi32[slotw * 4 + part - 4] = packed;
-              if (part == 0) sm.xd[slotw] = srcs[e] >= 0 ? h2f(f2h(d)) : 0.0f;
-            }
-          }
-        }
-      } else {
-        // large activation sets: plain loads now (they wait behind the stream)
-        for (int idx = threadIdx.x; idx < nblk; idx += kThreads) {
-          const int e = idx / G.U, u = idx - e * G.U;
-          u32x4 lo = {0u, 0u, 0u, 0u}, hi = lo;
-          float d = 0.0f;
-          if (srcs[e] >= 0) {
-            uint32_t qq[9];
+          for (int q = 0; q < kSlots; ++q) is_live = q == e ? live[q] != 0 : is_live;
+          if (is_live) {
+            const int row = hr0 + r;
             if constexpr (MODE == GU_COMPOSED) {
-              const uint32_t* pp = (const uint32_t*)(a.xq + ((size_t)srcs[e] * G.U + u) * 36);
-#pragma unroll
-              for (int q = 0; q < 9; ++q) qq[q] = pp[q];
-              d = h2f(qq[0] & 0xFFFFu);
+              a.g[(size_t)(e0 + c0 + e) * a.ld + row] = gv;
+              a.u[(size_t)(e0 + c0 + e) * a.ld + row] = uv;
             } else {
-              const float4* pp = (const float4*)(a.x + (size_t)srcs[e] * a.A.n_embd + 32 * u);
-              float v[32];
-#pragma unroll
-              for (int q = 0; q < 8; ++q) {
-                const float4 ff = pp[q];
-                v[4 * q] = ff.x;
-                v[4 * q + 1] = ff.y;
-                v[4 * q + 2] = ff.z;
-                v[4 * q + 3] = ff.w;
-              }
-              const QBlock bq = quant_block(v);
-#pragma unroll
-              for (int q = 0; q < 8; ++q) qq[1 + q] = bq.q[q];
-              d = bq.d;
+              const size_t o = (size_t)(c0 + e) * a.A.n_ff + row;
+              a.g[o] = gv;
+              a.u[o] = uv;
+              a.h[o] = swiglu(gv, uv);
             }
-            lo = u32x4{qq[1], qq[2], qq[3], qq[4]};
-            hi = u32x4{qq[5], qq[6], qq[7], qq[8]};
           }
-          sm.qlo[e * a.umax + u] = lo;
-          sm.qhi[e * a.umax + u] = hi;
-          sm.xd[e * a.umax + u] = d;
         }
+        wave_lds_sync();
       }
-      __syncthreads();
-      // 4. compute chunk by chunk as they land; refill the freed slot
-      const ActSplit act{sm.qlo, sm.qhi, sm.xd, a.umax};
-      int issued = pre;
-      for (int kc = 0; kc < nch; ++kc) {
-        const int m = kc / cpm, r0 = r_base + (kc - m * cpm) * G.rp;
-        const int rows = min(G.rp, r_base + 8 - r0);
-        const uint8_t* src = (m == 0 ? wg : wu) + (size_t)r0 * G.rb;
-        wait_vm((issued - 1 - kc) * a.S.M);
-        MOE_LDS uint8_t* slot = myring + (kc % a.S.NS) * a.S.M * 1024;
-        const uint32_t row0 = (uint32_t)(slot - sm.ring) + (uint32_t)((uintptr_t)src & 15);
-        const int rrel = 32 * m + (r0 - 32 * j);   // row of the h block, g: 0..31, u: 32..63
-        dot_pass<FMT>((const MOE_LDS uint32_t*)sm.ring, row0, rows, G, tb, act, ne,
-                      [&](int i, int e, float v) { sm.gu[e * 64 + rrel + i] = v; });
-        if (kc + a.S.NS < nch) {
-          MOE_WAIT_LGKM0;   // this wave's LDS reads of the slot have returned
-          const int k2 = kc + a.S.NS;
-          const int m2 = k2 / cpm, r2 = r_base + (k2 - m2 * cpm) * G.rp;
-          const int rows2 = min(G.rp, r_base + 8 - r2);
-          issue_chunk(slot, a.S.M, (m2 == 0 ? wg : wu) + (size_t)r2 * G.rb, (uint32_t)(rows2 * G.rb),
-                      nullptr, 0, 0);
-          ++issued;
-        }
-      }
-      __syncthreads();
-      // 5. outputs of the h block: g/u rows and, fused, SwiGLU + q8_1 of the block
-      for (int idx = threadIdx.x; idx < ne * 64; idx += kThreads) {
-        const int e = idx >> 6, r = idx & 63;
-        if (srcs[e] < 0) continue;
-        const float v = sm.gu[e * 64 + r];
-        const int row = 32 * j + (r & 31);
-        if constexpr (MODE == GU_COMPOSED)
-          (r < 32 ? a.g : a.u)[(size_t)(c0 + e) * a.ld + row] = v;
-        else
-          (r < 32 ? a.g : a.u)[(size_t)(c0 + e - call.e0) * a.A.n_ff + row] = v;
-      }
-      if constexpr (MODE != GU_COMPOSED) {
-        const int e = threadIdx.x >> 5, l32 = threadIdx.x & 31;
-        if (e < kMaxSlots) {   // 128 threads: 4 entries x 32 rows
-          const bool live = e < ne && srcs[e] >= 0;
-          const float gv = live ? sm.gu[e * 64 + l32] : 0.0f;
-          const float uv = live ? sm.gu[e * 64 + 32 + l32] : 0.0f;
-          uint8_t* blk = a.hq + (size_t)(c0 + e - call.e0) * nb * 36 + (size_t)j * 36;
-          swiglu_q81_lanes(gv, uv, l32, live, blk, nullptr);
-        }
-      }
-      __syncthreads();
+    }
+    if (kk + NS < nit) {
+      MOE_WAIT_LGKM0;   // this wave's LDS reads of the slot have returned
+      issue_item(kk + NS, slot);
+      ++issued;
     }
   }
 }
 
 // ------------------------------------------------------------------ down + scatter kernel ---
 
+enum DnMode : int { DN_DESC = 0, DN_PLAN = 1 };
+
 struct DnArgs {
   LayerArgs A;
   PlanArgs P;
   Geom G;
   Stream S;
-  const uint8_t* hq;   // q8_1 rows of h
-  int hq_abs;          // 1: rows by absolute entry; 0: by entry - grp_start[0]
+  const uint8_t* desc;  // DN_DESC: the call's descriptor
+  const float* h;       // DN_DESC: h rows (relative entry), stride n_ff
+  const uint8_t* hq;    // DN_PLAN: q8_1 rows by absolute entry
   float* Y;
   int n_rows, ldy;
-  int n_tokens;        // >= 0: also skip entries whose token is out of range
+  int lds_ring, lds_act;
 };
 
-__host__ __device__ inline int dn_smem_bytes(const Stream& S, int rp) {
-  return kWaves * S.NS * S.M * 1024 + kMaxEnt * rp * 4 + 4096 + kMaxEnt * 12 + 256 +
-         (MOE_MAX_GROUPS + 2) * 4 + MOE_MAX_GROUPS * 8;
+constexpr int kDnFixed = 4096 + kDescBytes + 4 * 3 * kMaxEnt + 256;
+
+__host__ __device__ inline int dn_smem_bytes(int lds_ring, int lds_act, int rp) {
+  return lds_ring + lds_act + kMaxEnt * rp * 4 + kDnFixed;
 }
 
-// One work item: rows [rp t, rp t + rp) of Y. Wave w takes the groups g = w, w + 4, ... in order;
-// a chunk is a group's down rows of the tile plus the q8_1 rows of (up to 4 of) its entries.
-// Per-entry rows of o stay in LDS; at the end every destination row is summed in ascending entry
-// order: Y[d][r] = ((Y[d][r] + w_a o_a[r]) + w_b o_b[r]) + ...
-template <int FMT>
-__global__ __launch_bounds__(kThreads) void k_down(DnArgs a) {
+// One work item: rows [rp t, rp t + rp) of Y. Wave w takes the groups g = w, w + 8, ... in
+// order; a chunk is a group's down rows of the tile. Per-entry rows of o stay in LDS; at the end
+// every destination row is summed in ascending entry order: Y[d][r] = ((Y[d][r] + w_a o_a[r]) +
+// w_b o_b[r]) + ...
+template <int FMT, int MODE>
+__global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const Geom& G = a.G;
+  const int tid = threadIdx.x, wave = tid >> 6;
   MOE_LDS uint8_t* ring = (MOE_LDS uint8_t*)smem;
-  MOE_LDS float* ores = (MOE_LDS float*)(ring + kWaves * a.S.NS * a.S.M * 1024);   // [kMaxEnt][rp]
+  const int U = G.U;
+  MOE_LDS uint8_t* actp = ring + a.lds_ring;
+  MOE_LDS float* ores = (MOE_LDS float*)(actp + a.lds_act);   // [kMaxEnt][rp]
   MOE_LDS uint32_t* g2 = (MOE_LDS uint32_t*)(ores + kMaxEnt * G.rp);
   MOE_LDS uint32_t* g3 = g2 + 512;
-  MOE_LDS int* mdst = (MOE_LDS int*)(g3 + 512);          // [kMaxEnt] dst (-1 = skip)
-  MOE_LDS int* mown = mdst + kMaxEnt;                     // [kMaxEnt] owner flag
-  MOE_LDS float* mw = (MOE_LDS float*)(mown + kMaxEnt);   // [kMaxEnt]
-  MOE_LDS int* misc = (MOE_LDS int*)(mw + kMaxEnt);       // [64]
-  MOE_LDS int* gs = misc + 64;                            // [MOE_MAX_GROUPS + 1] group starts
-  // [MOE_MAX_GROUPS] down pointers, 8-byte aligned after one pad int
-  MOE_LDS uint64_t* gw = (MOE_LDS uint64_t*)(gs + MOE_MAX_GROUPS + 2);
+  MOE_LDS int* dsc = (MOE_LDS int*)(g3 + 512);                 // the descriptor, as in memory
+  MOE_LDS uint64_t* dptr = (MOE_LDS uint64_t*)((MOE_LDS uint8_t*)dsc + kDescPtrByte);
+  MOE_LDS int* mdst = (MOE_LDS int*)((MOE_LDS uint8_t*)dsc + kDescBytes);   // [kMaxEnt] dst or -1
+  MOE_LDS int* mown = mdst + kMaxEnt;                        // [kMaxEnt] first live entry of its dst
+  MOE_LDS float* mw = (MOE_LDS float*)(mown + kMaxEnt);      // [kMaxEnt]
+  MOE_LDS int* misc = (MOE_LDS int*)(mw + kMaxEnt);          // [64]
+
+  // ---- 1. tables and the call (descriptor: one read; caller's plan: validated, two reads)
+  uint32_t t_nl4[4] = {0u, 0u, 0u, 0u};
+  if (a.A.nl4) {
+    const uint32_t* t = (const uint32_t*)a.A.nl4;
+    t_nl4[0] = t[0];
+    t_nl4[1] = t[1];
+    t_nl4[2] = t[2];
+    t_nl4[3] = t[3];
+  }
+  uint32_t t_cb = 0;
+  if constexpr (FMT == CB2 || FMT == CB3) {
+    const uint32_t* src = (const uint32_t*)(FMT == CB2 ? a.A.cb2 : a.A.cb3);
+    t_cb = src[tid];
+  }
+  if constexpr (MODE == DN_DESC) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (tid < kDescBytes / 16) v = ((const u32x4*)a.desc)[tid];
+    if (tid < kDescBytes / 16) ((MOE_LDS u32x4*)dsc)[tid] = v;
+  } else {
+    // raw group table: starts into the descriptor's start slots, experts into its dst slots
+    int r_ng = 0, r_gs = 0, r_ge = 0;
+    if (tid == 0) r_ng = *a.P.n_groups;
+    if (tid <= a.P.cap_groups) r_gs = a.P.grp_start[tid];
+    if (tid < a.P.cap_groups) r_ge = a.P.grp_expert[tid];
+    if (tid == 0) misc[3] = r_ng;
+    if (tid <= a.P.cap_groups) dsc[kDescGs + tid] = r_gs;
+    if (tid < a.P.cap_groups) dsc[kDescDst + tid] = r_ge;
+  }
   Tables tb;
-  load_tables(a.A, FMT == CB2, FMT == CB3, g2, g3, tb);
-  const Call call = read_call(a.P, misc);
-  if (call.ng == 0) return;
-  const int n = call.e1 - call.e0;
-  // the call's group table (starts and down pointers; 0 = skipped group), then entry metadata:
-  // destination (or -1), weight, owner = first live entry naming its dst
-  {
-    const int i = threadIdx.x;
-    if (i <= call.ng) gs[i] = a.P.grp_start[i];
-    if (i < call.ng) {
-      const int e = a.P.grp_expert[i];
-      uint64_t w = 0;
-      if (e < 0 || e >= a.A.n_experts) {
-        set_err(a.P.err, MOE_ERR_EXPERT);
-      } else {
-        w = (uint64_t)(uintptr_t)a.A.down[e];
-        if (w & 1) {
-          set_err(a.P.err, MOE_ERR_ALIGN);
-          w = 0;
+  tb.nl4[0] = t_nl4[0];
+  tb.nl4[1] = t_nl4[1];
+  tb.nl4[2] = t_nl4[2];
+  tb.nl4[3] = t_nl4[3];
+  tb.cb2 = g2;
+  tb.cb3 = g3;
+  if constexpr (FMT == CB2 || FMT == CB3) (FMT == CB2 ? g2 : g3)[tid] = t_cb;
+  __syncthreads();
+  if constexpr (MODE == DN_PLAN) {
+    validate_groups(dsc + kDescGs, misc[3], a.P, misc);
+    __syncthreads();
+    const int ng = uni(misc[0]), e0 = uni(misc[1]), n = uni(misc[2]) - e0;
+    int r_dst = 0;
+    float r_w = 0.0f;
+    uint64_t vd = 0;
+    int e = -1;
+    if (tid < n) {
+      r_dst = a.P.ent_dst[e0 + tid];
+      r_w = a.P.ent_w[e0 + tid];
+    }
+    if (tid < ng) {
+      e = dsc[kDescDst + tid];
+      if (e >= 0 && e < a.A.n_experts) vd = (uint64_t)(uintptr_t)a.A.down[e];
+    }
+    int gs = 0;
+    if (tid <= ng) gs = dsc[kDescGs + tid] - e0;
+    __syncthreads();
+    if (tid == 0) {
+      dsc[kDescNg] = ng;
+      dsc[kDescE0] = e0;
+      dsc[kDescN] = n;
+    }
+    if (tid <= ng) dsc[kDescGs + tid] = gs;
+    if (tid < ng) {
+      const bool e_ok = e >= 0 && e < a.A.n_experts;
+      if (!e_ok) set_err(a.P.err, MOE_ERR_EXPERT);
+      dptr[tid] = (e_ok && ptr_ok(vd, a.P.err)) ? vd : 0;
+    }
+    if (tid < n) {
+      dsc[kDescDst + tid] = r_dst;
+      ((MOE_LDS float*)dsc)[kDescW + tid] = r_w;
+      dsc[kDescLive + tid] = 1;
+    }
+    __syncthreads();
+  }
+  const int ng = uni(dsc[kDescNg]), e0 = uni(dsc[kDescE0]), n = uni(dsc[kDescN]);
+  if (ng == 0) return;
+  // entry metadata: destination (or -1), weight, owner = first live entry naming its dst
+  if (tid < n) {
+    int g = 0;
+    while (g + 1 < ng && dsc[kDescGs + g + 1] <= tid) ++g;
+    const int d = dsc[kDescDst + tid];
+    int live = dsc[kDescLive + tid] && dptr[g] != 0;
+    if (live && (d < 0 || d >= a.n_rows)) {
+      set_err(a.P.err, MOE_ERR_DST);
+      live = 0;
+    }
+    mdst[tid] = live ? d : -1;
+    mw[tid] = ((MOE_LDS float*)dsc)[kDescW + tid];
+  }
+  __syncthreads();
+  if (tid < n) {
+    const int d = mdst[tid];
+    int owner = d >= 0;
+    for (int q = 0; q < tid && owner; ++q) owner = mdst[q] != d;
+    mown[tid] = owner;
+  }
+
+  // ---- 2. h rows: their loads first, then the first chunks of the stream, then the h rows to LDS
+  const ActSplit act = act_layout(actp, n, U);
+  const int ntiles = (a.A.n_embd + G.rp - 1) / G.rp;
+  const int ntw = (int)blockIdx.x < ntiles ? (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+  const int cpt = wave < ng ? (ng - wave + kDnWaves - 1) / kDnWaves : 0;   // this wave's groups
+  const int nch = ntw * cpt;
+  const int M = a.S.M, NS = a.S.NS;
+  MOE_LDS uint8_t* myring = ring + wave * NS * M * 1024;
+  auto issue = [&](int kc, MOE_LDS uint8_t* slot) {
+    const int kt = kc / cpt, q = kc - kt * cpt;
+    const int t = (int)blockIdx.x + kt * (int)gridDim.x, g = wave + q * kDnWaves;
+    const int r0 = t * G.rp, nr = min(G.rp, a.A.n_embd - r0);
+    const uint64_t w = uni64(dptr[g]);
+    if (w)
+      issue_chunk(slot, M, (const uint8_t*)(uintptr_t)(w + (uint64_t)r0 * G.rb), (uint32_t)(nr * G.rb),
+                  nullptr, 0, 0);
+    else   // a skipped group keeps the count of loads: one 16-byte chunk every lane reloads
+      issue_chunk(slot, M, (const uint8_t*)a.P.err, 1, nullptr, 0, 0);
+  };
+  const int pre = min(NS, nch);
+  auto mid = [&](int) {
+    for (int kc = 0; kc < pre; ++kc) issue(kc, myring + kc * M * 1024);
+    wait_vm(pre * M);   // the h loads, older than every chunk, have landed
+  };
+  if constexpr (MODE == DN_DESC)
+    act_stage_f<kDnThreads, 16>(a.h, a.A.n_ff, n * U, U, act, mid);
+  else
+    act_stage_q<kDnThreads, 16>(a.hq + (size_t)e0 * U * 36, n * U, act, mid);
+  int issued = pre;
+  __syncthreads();
+
+  // ---- 3. tiles
+  int kc = 0;
+  for (int kt = 0; kt < ntw; ++kt) {
+    const int t = (int)blockIdx.x + kt * (int)gridDim.x;
+    const int r0 = t * G.rp, nr = min(G.rp, a.A.n_embd - r0);
+    for (int q = 0; q < cpt; ++q, ++kc) {
+      const int g = wave + q * kDnWaves;
+      wait_vm((issued - 1 - kc) * M);
+      MOE_LDS uint8_t* slot = myring + (kc % NS) * M * 1024;
+      const uint64_t w = uni64(dptr[g]);
+      if (w) {
+        const uint32_t ra = (uint32_t)(slot - ring) + (uint32_t)((w + (uint64_t)r0 * G.rb) & 15);
+        const int a0 = uni(dsc[kDescGs + g]), a1 = uni(dsc[kDescGs + g + 1]);
+        for (int c0 = a0; c0 < a1; c0 += kSlots) {
+          const int ne = min(kSlots, a1 - c0);
+          int sidx[kSlots];
+#pragma unroll
+          for (int e = 0; e < kSlots; ++e) sidx[e] = e < ne ? c0 + e : 0;
+          dot_pass<FMT>((const MOE_LDS uint32_t*)ring, ra, ra, nr, nr, G, tb, act, sidx, ne,
+                        [&](int i, int e, float v) { ores[(c0 + e) * G.rp + i] = v; });
         }
       }
-      gw[i] = w;
-    }
-    __syncthreads();
-    if (i < n) {
-      const int ab = call.e0 + i;
-      int gg = 0;
-      while (gg + 1 < call.ng && gs[gg + 1] <= ab) ++gg;
-      int dst = a.P.ent_dst[ab];
-      if (dst < 0 || dst >= a.n_rows) {
-        set_err(a.P.err, MOE_ERR_DST);
-        dst = -1;
-      }
-      if (gw[gg] == 0) dst = -1;
-      if (a.n_tokens >= 0) {
-        const int src = a.P.ent_src[ab];
-        if (src < 0 || src >= a.n_tokens) dst = -1;
-      }
-      mdst[i] = dst;
-      mw[i] = a.P.ent_w[ab];
-    }
-    __syncthreads();
-    if (i < n) {
-      const int d = mdst[i];
-      int owner = d >= 0;
-      for (int q = 0; q < i && owner; ++q) owner = mdst[q] != d;
-      mown[i] = owner;
-    }
-    __syncthreads();
-  }
-  const int wave = threadIdx.x >> 6;
-  MOE_LDS uint8_t* myring = ring + wave * a.S.NS * a.S.M * 1024;
-  const int hstride = G.U * 36;   // bytes per q8_1 row of h
-  const int ntiles = (a.A.n_embd + G.rp - 1) / G.rp;
-  // this wave's chunks: (group g = wave + 4 q, entries [c0, c0 + 4)), in ascending order
-  int nch = 0;
-  for (int g = wave; g < call.ng; g += kWaves) {
-    const int a0 = uni(gs[g]), a1 = uni(gs[g + 1]);
-    nch += (a1 - a0 + kMaxSlots - 1) / kMaxSlots;
-  }
-  struct Ck {
-    int c0, ne;
-    const uint8_t* w;
-  };
-  auto chunk_at = [&](int kc) -> Ck {
-    int k = 0;
-    for (int g = wave; g < call.ng; g += kWaves) {
-      const int a0 = uni(gs[g]), a1 = uni(gs[g + 1]);
-      const int np = (a1 - a0 + kMaxSlots - 1) / kMaxSlots;
-      if (kc < k + np) {
-        Ck c;
-        c.c0 = a0 + (kc - k) * kMaxSlots;
-        c.ne = min(kMaxSlots, a1 - c.c0);
-        c.w = uni_ptr((const uint8_t*)(uintptr_t)gw[g]);
-        return c;
-      }
-      k += np;
-    }
-    return Ck{0, 0, nullptr};
-  };
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int r0 = t * G.rp;
-    const int nr = min(G.rp, a.A.n_embd - r0);
-    const uint32_t nw = (uint32_t)(nr * G.rb);
-    auto hsrc_of = [&](const Ck& c) {
-      return a.hq + (size_t)(a.hq_abs ? c.c0 : c.c0 - call.e0) * hstride;
-    };
-    auto issue = [&](const Ck& c, MOE_LDS uint8_t* slot) {
-      const uint8_t* hsrc = hsrc_of(c);
-      if (c.w) {
-        const uint8_t* wsrc = c.w + (size_t)r0 * G.rb;
-        const uint32_t cb = (((uint32_t)((uintptr_t)wsrc & 15) + nw + 15) >> 4) + 1;
-        issue_chunk(slot, a.S.M, wsrc, nw, hsrc, (uint32_t)(c.ne * hstride), cb);
-      } else {
-        issue_chunk(slot, a.S.M, hsrc, (uint32_t)(c.ne * hstride), nullptr, 0, 0);
-      }
-    };
-    __builtin_amdgcn_s_waitcnt(MOE_VM(0));
-    const int pre = min(a.S.NS, nch);
-    for (int kc = 0; kc < pre; ++kc) issue(chunk_at(kc), myring + kc * a.S.M * 1024);
-    int issued = pre;
-    for (int kc = 0; kc < nch; ++kc) {
-      const Ck c = chunk_at(kc);
-      wait_vm((issued - 1 - kc) * a.S.M);
-      MOE_LDS uint8_t* slot = myring + (kc % a.S.NS) * a.S.M * 1024;
-      if (c.w) {
-        const uint32_t sb = (uint32_t)(slot - ring);
-        const uint8_t* wsrc = c.w + (size_t)r0 * G.rb;
-        const uint32_t cb = (((uint32_t)((uintptr_t)wsrc & 15) + nw + 15) >> 4) + 1;
-        const ActRaw act{(const MOE_LDS uint32_t*)ring, sb + 16 * cb + (uint32_t)((uintptr_t)hsrc_of(c) & 15),
-                         (uint32_t)hstride};
-        const int rel = c.c0 - call.e0;
-        dot_pass<FMT>((const MOE_LDS uint32_t*)ring, sb + (uint32_t)((uintptr_t)wsrc & 15), nr, G, tb,
-                      act, c.ne, [&](int i, int e, float v) { ores[(rel + e) * G.rp + i] = v; });
-      }
-      if (kc + a.S.NS < nch) {
+      if (kc + NS < nch) {
         MOE_WAIT_LGKM0;
-        issue(chunk_at(kc + a.S.NS), slot);
+        issue(kc + NS, slot);
         ++issued;
       }
     }
     __syncthreads();
     // scatter: one thread per (owner entry, row)
-    for (int idx = threadIdx.x; idx < n * nr; idx += kThreads) {
+    for (int idx = tid; idx < n * nr; idx += kDnThreads) {
       const int i = idx / nr, m = idx - i * nr;
       if (!mown[i]) continue;
       const int d = mdst[i];
@@ -981,52 +1258,65 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
   }
 }
 
-// One workgroup per token.
-__global__ __launch_bounds__(kThreads) void k_route(const float* __restrict__ logits, int E, int k,
-                                                    int32_t* __restrict__ ids, float* __restrict__ w) {
-  __shared__ float s_lg[1024 + 64];
+// One wave per token.
+__global__ __launch_bounds__(64) void k_route(const float* __restrict__ logits, int E, int k,
+                                              int32_t* __restrict__ ids, float* __restrict__ w) {
+  __shared__ float s_lg[1024];
   __shared__ int s_ids[32];
   __shared__ float s_w[32];
+  __shared__ uint32_t s_scr[96];
   const int t = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += kThreads) s_lg[e] = logits[(size_t)t * E + e];
-  __syncthreads();
-  route_token_wg((MOE_LDS float*)s_lg, E, k, (MOE_LDS int*)s_ids, (MOE_LDS float*)s_w,
-                 (MOE_LDS float*)(s_lg + 1024));
+  issue_logits(logits + (size_t)t * E, E, (MOE_LDS float*)s_lg);
+  __builtin_amdgcn_s_waitcnt(MOE_VM(0));
+  route_wave((MOE_LDS float*)s_lg, E, k, (MOE_LDS int*)s_ids, (MOE_LDS float*)s_w, (MOE_LDS uint32_t*)s_scr);
   if ((int)threadIdx.x < k) {
     ids[(size_t)t * k + threadIdx.x] = s_ids[threadIdx.x];
     w[(size_t)t * k + threadIdx.x] = s_w[threadIdx.x];
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_plan(const int32_t* __restrict__ ids, const float* __restrict__ w,
-                                                   const int32_t* __restrict__ dst_of_token, int T, int k,
-                                                   int E, int entry_base, PlanArgs P) {
-  __shared__ int s_plan[kPlanLdsInts];
-  const PlanLds p = plan_lds((MOE_LDS int*)s_plan);
+// One wave: group the T * k routed entries and write the plan.
+__global__ __launch_bounds__(64) void k_plan(const int32_t* __restrict__ ids, const float* __restrict__ w,
+                                             const int32_t* __restrict__ dst_of_token, int T, int k,
+                                             int E, int entry_base, PlanArgs P) {
+  __shared__ int s_plan[kPlanLInts];
+  const PlanL p = plan_l((MOE_LDS int*)s_plan);
   const int n = T * k;
-  if ((int)threadIdx.x < n) {
-    p.ids[threadIdx.x] = ids[threadIdx.x];
-    p.w[threadIdx.x] = w[threadIdx.x];
+  const int i = threadIdx.x;
+  if (i < n) {
+    p.rid[i] = ids[i];
+    p.rw[i] = w[i];
   }
+  if (i < T) p.dtok[i] = dst_of_token ? dst_of_token[i] : i;
   __syncthreads();
-  group_entries_wg(p, T, k, E, dst_of_token, entry_base, P.err);
-  publish_plan(p, P, entry_base);
+  group_wave(p, n, k, E, entry_base, P.err);
+  __syncthreads();
+  publish_plan<64>(p, P);
 }
 
 // Over (entry, h block) of the call: two blocks per wave.
 __global__ __launch_bounds__(kThreads) void k_swiglu(PlanArgs P, const float* __restrict__ g,
                                                      const float* __restrict__ u, int n_ff, int ld,
                                                      float* h, uint8_t* hq) {
-  __shared__ int s_misc[64];
-  const Call call = read_call(P, (MOE_LDS int*)s_misc);
+  __shared__ int s_gs[kMaxGrp + 1];
+  __shared__ int s_misc[4];
+  int r_ng = 0, r_gs = 0;
+  if ((int)threadIdx.x == 0) r_ng = *P.n_groups;
+  if ((int)threadIdx.x <= P.cap_groups) r_gs = P.grp_start[threadIdx.x];
+  if ((int)threadIdx.x == 0) s_misc[3] = r_ng;
+  if ((int)threadIdx.x <= P.cap_groups) s_gs[threadIdx.x] = r_gs;
+  __syncthreads();
+  validate_groups((MOE_LDS int*)s_gs, s_misc[3], P, (MOE_LDS int*)s_misc);
+  __syncthreads();
+  const int e0 = uni(s_misc[1]), e1 = uni(s_misc[2]);
   const int nb = n_ff / 32;
-  const int total = (call.e1 - call.e0) * nb;
+  const int total = (e1 - e0) * nb;
   const int half = threadIdx.x >> 5, l32 = threadIdx.x & 31;
   // every wave runs the loop the same number of times (shuffles need both halves present)
   for (int base = blockIdx.x * 8; base < total; base += gridDim.x * 8) {
     const int it = base + half;
     const bool live = it < total;
-    const int a = live ? call.e0 + it / nb : call.e0;
+    const int a = live ? e0 + it / nb : e0;
     const int b = live ? it % nb : 0;
     const float gv = live ? g[(size_t)a * ld + 32 * b + l32] : 0.0f;
     const float uv = live ? u[(size_t)a * ld + 32 * b + l32] : 0.0f;
@@ -1057,21 +1347,23 @@ int ilog2(int v) {
   return l;
 }
 
-// Lanes per row from the shape alone: among L = 4..64 whose wave pass (64 / L rows) keeps a chunk
-// within kChunkCap bytes (and, for gate/up, at most the 8 rows a wave owns), the best lane
-// utilisation U / (L ceil(U / L)); ties go to the smaller L.
+// Lanes per row from the shape alone: among the allowed L whose wave pass (64 / L rows) keeps a
+// chunk within kChunkCap bytes (the widest L always qualifies), the best lane utilisation
+// U / (L ceil(U / L)). Gate/up: L <= 32 (a pass holds gate and up rows of rp / 2 h rows), ties
+// to the smaller L (longer items); down: ties to the larger L (more, smaller row tiles).
 Geom make_geom(int fmt, int ncols, bool gate_up) {
   Geom G{};
   G.U = ncols / 32;
   G.rb = ncols / block_weights(fmt) * block_bytes(fmt);
-  int bestL = 64;
+  const int Lmax = gate_up ? 32 : 64;
+  int bestL = Lmax;
   double best = -1.0;
-  for (int L = 4; L <= 64; L <<= 1) {
+  for (int L = 4; L <= Lmax; L <<= 1) {
     const int rp = 64 / L;
-    if (gate_up && rp > 8) continue;
-    if (rp * G.rb > kChunkCap && L < 64) continue;
+    if (rp * G.rb > kChunkCap && L < Lmax) continue;
     const double util = (double)G.U / (double)(L * ((G.U + L - 1) / L));
-    if (util > best + 1e-9) {
+    const bool better = gate_up ? util > best + 1e-9 : util >= best - 1e-9;
+    if (better) {
       best = util;
       bestL = L;
     }
@@ -1083,38 +1375,38 @@ Geom make_geom(int fmt, int ncols, bool gate_up) {
   return G;
 }
 
-// Per-wave stream: a slot holds the largest chunk (+ alignment slack) in whole KB; as many slots
-// (up to 4) as fit in `budget` bytes per wave, and never more outstanding loads than vmcnt counts.
-Stream make_stream(int chunk_bytes, int budget) {
+// Slot size in KB: the chunk plus alignment slack (each span's head offset and 16-byte tail, the
+// 16-byte gap between spans, and the dwords past the end an unaligned read may touch). Two slots
+// per wave (the next item streams in while this one computes) where LDS allows, else one.
+Stream gu_stream(const Geom& G, int ns) {
   Stream S;
-  S.M = (chunk_bytes + 32 + 1023) / 1024;
-  S.NS = std::max(1, std::min(4, budget / (S.M * 1024)));
-  while (S.NS > 1 && S.M * (S.NS - 1) > 63) --S.NS;
+  S.M = (G.rp * G.rb + 96 + 1023) / 1024;
+  S.NS = ns;
+  return S;
+}
+Stream dn_stream(const Geom& G, int ns) {
+  Stream S;
+  S.M = (G.rp * G.rb + 48 + 1023) / 1024;
+  S.NS = ns;
   return S;
 }
 
-Stream gu_stream(const Geom& G) { return make_stream(G.rp * G.rb, 24 * 1024); }
-Stream dn_stream(const Geom& G) {
-  // weights + one 16-byte gap + the q8_1 rows of up to 4 entries, each span 16-byte aligned
-  return make_stream(G.rp * G.rb + kMaxSlots * G.U * 36 + 96, 24 * 1024);
-}
-
 struct WsLayout {
-  size_t g, u, hq, total;
+  size_t g, u, h, total;
 };
 
 size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 WsLayout ws_layout(const moe_layer* L, const moe_plan* P) {
   WsLayout w{};
-  size_t p = 256;
+  size_t p = kDescReserve;
   const size_t ce = (size_t)P->cap_entries;
   w.g = p;
   p += al256(ce * L->n_ff * 4);
   w.u = p;
   p += al256(ce * L->n_ff * 4);
-  w.hq = p;
-  p += al256(ce * (L->n_ff / 32) * 36);
+  w.h = p;
+  p += al256(ce * L->n_ff * 4);
   w.total = p;
   return w;
 }
@@ -1151,6 +1443,28 @@ PlanArgs plan_args(const moe_plan* P) {
                   P->ent_src, P->ent_dst, P->ent_w, P->err};
 }
 
+int num_cus() {
+  static int n = 0;
+  if (!n) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+// Workgroups for `items` work items: every item gets its own workgroup up to what the CUs hold
+// at once (LDS-limited, 8 per CU at most); beyond that workgroups take several items.
+int grid_for(int items, int lds_bytes, int grid_limit) {
+  const int per_cu = std::max(1, std::min(8, kLdsMax / std::max(lds_bytes, 1)));
+  int grid = std::min(items, num_cus() * per_cu);
+  if (grid_limit) grid = std::min(grid, grid_limit);
+  return std::max(1, grid);
+}
+
 template <class K>
 hipError_t allow_smem(K kern, int bytes) {
   if (bytes <= 65536) return hipSuccess;
@@ -1161,7 +1475,7 @@ hipError_t launch_gu(int fmt, int mode, const GuArgs& ga, int grid, int bytes, h
   auto go = [&](auto kern) -> hipError_t {
     hipError_t e = allow_smem(kern, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, st, ga);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGuThreads), bytes, st, ga);
     return hipGetLastError();
   };
 #define MOE_GU(F)                                              \
@@ -1179,73 +1493,121 @@ hipError_t launch_gu(int fmt, int mode, const GuArgs& ga, int grid, int bytes, h
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_dn(int fmt, const DnArgs& da, int grid, int bytes, hipStream_t st) {
+hipError_t launch_dn(int fmt, int mode, const DnArgs& da, int grid, int bytes, hipStream_t st) {
   auto go = [&](auto kern) -> hipError_t {
     hipError_t e = allow_smem(kern, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), bytes, st, da);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kDnThreads), bytes, st, da);
     return hipGetLastError();
   };
+#define MOE_DN(F) \
+  case F:         \
+    return mode == DN_DESC ? go(k_down<F, DN_DESC>) : go(k_down<F, DN_PLAN>);
   switch (fmt) {
-    case Q8_0: return go(k_down<Q8_0>);
-    case NL4: return go(k_down<NL4>);
-    case CB2: return go(k_down<CB2>);
-    case CB3: return go(k_down<CB3>);
+    MOE_DN(Q8_0)
+    MOE_DN(NL4)
+    MOE_DN(CB2)
+    MOE_DN(CB3)
   }
+#undef MOE_DN
   return hipErrorInvalidValue;
 }
 
-// The gate/up kernel of `mode` over one grid sized for the plan's capacity.
-int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, const void* act,
-                int n_tokens, float* g, float* u, int ld, uint8_t* hq, const float* logits, int T,
-                int k, const int32_t* dst_of_token, int entry_base, int grid_limit) {
+// LDS the gate/up kernel needs for n_tokens activation rows, its stream and how many of its waves
+// stream (all 16 when the slots fit, fewer for long rows), or -1 if it does not fit.
+int gu_lds(const moe_layer* L, int n_tokens, bool routed, Stream* S, int* sw, int* ring, int* actb) {
   const Geom G = make_geom(L->fmt_gate_up, L->n_embd, true);
-  const Stream S = gu_stream(G);
+  *actb = act_bytes(n_tokens, G.U);
+  if (*actb > kGuActMax) return -1;
+  // the routed prologue stages kRouteWaves tokens' logits in the ring before it streams
+  const int lg = routed ? kRouteWaves * logits_pad(L->n_experts) * 4 : 0;
+  const int avail = kLdsMax - gu_smem_bytes(0, *actb);
+  for (int ns = 2; ns >= 1; --ns) {
+    *S = gu_stream(G, ns);
+    const int per_wave = S->NS * S->M * 1024;
+    *sw = std::min(kGuWaves, avail / per_wave);
+    if (*sw >= (ns == 2 ? kGuWaves : 1)) {
+      *ring = std::max(*sw * per_wave, lg);
+      const int b = gu_smem_bytes(*ring, *actb);
+      if (b <= kLdsMax) return b;
+    }
+  }
+  return -1;
+}
+
+int dn_lds(const moe_layer* L, const moe_plan* P, Stream* S, int* ring, int* actb) {
+  const Geom G = make_geom(L->fmt_down, L->n_ff, false);
+  *actb = act_bytes(P->cap_entries, G.U);
+  if (*actb > kDnActMax) return -1;
+  for (int ns = 2; ns >= 1; --ns) {
+    *S = dn_stream(G, ns);
+    *ring = kDnWaves * S->NS * S->M * 1024;
+    const int b = dn_smem_bytes(*ring, *actb, G.rp);
+    if (b <= kLdsMax) return b;
+  }
+  return -1;
+}
+
+// The gate/up kernel of `mode`.
+int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, const void* act,
+                int n_tokens, float* g, float* u, int ld, float* h, uint8_t* desc, const float* logits,
+                int T, int k, const int32_t* dst_of_token, int entry_base, int grid_limit) {
+  const Geom G = make_geom(L->fmt_gate_up, L->n_embd, true);
+  int ring = 0, actb = 0, sw = 0;
+  Stream S{};
+  const int bytes = gu_lds(L, n_tokens, mode == GU_ROUTED, &S, &sw, &ring, &actb);
+  if (bytes < 0) return MOE_E_SHAPE;
   GuArgs ga{};
   ga.A = layer_args(L);
   ga.P = plan_args(P);
   ga.G = G;
   ga.S = S;
-  ga.umax = G.U;
   ga.n_tokens = n_tokens;
   ga.xq = mode == GU_COMPOSED ? (const uint8_t*)act : nullptr;
   ga.x = mode == GU_COMPOSED ? nullptr : (const float*)act;
   ga.g = g;
   ga.u = u;
   ga.ld = ld;
-  ga.hq = hq;
+  ga.h = h;
+  ga.desc = desc;
   ga.logits = logits;
   ga.T = T;
   ga.E = L->n_experts;
   ga.k = k;
   ga.dst_of_token = dst_of_token;
   ga.entry_base = entry_base;
-  const int bytes = gu_smem_bytes(S, G.U, mode == GU_ROUTED ? L->n_experts : 0);
-  const int items = P->cap_groups * (L->n_ff / 32);
-  const int grid = std::max(1, grid_limit ? std::min(grid_limit, items) : items);
+  ga.lds_ring = ring;
+  ga.lds_act = actb;
+  ga.sw = sw;
+  const int wave_items = P->cap_groups * (L->n_ff / (G.rp / 2));
+  const int grid = grid_for((wave_items + sw - 1) / sw, bytes, grid_limit);
   const hipError_t e = launch_gu(L->fmt_gate_up, mode, ga, grid, bytes, st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "gate/up kernel");
 }
 
-int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, const uint8_t* hq, int hq_abs,
-             float* Y, int n_rows, int ldy, int n_tokens, int grid_limit) {
+int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, const uint8_t* desc,
+             const float* h, const uint8_t* hq, float* Y, int n_rows, int ldy, int grid_limit) {
   const Geom G = make_geom(L->fmt_down, L->n_ff, false);
-  const Stream S = dn_stream(G);
+  int ring = 0, actb = 0;
+  Stream S{};
+  const int bytes = dn_lds(L, P, &S, &ring, &actb);
+  if (bytes < 0) return MOE_E_SHAPE;
   DnArgs da{};
   da.A = layer_args(L);
   da.P = plan_args(P);
   da.G = G;
   da.S = S;
+  da.desc = desc;
+  da.h = h;
   da.hq = hq;
-  da.hq_abs = hq_abs;
   da.Y = Y;
   da.n_rows = n_rows;
   da.ldy = ldy;
-  da.n_tokens = n_tokens;
-  const int bytes = dn_smem_bytes(S, G.rp);
+  da.lds_ring = ring;
+  da.lds_act = actb;
   const int tiles = (L->n_embd + G.rp - 1) / G.rp;
-  const int grid = std::max(1, grid_limit ? std::min(grid_limit, tiles) : tiles);
-  const hipError_t e = launch_dn(L->fmt_down, da, grid, bytes, st);
+  const int grid = grid_for(tiles, bytes, grid_limit);
+  const hipError_t e = launch_dn(L->fmt_down, mode, da, grid, bytes, st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "down kernel");
 }
 
@@ -1287,7 +1649,7 @@ int moe_route_topk(void* stream, const float* logits, int T, int E, int k, int32
   if (!logits || !ids || !w || T < 0 || E < 1 || E > 1024 || k < 1 || k > E || k > 32)
     return MOE_E_ARG;
   if (T == 0) return MOE_OK;
-  hipLaunchKernelGGL(k_route, dim3(T), dim3(kThreads), 0, (hipStream_t)stream, logits, E, k, ids, w);
+  hipLaunchKernelGGL(k_route, dim3(T), dim3(64), 0, (hipStream_t)stream, logits, E, k, ids, w);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route_topk");
 }
@@ -1298,8 +1660,8 @@ int moe_build_plan(void* stream, const int32_t* ids, const float* w, const int32
   if (rc) return rc;
   if (!ids || !w || T < 0 || k < 1 || E < 1 || entry_base < 0) return MOE_E_ARG;
   if (T * k > P->cap_entries || T * k > P->cap_groups || T * k > 64) return MOE_E_ARG;
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kThreads), 0, (hipStream_t)stream, ids, w, dst_of_token, T, k,
-                     E, entry_base, plan_args(P));
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(64), 0, (hipStream_t)stream, ids, w, dst_of_token, T, k, E,
+                     entry_base, plan_args(P));
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_build_plan");
 }
@@ -1311,7 +1673,7 @@ int moe_gate_up(void* stream, const moe_layer* L, const moe_plan* P, const void*
   if ((rc = check_plan(P))) return rc;
   if (!xq || !g || !u || ld < L->n_ff || n_tokens < 0 || grid_limit < 0) return MOE_E_ARG;
   if ((uintptr_t)xq & 3) return MOE_E_ARG;
-  return run_gate_up((hipStream_t)stream, L, P, GU_COMPOSED, xq, n_tokens, g, u, ld, nullptr,
+  return run_gate_up((hipStream_t)stream, L, P, GU_COMPOSED, xq, n_tokens, g, u, ld, nullptr, nullptr,
                      nullptr, 0, 0, nullptr, 0, grid_limit);
 }
 
@@ -1342,7 +1704,7 @@ int moe_workspace_layout(const moe_layer* L, const moe_plan* P, size_t off[3]) {
   const WsLayout w = ws_layout(L, P);
   off[0] = w.g;
   off[1] = w.u;
-  off[2] = w.hq;
+  off[2] = w.h;
   return MOE_OK;
 }
 
@@ -1353,43 +1715,62 @@ int moe_down_scatter(void* stream, const moe_layer* L, const moe_plan* P, const 
   if ((rc = check_plan(P))) return rc;
   if (!hq || !Y || n_rows < 0 || ldy < L->n_embd || grid_limit < 0) return MOE_E_ARG;
   if ((uintptr_t)hq & 3) return MOE_E_ARG;
-  return run_down((hipStream_t)stream, L, P, (const uint8_t*)hq, 1, Y, n_rows, ldy, -1, grid_limit);
+  return run_down((hipStream_t)stream, L, P, DN_PLAN, nullptr, nullptr, (const uint8_t*)hq, Y, n_rows,
+                  ldy, grid_limit);
+}
+
+int moe_layer_gate_up(void* stream, const moe_layer* L, const moe_plan* P, const float* logits, int T,
+                      int k, const int32_t* dst_of_token, int entry_base, const float* x, int n_tokens,
+                      void* ws, size_t ws_bytes, int grid_limit) {
+  int rc = check_layer(L, true);
+  if (rc) return rc;
+  if ((rc = check_plan(P))) return rc;
+  if (!x || n_tokens < 0 || grid_limit < 0) return MOE_E_ARG;
+  if ((uintptr_t)x & 15) return MOE_E_ARG;
+  if (logits) {
+    if (T < 1 || T != n_tokens || k < 1 || k > 32 || k > L->n_experts || L->n_experts > 1024 ||
+        entry_base < 0)
+      return MOE_E_ARG;
+    if (T * k > P->cap_entries || T * k > P->cap_groups || T * k > 64) return MOE_E_ARG;
+  }
+  const WsLayout wl = ws_layout(L, P);
+  if (!ws || ws_bytes < wl.total || ((uintptr_t)ws & 255)) return MOE_E_WS;
+  uint8_t* b = (uint8_t*)ws;
+  return run_gate_up((hipStream_t)stream, L, P, logits ? GU_ROUTED : GU_FUSED, x, n_tokens,
+                     (float*)(b + wl.g), (float*)(b + wl.u), L->n_ff, (float*)(b + wl.h), b, logits, T,
+                     k, dst_of_token, entry_base, grid_limit);
+}
+
+int moe_layer_down(void* stream, const moe_layer* L, const moe_plan* P, const void* ws, size_t ws_bytes,
+                   int n_tokens, float* Y, int n_rows, int ldy, int grid_limit) {
+  int rc = check_layer(L, true);
+  if (rc) return rc;
+  if ((rc = check_plan(P))) return rc;
+  if (!Y || n_tokens < 0 || n_rows < 0 || ldy < L->n_embd || grid_limit < 0) return MOE_E_ARG;
+  const WsLayout wl = ws_layout(L, P);
+  if (!ws || ws_bytes < wl.total || ((uintptr_t)ws & 255)) return MOE_E_WS;
+  const uint8_t* b = (const uint8_t*)ws;
+  return run_down((hipStream_t)stream, L, P, DN_DESC, b, (const float*)(b + wl.h), nullptr, Y, n_rows,
+                  ldy, grid_limit);
 }
 
 int moe_layer_decode(void* stream, const moe_layer* L, const moe_plan* P, const float* x, int n_tokens,
                      float* Y, int n_rows, int ldy, void* ws, size_t ws_bytes, int grid_limit) {
-  int rc = check_layer(L, true);
+  if (!Y || n_rows < 0 || (L && ldy < L->n_embd)) return MOE_E_ARG;
+  const int rc = moe_layer_gate_up(stream, L, P, nullptr, 0, 0, nullptr, 0, x, n_tokens, ws, ws_bytes,
+                                   grid_limit);
   if (rc) return rc;
-  if ((rc = check_plan(P))) return rc;
-  if (!x || !Y || n_tokens < 0 || n_rows < 0 || ldy < L->n_embd || grid_limit < 0) return MOE_E_ARG;
-  if ((uintptr_t)x & 15) return MOE_E_ARG;
-  const WsLayout wl = ws_layout(L, P);
-  if (!ws || ws_bytes < wl.total || ((uintptr_t)ws & 255)) return MOE_E_WS;
-  uint8_t* b = (uint8_t*)ws;
-  rc = run_gate_up((hipStream_t)stream, L, P, GU_FUSED, x, n_tokens, (float*)(b + wl.g),
-                   (float*)(b + wl.u), L->n_ff, b + wl.hq, nullptr, 0, 0, nullptr, 0, grid_limit);
-  if (rc) return rc;
-  return run_down((hipStream_t)stream, L, P, b + wl.hq, 0, Y, n_rows, ldy, n_tokens, grid_limit);
+  return moe_layer_down(stream, L, P, ws, ws_bytes, n_tokens, Y, n_rows, ldy, grid_limit);
 }
 
 int moe_layer_decode_routed(void* stream, const moe_layer* L, const moe_plan* P, const float* logits,
                             int T, int k, const int32_t* dst_of_token, int entry_base, const float* x,
                             float* Y, int n_rows, int ldy, void* ws, size_t ws_bytes, int grid_limit) {
-  int rc = check_layer(L, true);
+  if (!logits || !Y || n_rows < 0 || (L && ldy < L->n_embd)) return MOE_E_ARG;
+  const int rc = moe_layer_gate_up(stream, L, P, logits, T, k, dst_of_token, entry_base, x, T, ws,
+                                   ws_bytes, grid_limit);
   if (rc) return rc;
-  if ((rc = check_plan(P))) return rc;
-  if (!logits || !x || !Y || T < 1 || k < 1 || k > 32 || k > L->n_experts || L->n_experts > 1024 ||
-      entry_base < 0 || n_rows < 0 || ldy < L->n_embd || grid_limit < 0)
-    return MOE_E_ARG;
-  if (T * k > P->cap_entries || T * k > P->cap_groups || T * k > 64) return MOE_E_ARG;
-  if ((uintptr_t)x & 15) return MOE_E_ARG;
-  const WsLayout wl = ws_layout(L, P);
-  if (!ws || ws_bytes < wl.total || ((uintptr_t)ws & 255)) return MOE_E_WS;
-  uint8_t* b = (uint8_t*)ws;
-  rc = run_gate_up((hipStream_t)stream, L, P, GU_ROUTED, x, T, (float*)(b + wl.g), (float*)(b + wl.u),
-                   L->n_ff, b + wl.hq, logits, T, k, dst_of_token, entry_base, grid_limit);
-  if (rc) return rc;
-  return run_down((hipStream_t)stream, L, P, b + wl.hq, 0, Y, n_rows, ldy, T, grid_limit);
+  return moe_layer_down(stream, L, P, ws, ws_bytes, T, Y, n_rows, ldy, grid_limit);
 }
 
 }  // extern "C"

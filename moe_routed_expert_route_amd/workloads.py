@@ -25,7 +25,8 @@ CONFIGS = {
     "cb2nl4_2560x768_t4_zipf": dict(layers=48, E=128, n_embd=2560, n_ff=768, k=8, T=4,
                                     fg=synth.CB2, fd=synth.NL4, routing="zipf"),
     # T sweep geometry: 256 experts, 2560 x 640, CB3 gate/up, Q8_0 down, uniform routing
-    "cb3q8_2560x640": dict(layers=2, E=256, n_embd=2560, n_ff=640, k=8, T=1,
+    # (48 layers: a pass reads >= 0.6 GB, well above the 256 MB last-level cache)
+    "cb3q8_2560x640": dict(layers=48, E=256, n_embd=2560, n_ff=640, k=8, T=1,
                            fg=synth.CB3, fd=synth.Q8_0, routing="uniform"),
 }
 
@@ -123,11 +124,22 @@ class Workload:
                                   self.d_x[l], self.Y[l], self.ws[l], grid_limit=grid_limit,
                                   stream=stream)
 
+    def gate_up(self, l, stream=None):
+        """First launch of layer l: route, group, q8_1(x), gate/up, SwiGLU + q8_1 of h."""
+        B.moe_layer_gate_up(self.layers[l], self.plans[l], self.d_x[l], self.ws[l],
+                            logits=self.d_logits[l], k=self.k, stream=stream)
+
+    def down(self, l, stream=None):
+        """Second launch of layer l: grouped down + weighted scatter into Y."""
+        B.moe_layer_down(self.layers[l], self.plans[l], self.ws[l], self.T, self.Y[l], stream=stream)
+
     def step(self, stream=None):
         """One pass of the whole hot path over every layer: route, group, decode (two launches
-        per layer: routing and grouping run inside the gate/up launch)."""
+        per layer: routing and grouping run inside the gate/up launch). The same launches as
+        moe_layer_decode_routed, issued through its two halves."""
         for l in range(self.L):
-            self.decode_routed(l, stream)
+            self.gate_up(l, stream)
+            self.down(l, stream)
 
     def step_separate(self, stream=None):
         """The same pass with routing and grouping as launches of their own."""
@@ -143,6 +155,20 @@ class Workload:
         """Expert-weight bytes each layer call must read: every distinct routed expert once."""
         per = 2 * self.sz_g + self.sz_d
         return [len(r) * per for r in self.routed]
+
+    def launch_bytes(self, l):
+        """Algorithmic HBM bytes of layer l's two launches: (gate/up, down). Gate/up reads the
+        distinct experts' gate and up matrices once, the logits and x once, writes the plan, g, u
+        and the q8_1 rows of h; down reads the distinct experts' down matrices once, the plan,
+        the q8_1 rows of h once and the destination rows of Y, and writes those rows."""
+        ne = self.T * self.k
+        nd = len(self.routed[l])
+        hq = ne * (self.n_ff // 32) * 36
+        plan = 4 * (2 * nd + 1 + 1 + 3 * ne)
+        gu = (nd * 2 * self.sz_g + self.T * self.E * 4 + self.T * self.n_embd * 4 + plan
+              + 2 * ne * self.n_ff * 4 + hq)
+        dn = nd * self.sz_d + plan + hq + 2 * self.T * self.n_embd * 4
+        return gu, dn
 
     def host_expert(self, l, e):
         """Host copies of one expert's matrices (regenerated from the seed, not read back)."""

@@ -138,9 +138,9 @@ def test_layer_stages(name):
     ws, off = fused["ws"].cpu().numpy(), fused["off"]
     ne = int(ph["grp_start"][-1] - base)
     gw = ws[off[0]:off[0] + ne * c.n_ff * 4].view(np.float32).reshape(ne, c.n_ff)
-    hqw = ws[off[2]:off[2] + ne * (c.n_ff // 32) * 36].reshape(ne, -1)
+    hw = ws[off[2]:off[2] + ne * c.n_ff * 4].view(np.float32).reshape(ne, c.n_ff)
     assert np.array_equal(U.bits(gw), U.bits(comp["g"][base:base + ne]))
-    assert np.array_equal(hqw, comp["hq"][base:base + ne])
+    assert np.array_equal(U.bits(hw), U.bits(comp["h"][base:base + ne]))
     # routing + grouping inside the gate/up launch: same plan, same bits
     r = U.run_routed(c, c.x, Y0, entry_base=base, dst_of_token=dst)
     assert r["err"] == 0
@@ -148,6 +148,8 @@ def test_layer_stages(name):
         assert np.array_equal(np.asarray(r["plan"][key]), np.asarray(ph[key])), key
     assert np.array_equal(U.bits(r["plan"]["ent_w"]), U.bits(ph["ent_w"]))
     assert np.array_equal(U.bits(r["Y"]), U.bits(comp["Y"]))
+    r2 = U.run_routed(c, c.x, Y0, entry_base=base, dst_of_token=dst, split=True)
+    assert r2["err"] == 0 and np.array_equal(U.bits(r2["Y"]), U.bits(comp["Y"]))
 
 
 @pytest.mark.parametrize("name", ["nl4_t1", "cb2_nl4_t4_zipf"])
