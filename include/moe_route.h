@@ -149,7 +149,7 @@ int moe_down_scatter(void* stream, const moe_layer* L, const moe_plan* P, const 
                      float* Y, int n_rows, int ldy, int grid_limit);
 
 /* Host: bytes of workspace the single-call paths need for this layer and plan capacity (the
- * intermediates of the call: g, u and the q8_1 rows of h). The workspace is 256-byte aligned and
+ * call's descriptor for the down launch and the q8_1 rows of h). The workspace is 256-byte aligned and
  * needs no clearing: a call reads only bytes it wrote itself. */
 size_t moe_workspace_bytes(const moe_layer* L, const moe_plan* P);
 
@@ -173,21 +173,23 @@ int moe_layer_decode_routed(void* stream, const moe_layer* L, const moe_plan* P,
 
 /* The first of the two launches of moe_layer_decode (logits == NULL: the plan in P as built) or
  * of moe_layer_decode_routed (logits != NULL: route and group here, publish the plan into P;
- * then n_tokens must equal T). Leaves g, u and the q8_1 rows of h in the workspace
- * (moe_workspace_layout). For callers that put other work between the halves or time them. */
+ * then n_tokens must equal T). Leaves the call's descriptor and the q8_1 rows of h in the
+ * workspace (moe_workspace_layout). For callers that put other work between the halves or time
+ * them. Limits (else MOE_E_SHAPE): n_tokens * n_embd/32 * 36 B <= 48 KB of staged activations. */
 int moe_layer_gate_up(void* stream, const moe_layer* L, const moe_plan* P, const float* logits,
                       int T, int k, const int32_t* dst_of_token, int entry_base, const float* x,
                       int n_tokens, void* workspace, size_t ws_bytes, int grid_limit);
 
-/* The second launch: grouped down over the workspace's q8_1 rows of h + weighted scatter into Y,
- * as moe_down_scatter; entries whose token is not below n_tokens are skipped. */
+/* The second launch: grouped down over the workspace's q8_1 rows of h + weighted scatter into Y
+ * (limit, else MOE_E_SHAPE: cap_entries * n_ff/32 * 36 B <= 64 KB of staged h rows), as
+ * moe_down_scatter. n_tokens is the first launch's (that launch marked entries whose token is
+ * out of range, and this one skips them). */
 int moe_layer_down(void* stream, const moe_layer* L, const moe_plan* P, const void* workspace,
                    size_t ws_bytes, int n_tokens, float* Y, int n_rows, int ldy, int grid_limit);
 
-/* Host: byte offsets inside the workspace of the intermediates of the last single-call step:
- * off[0] g float32 [cap_entries][n_ff], off[1] u (same), off[2] hq [cap_entries][n_ff/32 * 36 B];
- * rows indexed by (entry - grp_start[0]). */
-int moe_workspace_layout(const moe_layer* L, const moe_plan* P, size_t off[3]);
+/* Host: byte offset inside the workspace of the q8_1 rows of h that the last single-call step
+ * left there: cap_entries rows of n_ff/32 blocks of 36 B, row = entry - grp_start[0]. */
+int moe_workspace_layout(const moe_layer* L, const moe_plan* P, size_t* hq_offset);
 
 const char* moe_status_string(int status);   /* host, static string */
 const char* moe_last_error(void);            /* host, text of the last MOE_E_HIP on this thread */

@@ -245,11 +245,12 @@ def workspace(layer: Layer, plan: Plan, device="cuda"):
     return ws
 
 
-def moe_workspace_layout(layer: Layer, plan: Plan):
-    off = (ctypes.c_size_t * 3)()
-    _check(lib().moe_workspace_layout(ctypes.byref(layer.struct), ctypes.byref(plan.struct), off),
-           "moe_workspace_layout")
-    return [int(v) for v in off]
+def moe_workspace_layout(layer: Layer, plan: Plan) -> int:
+    """Byte offset of the q8_1 rows of h (row = entry - grp_start[0]) inside the workspace."""
+    off = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_layout(ctypes.byref(layer.struct), ctypes.byref(plan.struct),
+                                      ctypes.byref(off)), "moe_workspace_layout")
+    return int(off.value)
 
 
 def moe_down_scatter(layer: Layer, plan: Plan, hq, Y, grid_limit=0, stream=None):

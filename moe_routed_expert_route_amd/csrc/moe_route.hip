@@ -744,10 +744,10 @@ struct GuArgs {
   int n_tokens;         // act rows (tokens)
   const uint8_t* xq;    // composed: q8_1 rows per token
   const float* x;       // fused / routed: float rows per token
-  float* g;             // composed: g rows (absolute entry, stride ld); fused: workspace rows
+  float* g;             // composed: g rows (absolute entry, stride ld)
   float* u;
   int ld;
-  float* h;             // fused / routed: workspace h rows (relative entry, stride n_ff)
+  uint8_t* hq;          // fused / routed: workspace q8_1 rows of h (relative entry)
   uint8_t* desc;        // fused / routed: the call's descriptor for the down launch
   const float* logits;  // routed: [T][E] router logits
   int T, E, k;
@@ -757,18 +757,18 @@ struct GuArgs {
   int sw;               // waves that stream items (the ring holds sw waves' slots)
 };
 
-constexpr int kGuStage = 64;   // floats of per-wave output staging (kSlots x 16 rows)
-constexpr int kGuFixed = 4096 + kPlanLBytes + 8 * 3 * kMaxGrp + 4 * kGuStage * kGuWaves;
+constexpr int kGuStage = 64 * kMaxEnt;   // floats of output staging: a 32-row block of g and u per entry
+constexpr int kGuFixed = 4096 + kPlanLBytes + 8 * 3 * kMaxGrp + 4 * kGuStage;
 constexpr int kGuXPass = 8;    // float4 (or q8_1 dword) register passes: 1024 float blocks, 910 q8_1
 
 __host__ __device__ inline int gu_smem_bytes(int lds_ring, int lds_act) {
   return lds_ring + lds_act + kGuFixed;
 }
 
-// One workgroup per CU; the work items are per wave: item (group g, j) = h rows
-// [j rp / 2, (j + 1) rp / 2) of group g, spread over the streaming waves of the grid (the first
-// sw waves of each workgroup; wave-granular balance). A wave streams its item's gate and up rows
-// as one two-span chunk.
+// Work item = one 32-row block of h of one group (so SwiGLU and the q8_1 quantization of the block
+// finish in the workgroup). The block's 64 weight rows are 64 / rp passes of rp rows (rp / 2 gate
+// rows and the same up rows, one two-span chunk); the first sw waves take the passes round
+// robin, each streaming its chunks through its own ring across the workgroup's items.
 template <int FMT, int MODE>
 __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -781,7 +781,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   MOE_LDS uint32_t* g3 = g2 + 512;
   const PlanL pl = plan_l((MOE_LDS int*)(p8 + 4096));
   MOE_LDS uint64_t* gptr = (MOE_LDS uint64_t*)(p8 + 4096 + kPlanLBytes);   // [group][gate, up, down]
-  MOE_LDS float* stage = (MOE_LDS float*)(p8 + 4096 + kPlanLBytes + 8 * 3 * kMaxGrp) + wave * kGuStage;
+  MOE_LDS float* stage = (MOE_LDS float*)(p8 + 4096 + kPlanLBytes + 8 * 3 * kMaxGrp);   // [entry][64]
   MOE_LDS float* lgs = (MOE_LDS float*)ring;   // routed: staged logits (prologue only)
   const int Epad = logits_pad(a.E);
 
@@ -933,22 +933,25 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     }
   }
 
-  // ---- 5. this wave's items, streamed through its ring
+  // ---- 5. items: the workgroup's blocks; this wave's passes of each, streamed through its ring
   const int half = G.rp >> 1;
-  const int nbw = a.A.n_ff / half;   // items per group
-  const int items = ng * nbw;
-  const int gw = (int)blockIdx.x * a.sw + wave, TW = (int)gridDim.x * a.sw;
-  const int nit = (wave < a.sw && gw < items) ? (items - gw + TW - 1) / TW : 0;
+  const int nb = a.A.n_ff / 32;          // blocks per group
+  const int npass = 64 / G.rp;           // passes per block
+  const int items = ng * nb;
+  const int nit = (int)blockIdx.x < items ? (items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+  const int cw = wave < min(a.sw, npass) ? (npass - wave + a.sw - 1) / a.sw : 0;   // passes per block
+  const int nch = nit * cw;
   const int M = a.S.M, NS = a.S.NS;
   MOE_LDS uint8_t* myring = ring + wave * NS * M * 1024;
   const uint32_t nspan = (uint32_t)(half * G.rb);
-  auto issue_item = [&](int kk, MOE_LDS uint8_t* slot) {
-    const int it = gw + kk * TW;
-    const int g = it / nbw, j = it - g * nbw;
+  auto issue = [&](int kc, MOE_LDS uint8_t* slot) {
+    const int kk = kc / cw, q = kc - kk * cw;
+    const int it = (int)blockIdx.x + kk * (int)gridDim.x;
+    const int g = it / nb, blk = it - g * nb;
     const uint64_t wg = uni64(gptr[3 * g]);
     if (wg) {
       const uint64_t wu = uni64(gptr[3 * g + 1]);
-      const uint64_t off = (uint64_t)(j * half) * (uint64_t)G.rb;
+      const uint64_t off = (uint64_t)(blk * 32 + (wave + q * a.sw) * half) * (uint64_t)G.rb;
       issue_chunk(slot, M, (const uint8_t*)(uintptr_t)(wg + off), nspan,
                   (const uint8_t*)(uintptr_t)(wu + off), nspan, span_b_chunk(wg + off, nspan));
     } else {   // a skipped group keeps the count of loads: one 16-byte chunk every lane reloads
@@ -956,62 +959,64 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     }
   };
   __builtin_amdgcn_s_waitcnt(MOE_VM(0));   // nothing of ours in flight before the stream
-  const int pre = min(NS, nit);
-  for (int kk = 0; kk < pre; ++kk) issue_item(kk, myring + kk * M * 1024);
+  const int pre = min(NS, nch);
+  for (int kc = 0; kc < pre; ++kc) issue(kc, myring + kc * M * 1024);
   int issued = pre;
+  int kc = 0;
   for (int kk = 0; kk < nit; ++kk) {
-    wait_vm((issued - 1 - kk) * M);
-    MOE_LDS uint8_t* slot = myring + (kk % NS) * M * 1024;
-    const int it = gw + kk * TW;
-    const int g = it / nbw, j = it - g * nbw;
+    const int it = (int)blockIdx.x + kk * (int)gridDim.x;
+    const int g = it / nb, blk = it - g * nb;
     const uint64_t wgv = uni64(gptr[3 * g]);
-    if (wgv) {
-      const uint64_t off = (uint64_t)(j * half) * (uint64_t)G.rb;
-      const uint32_t sb = (uint32_t)(slot - ring);
-      const uint32_t ra = sb + (uint32_t)((wgv + off) & 15);
-      const uint32_t rb0 = sb + 16 * span_b_chunk(wgv + off, nspan) +
-                           (uint32_t)((uni64(gptr[3 * g + 1]) + off) & 15);
-      const int a0 = uni(pl.gstart[g]) - e0, a1 = uni(pl.gstart[g + 1]) - e0;
-      const int hr0 = j * half;
-      for (int c0 = a0; c0 < a1; c0 += kSlots) {
-        const int ne = min(kSlots, a1 - c0);
-        int sidx[kSlots];
-        int live[kSlots];
+    const int a0 = uni(pl.gstart[g]) - e0, a1 = uni(pl.gstart[g + 1]) - e0;
+    for (int q = 0; q < cw; ++q, ++kc) {
+      wait_vm((issued - 1 - kc) * M);
+      MOE_LDS uint8_t* slot = myring + (kc % NS) * M * 1024;
+      if (wgv) {
+        const int prow = (wave + q * a.sw) * half;   // first h row of the pass inside the block
+        const uint64_t off = (uint64_t)(blk * 32 + prow) * (uint64_t)G.rb;
+        const uint32_t sb = (uint32_t)(slot - ring);
+        const uint32_t ra = sb + (uint32_t)((wgv + off) & 15);
+        const uint32_t rb0 = sb + 16 * span_b_chunk(wgv + off, nspan) +
+                             (uint32_t)((uni64(gptr[3 * g + 1]) + off) & 15);
+        for (int c0 = a0; c0 < a1; c0 += kSlots) {
+          const int ne = min(kSlots, a1 - c0);
+          int sidx[kSlots];
 #pragma unroll
-        for (int e = 0; e < kSlots; ++e) {
-          sidx[e] = e < ne ? uni(pl.esrc[c0 + e]) : 0;
-          live[e] = e < ne ? uni(pl.elive[c0 + e]) : 0;
+          for (int e = 0; e < kSlots; ++e) sidx[e] = e < ne ? uni(pl.esrc[c0 + e]) : 0;
+          MOE_LDS float* st = stage + (c0 - a0) * 64 + prow;
+          dot_pass<FMT>((const MOE_LDS uint32_t*)ring, ra, rb0, half, G.rp, G, tb, act, sidx, ne,
+                        [&](int i, int e, float v) { st[e * 64 + (i < half ? i : 32 + i - half)] = v; });
         }
-        dot_pass<FMT>((const MOE_LDS uint32_t*)ring, ra, rb0, half, G.rp, G, tb, act, sidx, ne,
-                      [&](int i, int e, float v) { stage[e * 16 + i] = v; });
-        wave_lds_sync();
-        if (lane < ne * half) {
-          const int e = lane / half, r = lane - e * half;
-          const float gv = stage[e * 16 + r], uv = stage[e * 16 + half + r];
-          bool is_live = false;
-#pragma unroll
-          for (int q = 0; q < kSlots; ++q) is_live = q == e ? live[q] != 0 : is_live;
-          if (is_live) {
-            const int row = hr0 + r;
-            if constexpr (MODE == GU_COMPOSED) {
-              a.g[(size_t)(e0 + c0 + e) * a.ld + row] = gv;
-              a.u[(size_t)(e0 + c0 + e) * a.ld + row] = uv;
-            } else {
-              const size_t o = (size_t)(c0 + e) * a.A.n_ff + row;
-              a.g[o] = gv;
-              a.u[o] = uv;
-              a.h[o] = swiglu(gv, uv);
-            }
-          }
-        }
-        wave_lds_sync();
+      }
+      if (kc + NS < nch) {
+        MOE_WAIT_LGKM0;   // this wave's LDS reads of the slot have returned
+        issue(kc + NS, slot);
+        ++issued;
       }
     }
-    if (kk + NS < nit) {
-      MOE_WAIT_LGKM0;   // this wave's LDS reads of the slot have returned
-      issue_item(kk + NS, slot);
-      ++issued;
+    __syncthreads();
+    // the block's outputs: composed, g and u rows; fused / routed, SwiGLU + q8_1 of h
+    const int ne = a1 - a0;
+    if (wgv) {
+      if constexpr (MODE == GU_COMPOSED) {
+        for (int idx = tid; idx < ne * 64; idx += kGuThreads) {
+          const int e = idx >> 6, r = idx & 63;
+          if (!pl.elive[a0 + e]) continue;
+          (r < 32 ? a.g : a.u)[(size_t)(e0 + a0 + e) * a.ld + blk * 32 + (r & 31)] = stage[idx];
+        }
+      } else {
+        // 32 lanes per entry; every half-wave runs each round (the shuffles need all 32 lanes)
+        for (int base = 0; base < ne; base += kGuThreads / 32) {
+          const int e = base + (tid >> 5), l32 = tid & 31;
+          const bool live = e < ne && pl.elive[a0 + (e < ne ? e : 0)] != 0;
+          const float gv = live ? stage[e * 64 + l32] : 0.0f;
+          const float uv = live ? stage[e * 64 + 32 + l32] : 0.0f;
+          uint8_t* blkp = a.hq + ((size_t)(a0 + (live ? e : 0)) * nb + blk) * 36;
+          swiglu_q81_lanes(gv, uv, l32, live, blkp, nullptr);
+        }
+      }
     }
+    __syncthreads();
   }
 }
 
@@ -1025,8 +1030,7 @@ struct DnArgs {
   Geom G;
   Stream S;
   const uint8_t* desc;  // DN_DESC: the call's descriptor
-  const float* h;       // DN_DESC: h rows (relative entry), stride n_ff
-  const uint8_t* hq;    // DN_PLAN: q8_1 rows by absolute entry
+  const uint8_t* hq;    // q8_1 rows of h: DN_DESC by entry - e0 (workspace), DN_PLAN by absolute entry
   float* Y;
   int n_rows, ldy;
   int lds_ring, lds_act;
@@ -1181,10 +1185,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
     for (int kc = 0; kc < pre; ++kc) issue(kc, myring + kc * M * 1024);
     wait_vm(pre * M);   // the h loads, older than every chunk, have landed
   };
-  if constexpr (MODE == DN_DESC)
-    act_stage_f<kDnThreads, 16>(a.h, a.A.n_ff, n * U, U, act, mid);
-  else
-    act_stage_q<kDnThreads, 16>(a.hq + (size_t)e0 * U * 36, n * U, act, mid);
+  act_stage_q<kDnThreads, 16>(a.hq + (MODE == DN_PLAN ? (size_t)e0 * U * 36 : 0), n * U, act, mid);
   int issued = pre;
   __syncthreads();
 
@@ -1392,22 +1393,16 @@ Stream dn_stream(const Geom& G, int ns) {
 }
 
 struct WsLayout {
-  size_t g, u, h, total;
+  size_t hq, total;
 };
 
 size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// The call's descriptor, then the q8_1 rows of h by entry - e0.
 WsLayout ws_layout(const moe_layer* L, const moe_plan* P) {
   WsLayout w{};
-  size_t p = kDescReserve;
-  const size_t ce = (size_t)P->cap_entries;
-  w.g = p;
-  p += al256(ce * L->n_ff * 4);
-  w.u = p;
-  p += al256(ce * L->n_ff * 4);
-  w.h = p;
-  p += al256(ce * L->n_ff * 4);
-  w.total = p;
+  w.hq = kDescReserve;
+  w.total = w.hq + al256((size_t)P->cap_entries * (L->n_ff / 32) * 36);
   return w;
 }
 
@@ -1550,7 +1545,7 @@ int dn_lds(const moe_layer* L, const moe_plan* P, Stream* S, int* ring, int* act
 
 // The gate/up kernel of `mode`.
 int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, const void* act,
-                int n_tokens, float* g, float* u, int ld, float* h, uint8_t* desc, const float* logits,
+                int n_tokens, float* g, float* u, int ld, uint8_t* hq, uint8_t* desc, const float* logits,
                 int T, int k, const int32_t* dst_of_token, int entry_base, int grid_limit) {
   const Geom G = make_geom(L->fmt_gate_up, L->n_embd, true);
   int ring = 0, actb = 0, sw = 0;
@@ -1568,7 +1563,7 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
   ga.g = g;
   ga.u = u;
   ga.ld = ld;
-  ga.h = h;
+  ga.hq = hq;
   ga.desc = desc;
   ga.logits = logits;
   ga.T = T;
@@ -1579,14 +1574,14 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
   ga.lds_ring = ring;
   ga.lds_act = actb;
   ga.sw = sw;
-  const int wave_items = P->cap_groups * (L->n_ff / (G.rp / 2));
-  const int grid = grid_for((wave_items + sw - 1) / sw, bytes, grid_limit);
+  const int items = P->cap_groups * (L->n_ff / 32);
+  const int grid = grid_for(items, bytes, grid_limit);
   const hipError_t e = launch_gu(L->fmt_gate_up, mode, ga, grid, bytes, st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "gate/up kernel");
 }
 
 int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, const uint8_t* desc,
-             const float* h, const uint8_t* hq, float* Y, int n_rows, int ldy, int grid_limit) {
+             const uint8_t* hq, float* Y, int n_rows, int ldy, int grid_limit) {
   const Geom G = make_geom(L->fmt_down, L->n_ff, false);
   int ring = 0, actb = 0;
   Stream S{};
@@ -1598,7 +1593,6 @@ int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, co
   da.G = G;
   da.S = S;
   da.desc = desc;
-  da.h = h;
   da.hq = hq;
   da.Y = Y;
   da.n_rows = n_rows;
@@ -1696,15 +1690,12 @@ size_t moe_workspace_bytes(const moe_layer* L, const moe_plan* P) {
   return ws_layout(L, P).total;
 }
 
-int moe_workspace_layout(const moe_layer* L, const moe_plan* P, size_t off[3]) {
+int moe_workspace_layout(const moe_layer* L, const moe_plan* P, size_t* hq_offset) {
   int rc = check_layer(L, true);
   if (rc) return rc;
   if ((rc = check_plan(P))) return rc;
-  if (!off) return MOE_E_ARG;
-  const WsLayout w = ws_layout(L, P);
-  off[0] = w.g;
-  off[1] = w.u;
-  off[2] = w.h;
+  if (!hq_offset) return MOE_E_ARG;
+  *hq_offset = ws_layout(L, P).hq;
   return MOE_OK;
 }
 
@@ -1715,8 +1706,8 @@ int moe_down_scatter(void* stream, const moe_layer* L, const moe_plan* P, const 
   if ((rc = check_plan(P))) return rc;
   if (!hq || !Y || n_rows < 0 || ldy < L->n_embd || grid_limit < 0) return MOE_E_ARG;
   if ((uintptr_t)hq & 3) return MOE_E_ARG;
-  return run_down((hipStream_t)stream, L, P, DN_PLAN, nullptr, nullptr, (const uint8_t*)hq, Y, n_rows,
-                  ldy, grid_limit);
+  return run_down((hipStream_t)stream, L, P, DN_PLAN, nullptr, (const uint8_t*)hq, Y, n_rows, ldy,
+                  grid_limit);
 }
 
 int moe_layer_gate_up(void* stream, const moe_layer* L, const moe_plan* P, const float* logits, int T,
@@ -1736,9 +1727,8 @@ int moe_layer_gate_up(void* stream, const moe_layer* L, const moe_plan* P, const
   const WsLayout wl = ws_layout(L, P);
   if (!ws || ws_bytes < wl.total || ((uintptr_t)ws & 255)) return MOE_E_WS;
   uint8_t* b = (uint8_t*)ws;
-  return run_gate_up((hipStream_t)stream, L, P, logits ? GU_ROUTED : GU_FUSED, x, n_tokens,
-                     (float*)(b + wl.g), (float*)(b + wl.u), L->n_ff, (float*)(b + wl.h), b, logits, T,
-                     k, dst_of_token, entry_base, grid_limit);
+  return run_gate_up((hipStream_t)stream, L, P, logits ? GU_ROUTED : GU_FUSED, x, n_tokens, nullptr,
+                     nullptr, 0, b + wl.hq, b, logits, T, k, dst_of_token, entry_base, grid_limit);
 }
 
 int moe_layer_down(void* stream, const moe_layer* L, const moe_plan* P, const void* ws, size_t ws_bytes,
@@ -1750,8 +1740,7 @@ int moe_layer_down(void* stream, const moe_layer* L, const moe_plan* P, const vo
   const WsLayout wl = ws_layout(L, P);
   if (!ws || ws_bytes < wl.total || ((uintptr_t)ws & 255)) return MOE_E_WS;
   const uint8_t* b = (const uint8_t*)ws;
-  return run_down((hipStream_t)stream, L, P, DN_DESC, b, (const float*)(b + wl.h), nullptr, Y, n_rows,
-                  ldy, grid_limit);
+  return run_down((hipStream_t)stream, L, P, DN_DESC, b, b + wl.hq, Y, n_rows, ldy, grid_limit);
 }
 
 int moe_layer_decode(void* stream, const moe_layer* L, const moe_plan* P, const float* x, int n_tokens,

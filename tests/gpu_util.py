@@ -127,8 +127,8 @@ def run_fused(c, plan, x_np, Y0_np, grid_limit=0, ws=None, stale=False):
     if ws is None:
         ws = B.workspace(c.layer, plan, device=d)
     off = B.moe_workspace_layout(c.layer, plan)
-    if stale:  # garbage in every intermediate (counters excepted)
-        ws[off[0]:].fill_(0x7F)
+    if stale:  # garbage in every byte the call will write and read back
+        ws.fill_(0x7F)
     B.moe_layer_decode(c.layer, plan, x, Y, ws, grid_limit=grid_limit)
     torch.cuda.synchronize()
     return dict(Y=Y.cpu().numpy(), ws=ws, off=off, err=plan.errors())
