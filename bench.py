@@ -12,8 +12,8 @@ SwiGLU + q8_1 of h; (2) grouped down + weighted scatter into Y. Steps are replay
 graph.
 
 Printed: one JSON line. value = expert-weight GB/s (distinct routed experts' bytes per pass / time
-per pass); us_per_layer_call = time per layer; roofline = the dominant kernel alone, timed with
-HIP events around each of its launches on the stream it runs on; t_sweep = the same measurement
+per pass); us_per_layer_call = time per layer; roofline = the dominant kernel alone (a HIP graph
+of its 48 launches replayed between HIP events on its stream); t_sweep = the same measurement
 at T = 1..4 (shared experts: the per-extra-row cost; the 256-expert CB3/Q8_0 geometry with
 uniform routing); cpu_baseline = the CPU oracle on a sample of layer calls.
 """
@@ -70,29 +70,35 @@ def time_graph(graph, n):
 
 
 def kernel_us(wl, reps):
-    """Average duration of each launch kind (gate/up, down), HIP events around every launch on
-    the stream the launch runs on (the current stream), eager, cycling over the layers."""
+    """Average duration of each launch kind (gate/up, down): a HIP graph of the kind's launches for
+    every layer, replayed `reps` times between HIP events on its stream, divided by the launch
+    count (kernels of one graph run back to back, so this is the kernels' own time)."""
     import torch
-    s = torch.cuda.current_stream()
-    evs = {"gate_up": [], "down": []}
-    for _ in range(reps):
-        for l in range(wl.L):
-            for kind, fn in (("gate_up", wl.gate_up), ("down", wl.down)):
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record(s)
-                fn(l)
-                b.record(s)
-                evs[kind].append((a, b))
-    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
     out = {}
-    for kind, lst in evs.items():
-        ts = sorted(a.elapsed_time(b) * 1e3 for a, b in lst)
-        out[kind] = (sum(ts) / len(ts), ts[len(ts) // 2])
+    for kind, fn in (("gate_up", wl.gate_up), ("down", wl.down)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for l in range(wl.L):
+                fn(l)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        with torch.cuda.stream(s):
+            for _ in range(reps):
+                g.replay()
+        b.record(s)
+        torch.cuda.synchronize()
+        out[kind] = a.elapsed_time(b) * 1e3 / (reps * wl.L)
+        del g
     return out
 
 
-def measure(wl, steps, warmup, reps=2):
+def measure(wl, steps, warmup, reps=5):
     """Graph-replayed step time, plain-stream step time and per-kernel launch times."""
     import torch
     wl.step()
@@ -138,13 +144,13 @@ def sweep_line(name, T, routing, steps, warmup):
 
     from moe_routed_expert_route_amd.workloads import Workload
     wl = Workload(name, device="cuda", T=T, routing=routing)
-    ms_step, _, ks = measure(wl, steps, warmup, reps=1)
+    ms_step, _, ks = measure(wl, steps, warmup, reps=2)
     bytes_pass = float(sum(wl.weight_bytes_per_layer()))
     us = ms_step * 1e3 / wl.L
     line = {"T": T, "routing": routing, "us_per_layer_call": round(us, 3),
             "gbs": round(bytes_pass / (ms_step * 1e-3) / 1e9, 1),
             "distinct_experts_per_layer": round(sum(wl.distinct_experts(l) for l in range(wl.L)) / wl.L, 2),
-            "gate_up_us": round(ks["gate_up"][0], 3), "down_us": round(ks["down"][0], 3)}
+            "gate_up_us": round(ks["gate_up"], 3), "down_us": round(ks["down"], 3)}
     del wl
     torch.cuda.empty_cache()
     return line
@@ -191,12 +197,12 @@ def main():
              "down": f"k_down<{fmt_names[wl.fd]}>"}
     kernels = {}
     for kind in ("gate_up", "down"):
-        avg, med = ks[kind]
+        avg = ks[kind]
         ach = kb[kind] / (avg * 1e-6) / 1e9
         kernels[kind] = {"kernel": kname[kind], "avg_launch_us": round(avg, 3),
-                         "median_launch_us": round(med, 3), "bytes_per_launch": int(kb[kind]),
+                         "bytes_per_launch": int(kb[kind]),
                          "achieved_gbs": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4)}
-    dom = max(kernels, key=lambda k: ks[k][0])
+    dom = max(kernels, key=lambda k: ks[k])
     dk = kernels[dom]
     traffic = traffic_for(args.workload, dom)
     res = {

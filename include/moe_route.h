@@ -187,9 +187,11 @@ int moe_layer_gate_up(void* stream, const moe_layer* L, const moe_plan* P, const
 int moe_layer_down(void* stream, const moe_layer* L, const moe_plan* P, const void* workspace,
                    size_t ws_bytes, int n_tokens, float* Y, int n_rows, int ldy, int grid_limit);
 
-/* Host: byte offset inside the workspace of the q8_1 rows of h that the last single-call step
- * left there: cap_entries rows of n_ff/32 blocks of 36 B, row = entry - grp_start[0]. */
-int moe_workspace_layout(const moe_layer* L, const moe_plan* P, size_t* hq_offset);
+/* Host: where the last single-call step left the q8_1 rows of h inside the workspace, in split
+ * form (row = entry - grp_start[0], n_ff/32 blocks per row, cap_entries rows): off[0] the 16-byte
+ * low halves of the blocks' quants (quants 0-15), off[1] the high halves (16-31), off[2] the
+ * blocks' scales as float32 (the fp16 d widened exactly). */
+int moe_workspace_layout(const moe_layer* L, const moe_plan* P, size_t off[3]);
 
 const char* moe_status_string(int status);   /* host, static string */
 const char* moe_last_error(void);            /* host, text of the last MOE_E_HIP on this thread */

@@ -69,8 +69,7 @@ def lib():
                                         _I, _P, _I, _P, _I, _P, ctypes.c_size_t, _I]
         L.moe_layer_down.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan), _P,
                                      ctypes.c_size_t, _I, _P, _I, _I, _I]
-        L.moe_workspace_layout.argtypes = [ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan),
-                                           ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_workspace_layout.argtypes = [ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan), _P]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [_I]
         L.moe_last_error.restype = ctypes.c_char_p
@@ -245,12 +244,13 @@ def workspace(layer: Layer, plan: Plan, device="cuda"):
     return ws
 
 
-def moe_workspace_layout(layer: Layer, plan: Plan) -> int:
-    """Byte offset of the q8_1 rows of h (row = entry - grp_start[0]) inside the workspace."""
-    off = ctypes.c_size_t(0)
-    _check(lib().moe_workspace_layout(ctypes.byref(layer.struct), ctypes.byref(plan.struct),
-                                      ctypes.byref(off)), "moe_workspace_layout")
-    return int(off.value)
+def moe_workspace_layout(layer: Layer, plan: Plan):
+    """Byte offsets of the split q8_1 rows of h in the workspace: low quant halves, high quant
+    halves, float scales."""
+    off = (ctypes.c_size_t * 3)()
+    _check(lib().moe_workspace_layout(ctypes.byref(layer.struct), ctypes.byref(plan.struct), off),
+           "moe_workspace_layout")
+    return [int(v) for v in off]
 
 
 def moe_down_scatter(layer: Layer, plan: Plan, hq, Y, grid_limit=0, stream=None):

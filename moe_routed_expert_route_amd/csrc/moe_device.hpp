@@ -17,6 +17,7 @@
 #define MOE_LDS __attribute__((address_space(3)))
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace moe {
 
@@ -144,14 +145,43 @@ __device__ __forceinline__ uint32_t ldw(const MOE_LDS uint32_t* W, uint32_t off)
   return __builtin_amdgcn_alignbyte(W[i + 1], W[i], off & 3u);
 }
 
-// 16-entry int8 lookup of four 4-bit codes (one per byte) with v_perm: entries 0-7 and 8-15 are
-// looked up separately and merged by the code's bit 3.
-__device__ __forceinline__ uint32_t lut16(uint32_t c, const uint32_t t[4]) {
-  const uint32_t s = c & 0x07070707u;
-  const uint32_t lo = __builtin_amdgcn_perm(t[1], t[0], s);
-  const uint32_t hi = __builtin_amdgcn_perm(t[3], t[2], s);
-  // selector 4 picks byte 0 of the first operand (0xFF), selector 12 yields 0x00
-  const uint32_t m = __builtin_amdgcn_perm(0xFFFFFFFFu, 0u, (c & 0x08080808u) | 0x04040404u);
+struct Tables {
+  uint32_t nl4[4];                       // NL4 table, in VGPRs (tables_init)
+  uint32_t k7, k8, k4;                   // byte-lane constants, in VGPRs (tables_init)
+  const MOE_LDS uint32_t* cb2;           // 256 x 8 B grid in LDS (2 dwords per row)
+  const MOE_LDS uint32_t* cb3;           // 512 x 4 B grid in LDS (1 dword per row)
+};
+
+// Put a value in a VGPR the compiler treats as opaque: the lookup below then reads its table and
+// masks from VGPRs (one VOP3 may read only one SGPR or literal on this target), with no copies
+// rematerialised inside the loops.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(v));
+  return r;
+}
+
+__device__ __forceinline__ void tables_init(Tables& tb, const uint32_t nl4[4], const MOE_LDS uint32_t* cb2,
+                                            const MOE_LDS uint32_t* cb3) {
+  tb.nl4[0] = in_vgpr(nl4[0]);
+  tb.nl4[1] = in_vgpr(nl4[1]);
+  tb.nl4[2] = in_vgpr(nl4[2]);
+  tb.nl4[3] = in_vgpr(nl4[3]);
+  tb.k7 = in_vgpr(0x07070707u);
+  tb.k8 = in_vgpr(0x08080808u);
+  tb.k4 = in_vgpr(0x04040404u);
+  tb.cb2 = cb2;
+  tb.cb3 = cb3;
+}
+
+// 16-entry int8 lookup of the four 4-bit codes in bits 0-3 of each byte of c (bits 4-7 ignored)
+// with v_perm: entries 0-7 and 8-15 are looked up separately and merged by the code's bit 3
+// (selector byte 4 picks byte 0 of 0xFFFFFFFF, selector 12 yields 0x00).
+__device__ __forceinline__ uint32_t lut16(uint32_t c, const Tables& tb) {
+  const uint32_t s = c & tb.k7;
+  const uint32_t lo = __builtin_amdgcn_perm(tb.nl4[1], tb.nl4[0], s);
+  const uint32_t hi = __builtin_amdgcn_perm(tb.nl4[3], tb.nl4[2], s);
+  const uint32_t m = __builtin_amdgcn_perm(0xFFFFFFFFu, 0u, (c & tb.k8) | tb.k4);
   return (lo & m) | (hi & ~m);
 }
 
@@ -162,11 +192,6 @@ __device__ __forceinline__ uint32_t apply_sign(uint32_t mag, uint32_t nib) {
   return (mag ^ m) + t;                                     // ~mag + 1 per selected byte
 }
 
-struct Tables {
-  uint32_t nl4[4];                       // NL4 table in registers
-  const MOE_LDS uint32_t* cb2;           // 256 x 8 B grid in LDS (2 dwords per row)
-  const MOE_LDS uint32_t* cb3;           // 512 x 4 B grid in LDS (1 dword per row)
-};
 
 // Decode weight unit u (32 weights, u = 32-weight index inside the row) of a row whose first byte
 // sits at LDS byte offset `row`. c[k] holds the codes of weights 4k..4k+3 of the unit.
@@ -192,8 +217,8 @@ __device__ __forceinline__ void decode_unit(const MOE_LDS uint32_t* W, uint32_t 
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t n = __builtin_amdgcn_alignbyte(w[k + 1], w[k], sh);
-      c[k] = lut16(n & 0x0F0F0F0Fu, tb.nl4);            // weights 4k..4k+3
-      c[k + 4] = lut16((n >> 4) & 0x0F0F0F0Fu, tb.nl4);  // weights 16+4k..16+4k+3
+      c[k] = lut16(n, tb);            // weights 4k..4k+3 (low nibbles)
+      c[k + 4] = lut16(n >> 4, tb);   // weights 16+4k..16+4k+3 (high nibbles)
     }
   } else if constexpr (FMT == CB2) {
     const uint32_t so = row + 70u * (uint32_t)(u >> 3);

@@ -132,6 +132,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroup barrier for handing LDS between waves while global loads stay in flight: each wave's
+// LDS operations before it have completed (lgkmcnt(0)), and the asm's memory clobber keeps the
+// compiler from moving memory operations across it. (__syncthreads would also wait for every
+// outstanding vector-memory load, direct-to-LDS stream chunks included.) Data a wave loaded into
+// LDS directly must have been waited for (vmcnt) by that wave before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // s_waitcnt vmcnt(n) for n = 0..63, leaving expcnt and lgkmcnt alone (gfx9 encoding: vmcnt low
 // bits [3:0], high bits [15:14], expcnt [6:4], lgkmcnt [11:8]).
 #define MOE_VM(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
@@ -176,6 +185,20 @@ __device__ __forceinline__ uint32_t span_b_chunk(uint64_t a, uint32_t na) {
   return (((uint32_t)(a & 15) + na + 15) >> 4) + 1;
 }
 
+// Copy `bytes` (a multiple of 16) from a 16-byte aligned global span into LDS with direct-to-LDS
+// 16-byte loads, 1 KB per instruction, the pieces spread over waves [0, nw); lanes past the end
+// stay masked off. Every instruction is issued before anything the caller issues afterwards.
+__device__ __forceinline__ void dma_span(const uint8_t* src, uint32_t bytes, MOE_LDS uint8_t* dst, int wave,
+                                         int nw) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t nc = bytes >> 4;
+  for (uint32_t p = (uint32_t)wave; 64 * p < nc; p += (uint32_t)nw) {
+    const uint32_t c = 64 * p + lane;
+    if (c < nc)
+      __builtin_amdgcn_global_load_lds((const void*)(src + 16ull * c), (MOE_LDS void*)(dst + 1024 * p), 16, 0, 0);
+  }
+}
+
 // ------------------------------------------------------------------ activations in LDS ------
 
 // q8_1 activations in split form: 16-byte halves of the quants and the float scale per 32-value
@@ -202,6 +225,21 @@ __device__ __forceinline__ ActSplit act_layout(MOE_LDS uint8_t* p, int rows, int
   return a;
 }
 __host__ __device__ inline int act_bytes(int rows, int U) { return (rows * U * 36 + 15) & ~15; }
+
+// The same split form with each of its three regions padded to whole KB, so that whole-KB
+// direct-to-LDS pieces land inside it.
+__host__ __device__ inline int kb_pad(int b) { return (b + 1023) & ~1023; }
+__device__ __forceinline__ ActSplit act_layout_kb(MOE_LDS uint8_t* p, int rows, int U) {
+  ActSplit a;
+  a.lo = (MOE_LDS u32x4*)p;
+  a.hi = (MOE_LDS u32x4*)(p + kb_pad(rows * U * 16));
+  a.d = (MOE_LDS float*)(p + 2 * kb_pad(rows * U * 16));
+  a.U = U;
+  return a;
+}
+__host__ __device__ inline int act_bytes_kb(int rows, int U) {
+  return 2 * kb_pad(rows * U * 16) + kb_pad(rows * U * 4);
+}
 
 // Activation rows are staged in a fixed unrolled shape (constant register indices, no scratch):
 // float rows as one float4 per lane and pass (8 lanes per 32-value block, quantized with an
@@ -463,6 +501,25 @@ __device__ __forceinline__ void swiglu_q81_lanes(float gv, float uv, int l32, bo
   }
 }
 
+// Same block, stored in split form: quants 0-15 to lo, 16-31 to hi, the scale as float f(d16).
+__device__ __forceinline__ void swiglu_q81_split(float gv, float uv, int l32, bool live, uint8_t* lo,
+                                                 uint8_t* hi, float* dq) {
+  const float h = live ? swiglu(gv, uv) : 0.0f;
+  const float amax = wave_max32(__builtin_fabsf(h));
+  const float d = amax / 127.0f;
+  int q = 0;
+  if (amax != 0.0f) {
+    float r = round_half_away(h / d);
+    r = r > 127.0f ? 127.0f : r;
+    r = r < -127.0f ? -127.0f : r;
+    q = (int)r;
+  }
+  if (live) {
+    (l32 < 16 ? lo : hi)[l32 & 15] = (uint8_t)(q & 0xFF);
+    if (l32 == 0) *dq = h2f(f2h(d));
+  }
+}
+
 // ------------------------------------------------------------------ routing (one wave) ------
 
 // Unsigned key with the order of the float (-0 and +0 share a key).
@@ -571,6 +628,82 @@ __device__ __forceinline__ void route_wave(const MOE_LDS float* lg, int E, int k
     route_wave_v<16>(lg, E, k, ids, w, scr);
 }
 
+// Top-k of up to T tokens at once by a workgroup, when every token's logits are staged in LDS (row
+// t at lg + t Epad), in three steps:
+//  1. route_keys: every logit becomes its order key in place (0 past E, below every real key);
+//  2. route_ranks: an expert's rank = the number of experts that beat it (larger key, or equal key
+//     and lower id), counted by P lanes over 1/P of the row each and summed across those lanes;
+//     ranks below k are the selection, already in rank order;
+//  3. route_weights: ex_j = exp(l_j - l_0), w_j = ex_j / (((ex_0 + ex_1) + ex_2) + ...).
+// Same selection, order and weights as route_wave. scr: 192 words of LDS.
+template <int NT>
+__device__ __forceinline__ void route_keys(MOE_LDS float* lg, int Epad, int T, int E) {
+  for (int i = threadIdx.x; i < T * Epad; i += NT) {
+    const int e = i - (i / Epad) * Epad;
+    const float v = lg[i];
+    ((MOE_LDS uint32_t*)lg)[i] = e < E ? fkey(v) : 0u;
+  }
+}
+__host__ __device__ inline int route_lanes(int T, int E) {   // P lanes per expert
+  const int TE = T * E;
+  return TE <= 128 ? 4 : (TE <= 256 ? 2 : 1);
+}
+// Threads tid < nthr (a multiple of 64, >= T E P) take the experts.
+__device__ __forceinline__ void route_ranks(const MOE_LDS uint32_t* keys, int Epad, int T, int E, int k, int nthr,
+                                            MOE_LDS int* ids, MOE_LDS float* scr) {
+  const int tid = threadIdx.x;
+  const int P = route_lanes(T, E), lgP = P == 4 ? 2 : (P == 2 ? 1 : 0);
+  const int SL4 = Epad / P / 4;   // 16-byte words per slice (a multiple of 4)
+  for (int cs = tid; cs < T * E * P; cs += nthr) {   // every lane of a P-lane group runs the same trips
+    int c = cs >> lgP, t = 0;
+    const int pp = cs & (P - 1);
+    while (c >= E) {
+      c -= E;
+      ++t;
+    }
+    const int e = c;
+    const MOE_LDS uint32_t* row = keys + t * Epad;
+    const uint32_t key = row[e];
+    const MOE_LDS u32x4* sl = (const MOE_LDS u32x4*)(row + pp * SL4 * 4);
+    int part = 0;
+    for (int q = 0; q < SL4; q += 4) {   // four 16-byte reads in flight
+      u32x4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = sl[q + j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int o = (pp * SL4 + q + j) * 4;
+        part += (v[j].x > key) | ((v[j].x == key) & (o + 0 < e));
+        part += (v[j].y > key) | ((v[j].y == key) & (o + 1 < e));
+        part += (v[j].z > key) | ((v[j].z == key) & (o + 2 < e));
+        part += (v[j].w > key) | ((v[j].w == key) & (o + 3 < e));
+      }
+    }
+    if (P >= 2) part += __shfl_xor(part, 1);
+    if (P >= 4) part += __shfl_xor(part, 2);
+    if (pp == 0 && part < k) {
+      ids[t * k + part] = e;
+      scr[t * k + part] = unkey(key);
+    }
+  }
+}
+template <int NT>
+__device__ __forceinline__ void route_weights(int T, int k, MOE_LDS float* w, MOE_LDS float* scr) {
+  const int tid = threadIdx.x;
+  MOE_LDS float* rlg = scr;          // [T k] selected logits in rank order
+  MOE_LDS float* rex = scr + 64;     // [T k] exp terms
+  MOE_LDS float* rsum = scr + 128;   // [T] sums
+  if (tid < T * k) rex[tid] = expf(rlg[tid] - rlg[(tid / k) * k]);
+  __syncthreads();
+  if (tid < T) {
+    float s = 0.0f;
+    for (int j = 0; j < k; ++j) s = s + rex[tid * k + j];
+    rsum[tid] = s;
+  }
+  __syncthreads();
+  if (tid < T * k) w[tid] = rex[tid] / rsum[tid / k];
+}
+
 // ------------------------------------------------------------------ plan in LDS -------------
 
 struct PlanL {
@@ -633,10 +766,15 @@ __device__ __forceinline__ void group_wave(const PlanL& p, int n, int k, int E, 
       e = -1;
     }
   }
-  p.skey[lane] = key;
+  p.skey[lane] = key;   // every lane: keys past n stay above every real key
   wave_lds_sync();
   int r = 0;
-  for (int o = 0; o < n; ++o) r += p.skey[o] < key;
+  u32x4 kk[16];
+#pragma unroll
+  for (int o4 = 0; o4 < 16; ++o4) kk[o4] = ((const MOE_LDS u32x4*)p.skey)[o4];
+#pragma unroll
+  for (int o4 = 0; o4 < 16; ++o4)
+    r += (kk[o4].x < key) + (kk[o4].y < key) + (kk[o4].z < key) + (kk[o4].w < key);
   const bool valid = e >= 0;
   const int nv = __popcll(__ballot(valid));
   if (valid) {
@@ -747,7 +885,9 @@ struct GuArgs {
   float* g;             // composed: g rows (absolute entry, stride ld)
   float* u;
   int ld;
-  uint8_t* hq;          // fused / routed: workspace q8_1 rows of h (relative entry)
+  uint32_t* hq_lo;      // fused / routed: workspace q8_1 rows of h in split form (relative entry):
+  uint32_t* hq_hi;      //   16-byte low and high halves of each block's quants, float scales
+  float* hq_d;
   uint8_t* desc;        // fused / routed: the call's descriptor for the down launch
   const float* logits;  // routed: [T][E] router logits
   int T, E, k;
@@ -785,7 +925,8 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   MOE_LDS float* lgs = (MOE_LDS float*)ring;   // routed: staged logits (prologue only)
   const int Epad = logits_pad(a.E);
 
-  // ---- 1. every load that depends on nothing, at once
+  // ---- 1. every load that depends on nothing, at once. The ring is free until the stream
+  //         starts: it stages the first kRouteWaves tokens' logits and the activation rows.
   uint32_t t_nl4[4] = {0u, 0u, 0u, 0u};
   if (a.A.nl4) {
     const uint32_t* t = (const uint32_t*)a.A.nl4;
@@ -814,40 +955,108 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     if (tid <= a.P.cap_groups) r_gs = a.P.grp_start[tid];
     if (tid < a.P.cap_groups) r_ge = a.P.grp_expert[tid];
   }
-
-  // ---- 2. activations of every token; while their loads fly, waves route their token
-  Tables tb;
-  tb.nl4[0] = t_nl4[0];
-  tb.nl4[1] = t_nl4[1];
-  tb.nl4[2] = t_nl4[2];
-  tb.nl4[3] = t_nl4[3];
-  tb.cb2 = g2;
-  tb.cb3 = g3;
-  const int rT = a.T, rE = a.E, rk = a.k;
-  auto mid = [=](int pending) {
-    if constexpr (MODE == GU_ROUTED) {
-      if (wave < kRouteWaves && wave < rT) {
-        wait_vm(pending);   // every load before this thread's activation loads, the logits too
-        route_wave(lgs + wave * Epad, rE, rk, pl.rid + wave * rk, pl.rw + wave * rk, pl.rscr + wave * 96);
+  // float activation rows: staged by every wave, quantized from LDS in passes of kGuThreads float4
+  const int lg_bytes = MODE == GU_ROUTED ? kRouteWaves * Epad * 4 : 0;
+  MOE_LDS uint8_t* xs = ring + lg_bytes;
+  const int row_bytes = a.A.n_embd * 4;
+  const int rows_per = MODE == GU_COMPOSED ? 0 : max(1, (a.lds_ring - lg_bytes) / row_bytes);
+  auto stage_rows = [&](int r0, int nr) {
+    dma_span((const uint8_t*)(a.x + (size_t)r0 * a.A.n_embd), (uint32_t)(nr * row_bytes), xs, wave, kGuWaves);
+  };
+  // threads q (0 <= q < nq, nq a multiple of 64) quantize: trips are uniform per wave (the DPP max
+  // needs every lane of the wave)
+  auto quant_rows = [&](int r0, int nr, int q, int nq) {
+    const int nf4 = nr * G.U * 8;
+    const MOE_LDS f32x4* xv = (const MOE_LDS f32x4*)xs;
+    MOE_LDS uint32_t* lo32 = (MOE_LDS uint32_t*)act.lo;
+    MOE_LDS uint32_t* hi32 = (MOE_LDS uint32_t*)act.hi;
+    for (int base = 0; base < nf4; base += nq) {
+      const int f = base + q;
+      const f32x4 v = f < nf4 ? xv[f] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      float m = fmaxf(fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
+                      fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w)));
+      m = fmaxf(m, dpp<0xB1>(m));    // xor 1
+      m = fmaxf(m, dpp<0x4E>(m));    // xor 2
+      m = fmaxf(m, dpp<0x141>(m));   // the other quad of the 8 lanes of a block
+      if (f < nf4) {
+        const int b = r0 * G.U + (f >> 3), part = f & 7;
+        const float d = m / 127.0f;
+        uint32_t packed = 0;
+        if (m != 0.0f) {
+          const float xs4[4] = {v.x, v.y, v.z, v.w};
+          for (int j = 0; j < 4; ++j) {
+            float r = round_half_away(xs4[j] / d);
+            r = r > 127.0f ? 127.0f : r;
+            r = r < -127.0f ? -127.0f : r;
+            packed |= ((uint32_t)(int)r & 0xFFu) << (8 * j);
+          }
+        }
+        if (part < 4)
+          lo32[b * 4 + part] = packed;
+        else
+          hi32[b * 4 + part - 4] = packed;
+        if (part == 0) act.d[b] = h2f(f2h(d));
       }
     }
   };
-  if constexpr (MODE == GU_COMPOSED)
-    act_stage_q<kGuThreads, kGuXPass>(a.xq, a.n_tokens * G.U, act, mid);
-  else
-    act_stage_f<kGuThreads, kGuXPass>(a.x, a.A.n_embd, a.n_tokens * G.U, G.U, act, mid);
+  if constexpr (MODE != GU_COMPOSED) stage_rows(0, min(a.n_tokens, rows_per));
+
+  // ---- 2. the loads land; routing (whole workgroup) and the activations' q8_1 blocks
+  Tables tb;
+  tables_init(tb, t_nl4, g2, g3);
+  if constexpr (MODE == GU_COMPOSED) {
+    act_stage_q<kGuThreads, kGuXPass>(a.xq, a.n_tokens * G.U, act, [](int) {});
+    __syncthreads();
+  } else {
+    __syncthreads();   // (waits for every load of round 1, the staged logits and rows included)
+    // routed: keys, then the ranks on the first threads while the others quantize x
+    int rthr = 0;
+    if constexpr (MODE == GU_ROUTED) {
+      if (a.T <= kRouteWaves) {
+        route_keys<kGuThreads>(lgs, Epad, a.T, a.E);
+        __syncthreads();
+        rthr = min(kGuThreads, (a.T * a.E * route_lanes(a.T, a.E) + 63) & ~63);
+        if (tid < rthr)
+          route_ranks((const MOE_LDS uint32_t*)lgs, Epad, a.T, a.E, a.k, rthr, pl.rid, (MOE_LDS float*)pl.rscr);
+      }
+    }
+    if (rthr < kGuThreads) {
+      if (tid >= rthr) quant_rows(0, min(a.n_tokens, rows_per), tid - rthr, kGuThreads - rthr);
+    } else {
+      quant_rows(0, min(a.n_tokens, rows_per), tid, kGuThreads);
+    }
+    if constexpr (MODE == GU_ROUTED) {
+      if (a.T <= kRouteWaves) {
+        __syncthreads();
+        route_weights<kGuThreads>(a.T, a.k, pl.rw, (MOE_LDS float*)pl.rscr);
+      }
+    }
+    for (int r0 = rows_per; r0 < a.n_tokens; r0 += rows_per) {   // more rows than the staging holds
+      __syncthreads();
+      stage_rows(r0, min(rows_per, a.n_tokens - r0));
+      __syncthreads();
+      quant_rows(r0, min(rows_per, a.n_tokens - r0), tid, kGuThreads);
+    }
+  }
   if constexpr (FMT == CB2 || FMT == CB3)
     if (tid < 512) (FMT == CB2 ? g2 : g3)[tid] = t_cb;
   if constexpr (MODE == GU_ROUTED) {
     if (tid < a.T) pl.dtok[tid] = r_dt;
     if (tid < a.E) pl.emap[tid] = -1;
-    // tokens past the first kRouteWaves: one more round per kRouteWaves tokens
-    if (wave < kRouteWaves) {
-      for (int t = wave + kRouteWaves; t < a.T; t += kRouteWaves) {
-        issue_logits(a.logits + (size_t)t * a.E, a.E, lgs + wave * Epad);
-        __builtin_amdgcn_s_waitcnt(MOE_VM(0));
-        route_wave(lgs + wave * Epad, a.E, a.k, pl.rid + t * a.k, pl.rw + t * a.k, pl.rscr + wave * 96);
-      }
+    // longer windows: kRouteWaves tokens per round, their logits staged again
+    for (int t0 = 0; a.T > kRouteWaves && t0 < a.T; t0 += kRouteWaves) {
+      const int nt = min(kRouteWaves, a.T - t0);
+      __syncthreads();
+      if (wave < nt) issue_logits(a.logits + (size_t)(t0 + wave) * a.E, a.E, lgs + wave * Epad);
+      __syncthreads();
+      route_keys<kGuThreads>(lgs, Epad, nt, a.E);
+      __syncthreads();
+      const int nthr = min(kGuThreads, (nt * a.E * route_lanes(nt, a.E) + 63) & ~63);
+      if (tid < nthr)
+        route_ranks((const MOE_LDS uint32_t*)lgs, Epad, nt, a.E, a.k, nthr, pl.rid + t0 * a.k,
+                    (MOE_LDS float*)pl.rscr);
+      __syncthreads();
+      route_weights<kGuThreads>(nt, a.k, pl.rw + t0 * a.k, (MOE_LDS float*)pl.rscr);
     }
   } else {
     if (tid == 0) pl.misc[3] = r_ng;
@@ -994,7 +1203,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
         ++issued;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // the block's outputs: composed, g and u rows; fused / routed, SwiGLU + q8_1 of h
     const int ne = a1 - a0;
     if (wgv) {
@@ -1011,12 +1220,13 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
           const bool live = e < ne && pl.elive[a0 + (e < ne ? e : 0)] != 0;
           const float gv = live ? stage[e * 64 + l32] : 0.0f;
           const float uv = live ? stage[e * 64 + 32 + l32] : 0.0f;
-          uint8_t* blkp = a.hq + ((size_t)(a0 + (live ? e : 0)) * nb + blk) * 36;
-          swiglu_q81_lanes(gv, uv, l32, live, blkp, nullptr);
+          const size_t b = (size_t)(a0 + (live ? e : 0)) * nb + blk;
+          swiglu_q81_split(gv, uv, l32, live, (uint8_t*)(a.hq_lo + 4 * b), (uint8_t*)(a.hq_hi + 4 * b),
+                           a.hq_d + b);
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -1030,13 +1240,17 @@ struct DnArgs {
   Geom G;
   Stream S;
   const uint8_t* desc;  // DN_DESC: the call's descriptor
-  const uint8_t* hq;    // q8_1 rows of h: DN_DESC by entry - e0 (workspace), DN_PLAN by absolute entry
+  const uint8_t* hq;    // DN_PLAN: q8_1 rows of h by absolute entry
+  const uint8_t* hq_lo; // DN_DESC: the workspace's split q8_1 rows of h (entry - e0)
+  const uint8_t* hq_hi;
+  const uint8_t* hq_d;
   float* Y;
   int n_rows, ldy;
   int lds_ring, lds_act;
 };
 
-constexpr int kDnFixed = 4096 + kDescBytes + 4 * 3 * kMaxEnt + 256;
+constexpr int kDnYBuf = kMaxEnt * 16;   // floats: the first tile's destination rows, per owner
+constexpr int kDnFixed = 4096 + kDescBytes + 4 * 5 * kMaxEnt + 256 + 4 * kDnYBuf;
 
 __host__ __device__ inline int dn_smem_bytes(int lds_ring, int lds_act, int rp) {
   return lds_ring + lds_act + kMaxEnt * rp * 4 + kDnFixed;
@@ -1062,7 +1276,10 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   MOE_LDS int* mdst = (MOE_LDS int*)((MOE_LDS uint8_t*)dsc + kDescBytes);   // [kMaxEnt] dst or -1
   MOE_LDS int* mown = mdst + kMaxEnt;                        // [kMaxEnt] first live entry of its dst
   MOE_LDS float* mw = (MOE_LDS float*)(mown + kMaxEnt);      // [kMaxEnt]
-  MOE_LDS int* misc = (MOE_LDS int*)(mw + kMaxEnt);          // [64]
+  MOE_LDS int* omap = (MOE_LDS int*)(mw + kMaxEnt);          // [kMaxEnt] owner index of an owner entry
+  MOE_LDS int* ownl = omap + kMaxEnt;                        // [kMaxEnt] owner entries in order
+  MOE_LDS int* misc = ownl + kMaxEnt;                        // [64]
+  MOE_LDS float* ybuf = (MOE_LDS float*)(misc + 64);         // [owner][rp] first tile's Y rows
 
   // ---- 1. tables and the call (descriptor: one read; caller's plan: validated, two reads)
   uint32_t t_nl4[4] = {0u, 0u, 0u, 0u};
@@ -1093,12 +1310,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
     if (tid < a.P.cap_groups) dsc[kDescDst + tid] = r_ge;
   }
   Tables tb;
-  tb.nl4[0] = t_nl4[0];
-  tb.nl4[1] = t_nl4[1];
-  tb.nl4[2] = t_nl4[2];
-  tb.nl4[3] = t_nl4[3];
-  tb.cb2 = g2;
-  tb.cb3 = g3;
+  tables_init(tb, t_nl4, g2, g3);
   if constexpr (FMT == CB2 || FMT == CB3) (FMT == CB2 ? g2 : g3)[tid] = t_cb;
   __syncthreads();
   if constexpr (MODE == DN_PLAN) {
@@ -1154,15 +1366,29 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
     mw[tid] = ((MOE_LDS float*)dsc)[kDescW + tid];
   }
   __syncthreads();
-  if (tid < n) {
-    const int d = mdst[tid];
-    int owner = d >= 0;
-    for (int q = 0; q < tid && owner; ++q) owner = mdst[q] != d;
-    mown[tid] = owner;
+  if (wave == 0) {   // n <= 64: one lane per entry
+    const int lane = tid;
+    int owner = 0;
+    if (lane < n) {
+      const int d = mdst[lane];
+      owner = d >= 0;
+      for (int q = 0; q < lane && owner; ++q) owner = mdst[q] != d;
+      mown[lane] = owner;
+    }
+    const uint64_t om = __ballot(owner);
+    if (owner) {
+      const int o = __popcll(om & ((1ull << lane) - 1ull));
+      omap[lane] = o;
+      ownl[o] = lane;
+    }
+    if (lane == 0) misc[8] = __popcll(om);
   }
+  __syncthreads();
+  const int nown = uni(misc[8]);
 
-  // ---- 2. h rows: their loads first, then the first chunks of the stream, then the h rows to LDS
-  const ActSplit act = act_layout(actp, n, U);
+  // ---- 2. h rows and the first tile's destination rows first, then the first chunks of the
+  //         stream, then (DN_PLAN) the h rows to LDS
+  const ActSplit act = MODE == DN_DESC ? act_layout_kb(actp, n, U) : act_layout(actp, n, U);
   const int ntiles = (a.A.n_embd + G.rp - 1) / G.rp;
   const int ntw = (int)blockIdx.x < ntiles ? (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
   const int cpt = wave < ng ? (ng - wave + kDnWaves - 1) / kDnWaves : 0;   // this wave's groups
@@ -1181,13 +1407,33 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
       issue_chunk(slot, M, (const uint8_t*)a.P.err, 1, nullptr, 0, 0);
   };
   const int pre = min(NS, nch);
+  const int r00 = (int)blockIdx.x * G.rp, nr0 = min(G.rp, a.A.n_embd - r00);   // first tile
   auto mid = [&](int) {
+    // the first tile's rows of every destination: one float per lane, wave 0
+    if (wave == 0 && ntw > 0) {
+      for (int p = 0; p * 64 < nown * nr0; ++p) {
+        const int l = p * 64 + (tid & 63);
+        if (l < nown * nr0) {
+          const int o = l / nr0, m = l - o * nr0;
+          const float* src = a.Y + (size_t)mdst[ownl[o]] * a.ldy + r00 + m;
+          __builtin_amdgcn_global_load_lds((const void*)src, (MOE_LDS void*)(ybuf + 64 * p), 4, 0, 0);
+        }
+      }
+    }
     for (int kc = 0; kc < pre; ++kc) issue(kc, myring + kc * M * 1024);
-    wait_vm(pre * M);   // the h loads, older than every chunk, have landed
+    wait_vm(pre * M);   // the h rows and Y rows, older than every chunk, have landed
   };
-  act_stage_q<kDnThreads, 16>(a.hq + (MODE == DN_PLAN ? (size_t)e0 * U * 36 : 0), n * U, act, mid);
+  if constexpr (MODE == DN_DESC) {
+    const uint32_t qb = (uint32_t)(n * U * 16), db = (uint32_t)((n * U * 4 + 15) & ~15);
+    dma_span(a.hq_lo, qb, (MOE_LDS uint8_t*)act.lo, wave, kDnWaves);
+    dma_span(a.hq_hi, qb, (MOE_LDS uint8_t*)act.hi, (wave + 3) % kDnWaves, kDnWaves);
+    dma_span(a.hq_d, db, (MOE_LDS uint8_t*)act.d, (wave + 6) % kDnWaves, kDnWaves);
+    mid(0);
+  } else {
+    act_stage_q<kDnThreads, 16>(a.hq + (size_t)e0 * U * 36, n * U, act, mid);
+  }
   int issued = pre;
-  __syncthreads();
+  lds_barrier();
 
   // ---- 3. tiles
   int kc = 0;
@@ -1217,19 +1463,19 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
         ++issued;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // scatter: one thread per (owner entry, row)
     for (int idx = tid; idx < n * nr; idx += kDnThreads) {
       const int i = idx / nr, m = idx - i * nr;
       if (!mown[i]) continue;
       const int d = mdst[i];
       float* y = a.Y + (size_t)d * a.ldy + r0 + m;
-      float acc = *y;
+      float acc = kt == 0 ? ybuf[omap[i] * nr + m] : *y;
       for (int q = i; q < n; ++q)
         if (mdst[q] == d) acc = acc + mw[q] * ores[q * G.rp + m];
       *y = acc;
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -1393,16 +1639,20 @@ Stream dn_stream(const Geom& G, int ns) {
 }
 
 struct WsLayout {
-  size_t hq, total;
+  size_t lo, hi, d, total;
 };
 
 size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// The call's descriptor, then the q8_1 rows of h by entry - e0.
+// The call's descriptor, then the q8_1 rows of h in split form (row = entry - e0): the 16-byte low
+// halves of every block's quants, the high halves, the float scales.
 WsLayout ws_layout(const moe_layer* L, const moe_plan* P) {
   WsLayout w{};
-  w.hq = kDescReserve;
-  w.total = w.hq + al256((size_t)P->cap_entries * (L->n_ff / 32) * 36);
+  const size_t blocks = (size_t)P->cap_entries * (L->n_ff / 32);
+  w.lo = kDescReserve;
+  w.hi = w.lo + al256(blocks * 16);
+  w.d = w.hi + al256(blocks * 16);
+  w.total = w.d + al256(blocks * 4);
   return w;
 }
 
@@ -1514,8 +1764,9 @@ int gu_lds(const moe_layer* L, int n_tokens, bool routed, Stream* S, int* sw, in
   const Geom G = make_geom(L->fmt_gate_up, L->n_embd, true);
   *actb = act_bytes(n_tokens, G.U);
   if (*actb > kGuActMax) return -1;
-  // the routed prologue stages kRouteWaves tokens' logits in the ring before it streams
-  const int lg = routed ? kRouteWaves * logits_pad(L->n_experts) * 4 : 0;
+  // the prologue stages (routed) kRouteWaves tokens' logits and at least one float row of x in
+  // the ring before it streams
+  const int lg = (routed ? kRouteWaves * logits_pad(L->n_experts) * 4 : 0) + L->n_embd * 4;
   const int avail = kLdsMax - gu_smem_bytes(0, *actb);
   for (int ns = 2; ns >= 1; --ns) {
     *S = gu_stream(G, ns);
@@ -1532,21 +1783,24 @@ int gu_lds(const moe_layer* L, int n_tokens, bool routed, Stream* S, int* sw, in
 
 int dn_lds(const moe_layer* L, const moe_plan* P, Stream* S, int* ring, int* actb) {
   const Geom G = make_geom(L->fmt_down, L->n_ff, false);
-  *actb = act_bytes(P->cap_entries, G.U);
+  *actb = act_bytes_kb(P->cap_entries, G.U);
   if (*actb > kDnActMax) return -1;
+  const int tiles = (L->n_embd + G.rp - 1) / G.rp;
+  // two slots per wave only while every tile still gets a workgroup of its own at once
   for (int ns = 2; ns >= 1; --ns) {
     *S = dn_stream(G, ns);
     *ring = kDnWaves * S->NS * S->M * 1024;
     const int b = dn_smem_bytes(*ring, *actb, G.rp);
-    if (b <= kLdsMax) return b;
+    if (b > kLdsMax) continue;
+    if (ns == 1 || (kLdsMax / b) * num_cus() >= tiles) return b;
   }
   return -1;
 }
 
 // The gate/up kernel of `mode`.
 int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, const void* act,
-                int n_tokens, float* g, float* u, int ld, uint8_t* hq, uint8_t* desc, const float* logits,
-                int T, int k, const int32_t* dst_of_token, int entry_base, int grid_limit) {
+                int n_tokens, float* g, float* u, int ld, uint8_t* ws, const float* logits, int T, int k,
+                const int32_t* dst_of_token, int entry_base, int grid_limit) {
   const Geom G = make_geom(L->fmt_gate_up, L->n_embd, true);
   int ring = 0, actb = 0, sw = 0;
   Stream S{};
@@ -1563,8 +1817,13 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
   ga.g = g;
   ga.u = u;
   ga.ld = ld;
-  ga.hq = hq;
-  ga.desc = desc;
+  if (ws) {
+    const WsLayout wl = ws_layout(L, P);
+    ga.hq_lo = (uint32_t*)(ws + wl.lo);
+    ga.hq_hi = (uint32_t*)(ws + wl.hi);
+    ga.hq_d = (float*)(ws + wl.d);
+  }
+  ga.desc = ws;
   ga.logits = logits;
   ga.T = T;
   ga.E = L->n_experts;
@@ -1580,7 +1839,7 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
   return e == hipSuccess ? MOE_OK : hip_fail(e, "gate/up kernel");
 }
 
-int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, const uint8_t* desc,
+int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, const uint8_t* ws,
              const uint8_t* hq, float* Y, int n_rows, int ldy, int grid_limit) {
   const Geom G = make_geom(L->fmt_down, L->n_ff, false);
   int ring = 0, actb = 0;
@@ -1592,8 +1851,14 @@ int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, co
   da.P = plan_args(P);
   da.G = G;
   da.S = S;
-  da.desc = desc;
+  da.desc = ws;
   da.hq = hq;
+  if (ws) {
+    const WsLayout wl = ws_layout(L, P);
+    da.hq_lo = ws + wl.lo;
+    da.hq_hi = ws + wl.hi;
+    da.hq_d = ws + wl.d;
+  }
   da.Y = Y;
   da.n_rows = n_rows;
   da.ldy = ldy;
@@ -1667,8 +1932,8 @@ int moe_gate_up(void* stream, const moe_layer* L, const moe_plan* P, const void*
   if ((rc = check_plan(P))) return rc;
   if (!xq || !g || !u || ld < L->n_ff || n_tokens < 0 || grid_limit < 0) return MOE_E_ARG;
   if ((uintptr_t)xq & 3) return MOE_E_ARG;
-  return run_gate_up((hipStream_t)stream, L, P, GU_COMPOSED, xq, n_tokens, g, u, ld, nullptr, nullptr,
-                     nullptr, 0, 0, nullptr, 0, grid_limit);
+  return run_gate_up((hipStream_t)stream, L, P, GU_COMPOSED, xq, n_tokens, g, u, ld, nullptr, nullptr, 0,
+                     0, nullptr, 0, grid_limit);
 }
 
 int moe_swiglu_q8_1(void* stream, const moe_plan* P, const float* g, const float* u, int n_ff, int ld,
@@ -1690,12 +1955,15 @@ size_t moe_workspace_bytes(const moe_layer* L, const moe_plan* P) {
   return ws_layout(L, P).total;
 }
 
-int moe_workspace_layout(const moe_layer* L, const moe_plan* P, size_t* hq_offset) {
+int moe_workspace_layout(const moe_layer* L, const moe_plan* P, size_t off[3]) {
   int rc = check_layer(L, true);
   if (rc) return rc;
   if ((rc = check_plan(P))) return rc;
-  if (!hq_offset) return MOE_E_ARG;
-  *hq_offset = ws_layout(L, P).hq;
+  if (!off) return MOE_E_ARG;
+  const WsLayout w = ws_layout(L, P);
+  off[0] = w.lo;
+  off[1] = w.hi;
+  off[2] = w.d;
   return MOE_OK;
 }
 
@@ -1728,7 +1996,7 @@ int moe_layer_gate_up(void* stream, const moe_layer* L, const moe_plan* P, const
   if (!ws || ws_bytes < wl.total || ((uintptr_t)ws & 255)) return MOE_E_WS;
   uint8_t* b = (uint8_t*)ws;
   return run_gate_up((hipStream_t)stream, L, P, logits ? GU_ROUTED : GU_FUSED, x, n_tokens, nullptr,
-                     nullptr, 0, b + wl.hq, b, logits, T, k, dst_of_token, entry_base, grid_limit);
+                     nullptr, 0, b, logits, T, k, dst_of_token, entry_base, grid_limit);
 }
 
 int moe_layer_down(void* stream, const moe_layer* L, const moe_plan* P, const void* ws, size_t ws_bytes,
@@ -1740,7 +2008,7 @@ int moe_layer_down(void* stream, const moe_layer* L, const moe_plan* P, const vo
   const WsLayout wl = ws_layout(L, P);
   if (!ws || ws_bytes < wl.total || ((uintptr_t)ws & 255)) return MOE_E_WS;
   const uint8_t* b = (const uint8_t*)ws;
-  return run_down((hipStream_t)stream, L, P, DN_DESC, b, b + wl.hq, Y, n_rows, ldy, grid_limit);
+  return run_down((hipStream_t)stream, L, P, DN_DESC, b, nullptr, Y, n_rows, ldy, grid_limit);
 }
 
 int moe_layer_decode(void* stream, const moe_layer* L, const moe_plan* P, const float* x, int n_tokens,

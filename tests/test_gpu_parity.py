@@ -136,9 +136,14 @@ def test_layer_stages(name):
     assert fused["err"] == 0
     assert np.array_equal(U.bits(fused["Y"]), U.bits(comp["Y"]))
     ws, off = fused["ws"].cpu().numpy(), fused["off"]
-    ne = int(ph["grp_start"][-1] - base)
-    hqw = ws[off:off + ne * (c.n_ff // 32) * 36].reshape(ne, -1)
-    assert np.array_equal(hqw, comp["hq"][base:base + ne])
+    ne, nb = int(ph["grp_start"][-1] - base), c.n_ff // 32
+    ref = comp["hq"][base:base + ne].reshape(ne, nb, 36)
+    lo = ws[off[0]:off[0] + ne * nb * 16].reshape(ne, nb, 16)
+    hi = ws[off[1]:off[1] + ne * nb * 16].reshape(ne, nb, 16)
+    dq = ws[off[2]:off[2] + ne * nb * 4].view(np.float32).reshape(ne, nb)
+    assert np.array_equal(lo, ref[:, :, 4:20]) and np.array_equal(hi, ref[:, :, 20:36])
+    d16 = ref[:, :, 0].astype(np.uint16) | (ref[:, :, 1].astype(np.uint16) << 8)
+    assert np.array_equal(U.bits(dq), U.bits(d16.view(np.float16).astype(np.float32)))
     # routing + grouping inside the gate/up launch: same plan, same bits
     r = U.run_routed(c, c.x, Y0, entry_base=base, dst_of_token=dst)
     assert r["err"] == 0
