@@ -165,6 +165,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time to measure")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the T = 1..4 lines")
+    ap.add_argument("--calib", action="store_true",
+                    help="first copy 256 MiB device to device (a known-size kernel for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this build "
@@ -179,6 +181,13 @@ def main():
 
     B.lib()
     torch.cuda.set_device(0)
+    if args.calib:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copy: 256 MiB read, 256 MiB written")
     log(f"building workload {args.workload}")
     wl = Workload(args.workload, device="cuda", log=log)
     per_layer = wl.weight_bytes_per_layer()
