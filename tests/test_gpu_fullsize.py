@@ -1,0 +1,159 @@
+"""Full-size GPU parity: the benchmark's own workloads and launch configuration against the oracle.
+
+The workloads are the benchmark's (``moe_routed_expert_route_amd.workloads``): 2560 x 768 NL4
+experts, 128 per layer, top-8, T = 1; the same geometry with CB2 gate/up, NL4 down and a T = 4
+Zipf window; 2560 x 640 CB3 gate/up + Q8_0 down, 256 experts, uniform routing at T = 4. A few
+layers of each are built (every layer has the same shape, grid and LDS plan as the 48 the
+benchmark runs), one step (gate/up launch + down launch per layer, routed from the logits) is
+captured in a HIP graph exactly as the benchmark captures it, and the graph is replayed with the
+program's own eager work in between. After each replay, per layer:
+
+* the plan the gate/up launch published equals the oracle's route + group, bit for bit (the
+  router weights, float32 on the device and double in the oracle, within 4 ulp);
+* the q8_1 rows of h the workspace holds match the oracle's chain (x -> q8_1 -> g, u -> SwiGLU
+  -> q8_1): identical blocks except where the device's float32 g or u sits a rounding away from
+  the double reference, which may move one quant by one step or the fp16 scale by one ulp;
+* Y is within 2e-5 x S of the oracle's down + weighted scatter fed the device's own q8_1 rows of
+  h (S = |Y0| + sum |w| sum |c_b|), and every replay gives the same bits.
+
+("#363 experts: smaller and fewer launches for the verify window's PCIe call", "Measured": the
+2560 x 768 call captured 48 times in a graph; "#2058 Verify window ...", "What changed": n_embd
+2560 with n_ff 640.)
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_routed_expert_route_amd import binding as B
+from moe_routed_expert_route_amd.workloads import Workload
+
+from . import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+LAYERS = 3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    B.lib()
+
+
+def _hq_rows(ws_np, off, ne, nb):
+    """36-byte q8_1 rows of h rebuilt from the workspace's split form (lo, hi, float d)."""
+    lo = ws_np[off[0]:off[0] + ne * nb * 16].reshape(ne, nb, 16)
+    hi = ws_np[off[1]:off[1] + ne * nb * 16].reshape(ne, nb, 16)
+    d = ws_np[off[2]:off[2] + ne * nb * 4].view(np.float32).reshape(ne, nb)
+    d16 = d.astype(np.float16)
+    assert np.array_equal(d16.astype(np.float32).view(np.uint32), d.view(np.uint32)), \
+        "workspace scale is not an fp16 value"
+    qsum = (lo.view(np.int8).astype(np.int32).sum(-1) + hi.view(np.int8).astype(np.int32).sum(-1))
+    s16 = (d * qsum.astype(np.float32)).astype(np.float16)   # exact product, then RNE
+    out = np.empty((ne, nb, 36), np.uint8)
+    out[:, :, 0:2] = d16.view(np.uint8).reshape(ne, nb, 2)
+    out[:, :, 2:4] = s16.view(np.uint8).reshape(ne, nb, 2)
+    out[:, :, 4:20] = lo
+    out[:, :, 20:36] = hi
+    return out
+
+
+def _near(got, ref):
+    """Blocks of h that differ: each quant by at most one step, the fp16 scale by at most one
+    ulp. Returns the number of differing blocks."""
+    got = got.reshape(-1, 36)
+    ref = ref.reshape(-1, 36)
+    bad = np.flatnonzero((got != ref).any(axis=1))
+    for b in bad:
+        dg = int(got[b, 0]) | int(got[b, 1]) << 8
+        dr = int(ref[b, 0]) | int(ref[b, 1]) << 8
+        assert abs(dg - dr) <= 1, f"block {b}: fp16 scale {hex(dg)} vs {hex(dr)}"
+        qg = got[b, 4:].view(np.int8).astype(np.int32)
+        qr = ref[b, 4:].view(np.int8).astype(np.int32)
+        assert np.abs(qg - qr).max() <= 1, f"block {b}: quants differ by more than one step"
+    return bad.size
+
+
+def _check_layer(wl, l, Y_np, Y0_np):
+    T, k, E = wl.T, wl.k, wl.E
+    # plan: bit-exact against the oracle's route + group
+    oids, ow = oracle.route_topk(wl.logits[l], k)
+    ref = oracle.build_plan(oids, ow.astype(np.float32), None, E, 0)
+    got = wl.plans[l].get()
+    for key in ("n_groups", "grp_expert", "grp_start", "ent_src", "ent_dst"):
+        assert np.array_equal(np.asarray(got[key]), np.asarray(ref[key])), (l, key)
+    # router weights: float32 on the device, double in the oracle (4 ulp, as in the router test);
+    # the scatter below takes the device's weights (its own upstream values)
+    ent_w = np.asarray(got["ent_w"], np.float32)
+    for gi in range(int(ref["n_groups"])):
+        e = int(ref["grp_expert"][gi])
+        for a in range(int(ref["grp_start"][gi]), int(ref["grp_start"][gi + 1])):
+            t = int(ref["ent_src"][a])
+            wo = float(ow[t][list(oids[t]).index(e)])
+            assert abs(float(ent_w[a]) - wo) <= 4 * float(np.spacing(np.float32(wo))), (l, a)
+    ref = dict(ref, ent_w=ent_w.copy())
+    assert wl.plans[l].errors() == 0
+    # the oracle's own chain, expert bytes regenerated from the seed (never read back)
+    experts = sorted(set(int(e) for e in ref["grp_expert"]))
+    gate, up, down = {}, {}, {}
+    for e in experts:
+        gate[e], up[e], down[e] = wl.host_expert(l, e)
+    tb = oracle.Tables(wl.tables["nl4"], wl.tables["cb2"], wl.tables["cb3"])
+    chain = oracle.layer(wl.x[l], ref, wl.fg, wl.fd, gate, up, down, wl.n_embd, wl.n_ff, Y0_np, tb)
+    # q8_1 rows of h from the workspace
+    ne, nb = T * k, wl.n_ff // 32
+    off = B.moe_workspace_layout(wl.layers[l], wl.plans[l])
+    hq = _hq_rows(wl.ws[l].cpu().numpy(), off, ne, nb)
+    hq_ref = np.stack([chain["hq"][a] for a in range(ne)]).reshape(ne, nb, 36)
+    nflip = _near(hq, hq_ref)
+    assert nflip <= max(2, ne * nb // 100), f"layer {l}: {nflip} of {ne * nb} h blocks differ"
+    # Y on the device's own q8_1 rows of h
+    o = oracle.down(ref, wl.fd, down, wl.n_embd, wl.n_ff, {a: hq[a] for a in range(ne)}, tb)
+    Yr, SY = oracle.scatter(ref, Y0_np, o)
+    return U.check_close(Y_np, Yr, SY, f"Y layer {l}"), nflip
+
+
+@pytest.mark.parametrize("name,T,routing", [
+    ("nl4_2560x768_t1", 1, None),
+    ("cb2nl4_2560x768_t4_zipf", 4, "zipf"),
+    ("cb3q8_2560x640", 4, "uniform"),
+])
+def test_fullsize_graph_step(name, T, routing):
+    wl = Workload(name, device="cuda", T=T, routing=routing, layers=LAYERS, key=0)
+    Y0 = [np.random.default_rng([7, l]).standard_normal((wl.T, wl.n_embd)).astype(np.float32)
+          for l in range(wl.L)]
+
+    def reset():
+        for l in range(wl.L):
+            wl.Y[l].copy_(torch.from_numpy(Y0[l]))
+
+    # eager first (as the benchmark does before capturing), then the captured step
+    reset()
+    wl.step()
+    torch.cuda.synchronize()
+    eager = [wl.Y[l].cpu().numpy() for l in range(wl.L)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        wl.step()
+    torch.cuda.synchronize()
+    worst = 0.0
+    for rep in range(3):
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(wl.L):
+            Y = wl.Y[l].cpu().numpy()
+            assert np.array_equal(U.bits(Y), U.bits(eager[l])), f"replay {rep} layer {l}"
+            if rep == 0:
+                err, nflip = _check_layer(wl, l, Y, Y0[l])
+                worst = max(worst, err)
+                print(f"{name} T={wl.T} layer {l}: max err/S {err:.3g}, h blocks off by a "
+                      f"rounding: {nflip}", flush=True)
+        # eager work of the program between replays
+        torch.zeros(1 << 20, device="cuda").sum().item()
+    del g
+    print(f"{name}: worst err/S {worst:.3g}")
