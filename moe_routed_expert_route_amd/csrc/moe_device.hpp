@@ -193,40 +193,81 @@ __device__ __forceinline__ uint32_t apply_sign(uint32_t mag, uint32_t nib) {
 }
 
 
-// Decode weight unit u (32 weights, u = 32-weight index inside the row) of a row whose first byte
-// sits at LDS byte offset `row`. c[k] holds the codes of weights 4k..4k+3 of the unit.
+// A weight unit (32 weights, u = 32-weight index inside its row) is read from LDS in two steps so
+// that the reads of the next unit can be in flight while this one is decoded: unit_load issues the
+// aligned dword reads covering the unit's fields, unit_decode turns them into codes. c[k] holds the
+// codes of weights 4k..4k+3 of the unit, sc the unit's scale.
 template <int FMT>
-__device__ __forceinline__ void decode_unit(const MOE_LDS uint32_t* W, uint32_t row, int u,
-                                            const Tables& tb, uint32_t c[8], float& sc) {
+struct URaw {
+  // Q8_0: scale pair, 9 quant dwords; NL4: scale pair, 5 nibble dwords; CB2: D, index, sign and
+  // sub-scale pairs; CB3: D, two index pairs, high-bit, sign and sub-scale pairs
+  uint32_t v[FMT == Q8_0 ? 11 : FMT == NL4 ? 7 : FMT == CB2 ? 8 : 12];
+  uint32_t o;   // byte offset of the unit (Q8_0, NL4) or of its 256-weight block (CB2, CB3)
+};
+
+template <int FMT>
+__device__ __forceinline__ void unit_load(const MOE_LDS uint32_t* W, uint32_t row, int u, URaw<FMT>& r) {
+  auto pair = [&](int j, uint32_t off) {
+    r.v[2 * j] = W[off >> 2];
+    r.v[2 * j + 1] = W[(off >> 2) + 1];
+  };
   if constexpr (FMT == Q8_0) {
     const uint32_t o = row + 34u * (uint32_t)u;
-    sc = h2f(ldw(W, o) & 0xFFFFu);
-    const uint32_t b = (o + 2) >> 2, sh = (o + 2) & 3u;
-    uint32_t w[9];
+    r.o = o;
+    pair(0, o);
+    const uint32_t b = (o + 2) >> 2;
 #pragma unroll
-    for (int i = 0; i < 9; ++i) w[i] = W[b + i];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_alignbyte(w[k + 1], w[k], sh);
+    for (int i = 0; i < 9; ++i) r.v[2 + i] = W[b + i];
   } else if constexpr (FMT == NL4) {
     const uint32_t o = row + 18u * (uint32_t)u;
-    sc = h2f(ldw(W, o) & 0xFFFFu);
-    const uint32_t b = (o + 2) >> 2, sh = (o + 2) & 3u;
-    uint32_t w[5];
+    r.o = o;
+    pair(0, o);
+    const uint32_t b = (o + 2) >> 2;
 #pragma unroll
-    for (int i = 0; i < 5; ++i) w[i] = W[b + i];
+    for (int i = 0; i < 5; ++i) r.v[2 + i] = W[b + i];
+  } else if constexpr (FMT == CB2) {
+    const uint32_t so = row + 70u * (uint32_t)(u >> 3), su = (uint32_t)u & 7u;
+    r.o = so;
+    pair(0, so);
+    pair(1, so + 2 + 4 * su);
+    pair(2, so + 34 + 4 * su);
+    pair(3, so + 66);
+  } else {  // CB3
+    const uint32_t so = row + 110u * (uint32_t)(u >> 3), su = (uint32_t)u & 7u;
+    r.o = so;
+    pair(0, so);
+    pair(1, so + 2 + 8 * su);
+    pair(2, so + 6 + 8 * su);
+    pair(3, so + 66 + su);
+    pair(4, so + 74 + 4 * su);
+    pair(5, so + 106);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void unit_decode(const URaw<FMT>& r, int u, const Tables& tb, uint32_t c[8], float& sc) {
+  // the dword at byte offset off of a pair read from off & ~3
+  auto at = [&](int j, uint32_t off) { return __builtin_amdgcn_alignbyte(r.v[2 * j + 1], r.v[2 * j], off & 3u); };
+  if constexpr (FMT == Q8_0) {
+    sc = h2f(at(0, r.o) & 0xFFFFu);
+    const uint32_t sh = (r.o + 2) & 3u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_alignbyte(r.v[3 + k], r.v[2 + k], sh);
+  } else if constexpr (FMT == NL4) {
+    sc = h2f(at(0, r.o) & 0xFFFFu);
+    const uint32_t sh = (r.o + 2) & 3u;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t n = __builtin_amdgcn_alignbyte(w[k + 1], w[k], sh);
+      const uint32_t n = __builtin_amdgcn_alignbyte(r.v[3 + k], r.v[2 + k], sh);
       c[k] = lut16(n, tb);            // weights 4k..4k+3 (low nibbles)
       c[k + 4] = lut16(n >> 4, tb);   // weights 16+4k..16+4k+3 (high nibbles)
     }
   } else if constexpr (FMT == CB2) {
-    const uint32_t so = row + 70u * (uint32_t)(u >> 3);
-    const uint32_t su = (uint32_t)u & 7u;
-    const float D = h2f(ldw(W, so) & 0xFFFFu);
-    const uint32_t idx4 = ldw(W, so + 2 + 4 * su);
-    const uint32_t sg4 = ldw(W, so + 34 + 4 * su);
-    const uint32_t s = (ldw(W, so + 66) >> (4 * su)) & 15u;
+    const uint32_t so = r.o, su = (uint32_t)u & 7u;
+    const float D = h2f(at(0, so) & 0xFFFFu);
+    const uint32_t idx4 = at(1, so + 2);
+    const uint32_t sg4 = at(2, so + 34);
+    const uint32_t s = (at(3, so + 66) >> (4 * su)) & 15u;
     sc = D * (float)(2 * s + 1);
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
@@ -236,14 +277,13 @@ __device__ __forceinline__ void decode_unit(const MOE_LDS uint32_t* W, uint32_t 
       c[2 * gq + 1] = apply_sign(tb.cb2[2 * idx + 1], sg >> 4);
     }
   } else {  // CB3
-    const uint32_t so = row + 110u * (uint32_t)(u >> 3);
-    const uint32_t su = (uint32_t)u & 7u;
-    const float D = h2f(ldw(W, so) & 0xFFFFu);
-    const uint32_t lo0 = ldw(W, so + 2 + 8 * su);
-    const uint32_t lo1 = ldw(W, so + 6 + 8 * su);
-    const uint32_t hib = ldw(W, so + 66 + su);
-    const uint32_t sg4 = ldw(W, so + 74 + 4 * su);
-    const uint32_t s = (ldw(W, so + 106) >> (4 * su)) & 15u;
+    const uint32_t so = r.o, su = (uint32_t)u & 7u;
+    const float D = h2f(at(0, so) & 0xFFFFu);
+    const uint32_t lo0 = at(1, so + 2);
+    const uint32_t lo1 = at(2, so + 6);
+    const uint32_t hib = at(3, so + 66 + su);
+    const uint32_t sg4 = at(4, so + 74);
+    const uint32_t s = (at(5, so + 106) >> (4 * su)) & 15u;
     sc = D * (float)(2 * s + 1);
 #pragma unroll
     for (int gq = 0; gq < 8; ++gq) {

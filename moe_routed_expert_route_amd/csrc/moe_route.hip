@@ -55,7 +55,7 @@ constexpr int kGuActMax = 48 * 1024;     // LDS for the call's token activations
 constexpr int kDnActMax = 64 * 1024;     // LDS for the call's h rows (q8_1)
 constexpr int kLdsMax = 160 * 1024;      // LDS per workgroup on gfx950
 constexpr int kMaxE = 1024;              // most experts a routed call handles
-constexpr int kRouteWaves = 4;           // tokens routed at once (their logits staged in LDS)
+constexpr int kRtWaves = 8;              // routed mode: waves that route tokens (w, w + 8, ...)
 
 // ------------------------------------------------------------------ argument blocks ---------
 
@@ -245,14 +245,15 @@ __host__ __device__ inline int act_bytes_kb(int rows, int U) {
 // float rows as one float4 per lane and pass (8 lanes per 32-value block, quantized with an
 // 8-lane DPP max), q8_1 rows as one dword per lane and pass (9 per 36-byte block).
 // Loads are branch-free (an index past the data reloads element 0, whose value is never used),
-// so they all issue back to back and the register arrays stay plain registers.
+// so they all issue back to back and the register arrays stay plain registers. `q` is the
+// thread's index among the NT threads (whole waves) that stage.
 template <int NT, int NP>
-__device__ __forceinline__ void act_issue_f(const float* base, long stride, int nblk, int U,
+__device__ __forceinline__ void act_issue_f(const float* base, long stride, int nblk, int U, int q,
                                             float4 (&xr)[NP]) {
   if (nblk <= 0) return;
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    int f = (int)threadIdx.x + p * NT;   // float4 f % 8 of block f / 8
+    int f = q + p * NT;   // float4 f % 8 of block f / 8
     f = f < nblk * 8 ? f : 0;
     const int b = f >> 3, r = b / U, u = b - r * U;
     xr[p] = ((const float4*)(base + (long)r * stride + 32 * u))[f & 7];
@@ -260,14 +261,14 @@ __device__ __forceinline__ void act_issue_f(const float* base, long stride, int 
 }
 
 template <int NT, int NP>
-__device__ __forceinline__ void act_store_f(const float4 (&xr)[NP], int nblk, const ActSplit& act) {
+__device__ __forceinline__ void act_store_f(const float4 (&xr)[NP], int nblk, int q, const ActSplit& act) {
   if (nblk <= 0) return;
   MOE_LDS uint32_t* lo32 = (MOE_LDS uint32_t*)act.lo;
   MOE_LDS uint32_t* hi32 = (MOE_LDS uint32_t*)act.hi;
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     // every lane of the wave takes part in the 8-lane max (full-wave DPP)
-    const int f = (int)threadIdx.x + p * NT;
+    const int f = q + p * NT;
     const float4 v = xr[p];
     float m = fmaxf(fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
                     fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w)));
@@ -299,18 +300,18 @@ __device__ __forceinline__ void act_store_f(const float4 (&xr)[NP], int nblk, co
 
 // The blocks past what the registers held: plain loads and the scalar quantizer.
 template <int NT>
-__device__ void act_rest_f(const float* base, long stride, int b0, int nblk, int U, ActSplit act) {
-  for (int b = b0 + (int)threadIdx.x; b < nblk; b += NT) {
+__device__ void act_rest_f(const float* base, long stride, int b0, int nblk, int U, int q, ActSplit act) {
+  for (int b = b0 + q; b < nblk; b += NT) {
     const int r = b / U, u = b - r * U;
     const float4* pp = (const float4*)(base + (long)r * stride + 32 * u);
     float v[32];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float4 ff = pp[q];
-      v[4 * q] = ff.x;
-      v[4 * q + 1] = ff.y;
-      v[4 * q + 2] = ff.z;
-      v[4 * q + 3] = ff.w;
+    for (int i = 0; i < 8; ++i) {
+      const float4 ff = pp[i];
+      v[4 * i] = ff.x;
+      v[4 * i + 1] = ff.y;
+      v[4 * i + 2] = ff.z;
+      v[4 * i + 3] = ff.w;
     }
     const QBlock bq = quant_block(v);
     act.lo[b] = u32x4{bq.q[0], bq.q[1], bq.q[2], bq.q[3]};
@@ -369,31 +370,31 @@ __device__ void act_rest_q(const uint8_t* base, int b0, int nblk, ActSplit act) 
 // not wait for those loads), then the blocks are quantized or split into LDS; blocks past the
 // register passes follow with plain loads.
 template <int NT, int NP, class Mid>
-__device__ __forceinline__ void act_stage_f_np(const float* base, long stride, int nreg, int U,
+__device__ __forceinline__ void act_stage_f_np(const float* base, long stride, int nreg, int U, int q,
                                                const ActSplit& act, Mid& mid) {
   float4 xr[NP];
-  act_issue_f<NT, NP>(base, stride, nreg, U, xr);
+  act_issue_f<NT, NP>(base, stride, nreg, U, q, xr);
   mid(NP);
-  act_store_f<NT, NP>(xr, nreg, act);
+  act_store_f<NT, NP>(xr, nreg, q, act);
 }
 template <int NT, int NPMAX, class Mid>
-__device__ __forceinline__ void act_stage_f(const float* base, long stride, int nblk, int U,
+__device__ __forceinline__ void act_stage_f(const float* base, long stride, int nblk, int U, int q,
                                             const ActSplit& act, Mid mid) {
   const int nreg = min(nblk, NT * NPMAX / 8);
   const int np = (nreg * 8 + NT - 1) / NT;
   if (np == 0)
     mid(0);
   else if (np == 1)
-    act_stage_f_np<NT, 1>(base, stride, nreg, U, act, mid);
+    act_stage_f_np<NT, 1>(base, stride, nreg, U, q, act, mid);
   else if (np == 2)
-    act_stage_f_np<NT, 2>(base, stride, nreg, U, act, mid);
+    act_stage_f_np<NT, 2>(base, stride, nreg, U, q, act, mid);
   else if (np <= 4 || NPMAX < 8)
-    act_stage_f_np<NT, (NPMAX < 4 ? NPMAX : 4)>(base, stride, nreg, U, act, mid);
+    act_stage_f_np<NT, (NPMAX < 4 ? NPMAX : 4)>(base, stride, nreg, U, q, act, mid);
   else if (np <= 8 || NPMAX < 16)
-    act_stage_f_np<NT, (NPMAX < 8 ? NPMAX : 8)>(base, stride, nreg, U, act, mid);
+    act_stage_f_np<NT, (NPMAX < 8 ? NPMAX : 8)>(base, stride, nreg, U, q, act, mid);
   else
-    act_stage_f_np<NT, NPMAX>(base, stride, nreg, U, act, mid);
-  if (nblk > nreg) act_rest_f<NT>(base, stride, nreg, nblk, U, act);
+    act_stage_f_np<NT, NPMAX>(base, stride, nreg, U, q, act, mid);
+  if (nblk > nreg) act_rest_f<NT>(base, stride, nreg, nblk, U, q, act);
 }
 
 template <int NT, int NP, class Mid>
@@ -424,53 +425,90 @@ __device__ __forceinline__ void act_stage_q(const uint8_t* base, int nblk, const
 
 // ------------------------------------------------------------------ one row-pass of dots ----
 
-// Dot the rows of one wave pass with ne (<= 4) activation rows sidx[0..ne). The wave's lanes
+// Dot the rows of one wave pass with NE (<= 4) activation rows sidx[0..NE). The wave's lanes
 // cover nrows rows (row i = lane >> lgL) of L lanes; rows i < half start at LDS byte ra + i rb,
-// the others at rb0 + (i - half) rb. out(i, e, value) is called by one lane per (row, entry)
-// after the fixed-order lane reduction.
-template <int FMT, class Out>
-__device__ __forceinline__ void dot_pass(const MOE_LDS uint32_t* W, uint32_t ra, uint32_t rb0, int half,
-                                         int nrows, const Geom& G, const Tables& tb, const ActSplit& act,
-                                         const int (&sidx)[kSlots], int ne, Out out) {
+// the others at rb0 + (i - half) rb. Lane li takes units li, li + L, ... of its row, in that order;
+// the weight reads of the next unit and the activation reads of this one are in flight while this
+// unit is decoded (straight-line reads: past the row's end a lane rereads unit 0 and drops the
+// result). out(i, e, value) is called by one lane per (row, entry) after the fixed-order lane
+// reduction.
+template <int FMT, int NE, class Out>
+__device__ __forceinline__ void dot_pass_n(const MOE_LDS uint32_t* W, uint32_t ra, uint32_t rb0, int half,
+                                           int nrows, const Geom& G, const Tables& tb, const ActSplit& act,
+                                           const int (&sidx)[kSlots], Out& out) {
   const int lane = threadIdx.x & 63;
   const int i = lane >> G.lgL, li = lane & (G.L - 1);
-  float acc[kSlots] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = 0.0f;
   if (i < nrows) {
     const uint32_t row = i < half ? ra + (uint32_t)(i * G.rb) : rb0 + (uint32_t)((i - half) * G.rb);
-    for (int k = 0; k < G.upl; ++k) {
+    auto unit_at = [&](int k) {
       const int u = li + (k << G.lgL);
-      if (u < G.U) {
-        uint32_t c[8];
-        float sc;
-        decode_unit<FMT>(W, row, u, tb, c, sc);
+      return u < G.U ? u : 0;
+    };
+    auto step = [&](const URaw<FMT>& r, int k) {
+      const bool valid = li + (k << G.lgL) < G.U;
+      const int u = unit_at(k);
+      uint32_t q[NE][8];
+      float dx[NE];
 #pragma unroll
-        for (int e = 0; e < kSlots; ++e) {
-          if (e < ne) {
-            uint32_t q[8];
-            float dx;
-            act.get(sidx[e], u, q, dx);
-            int s = __builtin_amdgcn_sdot4((int)c[0], (int)q[0], 0, false);
-            s = __builtin_amdgcn_sdot4((int)c[1], (int)q[1], s, false);
-            s = __builtin_amdgcn_sdot4((int)c[2], (int)q[2], s, false);
-            s = __builtin_amdgcn_sdot4((int)c[3], (int)q[3], s, false);
-            s = __builtin_amdgcn_sdot4((int)c[4], (int)q[4], s, false);
-            s = __builtin_amdgcn_sdot4((int)c[5], (int)q[5], s, false);
-            s = __builtin_amdgcn_sdot4((int)c[6], (int)q[6], s, false);
-            s = __builtin_amdgcn_sdot4((int)c[7], (int)q[7], s, false);
-            acc[e] = acc[e] + (sc * dx) * (float)s;
-          }
-        }
+      for (int e = 0; e < NE; ++e) act.get(sidx[e], u, q[e], dx[e]);
+      __builtin_amdgcn_sched_barrier(0);   // keep the reads above ahead of the decode
+      uint32_t c[8];
+      float sc;
+      unit_decode<FMT>(r, u, tb, c, sc);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        int s = __builtin_amdgcn_sdot4((int)c[0], (int)q[e][0], 0, false);
+        s = __builtin_amdgcn_sdot4((int)c[1], (int)q[e][1], s, false);
+        s = __builtin_amdgcn_sdot4((int)c[2], (int)q[e][2], s, false);
+        s = __builtin_amdgcn_sdot4((int)c[3], (int)q[e][3], s, false);
+        s = __builtin_amdgcn_sdot4((int)c[4], (int)q[e][4], s, false);
+        s = __builtin_amdgcn_sdot4((int)c[5], (int)q[e][5], s, false);
+        s = __builtin_amdgcn_sdot4((int)c[6], (int)q[e][6], s, false);
+        s = __builtin_amdgcn_sdot4((int)c[7], (int)q[e][7], s, false);
+        // a unit past the row's end adds +0.0f: acc never holds -0 (it starts at +0), so this
+        // equals skipping the add
+        const float prod = (sc * dx[e]) * (float)s;
+        acc[e] = acc[e] + (valid ? prod : 0.0f);
+      }
+    };
+    URaw<FMT> r0, r1;
+    unit_load<FMT>(W, row, unit_at(0), r0);
+    // (landed before the loop: the loop is entered with no read of r0 in flight, as it leaves
+    // each trip, so the waits inside it count only the reads issued in the trip)
+    MOE_WAIT_LGKM0;
+    for (int k = 0; k < G.upl; k += 2) {
+      unit_load<FMT>(W, row, unit_at(k + 1), r1);
+      __builtin_amdgcn_sched_barrier(0);
+      step(r0, k);
+      if (k + 1 < G.upl) {
+        unit_load<FMT>(W, row, unit_at(k + 2), r0);
+        __builtin_amdgcn_sched_barrier(0);
+        step(r1, k + 1);
       }
     }
   }
 #pragma unroll
-  for (int e = 0; e < kSlots; ++e)
-    if (e < ne) acc[e] = group_sum(acc[e], G.L);
+  for (int e = 0; e < NE; ++e) acc[e] = group_sum(acc[e], G.L);
   // every lane of the row holds every sum; lane li stores the entries e = li (mod L)
   if (i < nrows) {
 #pragma unroll
-    for (int e = 0; e < kSlots; ++e)
-      if (e < ne && (e & (G.L - 1)) == li) out(i, e, acc[e]);
+    for (int e = 0; e < NE; ++e)
+      if ((e & (G.L - 1)) == li) out(i, e, acc[e]);
+  }
+}
+
+template <int FMT, class Out>
+__device__ __forceinline__ void dot_pass(const MOE_LDS uint32_t* W, uint32_t ra, uint32_t rb0, int half,
+                                         int nrows, const Geom& G, const Tables& tb, const ActSplit& act,
+                                         const int (&sidx)[kSlots], int ne, Out out) {
+  switch (ne) {
+    case 1: dot_pass_n<FMT, 1>(W, ra, rb0, half, nrows, G, tb, act, sidx, out); break;
+    case 2: dot_pass_n<FMT, 2>(W, ra, rb0, half, nrows, G, tb, act, sidx, out); break;
+    case 3: dot_pass_n<FMT, 3>(W, ra, rb0, half, nrows, G, tb, act, sidx, out); break;
+    default: dot_pass_n<FMT, 4>(W, ra, rb0, half, nrows, G, tb, act, sidx, out); break;
   }
 }
 
@@ -520,9 +558,10 @@ __device__ __forceinline__ void swiglu_q81_split(float gv, float uv, int l32, bo
   }
 }
 
-// ------------------------------------------------------------------ routing (one wave) ------
+// ------------------------------------------------------------------ routing (one wave per token)
 
-// Unsigned key with the order of the float (-0 and +0 share a key).
+// Unsigned key with the order of the float (-0 and +0 share a key). Finite floats map to keys of at
+// least 0x00800000, so 0 sorts below every real key.
 __device__ __forceinline__ uint32_t fkey(float f) {
   const uint32_t b = __float_as_uint(f + 0.0f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
@@ -531,8 +570,29 @@ __device__ __forceinline__ float unkey(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Exclusive prefix sum over the wave's lanes of values in [0, 2^bits), from ballots of their bit
+// planes (lane l gets the sum over lanes below l); and the whole wave's sum (uniform).
+__device__ __forceinline__ int lane_prefix(int v, int bits) {
+  int s = 0;
+  for (int b = 0; b < bits; ++b) {
+    const uint64_t m = __ballot((v >> b) & 1);
+    s += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+  }
+  return s;
+}
+__device__ __forceinline__ int lane_sum(int v, int bits) {
+  int s = 0;
+  for (int b = 0; b < bits; ++b) s += __popcll(__ballot((v >> b) & 1)) << b;
+  return s;
+}
+
 // One token's E (<= 1024) logits into LDS (dst[e], e < 64 ceil(E / 64)) with direct-to-LDS 4-byte
-// loads of one wave; past E a lane reloads row[0], which route_wave ignores.
+// loads of one wave; past E a lane reloads row[0], which the routing ignores.
 __device__ __forceinline__ void issue_logits(const float* row, int E, MOE_LDS float* dst) {
   const int lane = threadIdx.x & 63;
   for (int j = 0; 64 * j < E; ++j) {
@@ -543,165 +603,125 @@ __device__ __forceinline__ void issue_logits(const float* row, int E, MOE_LDS fl
 }
 __host__ __device__ inline int logits_pad(int E) { return (E + 63) & ~63; }
 
-// Top-k (k <= min(E, 32)) of the logits one wave holds, by (logit descending, expert id
-// ascending): a radix select over ballots finds the k-th largest key (bit by bit, the largest
-// prefix that at least k keys reach), ties at that key go to the lowest ids, and the k chosen get
-// their exact ranks by comparison. Weights: ex_j = exp(l_j - l_0) in rank order,
-// w_j = ex_j / (((ex_0 + ex_1) + ex_2) + ...). Writes ids/w[0..k) (LDS) in rank order.
-// lg_in: the token's logits in LDS (issue_logits); V = logits per lane (E <= 64 V); scr: 96 words
-// of LDS for this wave.
+// LDS words of one routing wave's scratch: the logits, the candidate (key, id) pairs plus two pad
+// pairs, 64 group maxima, 32 selected logits.
+__host__ __device__ inline int route_scr_words(int E) { return 3 * logits_pad(E) + 100; }
+
+// Top-k (k <= min(E, 32)) of one token's logits by one wave, by (logit descending, expert id
+// ascending), then the router weights over the k chosen ("#363 ...", opening paragraph: each
+// token of the window picks its top-k experts):
+//  1. threshold: the lanes form G groups (G a power of two, at least 2k and enough that k groups
+//     hold experts); the k-th largest of the G group maxima is a key that at least k keys reach,
+//     so every key among the top k reaches it;
+//  2. the keys that reach it are the candidates (typically a little over k); an expert's rank is
+//     the number of candidates that beat it (larger key, or equal key and lower id), which equals
+//     its rank among all E since whatever beats a candidate is a candidate;
+//  3. weights in rank order: ex_j = exp(l_j - l_0), w_j = ex_j / (((ex_0 + ex_1) + ex_2) + ...).
+// scr: route_scr_words(E) words holding the logits (issue_logits into its start). Writes ids[0..k)
+// and w[0..k) in rank order and this token's selection as a bitmap bits[0..ceil(E / 32)) (bit e of
+// word e / 32), all in LDS.
 template <int V>
-__device__ __forceinline__ void route_wave_v(const MOE_LDS float* lg_in, int E, int k, MOE_LDS int* ids, MOE_LDS float* w,
-                             MOE_LDS uint32_t* scr) {
+__device__ __forceinline__ void route_token_v(MOE_LDS uint32_t* scr, int E, int k, MOE_LDS int* ids,
+                                              MOE_LDS float* w, MOE_LDS uint32_t* bits) {
   const int lane = threadIdx.x & 63;
   const uint64_t lt = (1ull << lane) - 1ull;
+  const int Epad = logits_pad(E);
+  const MOE_LDS float* lg = (const MOE_LDS float*)scr;
+  MOE_LDS uint32_t* cand = scr + Epad;
+  MOE_LDS uint32_t* gmx = cand + 2 * Epad + 4;
+  MOE_LDS float* lsel = (MOE_LDS float*)(gmx + 64);
   uint32_t key[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) key[j] = (64 * j + lane < E) ? fkey(lg_in[64 * j + lane]) : 0u;   // 0: no expert
-  uint32_t tau = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = tau | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < V; ++j) cnt += __popcll(__ballot(key[j] >= c));
-    tau = cnt >= k ? c : tau;
-  }
-  int ngt = 0;
-#pragma unroll
-  for (int j = 0; j < V; ++j) ngt += __popcll(__ballot(key[j] > tau));
-  const int need = k - ngt;   // keys equal to tau to take, lowest ids first
-  int eqb = 0, selb = 0;
+  uint32_t m = 0u;
 #pragma unroll
   for (int j = 0; j < V; ++j) {
-    const uint64_t eqm = __ballot(key[j] == tau);
-    const bool sel = key[j] > tau || (key[j] == tau && eqb + __popcll(eqm & lt) < need);
-    const uint64_t sm = __ballot(sel);
-    if (sel) {
-      const int pos = selb + __popcll(sm & lt);
-      scr[pos] = key[j];
-      scr[32 + pos] = (uint32_t)(64 * j + lane);
-    }
-    eqb += __popcll(eqm);
-    selb += __popcll(sm);
+    key[j] = (64 * j + lane < E) ? fkey(lg[64 * j + lane]) : 0u;   // 0: no expert
+    m = max(m, key[j]);
   }
+  // 1. threshold
+  int G = 4;
+  while (G < 64 && (G < 2 * k || E * G < 64 * k)) G <<= 1;
+  const int gsz = 64 / G;
+  if (gsz >= 2) m = max(m, dppu<0xB1>(m));    // xor 1
+  if (gsz >= 4) m = max(m, dppu<0x4E>(m));    // xor 2
+  if (gsz >= 8) m = max(m, dppu<0x141>(m));   // row_half_mirror
+  if (gsz >= 16) m = max(m, dppu<0x140>(m));  // row_mirror
+  if ((lane & (gsz - 1)) == 0) gmx[lane / gsz] = m;
   wave_lds_sync();
-  MOE_LDS float* lg = (MOE_LDS float*)(scr + 64);
-  if (lane < k) {
-    const uint32_t mk = scr[lane];
-    const uint32_t mid = scr[32 + lane];
+  uint32_t thr = 0xFFFFFFFFu;
+  if (lane < G) {
+    const uint32_t mine = gmx[lane];
     int r = 0;
-    for (int o = 0; o < k; ++o) {
-      const uint32_t ok = scr[o], oid = scr[32 + o];
-      r += (ok > mk) | ((ok == mk) & (oid < mid));
+    for (int o = 0; o < G; o += 4) {
+      const u32x4 v = *(const MOE_LDS u32x4*)(gmx + o);
+      r += (int)(v.x > mine) + (int)(v.y > mine) + (int)(v.z > mine) + (int)(v.w > mine);
     }
-    ids[r] = (int)mid;
-    lg[r] = unkey(mk);
+    if (r < k) thr = mine;
+  }
+  thr = min(thr, dppu<0xB1>(thr));
+  thr = min(thr, dppu<0x4E>(thr));
+  thr = min(thr, dppu<0x141>(thr));
+  thr = min(thr, dppu<0x140>(thr));
+  thr = min(min((uint32_t)__builtin_amdgcn_readlane((int)thr, 0), (uint32_t)__builtin_amdgcn_readlane((int)thr, 16)),
+            min((uint32_t)__builtin_amdgcn_readlane((int)thr, 32), (uint32_t)__builtin_amdgcn_readlane((int)thr, 48)));
+  // 2. candidates, then exact ranks among them
+  int C = 0;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const bool c = key[j] >= thr;   // thr is a real key, so key 0 never qualifies
+    const uint64_t bm = __ballot(c);
+    if (c) {
+      const int pos = C + __popcll(bm & lt);
+      cand[2 * pos] = key[j];
+      cand[2 * pos + 1] = (uint32_t)(64 * j + lane);
+    }
+    C += __popcll(bm);
+  }
+  if (lane < 4) cand[2 * C + lane] = (lane & 1) ? 0xFFFFFFFFu : 0u;   // pad pairs: key 0 beats nothing
+  wave_lds_sync();
+  for (int c0 = 0; c0 < C; c0 += 64) {
+    const int c = c0 + lane;
+    const bool live = c < C;
+    const uint32_t kc = live ? cand[2 * c] : 0u;
+    const uint32_t ic = live ? cand[2 * c + 1] : 0u;
+    int r = 0;
+    for (int o = 0; o < C; o += 2) {
+      const u32x4 v = *(const MOE_LDS u32x4*)(cand + 2 * o);
+      r += (int)((v.x > kc) | ((v.x == kc) & (v.y < ic)));
+      r += (int)((v.z > kc) | ((v.z == kc) & (v.w < ic)));
+    }
+    if (live && r < k) {
+      ids[r] = (int)ic;
+      lsel[r] = unkey(kc);
+    }
   }
   wave_lds_sync();
+  // this token's selection as a bitmap (word = lane)
+  const int nW = (E + 31) >> 5;
+  if (lane < nW) {
+    uint32_t bw = 0u;
+    for (int r = 0; r < k; ++r) {
+      const int e = ids[r];
+      bw |= ((e >> 5) == lane) ? (1u << (e & 31)) : 0u;
+    }
+    bits[lane] = bw;
+  }
+  // 3. weights
   float ex = 0.0f;
-  if (lane < k) ex = expf(lg[lane] - lg[0]);
-  wave_lds_sync();
-  if (lane < k) lg[lane] = ex;
-  wave_lds_sync();
-  MOE_LDS float* sum = (MOE_LDS float*)scr;   // the keys are no longer needed
-  if (lane == 0) {
-    float s = 0.0f;
-    for (int j = 0; j < k; ++j) s = s + lg[j];
-    sum[0] = s;
-  }
-  wave_lds_sync();
-  if (lane < k) w[lane] = ex / sum[0];
+  if (lane < k) ex = expf(lsel[lane] - lsel[0]);
+  float sum = 0.0f;
+  for (int j = 0; j < k; ++j) sum = sum + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+  if (lane < k) w[lane] = ex / sum;
   wave_lds_sync();
 }
 
-__device__ __forceinline__ void route_wave(const MOE_LDS float* lg, int E, int k, MOE_LDS int* ids,
-                                           MOE_LDS float* w, MOE_LDS uint32_t* scr) {
-  if (E <= 64)
-    route_wave_v<1>(lg, E, k, ids, w, scr);
-  else if (E <= 128)
-    route_wave_v<2>(lg, E, k, ids, w, scr);
+__device__ __forceinline__ void route_token(MOE_LDS uint32_t* scr, int E, int k, MOE_LDS int* ids,
+                                            MOE_LDS float* w, MOE_LDS uint32_t* bits) {
+  if (E <= 128)
+    route_token_v<2>(scr, E, k, ids, w, bits);
   else if (E <= 256)
-    route_wave_v<4>(lg, E, k, ids, w, scr);
-  else if (E <= 512)
-    route_wave_v<8>(lg, E, k, ids, w, scr);
+    route_token_v<4>(scr, E, k, ids, w, bits);
   else
-    route_wave_v<16>(lg, E, k, ids, w, scr);
-}
-
-// Top-k of up to T tokens at once by a workgroup, when every token's logits are staged in LDS (row
-// t at lg + t Epad), in three steps:
-//  1. route_keys: every logit becomes its order key in place (0 past E, below every real key);
-//  2. route_ranks: an expert's rank = the number of experts that beat it (larger key, or equal key
-//     and lower id), counted by P lanes over 1/P of the row each and summed across those lanes;
-//     ranks below k are the selection, already in rank order;
-//  3. route_weights: ex_j = exp(l_j - l_0), w_j = ex_j / (((ex_0 + ex_1) + ex_2) + ...).
-// Same selection, order and weights as route_wave. scr: 192 words of LDS.
-template <int NT>
-__device__ __forceinline__ void route_keys(MOE_LDS float* lg, int Epad, int T, int E) {
-  for (int i = threadIdx.x; i < T * Epad; i += NT) {
-    const int e = i - (i / Epad) * Epad;
-    const float v = lg[i];
-    ((MOE_LDS uint32_t*)lg)[i] = e < E ? fkey(v) : 0u;
-  }
-}
-__host__ __device__ inline int route_lanes(int T, int E) {   // P lanes per expert
-  const int TE = T * E;
-  return TE <= 128 ? 4 : (TE <= 256 ? 2 : 1);
-}
-// Threads tid < nthr (a multiple of 64, >= T E P) take the experts.
-__device__ __forceinline__ void route_ranks(const MOE_LDS uint32_t* keys, int Epad, int T, int E, int k, int nthr,
-                                            MOE_LDS int* ids, MOE_LDS float* scr) {
-  const int tid = threadIdx.x;
-  const int P = route_lanes(T, E), lgP = P == 4 ? 2 : (P == 2 ? 1 : 0);
-  const int SL4 = Epad / P / 4;   // 16-byte words per slice (a multiple of 4)
-  for (int cs = tid; cs < T * E * P; cs += nthr) {   // every lane of a P-lane group runs the same trips
-    int c = cs >> lgP, t = 0;
-    const int pp = cs & (P - 1);
-    while (c >= E) {
-      c -= E;
-      ++t;
-    }
-    const int e = c;
-    const MOE_LDS uint32_t* row = keys + t * Epad;
-    const uint32_t key = row[e];
-    const MOE_LDS u32x4* sl = (const MOE_LDS u32x4*)(row + pp * SL4 * 4);
-    int part = 0;
-    for (int q = 0; q < SL4; q += 4) {   // four 16-byte reads in flight
-      u32x4 v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = sl[q + j];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int o = (pp * SL4 + q + j) * 4;
-        part += (v[j].x > key) | ((v[j].x == key) & (o + 0 < e));
-        part += (v[j].y > key) | ((v[j].y == key) & (o + 1 < e));
-        part += (v[j].z > key) | ((v[j].z == key) & (o + 2 < e));
-        part += (v[j].w > key) | ((v[j].w == key) & (o + 3 < e));
-      }
-    }
-    if (P >= 2) part += __shfl_xor(part, 1);
-    if (P >= 4) part += __shfl_xor(part, 2);
-    if (pp == 0 && part < k) {
-      ids[t * k + part] = e;
-      scr[t * k + part] = unkey(key);
-    }
-  }
-}
-template <int NT>
-__device__ __forceinline__ void route_weights(int T, int k, MOE_LDS float* w, MOE_LDS float* scr) {
-  const int tid = threadIdx.x;
-  MOE_LDS float* rlg = scr;          // [T k] selected logits in rank order
-  MOE_LDS float* rex = scr + 64;     // [T k] exp terms
-  MOE_LDS float* rsum = scr + 128;   // [T] sums
-  if (tid < T * k) rex[tid] = expf(rlg[tid] - rlg[(tid / k) * k]);
-  __syncthreads();
-  if (tid < T) {
-    float s = 0.0f;
-    for (int j = 0; j < k; ++j) s = s + rex[tid * k + j];
-    rsum[tid] = s;
-  }
-  __syncthreads();
-  if (tid < T * k) w[tid] = rex[tid] / rsum[tid / k];
+    route_token_v<16>(scr, E, k, ids, w, bits);
 }
 
 // ------------------------------------------------------------------ plan in LDS -------------
@@ -720,10 +740,8 @@ struct PlanL {
   MOE_LDS int* elive;      // [64] entry computed (source in range)
   MOE_LDS int* dtok;       // [64] destination of each token (routing)
   MOE_LDS int* misc;       // [16] 0: n_groups, 1: e0 (absolute), 2: e1, 3: raw n_groups
-  MOE_LDS uint32_t* rscr;  // [4 waves][96] routing scratch
-  MOE_LDS int* emap;       // [kMaxE] expert -> group (routing with prefetched pointers)
 };
-constexpr int kPlanLInts = 64 * 5 + 64 + 68 + 64 * 5 + 16 + 4 * 96 + kMaxE;
+constexpr int kPlanLInts = 64 * 5 + 64 + 68 + 64 * 5 + 16;
 constexpr int kPlanLBytes = (4 * kPlanLInts + 15) & ~15;
 
 __device__ inline PlanL plan_l(MOE_LDS int* b) {
@@ -741,11 +759,9 @@ __device__ inline PlanL plan_l(MOE_LDS int* b) {
   p.elive = b + 644;
   p.dtok = b + 708;
   p.misc = b + 772;
-  p.rscr = (MOE_LDS uint32_t*)(b + 788);
-  p.emap = b + 788 + 4 * 96;
   return p;
 }
-static_assert(788 + 4 * 96 + kMaxE == kPlanLInts, "plan layout");
+static_assert(788 == kPlanLInts, "plan layout");
 
 // Group n (<= 64) entries (rid/rw, token-major with k per token) by expert with one wave: each
 // entry's key (expert, entry index) gets its rank among all keys, the entries land in key order
@@ -897,23 +913,38 @@ struct GuArgs {
   int sw;               // waves that stream items (the ring holds sw waves' slots)
 };
 
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kGuStage = 64 * kMaxEnt;   // floats of output staging: a 32-row block of g and u per entry
 constexpr int kGuFixed = 4096 + kPlanLBytes + 8 * 3 * kMaxGrp + 4 * kGuStage;
 constexpr int kGuXPass = 8;    // float4 (or q8_1 dword) register passes: 1024 float blocks, 910 q8_1
+constexpr int kGuQThreads = kGuThreads - 64 * kRtWaves;   // routed: the waves that quantize x
 
-__host__ __device__ inline int gu_smem_bytes(int lds_ring, int lds_act) {
-  return lds_ring + lds_act + kGuFixed;
+// Routed mode: LDS after the fixed part: [E] gate and up pointers, [E] down pointers (0: the
+// expert's pointers are unusable), [T][ceil(E / 32)] each token's selection bitmap.
+__host__ __device__ inline int gu_tail_bytes(int E, int T) {
+  return 24 * E + ((4 * T * ((E + 31) >> 5) + 15) & ~15);
+}
+__host__ __device__ inline int gu_smem_bytes(int lds_ring, int lds_act, int lds_tail) {
+  return lds_ring + lds_act + kGuFixed + lds_tail;
 }
 
 // Work item = one 32-row block of h of one group (so SwiGLU and the q8_1 quantization of the block
 // finish in the workgroup). The block's 64 weight rows are 64 / rp passes of rp rows (rp / 2 gate
 // rows and the same up rows, one two-span chunk); the first sw waves take the passes round
 // robin, each streaming its chunks through its own ring across the workgroup's items.
+//
+// Routed mode: waves 0..7 route the tokens (one wave per token, its logits staged in the ring) while
+// waves 8..15 quantize x into LDS; after one workgroup barrier every wave finds, from the tokens'
+// selection bitmaps, the expert of each group it streams (groups ascending by expert id; the g-th
+// set bit of the union of the bitmaps) and that group's entries (tokens ascending), so the weight
+// loads go out with no further barrier. Workgroup 0 then writes the plan and the descriptor.
 template <int FMT, int MODE>
 __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const Geom& G = a.G;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint64_t lt = (1ull << lane) - 1ull;
   MOE_LDS uint8_t* ring = (MOE_LDS uint8_t*)smem;
   const ActSplit act = act_layout(ring + a.lds_ring, a.n_tokens, G.U);
   MOE_LDS uint8_t* p8 = ring + a.lds_ring + a.lds_act;
@@ -922,11 +953,13 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   const PlanL pl = plan_l((MOE_LDS int*)(p8 + 4096));
   MOE_LDS uint64_t* gptr = (MOE_LDS uint64_t*)(p8 + 4096 + kPlanLBytes);   // [group][gate, up, down]
   MOE_LDS float* stage = (MOE_LDS float*)(p8 + 4096 + kPlanLBytes + 8 * 3 * kMaxGrp);   // [entry][64]
-  MOE_LDS float* lgs = (MOE_LDS float*)ring;   // routed: staged logits (prologue only)
-  const int Epad = logits_pad(a.E);
+  MOE_LDS uint8_t* tail = p8 + kGuFixed;
+  MOE_LDS u64x2* ptab = (MOE_LDS u64x2*)tail;                        // routed: [E] gate, up
+  MOE_LDS uint64_t* ptabd = (MOE_LDS uint64_t*)(tail + 16 * a.E);    // routed: [E] down
+  const int nW = (a.E + 31) >> 5;
+  MOE_LDS uint32_t* selT = (MOE_LDS uint32_t*)(tail + 24 * a.E);     // routed: [T][nW]
 
-  // ---- 1. every load that depends on nothing, at once. The ring is free until the stream
-  //         starts: it stages the first kRouteWaves tokens' logits and the activation rows.
+  // ---- 1. every load that depends on nothing, at once
   uint32_t t_nl4[4] = {0u, 0u, 0u, 0u};
   if (a.A.nl4) {
     const uint32_t* t = (const uint32_t*)a.A.nl4;
@@ -949,152 +982,133 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
       pu = (uint64_t)(uintptr_t)a.A.up[tid];
       pd = (uint64_t)(uintptr_t)a.A.down[tid];
     }
-    if (wave < kRouteWaves && wave < a.T) issue_logits(a.logits + (size_t)wave * a.E, a.E, lgs + wave * Epad);
   } else {
     if (tid == 0) r_ng = *a.P.n_groups;
     if (tid <= a.P.cap_groups) r_gs = a.P.grp_start[tid];
     if (tid < a.P.cap_groups) r_ge = a.P.grp_expert[tid];
   }
-  // float activation rows: staged by every wave, quantized from LDS in passes of kGuThreads float4
-  const int lg_bytes = MODE == GU_ROUTED ? kRouteWaves * Epad * 4 : 0;
-  MOE_LDS uint8_t* xs = ring + lg_bytes;
-  const int row_bytes = a.A.n_embd * 4;
-  const int rows_per = MODE == GU_COMPOSED ? 0 : max(1, (a.lds_ring - lg_bytes) / row_bytes);
-  auto stage_rows = [&](int r0, int nr) {
-    dma_span((const uint8_t*)(a.x + (size_t)r0 * a.A.n_embd), (uint32_t)(nr * row_bytes), xs, wave, kGuWaves);
-  };
-  // threads q (0 <= q < nq, nq a multiple of 64) quantize: trips are uniform per wave (the DPP max
-  // needs every lane of the wave)
-  auto quant_rows = [&](int r0, int nr, int q, int nq) {
-    const int nf4 = nr * G.U * 8;
-    const MOE_LDS f32x4* xv = (const MOE_LDS f32x4*)xs;
-    MOE_LDS uint32_t* lo32 = (MOE_LDS uint32_t*)act.lo;
-    MOE_LDS uint32_t* hi32 = (MOE_LDS uint32_t*)act.hi;
-    for (int base = 0; base < nf4; base += nq) {
-      const int f = base + q;
-      const f32x4 v = f < nf4 ? xv[f] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      float m = fmaxf(fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
-                      fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w)));
-      m = fmaxf(m, dpp<0xB1>(m));    // xor 1
-      m = fmaxf(m, dpp<0x4E>(m));    // xor 2
-      m = fmaxf(m, dpp<0x141>(m));   // the other quad of the 8 lanes of a block
-      if (f < nf4) {
-        const int b = r0 * G.U + (f >> 3), part = f & 7;
-        const float d = m / 127.0f;
-        uint32_t packed = 0;
-        if (m != 0.0f) {
-          const float xs4[4] = {v.x, v.y, v.z, v.w};
-          for (int j = 0; j < 4; ++j) {
-            float r = round_half_away(xs4[j] / d);
-            r = r > 127.0f ? 127.0f : r;
-            r = r < -127.0f ? -127.0f : r;
-            packed |= ((uint32_t)(int)r & 0xFFu) << (8 * j);
-          }
-        }
-        if (part < 4)
-          lo32[b * 4 + part] = packed;
-        else
-          hi32[b * 4 + part - 4] = packed;
-        if (part == 0) act.d[b] = h2f(f2h(d));
-      }
-    }
-  };
-  if constexpr (MODE != GU_COMPOSED) stage_rows(0, min(a.n_tokens, rows_per));
 
-  // ---- 2. the loads land; routing (whole workgroup) and the activations' q8_1 blocks
-  Tables tb;
-  tables_init(tb, t_nl4, g2, g3);
-  if constexpr (MODE == GU_COMPOSED) {
-    act_stage_q<kGuThreads, kGuXPass>(a.xq, a.n_tokens * G.U, act, [](int) {});
-    __syncthreads();
-  } else {
-    __syncthreads();   // (waits for every load of round 1, the staged logits and rows included)
-    // routed: keys, then the ranks on the first threads while the others quantize x
-    int rthr = 0;
-    if constexpr (MODE == GU_ROUTED) {
-      if (a.T <= kRouteWaves) {
-        route_keys<kGuThreads>(lgs, Epad, a.T, a.E);
-        __syncthreads();
-        rthr = min(kGuThreads, (a.T * a.E * route_lanes(a.T, a.E) + 63) & ~63);
-        if (tid < rthr)
-          route_ranks((const MOE_LDS uint32_t*)lgs, Epad, a.T, a.E, a.k, rthr, pl.rid, (MOE_LDS float*)pl.rscr);
+  // ---- 2. routing and the activations' q8_1 blocks
+  if constexpr (MODE == GU_ROUTED) {
+    if (wave < kRtWaves) {
+      MOE_LDS uint32_t* rscr = (MOE_LDS uint32_t*)ring + wave * route_scr_words(a.E);
+      for (int t = wave; t < a.T; t += kRtWaves) {
+        issue_logits(a.logits + (size_t)t * a.E, a.E, (MOE_LDS float*)rscr);
+        __builtin_amdgcn_s_waitcnt(MOE_VM(0));
+        route_token(rscr, a.E, a.k, pl.rid + t * a.k, pl.rw + t * a.k, selT + t * nW);
       }
-    }
-    if (rthr < kGuThreads) {
-      if (tid >= rthr) quant_rows(0, min(a.n_tokens, rows_per), tid - rthr, kGuThreads - rthr);
     } else {
-      quant_rows(0, min(a.n_tokens, rows_per), tid, kGuThreads);
-    }
-    if constexpr (MODE == GU_ROUTED) {
-      if (a.T <= kRouteWaves) {
-        __syncthreads();
-        route_weights<kGuThreads>(a.T, a.k, pl.rw, (MOE_LDS float*)pl.rscr);
+      // two register passes cover one 4096-wide row; eight cover four (more: plain loads after)
+      const int q = tid - 64 * kRtWaves, nblk = a.n_tokens * G.U;
+      auto none = [](int) {};
+      if (nblk * 8 <= 2 * kGuQThreads) {
+        act_stage_f_np<kGuQThreads, 2>(a.x, a.A.n_embd, nblk, G.U, q, act, none);
+      } else {
+        const int nreg = min(nblk, kGuQThreads * kGuXPass / 8);
+        act_stage_f_np<kGuQThreads, kGuXPass>(a.x, a.A.n_embd, nreg, G.U, q, act, none);
+        if (nblk > nreg) act_rest_f<kGuQThreads>(a.x, a.A.n_embd, nreg, nblk, G.U, q, act);
       }
     }
-    for (int r0 = rows_per; r0 < a.n_tokens; r0 += rows_per) {   // more rows than the staging holds
-      __syncthreads();
-      stage_rows(r0, min(rows_per, a.n_tokens - r0));
-      __syncthreads();
-      quant_rows(r0, min(rows_per, a.n_tokens - r0), tid, kGuThreads);
+    if (tid < a.E) {
+      const bool ok = ptr_ok(pg | pu, a.P.err);
+      ptab[tid] = u64x2{ok ? pg : 0ull, ok ? pu : 0ull};
+      ptabd[tid] = ptr_ok(pd, a.P.err) ? pd : 0ull;
+    }
+    if (tid < a.T) pl.dtok[tid] = r_dt;
+  } else if constexpr (MODE == GU_COMPOSED) {
+    act_stage_q<kGuThreads, kGuXPass>(a.xq, a.n_tokens * G.U, act, [](int) {});
+  } else {
+    // float activation rows staged in the ring (free until the stream starts), then quantized
+    MOE_LDS uint8_t* xs = ring;
+    const int row_bytes = a.A.n_embd * 4;
+    const int rows_per = max(1, a.lds_ring / row_bytes);
+    const int nf4row = G.U * 8;
+    for (int r0 = 0; r0 < a.n_tokens; r0 += rows_per) {
+      const int nr = min(rows_per, a.n_tokens - r0);
+      if (r0) __syncthreads();
+      dma_span((const uint8_t*)(a.x + (size_t)r0 * a.A.n_embd), (uint32_t)(nr * row_bytes), xs, wave, kGuWaves);
+      __syncthreads();   // (waits for every load issued so far, the staged rows included)
+      const int nf4 = nr * nf4row;
+      const MOE_LDS f32x4* xv = (const MOE_LDS f32x4*)xs;
+      MOE_LDS uint32_t* lo32 = (MOE_LDS uint32_t*)act.lo;
+      MOE_LDS uint32_t* hi32 = (MOE_LDS uint32_t*)act.hi;
+      // trips are uniform per wave: the DPP max needs every lane of the wave
+      for (int base = 0; base < nf4; base += kGuThreads) {
+        const int f = base + tid;
+        const f32x4 v = f < nf4 ? xv[f] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        float m = fmaxf(fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
+                        fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w)));
+        m = fmaxf(m, dpp<0xB1>(m));    // xor 1
+        m = fmaxf(m, dpp<0x4E>(m));    // xor 2
+        m = fmaxf(m, dpp<0x141>(m));   // the other quad of the 8 lanes of a block
+        if (f < nf4) {
+          const int bk = r0 * G.U + (f >> 3), part = f & 7;
+          const float d = m / 127.0f;
+          uint32_t packed = 0;
+          if (m != 0.0f) {
+            const float xs4[4] = {v.x, v.y, v.z, v.w};
+            for (int j = 0; j < 4; ++j) {
+              float r = round_half_away(xs4[j] / d);
+              r = r > 127.0f ? 127.0f : r;
+              r = r < -127.0f ? -127.0f : r;
+              packed |= ((uint32_t)(int)r & 0xFFu) << (8 * j);
+            }
+          }
+          if (part < 4)
+            lo32[bk * 4 + part] = packed;
+          else
+            hi32[bk * 4 + part - 4] = packed;
+          if (part == 0) act.d[bk] = h2f(f2h(d));
+        }
+      }
     }
   }
   if constexpr (FMT == CB2 || FMT == CB3)
     if (tid < 512) (FMT == CB2 ? g2 : g3)[tid] = t_cb;
-  if constexpr (MODE == GU_ROUTED) {
-    if (tid < a.T) pl.dtok[tid] = r_dt;
-    if (tid < a.E) pl.emap[tid] = -1;
-    // longer windows: kRouteWaves tokens per round, their logits staged again
-    for (int t0 = 0; a.T > kRouteWaves && t0 < a.T; t0 += kRouteWaves) {
-      const int nt = min(kRouteWaves, a.T - t0);
-      __syncthreads();
-      if (wave < nt) issue_logits(a.logits + (size_t)(t0 + wave) * a.E, a.E, lgs + wave * Epad);
-      __syncthreads();
-      route_keys<kGuThreads>(lgs, Epad, nt, a.E);
-      __syncthreads();
-      const int nthr = min(kGuThreads, (nt * a.E * route_lanes(nt, a.E) + 63) & ~63);
-      if (tid < nthr)
-        route_ranks((const MOE_LDS uint32_t*)lgs, Epad, nt, a.E, a.k, nthr, pl.rid + t0 * a.k,
-                    (MOE_LDS float*)pl.rscr);
-      __syncthreads();
-      route_weights<kGuThreads>(nt, a.k, pl.rw + t0 * a.k, (MOE_LDS float*)pl.rscr);
-    }
-  } else {
+  if constexpr (MODE != GU_ROUTED) {
     if (tid == 0) pl.misc[3] = r_ng;
     if (tid <= a.P.cap_groups) pl.gstart[tid] = r_gs;
     if (tid < a.P.cap_groups) pl.gexp[tid] = r_ge;
   }
+  Tables tb;
+  tables_init(tb, t_nl4, g2, g3);
   __syncthreads();
 
-  // ---- 3. the plan: grouped here, or the caller's, validated
+  // ---- 3. the plan: the routed selections (every wave reads them itself), or the caller's,
+  //         validated
+  // routed: lane l < nW holds word l of the union of the tokens' selections, the groups and the
+  // entries of the words below it
+  uint32_t uw = 0u;
+  int upc = 0, upre = 0, cpre = 0;
+  int ng = 0, e0 = 0, n = 0;
   if constexpr (MODE == GU_ROUTED) {
-    if (wave == 0) group_wave(pl, a.T * a.k, a.k, a.E, a.entry_base, a.P.err);
-    __syncthreads();
-    const int ng = uni(pl.misc[0]);
-    if (tid < ng) pl.emap[pl.gexp[tid]] = tid;
-    __syncthreads();
-    if (tid < a.E) {
-      const int g = pl.emap[tid];
-      if (g >= 0) {
-        gptr[3 * g] = ptr_ok(pg | pu, a.P.err) ? pg : 0;
-        gptr[3 * g + 1] = pu;
-        gptr[3 * g + 2] = ptr_ok(pd, a.P.err) ? pd : 0;
+    int ucnt = 0;
+    if (lane < nW)
+      for (int t = 0; t < a.T; ++t) {
+        const uint32_t bw = selT[t * nW + lane];
+        uw |= bw;
+        ucnt += __popc(bw);
       }
-    }
-    __syncthreads();
+    upc = __popc(uw);
+    upre = lane_prefix(upc, 6);
+    cpre = lane_prefix(ucnt, 7);   // at most 64 entries in all
+    ng = __builtin_amdgcn_readlane(upre + upc, 63);
+    e0 = a.entry_base;
+    n = a.T * a.k;
   } else {
     validate_groups(pl.gstart, pl.misc[3], a.P, pl.misc);
     __syncthreads();
-    const int ng = uni(pl.misc[0]), e0 = uni(pl.misc[1]), n = uni(pl.misc[2]) - e0;
+    const int vng = uni(pl.misc[0]), ve0 = uni(pl.misc[1]), vn = uni(pl.misc[2]) - ve0;
     int r_src = 0, r_dst = 0;
     float r_w = 0.0f;
     uint64_t vg = 0, vu = 0, vd = 0;
     int e = -1;
-    if (tid < n) {
-      r_src = a.P.ent_src[e0 + tid];
-      r_dst = a.P.ent_dst[e0 + tid];
-      r_w = a.P.ent_w[e0 + tid];
+    if (tid < vn) {
+      r_src = a.P.ent_src[ve0 + tid];
+      r_dst = a.P.ent_dst[ve0 + tid];
+      r_w = a.P.ent_w[ve0 + tid];
     }
-    if (tid < ng) {
+    if (tid < vng) {
       e = pl.gexp[tid];
       if (e >= 0 && e < a.A.n_experts) {
         vg = (uint64_t)(uintptr_t)a.A.gate[e];
@@ -1102,7 +1116,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
         if (MODE == GU_FUSED) vd = (uint64_t)(uintptr_t)a.A.down[e];
       }
     }
-    if (tid < n) {
+    if (tid < vn) {
       const bool src_ok = r_src >= 0 && r_src < a.n_tokens;
       if (!src_ok) set_err(a.P.err, MOE_ERR_SRC);
       pl.esrc[tid] = src_ok ? r_src : 0;
@@ -1110,7 +1124,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
       pl.ew[tid] = r_w;
       pl.elive[tid] = src_ok;
     }
-    if (tid < ng) {
+    if (tid < vng) {
       const bool e_ok = e >= 0 && e < a.A.n_experts;
       if (!e_ok) set_err(a.P.err, MOE_ERR_EXPERT);
       gptr[3 * tid] = (e_ok && ptr_ok(vg | vu, a.P.err)) ? vg : 0;
@@ -1118,31 +1132,45 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
       gptr[3 * tid + 2] = (e_ok && MODE == GU_FUSED && ptr_ok(vd, a.P.err)) ? vd : 0;
     }
     __syncthreads();
+    ng = vng;
+    e0 = ve0;
+    n = vn;
   }
-  const int ng = uni(pl.misc[0]), e0 = uni(pl.misc[1]), n = uni(pl.misc[2]) - e0;
-
-  // ---- 4. workgroup 0 leaves the plan (routed) and the call's descriptor (fused / routed)
-  if (MODE != GU_COMPOSED && blockIdx.x == 0) {
-    if constexpr (MODE == GU_ROUTED) publish_plan<kGuThreads>(pl, a.P);
-    int* dw = (int*)a.desc;
-    uint64_t* dp = (uint64_t*)(a.desc + kDescPtrByte);
-    if (tid == 0) {
-      dw[kDescNg] = ng;
-      dw[kDescE0] = e0;
-      dw[kDescN] = n;
+  // routed: the g-th group's expert (word l, bit b of the union) ...
+  auto find_expert = [&](int g, int& l, int& b) {
+    const uint64_t hit = __ballot(lane < nW && upre + upc > g);
+    l = (int)__builtin_ctzll(hit);
+    const uint32_t wv = (uint32_t)__builtin_amdgcn_readlane((int)uw, l);
+    const int r = g - __builtin_amdgcn_readlane(upre, l);
+    const uint32_t below = lane < 32 ? ((1u << (lane & 31)) - 1u) : 0u;
+    const uint64_t bm = __ballot(lane < 32 && ((wv >> (lane & 31)) & 1u) && __popc(wv & below) == r);
+    b = (int)__builtin_ctzll(bm);
+  };
+  // ... and its entries: the tokens that chose it (bit t of tm), first entry a0 (relative to e0)
+  auto entries_of = [&](int l, int b, int& a0, int& cnt, uint64_t& tm) {
+    const uint32_t mine = lane < a.T ? selT[lane * nW + l] : 0u;
+    tm = __ballot((mine >> b) & 1u);
+    cnt = __popcll(tm);
+    a0 = __builtin_amdgcn_readlane(cpre, l) + lane_sum(__popc(mine & ((1u << b) - 1u)), 6);
+  };
+  // the gate and up pointers of group g (0 when the group is skipped)
+  auto group_ptrs = [&](int g, uint64_t& wg, uint64_t& wu) {
+    wg = 0;
+    wu = 0;
+    if (g >= ng) return;
+    if constexpr (MODE == GU_ROUTED) {
+      int l, b;
+      find_expert(g, l, b);
+      const u64x2 pp = ptab[32 * l + b];
+      wg = uni64(pp.x);
+      wu = uni64(pp.y);
+    } else {
+      wg = uni64(gptr[3 * g]);
+      wu = uni64(gptr[3 * g + 1]);
     }
-    if (tid <= ng) dw[kDescGs + tid] = pl.gstart[tid] - e0;
-    if (tid < ng) dp[tid] = gptr[3 * tid] ? gptr[3 * tid + 2] : 0;
-    if (tid < n) {
-      int g = 0;
-      while (g + 1 < ng && pl.gstart[g + 1] - e0 <= tid) ++g;
-      dw[kDescDst + tid] = pl.edst[tid];
-      ((float*)dw)[kDescW + tid] = pl.ew[tid];
-      dw[kDescLive + tid] = pl.elive[tid] && gptr[3 * g] != 0;
-    }
-  }
+  };
 
-  // ---- 5. items: the workgroup's blocks; this wave's passes of each, streamed through its ring
+  // ---- 4. items: the workgroup's blocks; this wave's passes of each, streamed through its ring
   const int half = G.rp >> 1;
   const int nb = a.A.n_ff / 32;          // blocks per group
   const int npass = 64 / G.rp;           // passes per block
@@ -1157,9 +1185,9 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     const int kk = kc / cw, q = kc - kk * cw;
     const int it = (int)blockIdx.x + kk * (int)gridDim.x;
     const int g = it / nb, blk = it - g * nb;
-    const uint64_t wg = uni64(gptr[3 * g]);
+    uint64_t wg, wu;
+    group_ptrs(g, wg, wu);
     if (wg) {
-      const uint64_t wu = uni64(gptr[3 * g + 1]);
       const uint64_t off = (uint64_t)(blk * 32 + (wave + q * a.sw) * half) * (uint64_t)G.rb;
       issue_chunk(slot, M, (const uint8_t*)(uintptr_t)(wg + off), nspan,
                   (const uint8_t*)(uintptr_t)(wu + off), nspan, span_b_chunk(wg + off, nspan));
@@ -1171,12 +1199,78 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   const int pre = min(NS, nch);
   for (int kc = 0; kc < pre; ++kc) issue(kc, myring + kc * M * 1024);
   int issued = pre;
+
+  // ---- 5. workgroup 0 leaves the plan (routed) and the call's descriptor (fused / routed)
+  if (MODE != GU_COMPOSED && blockIdx.x == 0) {
+    int* dw = (int*)a.desc;
+    uint64_t* dp = (uint64_t*)(a.desc + kDescPtrByte);
+    if constexpr (MODE == GU_ROUTED) {
+      for (int g = wave; g < ng; g += kGuWaves) {
+        int l, b, a0, cnt;
+        uint64_t tm;
+        find_expert(g, l, b);
+        entries_of(l, b, a0, cnt, tm);
+        const int e = 32 * l + b;
+        const bool ok = uni64(ptab[e].x) != 0;
+        if (lane == 0) {
+          a.P.grp_expert[g] = e;
+          a.P.grp_start[g] = e0 + a0;
+          dw[kDescGs + g] = a0;
+          dp[g] = ok ? ptabd[e] : 0ull;
+        }
+        if ((tm >> lane) & 1ull) {   // lane = token
+          const int ent = a0 + __popcll(tm & lt);
+          int r = 0;
+          while (r < a.k - 1 && pl.rid[lane * a.k + r] != e) ++r;
+          const float wv = pl.rw[lane * a.k + r];
+          const int dst = pl.dtok[lane];
+          a.P.ent_src[e0 + ent] = lane;
+          a.P.ent_dst[e0 + ent] = dst;
+          a.P.ent_w[e0 + ent] = wv;
+          dw[kDescDst + ent] = dst;
+          ((float*)dw)[kDescW + ent] = wv;
+          dw[kDescLive + ent] = ok ? 1 : 0;
+        }
+      }
+      if (tid == 0) {
+        *a.P.n_groups = ng;
+        a.P.grp_start[ng] = e0 + n;
+        dw[kDescGs + ng] = n;
+      }
+    } else {
+      if (tid <= ng) dw[kDescGs + tid] = pl.gstart[tid] - e0;
+      if (tid < ng) dp[tid] = gptr[3 * tid] ? gptr[3 * tid + 2] : 0;
+      if (tid < n) {
+        int g = 0;
+        while (g + 1 < ng && pl.gstart[g + 1] - e0 <= tid) ++g;
+        dw[kDescDst + tid] = pl.edst[tid];
+        ((float*)dw)[kDescW + tid] = pl.ew[tid];
+        dw[kDescLive + tid] = pl.elive[tid] && gptr[3 * g] != 0;
+      }
+    }
+    if (tid == 0) {
+      dw[kDescNg] = ng;
+      dw[kDescE0] = e0;
+      dw[kDescN] = n;
+    }
+  }
+
   int kc = 0;
   for (int kk = 0; kk < nit; ++kk) {
     const int it = (int)blockIdx.x + kk * (int)gridDim.x;
     const int g = it / nb, blk = it - g * nb;
-    const uint64_t wgv = uni64(gptr[3 * g]);
-    const int a0 = uni(pl.gstart[g]) - e0, a1 = uni(pl.gstart[g + 1]) - e0;
+    uint64_t wgv, wuv;
+    group_ptrs(g, wgv, wuv);
+    int a0 = 0, ne = 0;
+    uint64_t tm = 0;
+    if constexpr (MODE == GU_ROUTED) {
+      int l, b;
+      find_expert(g, l, b);
+      entries_of(l, b, a0, ne, tm);
+    } else {
+      a0 = uni(pl.gstart[g]) - e0;
+      ne = uni(pl.gstart[g + 1]) - e0 - a0;
+    }
     for (int q = 0; q < cw; ++q, ++kc) {
       wait_vm((issued - 1 - kc) * M);
       MOE_LDS uint8_t* slot = myring + (kc % NS) * M * 1024;
@@ -1185,15 +1279,25 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
         const uint64_t off = (uint64_t)(blk * 32 + prow) * (uint64_t)G.rb;
         const uint32_t sb = (uint32_t)(slot - ring);
         const uint32_t ra = sb + (uint32_t)((wgv + off) & 15);
-        const uint32_t rb0 = sb + 16 * span_b_chunk(wgv + off, nspan) +
-                             (uint32_t)((uni64(gptr[3 * g + 1]) + off) & 15);
-        for (int c0 = a0; c0 < a1; c0 += kSlots) {
-          const int ne = min(kSlots, a1 - c0);
+        const uint32_t rb0 = sb + 16 * span_b_chunk(wgv + off, nspan) + (uint32_t)((wuv + off) & 15);
+        uint64_t rest = tm;   // routed: the group's tokens not yet dotted
+        for (int c0 = 0; c0 < ne; c0 += kSlots) {
+          const int nc = min(kSlots, ne - c0);
           int sidx[kSlots];
 #pragma unroll
-          for (int e = 0; e < kSlots; ++e) sidx[e] = e < ne ? uni(pl.esrc[c0 + e]) : 0;
-          MOE_LDS float* st = stage + (c0 - a0) * 64 + prow;
-          dot_pass<FMT>((const MOE_LDS uint32_t*)ring, ra, rb0, half, G.rp, G, tb, act, sidx, ne,
+          for (int e = 0; e < kSlots; ++e) {
+            if constexpr (MODE == GU_ROUTED) {
+              sidx[e] = 0;
+              if (e < nc) {
+                sidx[e] = (int)__builtin_ctzll(rest);
+                rest &= rest - 1ull;
+              }
+            } else {
+              sidx[e] = e < nc ? uni(pl.esrc[a0 + c0 + e]) : 0;
+            }
+          }
+          MOE_LDS float* st = stage + c0 * 64 + prow;
+          dot_pass<FMT>((const MOE_LDS uint32_t*)ring, ra, rb0, half, G.rp, G, tb, act, sidx, nc,
                         [&](int i, int e, float v) { st[e * 64 + (i < half ? i : 32 + i - half)] = v; });
         }
       }
@@ -1205,7 +1309,6 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     }
     lds_barrier();
     // the block's outputs: composed, g and u rows; fused / routed, SwiGLU + q8_1 of h
-    const int ne = a1 - a0;
     if (wgv) {
       if constexpr (MODE == GU_COMPOSED) {
         for (int idx = tid; idx < ne * 64; idx += kGuThreads) {
@@ -1217,12 +1320,13 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
         // 32 lanes per entry; every half-wave runs each round (the shuffles need all 32 lanes)
         for (int base = 0; base < ne; base += kGuThreads / 32) {
           const int e = base + (tid >> 5), l32 = tid & 31;
-          const bool live = e < ne && pl.elive[a0 + (e < ne ? e : 0)] != 0;
+          bool live = e < ne;
+          if constexpr (MODE != GU_ROUTED) live = live && pl.elive[a0 + (e < ne ? e : 0)] != 0;
           const float gv = live ? stage[e * 64 + l32] : 0.0f;
           const float uv = live ? stage[e * 64 + 32 + l32] : 0.0f;
-          const size_t b = (size_t)(a0 + (live ? e : 0)) * nb + blk;
-          swiglu_q81_split(gv, uv, l32, live, (uint8_t*)(a.hq_lo + 4 * b), (uint8_t*)(a.hq_hi + 4 * b),
-                           a.hq_d + b);
+          const size_t bk = (size_t)(a0 + (live ? e : 0)) * nb + blk;
+          swiglu_q81_split(gv, uv, l32, live, (uint8_t*)(a.hq_lo + 4 * bk), (uint8_t*)(a.hq_hi + 4 * bk),
+                           a.hq_d + bk);
         }
       }
     }
@@ -1508,14 +1612,14 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
 // One wave per token.
 __global__ __launch_bounds__(64) void k_route(const float* __restrict__ logits, int E, int k,
                                               int32_t* __restrict__ ids, float* __restrict__ w) {
-  __shared__ float s_lg[1024];
+  __shared__ __align__(16) uint32_t s_scr[3 * 1024 + 100];
   __shared__ int s_ids[32];
   __shared__ float s_w[32];
-  __shared__ uint32_t s_scr[96];
+  __shared__ uint32_t s_bits[32];
   const int t = blockIdx.x;
-  issue_logits(logits + (size_t)t * E, E, (MOE_LDS float*)s_lg);
+  issue_logits(logits + (size_t)t * E, E, (MOE_LDS float*)s_scr);
   __builtin_amdgcn_s_waitcnt(MOE_VM(0));
-  route_wave((MOE_LDS float*)s_lg, E, k, (MOE_LDS int*)s_ids, (MOE_LDS float*)s_w, (MOE_LDS uint32_t*)s_scr);
+  route_token((MOE_LDS uint32_t*)s_scr, E, k, (MOE_LDS int*)s_ids, (MOE_LDS float*)s_w, (MOE_LDS uint32_t*)s_bits);
   if ((int)threadIdx.x < k) {
     ids[(size_t)t * k + threadIdx.x] = s_ids[threadIdx.x];
     w[(size_t)t * k + threadIdx.x] = s_w[threadIdx.x];
@@ -1760,21 +1864,28 @@ hipError_t launch_dn(int fmt, int mode, const DnArgs& da, int grid, int bytes, h
 
 // LDS the gate/up kernel needs for n_tokens activation rows, its stream and how many of its waves
 // stream (all 16 when the slots fit, fewer for long rows), or -1 if it does not fit.
-int gu_lds(const moe_layer* L, int n_tokens, bool routed, Stream* S, int* sw, int* ring, int* actb) {
+int gu_lds(const moe_layer* L, int n_tokens, int mode, Stream* S, int* sw, int* ring, int* actb, int* tailb) {
   const Geom G = make_geom(L->fmt_gate_up, L->n_embd, true);
   *actb = act_bytes(n_tokens, G.U);
   if (*actb > kGuActMax) return -1;
-  // the prologue stages (routed) kRouteWaves tokens' logits and at least one float row of x in
-  // the ring before it streams
-  const int lg = (routed ? kRouteWaves * logits_pad(L->n_experts) * 4 : 0) + L->n_embd * 4;
-  const int avail = kLdsMax - gu_smem_bytes(0, *actb);
+  // the prologue uses the ring before the stream: routed, the routing waves' scratch; fused, at
+  // least one float row of x
+  int lg = 0;
+  *tailb = 0;
+  if (mode == GU_ROUTED) {
+    lg = std::min(n_tokens, kRtWaves) * route_scr_words(L->n_experts) * 4;
+    *tailb = gu_tail_bytes(L->n_experts, n_tokens);
+  } else if (mode == GU_FUSED) {
+    lg = L->n_embd * 4;
+  }
+  const int avail = kLdsMax - gu_smem_bytes(0, *actb, *tailb);
   for (int ns = 2; ns >= 1; --ns) {
     *S = gu_stream(G, ns);
     const int per_wave = S->NS * S->M * 1024;
     *sw = std::min(kGuWaves, avail / per_wave);
     if (*sw >= (ns == 2 ? kGuWaves : 1)) {
       *ring = std::max(*sw * per_wave, lg);
-      const int b = gu_smem_bytes(*ring, *actb);
+      const int b = gu_smem_bytes(*ring, *actb, *tailb);
       if (b <= kLdsMax) return b;
     }
   }
@@ -1802,9 +1913,9 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
                 int n_tokens, float* g, float* u, int ld, uint8_t* ws, const float* logits, int T, int k,
                 const int32_t* dst_of_token, int entry_base, int grid_limit) {
   const Geom G = make_geom(L->fmt_gate_up, L->n_embd, true);
-  int ring = 0, actb = 0, sw = 0;
+  int ring = 0, actb = 0, sw = 0, tailb = 0;
   Stream S{};
-  const int bytes = gu_lds(L, n_tokens, mode == GU_ROUTED, &S, &sw, &ring, &actb);
+  const int bytes = gu_lds(L, n_tokens, mode, &S, &sw, &ring, &actb, &tailb);
   if (bytes < 0) return MOE_E_SHAPE;
   GuArgs ga{};
   ga.A = layer_args(L);
