@@ -622,7 +622,7 @@ __host__ __device__ inline int route_scr_words(int E) { return 3 * logits_pad(E)
 // word e / 32), all in LDS.
 template <int V>
 __device__ __forceinline__ void route_token_v(MOE_LDS uint32_t* scr, int E, int k, MOE_LDS int* ids,
-                                              MOE_LDS float* w, MOE_LDS uint32_t* bits) {
+                                              MOE_LDS float* w, MOE_LDS uint32_t* bits, bool need_w) {
   const int lane = threadIdx.x & 63;
   const uint64_t lt = (1ull << lane) - 1ull;
   const int Epad = logits_pad(E);
@@ -706,6 +706,7 @@ __device__ __forceinline__ void route_token_v(MOE_LDS uint32_t* scr, int E, int 
     bits[lane] = bw;
   }
   // 3. weights
+  if (!need_w) return;
   float ex = 0.0f;
   if (lane < k) ex = expf(lsel[lane] - lsel[0]);
   float sum = 0.0f;
@@ -714,14 +715,15 @@ __device__ __forceinline__ void route_token_v(MOE_LDS uint32_t* scr, int E, int 
   wave_lds_sync();
 }
 
+// need_w: also the weights (a caller that only needs the selection skips them)
 __device__ __forceinline__ void route_token(MOE_LDS uint32_t* scr, int E, int k, MOE_LDS int* ids,
-                                            MOE_LDS float* w, MOE_LDS uint32_t* bits) {
+                                            MOE_LDS float* w, MOE_LDS uint32_t* bits, bool need_w = true) {
   if (E <= 128)
-    route_token_v<2>(scr, E, k, ids, w, bits);
+    route_token_v<2>(scr, E, k, ids, w, bits, need_w);
   else if (E <= 256)
-    route_token_v<4>(scr, E, k, ids, w, bits);
+    route_token_v<4>(scr, E, k, ids, w, bits, need_w);
   else
-    route_token_v<16>(scr, E, k, ids, w, bits);
+    route_token_v<16>(scr, E, k, ids, w, bits, need_w);
 }
 
 // ------------------------------------------------------------------ plan in LDS -------------
@@ -995,7 +997,8 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
       for (int t = wave; t < a.T; t += kRtWaves) {
         issue_logits(a.logits + (size_t)t * a.E, a.E, (MOE_LDS float*)rscr);
         __builtin_amdgcn_s_waitcnt(MOE_VM(0));
-        route_token(rscr, a.E, a.k, pl.rid + t * a.k, pl.rw + t * a.k, selT + t * nW);
+        // only workgroup 0 writes the plan, so only it needs the router weights
+        route_token(rscr, a.E, a.k, pl.rid + t * a.k, pl.rw + t * a.k, selT + t * nW, blockIdx.x == 0);
       }
     } else {
       // two register passes cover one 4096-wide row; eight cover four (more: plain loads after)
@@ -1456,42 +1459,6 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   }
   const int ng = uni(dsc[kDescNg]), e0 = uni(dsc[kDescE0]), n = uni(dsc[kDescN]);
   if (ng == 0) return;
-  // entry metadata: destination (or -1), weight, owner = first live entry naming its dst
-  if (tid < n) {
-    int g = 0;
-    while (g + 1 < ng && dsc[kDescGs + g + 1] <= tid) ++g;
-    const int d = dsc[kDescDst + tid];
-    int live = dsc[kDescLive + tid] && dptr[g] != 0;
-    if (live && (d < 0 || d >= a.n_rows)) {
-      set_err(a.P.err, MOE_ERR_DST);
-      live = 0;
-    }
-    mdst[tid] = live ? d : -1;
-    mw[tid] = ((MOE_LDS float*)dsc)[kDescW + tid];
-  }
-  __syncthreads();
-  if (wave == 0) {   // n <= 64: one lane per entry
-    const int lane = tid;
-    int owner = 0;
-    if (lane < n) {
-      const int d = mdst[lane];
-      owner = d >= 0;
-      for (int q = 0; q < lane && owner; ++q) owner = mdst[q] != d;
-      mown[lane] = owner;
-    }
-    const uint64_t om = __ballot(owner);
-    if (owner) {
-      const int o = __popcll(om & ((1ull << lane) - 1ull));
-      omap[lane] = o;
-      ownl[o] = lane;
-    }
-    if (lane == 0) misc[8] = __popcll(om);
-  }
-  __syncthreads();
-  const int nown = uni(misc[8]);
-
-  // ---- 2. h rows and the first tile's destination rows first, then the first chunks of the
-  //         stream, then (DN_PLAN) the h rows to LDS
   const ActSplit act = MODE == DN_DESC ? act_layout_kb(actp, n, U) : act_layout(actp, n, U);
   const int ntiles = (a.A.n_embd + G.rp - 1) / G.rp;
   const int ntw = (int)blockIdx.x < ntiles ? (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
@@ -1511,11 +1478,55 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
       issue_chunk(slot, M, (const uint8_t*)a.P.err, 1, nullptr, 0, 0);
   };
   const int pre = min(NS, nch);
+  // ---- 2. descriptor path: the h rows and the first chunks of the stream go out at once; the
+  //         entries' metadata is worked out while they are in flight
+  if constexpr (MODE == DN_DESC) {
+    const uint32_t qb = (uint32_t)(n * U * 16), db = (uint32_t)((n * U * 4 + 15) & ~15);
+    dma_span(a.hq_lo, qb, (MOE_LDS uint8_t*)act.lo, wave, kDnWaves);
+    dma_span(a.hq_hi, qb, (MOE_LDS uint8_t*)act.hi, (wave + 3) % kDnWaves, kDnWaves);
+    dma_span(a.hq_d, db, (MOE_LDS uint8_t*)act.d, (wave + 6) % kDnWaves, kDnWaves);
+    for (int kc = 0; kc < pre; ++kc) issue(kc, myring + kc * M * 1024);
+  }
+  // entry metadata: destination (or -1), weight, owner = first live entry naming its dst
+  if (tid < n) {
+    int g = 0;
+    while (g + 1 < ng && dsc[kDescGs + g + 1] <= tid) ++g;
+    const int d = dsc[kDescDst + tid];
+    int live = dsc[kDescLive + tid] && dptr[g] != 0;
+    if (live && (d < 0 || d >= a.n_rows)) {
+      set_err(a.P.err, MOE_ERR_DST);
+      live = 0;
+    }
+    mdst[tid] = live ? d : -1;
+    mw[tid] = ((MOE_LDS float*)dsc)[kDescW + tid];
+  }
+  lds_barrier();
+  if (wave == 0) {   // n <= 64: one lane per entry
+    const int lane = tid;
+    int owner = 0;
+    if (lane < n) {
+      const int d = mdst[lane];
+      owner = d >= 0;
+      for (int q = 0; q < lane && owner; ++q) owner = mdst[q] != d;
+      mown[lane] = owner;
+    }
+    const uint64_t om = __ballot(owner);
+    if (owner) {
+      const int o = __popcll(om & ((1ull << lane) - 1ull));
+      omap[lane] = o;
+      ownl[o] = lane;
+    }
+    if (lane == 0) misc[8] = __popcll(om);
+  }
+  lds_barrier();
+  const int nown = uni(misc[8]);
+
+  // the first tile's rows of every destination (wave 0, one float per lane): ny loads
   const int r00 = (int)blockIdx.x * G.rp, nr0 = min(G.rp, a.A.n_embd - r00);   // first tile
-  auto mid = [&](int) {
-    // the first tile's rows of every destination: one float per lane, wave 0
+  auto stage_y = [&]() {
+    int ny = 0;
     if (wave == 0 && ntw > 0) {
-      for (int p = 0; p * 64 < nown * nr0; ++p) {
+      for (int p = 0; p * 64 < nown * nr0; ++p, ++ny) {
         const int l = p * 64 + (tid & 63);
         if (l < nown * nr0) {
           const int o = l / nr0, m = l - o * nr0;
@@ -1524,16 +1535,19 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
         }
       }
     }
-    for (int kc = 0; kc < pre; ++kc) issue(kc, myring + kc * M * 1024);
-    wait_vm(pre * M);   // the h rows and Y rows, older than every chunk, have landed
+    return ny;
   };
+  int ny = 0;   // wave 0: loads issued after the first chunks (their waits allow for them)
   if constexpr (MODE == DN_DESC) {
-    const uint32_t qb = (uint32_t)(n * U * 16), db = (uint32_t)((n * U * 4 + 15) & ~15);
-    dma_span(a.hq_lo, qb, (MOE_LDS uint8_t*)act.lo, wave, kDnWaves);
-    dma_span(a.hq_hi, qb, (MOE_LDS uint8_t*)act.hi, (wave + 3) % kDnWaves, kDnWaves);
-    dma_span(a.hq_d, db, (MOE_LDS uint8_t*)act.d, (wave + 6) % kDnWaves, kDnWaves);
-    mid(0);
+    ny = uni(stage_y());
+    wait_vm(pre * M + ny);   // this wave's pieces of the h rows, older than every chunk, have landed
   } else {
+    // the caller's plan: q8_1 rows of h by absolute entry, staged after the first chunks go out
+    auto mid = [&](int) {
+      stage_y();
+      for (int kc = 0; kc < pre; ++kc) issue(kc, myring + kc * M * 1024);
+      wait_vm(pre * M);   // the Y rows, older than every chunk, have landed
+    };
     act_stage_q<kDnThreads, 16>(a.hq + (size_t)e0 * U * 36, n * U, act, mid);
   }
   int issued = pre;
@@ -1546,7 +1560,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
     const int r0 = t * G.rp, nr = min(G.rp, a.A.n_embd - r0);
     for (int q = 0; q < cpt; ++q, ++kc) {
       const int g = wave + q * kDnWaves;
-      wait_vm((issued - 1 - kc) * M);
+      wait_vm((issued - 1 - kc) * M + (kc < pre ? ny : 0));
       MOE_LDS uint8_t* slot = myring + (kc % NS) * M * 1024;
       const uint64_t w = uni64(dptr[g]);
       if (w) {
@@ -1567,6 +1581,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
         ++issued;
       }
     }
+    if (kt == 0 && ny) wait_vm(0);   // wave 0: the first tile's Y rows (issued after its first chunks)
     lds_barrier();
     // scatter: one thread per (owner entry, row)
     for (int idx = tid; idx < n * nr; idx += kDnThreads) {
