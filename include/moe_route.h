@@ -81,6 +81,8 @@ typedef enum {
 #define MOE_ERR_SRC 8u       /* ent_src out of [0, n_tokens): that entry skipped */
 #define MOE_ERR_DST 16u      /* ent_dst out of [0, n_rows): that entry skipped */
 #define MOE_ERR_ALIGN 32u    /* a weight pointer not 2-byte aligned: that group skipped */
+#define MOE_ERR_WAIT 64u     /* moe_layer_step: a workgroup gave up waiting for the others (its
+                                down tiles were not written); see moe_layer_step */
 
 /* One MoE layer's experts. Host struct, read during the call only. */
 typedef struct moe_layer {
@@ -170,6 +172,20 @@ int moe_layer_decode_routed(void* stream, const moe_layer* L, const moe_plan* P,
                             const float* logits, int T, int k, const int32_t* dst_of_token,
                             int entry_base, const float* x, float* Y, int n_rows, int ldy,
                             void* workspace, size_t ws_bytes, int grid_limit);
+
+/* The whole step from the router logits in ONE launch (same results, bit for bit, as
+ * moe_layer_decode_routed): every workgroup routes and groups, runs its gate/up blocks with SwiGLU
+ * and q8_1 ("#363 ...", "What changes"), then, once every workgroup of the launch has finished its
+ * blocks, the grouped down projection and the weighted scatter ("#2058 ...", "Why"; "#363 ...",
+ * "Exactness"). The workgroups meet through two 32-bit counts inside the workspace: they must be
+ * zero before the first call on a workspace (a zero-filled allocation), and every call leaves them
+ * zero. The launch uses at most one workgroup per CU and needs all of them resident at once (the
+ * device not shared with other work that holds CUs); a workgroup that has not seen the others
+ * within a bounded wait sets MOE_ERR_WAIT and leaves its rows of Y unwritten. Calls that overlap on
+ * one workspace race. Limits as moe_layer_gate_up and moe_layer_down together. */
+int moe_layer_step(void* stream, const moe_layer* L, const moe_plan* P, const float* logits, int T,
+                   int k, const int32_t* dst_of_token, int entry_base, const float* x, float* Y,
+                   int n_rows, int ldy, void* workspace, size_t ws_bytes, int grid_limit);
 
 /* The first of the two launches of moe_layer_decode (logits == NULL: the plan in P as built) or
  * of moe_layer_decode_routed (logits != NULL: route and group here, publish the plan into P;

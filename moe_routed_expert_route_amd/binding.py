@@ -22,7 +22,8 @@ ERR_BITS = {1: "NGROUPS", 2: "ENTRIES", 4: "EXPERT", 8: "SRC", 16: "DST", 32: "A
 
 EXPORTS = ("moe_route_topk", "moe_build_plan", "moe_quantize_q8_1", "moe_gate_up",
            "moe_swiglu_q8_1", "moe_down_scatter", "moe_workspace_bytes",
-           "moe_layer_decode", "moe_layer_decode_routed", "moe_layer_gate_up", "moe_layer_down",
+           "moe_layer_decode", "moe_layer_decode_routed", "moe_layer_step", "moe_layer_gate_up",
+           "moe_layer_down",
            "moe_workspace_layout",
            "moe_status_string", "moe_last_error")
 
@@ -65,6 +66,8 @@ def lib():
         L.moe_layer_decode_routed.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan),
                                               _P, _I, _I, _P, _I, _P, _P, _I, _I, _P,
                                               ctypes.c_size_t, _I]
+        L.moe_layer_step.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan),
+                                     _P, _I, _I, _P, _I, _P, _P, _I, _I, _P, ctypes.c_size_t, _I]
         L.moe_layer_gate_up.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan), _P, _I,
                                         _I, _P, _I, _P, _I, _P, ctypes.c_size_t, _I]
         L.moe_layer_down.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan), _P,
@@ -233,12 +236,13 @@ def moe_workspace_bytes(layer: Layer, plan: Plan) -> int:
 
 
 def workspace(layer: Layer, plan: Plan, device="cuda"):
-    """Allocate a workspace for this layer geometry and plan capacity (no clearing needed: a
-    call reads only bytes it wrote itself)."""
+    """Allocate a zero-filled workspace for this layer geometry and plan capacity (the one-launch
+    step needs its two counts zero before the first call; every other call reads only bytes it
+    wrote itself)."""
     nb = moe_workspace_bytes(layer, plan)
     if nb == 0:
         raise RuntimeError("moe_workspace_bytes: bad layer or plan")
-    ws = torch.empty(nb, dtype=torch.uint8, device=device)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=device)
     if ws.data_ptr() % 256:
         raise RuntimeError("workspace not 256-byte aligned")
     return ws
@@ -273,6 +277,16 @@ def moe_layer_decode_routed(layer: Layer, plan: Plan, logits, k, x, Y, ws, dst_o
                                          _ptr(dst_of_token), entry_base, _ptr(x), _ptr(Y), Y.shape[0],
                                          Y.stride(0), _ptr(ws), ws.numel(), grid_limit),
            "moe_layer_decode_routed")
+
+
+def moe_layer_step(layer: Layer, plan: Plan, logits, k, x, Y, ws, dst_of_token=None, entry_base=0,
+                   grid_limit=0, stream=None):
+    """The whole step from the logits in one launch (workgroups meet through counts in ws)."""
+    T = logits.shape[0]
+    _check(lib().moe_layer_step(_stream(stream), ctypes.byref(layer.struct), ctypes.byref(plan.struct),
+                                _ptr(logits), T, k, _ptr(dst_of_token), entry_base, _ptr(x), _ptr(Y),
+                                Y.shape[0], Y.stride(0), _ptr(ws), ws.numel(), grid_limit),
+           "moe_layer_step")
 
 
 def moe_layer_gate_up(layer: Layer, plan: Plan, x, ws, logits=None, k=0, dst_of_token=None,

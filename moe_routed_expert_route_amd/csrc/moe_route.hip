@@ -106,7 +106,9 @@ constexpr int kDescLive = kDescW + kMaxEnt;   // [kMaxEnt] 1 = compute and scatt
 constexpr int kDescPtrByte = 4 * (kDescLive + kMaxEnt);   // [kMaxGrp] down pointers (u64)
 constexpr int kDescBytes = kDescPtrByte + 8 * kMaxGrp;
 constexpr int kDescReserve = 2048;            // workspace bytes reserved for it
+constexpr int kCtrOff = kDescReserve - 64;    // layer mode: two device-scope counts (zero between calls)
 static_assert(kDescPtrByte % 16 == 0 && kDescBytes % 16 == 0 && kDescBytes <= kDescReserve, "desc");
+static_assert(kDescBytes <= kCtrOff && kCtrOff % 64 == 0, "counts");
 
 // ------------------------------------------------------------------ small helpers -----------
 
@@ -188,6 +190,8 @@ __device__ __forceinline__ uint32_t span_b_chunk(uint64_t a, uint32_t na) {
 // Copy `bytes` (a multiple of 16) from a 16-byte aligned global span into LDS with direct-to-LDS
 // 16-byte loads, 1 KB per instruction, the pieces spread over waves [0, nw); lanes past the end
 // stay masked off. Every instruction is issued before anything the caller issues afterwards.
+// DEV: device-scope loads (sc1: data another XCD wrote during this launch, not a stale L2 copy).
+template <bool DEV = false>
 __device__ __forceinline__ void dma_span(const uint8_t* src, uint32_t bytes, MOE_LDS uint8_t* dst, int wave,
                                          int nw) {
   const uint32_t lane = threadIdx.x & 63;
@@ -195,7 +199,8 @@ __device__ __forceinline__ void dma_span(const uint8_t* src, uint32_t bytes, MOE
   for (uint32_t p = (uint32_t)wave; 64 * p < nc; p += (uint32_t)nw) {
     const uint32_t c = 64 * p + lane;
     if (c < nc)
-      __builtin_amdgcn_global_load_lds((const void*)(src + 16ull * c), (MOE_LDS void*)(dst + 1024 * p), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(src + 16ull * c), (MOE_LDS void*)(dst + 1024 * p), 16, 0,
+                                       DEV ? 16 : 0);
   }
 }
 
@@ -512,6 +517,11 @@ __device__ __forceinline__ void dot_pass(const MOE_LDS uint32_t* W, uint32_t ra,
   }
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
 // ------------------------------------------------------------------ SwiGLU + q8_1 -----------
 
 // 32 lanes (an aligned half-wave) turn 32 (g, u) pairs into one q8_1 block of h. Same arithmetic
@@ -540,8 +550,11 @@ __device__ __forceinline__ void swiglu_q81_lanes(float gv, float uv, int l32, bo
 }
 
 // Same block, stored in split form: quants 0-15 to lo, 16-31 to hi, the scale as float f(d16).
-__device__ __forceinline__ void swiglu_q81_split(float gv, float uv, int l32, bool live, uint8_t* lo,
-                                                 uint8_t* hi, float* dq) {
+// Each quad of lanes packs its four quants into a dword; the stores are device-scope (they reach
+// memory past this XCD's L2), so another workgroup of the same launch can read them once it has
+// seen this workgroup's count.
+__device__ __forceinline__ void swiglu_q81_split(float gv, float uv, int l32, bool live, uint32_t* lo,
+                                                 uint32_t* hi, float* dq) {
   const float h = live ? swiglu(gv, uv) : 0.0f;
   const float amax = wave_max32(__builtin_fabsf(h));
   const float d = amax / 127.0f;
@@ -552,9 +565,13 @@ __device__ __forceinline__ void swiglu_q81_split(float gv, float uv, int l32, bo
     r = r < -127.0f ? -127.0f : r;
     q = (int)r;
   }
+  const uint32_t b = (uint32_t)q & 0xFFu;
+  const uint32_t w = b | (dppu<0x55>(b) << 8) | (dppu<0xAA>(b) << 16) | (dppu<0xFF>(b) << 24);   // quad lanes 1, 2, 3
   if (live) {
-    (l32 < 16 ? lo : hi)[l32 & 15] = (uint8_t)(q & 0xFF);
-    if (l32 == 0) *dq = h2f(f2h(d));
+    if ((l32 & 3) == 0)
+      __hip_atomic_store((l32 < 16 ? lo : hi) + ((l32 >> 2) & 3), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (l32 == 0)
+      __hip_atomic_store((uint32_t*)dq, __float_as_uint(h2f(f2h(d))), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -568,11 +585,6 @@ __device__ __forceinline__ uint32_t fkey(float f) {
 }
 __device__ __forceinline__ float unkey(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dppu(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
 // Exclusive prefix sum over the wave's lanes of values in [0, 2^bits), from ballots of their bit
@@ -890,7 +902,9 @@ __device__ __forceinline__ bool ptr_ok(uint64_t v, uint32_t* err) {
 
 // ------------------------------------------------------------------ gate/up kernel ----------
 
-enum GuMode : int { GU_COMPOSED = 0, GU_FUSED = 1, GU_ROUTED = 2 };
+// GU_LAYER: routed, and after every workgroup has finished its blocks (a device-scope count in the
+// workspace) the same launch runs the grouped down projection and the weighted scatter.
+enum GuMode : int { GU_COMPOSED = 0, GU_FUSED = 1, GU_ROUTED = 2, GU_LAYER = 3 };
 
 struct GuArgs {
   LayerArgs A;
@@ -913,6 +927,14 @@ struct GuArgs {
   int entry_base;
   int lds_ring, lds_act;
   int sw;               // waves that stream items (the ring holds sw waves' slots)
+  // layer mode: the down half
+  Geom Gd;              // down row geometry (rows of n_ff columns)
+  Stream Sd;            // down stream: kDnWaves waves, NS slots of M KB each, in the ring
+  float* Y;
+  int n_rows, ldy;
+  int lds_tail;         // bytes of the routed tail (the down region follows it)
+  uint32_t* ctr;        // workspace: [0] workgroups done with their blocks, [1] workgroups done
+  int spin_limit;       // bounded wait for the other workgroups (then MOE_ERR_WAIT)
 };
 
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
@@ -930,6 +952,13 @@ __host__ __device__ inline int gu_tail_bytes(int E, int T) {
 __host__ __device__ inline int gu_smem_bytes(int lds_ring, int lds_act, int lds_tail) {
   return lds_ring + lds_act + kGuFixed + lds_tail;
 }
+// Layer mode, after the tail: the q8_1 rows of h (split form, KB-padded regions), the per-entry
+// outputs of a down tile, the entries' metadata and the first tile's destination rows of Y.
+constexpr int kLyMeta = 4 * (5 * kMaxEnt + 16);
+constexpr int kLyYBuf = 4 * kMaxEnt * 16;
+__host__ __device__ inline int ly_down_bytes(int cap_entries, int Ud, int rpd) {
+  return act_bytes_kb(cap_entries, Ud) + 4 * kMaxEnt * rpd + kLyMeta + kLyYBuf;
+}
 
 // Work item = one 32-row block of h of one group (so SwiGLU and the q8_1 quantization of the block
 // finish in the workgroup). The block's 64 weight rows are 64 / rp passes of rp rows (rp / 2 gate
@@ -941,8 +970,16 @@ __host__ __device__ inline int gu_smem_bytes(int lds_ring, int lds_act, int lds_
 // selection bitmaps, the expert of each group it streams (groups ascending by expert id; the g-th
 // set bit of the union of the bitmaps) and that group's entries (tokens ascending), so the weight
 // loads go out with no further barrier. Workgroup 0 then writes the plan and the descriptor.
-template <int FMT, int MODE>
+//
+// Layer mode: the grid is at most one workgroup per CU and every workgroup is resident. After its
+// blocks, a workgroup's q8_1 rows of h are in memory (device-scope stores) and it adds one to a
+// count; its down chunks (the rows of its down tiles, taken from the last tile backwards so the
+// workgroups without a block take the extra tiles) go out at once; it waits until the count reaches
+// the grid (bounded), reads every entry's q8_1 rows of h and runs the down tiles and the scatter as
+// the down launch does. The last workgroup to finish clears the counts for the next call.
+template <int FMT, int MODE, int FD = FMT>
 __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
+  constexpr bool RT = MODE == GU_ROUTED || MODE == GU_LAYER;
   extern __shared__ __align__(16) uint8_t smem[];
   const Geom& G = a.G;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -975,9 +1012,14 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     const uint32_t* src = (const uint32_t*)(FMT == CB2 ? a.A.cb2 : a.A.cb3);
     if (tid < 512) t_cb = src[tid];
   }
+  uint32_t t_cbd = 0;   // layer mode: the down format's grid, when it differs
+  if constexpr (MODE == GU_LAYER && FD != FMT && (FD == CB2 || FD == CB3)) {
+    const uint32_t* src = (const uint32_t*)(FD == CB2 ? a.A.cb2 : a.A.cb3);
+    if (tid < 512) t_cbd = src[tid];
+  }
   int r_dt = 0, r_gs = 0, r_ge = 0, r_ng = 0;
   uint64_t pg = 0, pu = 0, pd = 0;
-  if constexpr (MODE == GU_ROUTED) {
+  if constexpr (RT) {
     if (tid < a.T) r_dt = a.dst_of_token ? a.dst_of_token[tid] : tid;
     if (tid < a.E) {
       pg = (uint64_t)(uintptr_t)a.A.gate[tid];
@@ -991,14 +1033,15 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   }
 
   // ---- 2. routing and the activations' q8_1 blocks
-  if constexpr (MODE == GU_ROUTED) {
+  if constexpr (RT) {
     if (wave < kRtWaves) {
       MOE_LDS uint32_t* rscr = (MOE_LDS uint32_t*)ring + wave * route_scr_words(a.E);
       for (int t = wave; t < a.T; t += kRtWaves) {
         issue_logits(a.logits + (size_t)t * a.E, a.E, (MOE_LDS float*)rscr);
         __builtin_amdgcn_s_waitcnt(MOE_VM(0));
-        // only workgroup 0 writes the plan, so only it needs the router weights
-        route_token(rscr, a.E, a.k, pl.rid + t * a.k, pl.rw + t * a.k, selT + t * nW, blockIdx.x == 0);
+        // routed: only workgroup 0 writes the plan, so only it needs the router weights
+        route_token(rscr, a.E, a.k, pl.rid + t * a.k, pl.rw + t * a.k, selT + t * nW,
+                    MODE == GU_LAYER || blockIdx.x == 0);
       }
     } else {
       // two register passes cover one 4096-wide row; eight cover four (more: plain loads after)
@@ -1068,7 +1111,9 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   }
   if constexpr (FMT == CB2 || FMT == CB3)
     if (tid < 512) (FMT == CB2 ? g2 : g3)[tid] = t_cb;
-  if constexpr (MODE != GU_ROUTED) {
+  if constexpr (MODE == GU_LAYER && FD != FMT && (FD == CB2 || FD == CB3))
+    if (tid < 512) (FD == CB2 ? g2 : g3)[tid] = t_cbd;
+  if constexpr (!RT) {
     if (tid == 0) pl.misc[3] = r_ng;
     if (tid <= a.P.cap_groups) pl.gstart[tid] = r_gs;
     if (tid < a.P.cap_groups) pl.gexp[tid] = r_ge;
@@ -1084,7 +1129,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   uint32_t uw = 0u;
   int upc = 0, upre = 0, cpre = 0;
   int ng = 0, e0 = 0, n = 0;
-  if constexpr (MODE == GU_ROUTED) {
+  if constexpr (RT) {
     int ucnt = 0;
     if (lane < nW)
       for (int t = 0; t < a.T; ++t) {
@@ -1161,7 +1206,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     wg = 0;
     wu = 0;
     if (g >= ng) return;
-    if constexpr (MODE == GU_ROUTED) {
+    if constexpr (RT) {
       int l, b;
       find_expert(g, l, b);
       const u64x2 pp = ptab[32 * l + b];
@@ -1207,7 +1252,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   if (MODE != GU_COMPOSED && blockIdx.x == 0) {
     int* dw = (int*)a.desc;
     uint64_t* dp = (uint64_t*)(a.desc + kDescPtrByte);
-    if constexpr (MODE == GU_ROUTED) {
+    if constexpr (RT) {
       for (int g = wave; g < ng; g += kGuWaves) {
         int l, b, a0, cnt;
         uint64_t tm;
@@ -1266,7 +1311,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     group_ptrs(g, wgv, wuv);
     int a0 = 0, ne = 0;
     uint64_t tm = 0;
-    if constexpr (MODE == GU_ROUTED) {
+    if constexpr (RT) {
       int l, b;
       find_expert(g, l, b);
       entries_of(l, b, a0, ne, tm);
@@ -1289,7 +1334,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
           int sidx[kSlots];
 #pragma unroll
           for (int e = 0; e < kSlots; ++e) {
-            if constexpr (MODE == GU_ROUTED) {
+            if constexpr (RT) {
               sidx[e] = 0;
               if (e < nc) {
                 sidx[e] = (int)__builtin_ctzll(rest);
@@ -1324,16 +1369,210 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
         for (int base = 0; base < ne; base += kGuThreads / 32) {
           const int e = base + (tid >> 5), l32 = tid & 31;
           bool live = e < ne;
-          if constexpr (MODE != GU_ROUTED) live = live && pl.elive[a0 + (e < ne ? e : 0)] != 0;
+          if constexpr (!RT) live = live && pl.elive[a0 + (e < ne ? e : 0)] != 0;
           const float gv = live ? stage[e * 64 + l32] : 0.0f;
           const float uv = live ? stage[e * 64 + 32 + l32] : 0.0f;
           const size_t bk = (size_t)(a0 + (live ? e : 0)) * nb + blk;
-          swiglu_q81_split(gv, uv, l32, live, (uint8_t*)(a.hq_lo + 4 * bk), (uint8_t*)(a.hq_hi + 4 * bk),
-                           a.hq_d + bk);
+          swiglu_q81_split(gv, uv, l32, live, a.hq_lo + 4 * bk, a.hq_hi + 4 * bk, a.hq_d + bk);
         }
       }
     }
     lds_barrier();
+  }
+
+  // ---- 7. layer mode: the grouped down projection and the weighted scatter
+  if constexpr (MODE == GU_LAYER) {
+    const Geom& Gd = a.Gd;
+    const int Ud = Gd.U;
+    MOE_LDS uint8_t* dreg = tail + a.lds_tail;
+    const ActSplit actd = act_layout_kb(dreg, a.P.cap_entries, Ud);
+    MOE_LDS float* ores = (MOE_LDS float*)(dreg + act_bytes_kb(a.P.cap_entries, Ud));   // [kMaxEnt][rpd]
+    MOE_LDS int* mdst = (MOE_LDS int*)(ores + kMaxEnt * Gd.rp);   // [kMaxEnt] dst or -1
+    MOE_LDS int* mown = mdst + kMaxEnt;                           // first live entry of its dst
+    MOE_LDS float* mw = (MOE_LDS float*)(mown + kMaxEnt);
+    MOE_LDS int* omap = (MOE_LDS int*)(mw + kMaxEnt);             // owner index of an owner entry
+    MOE_LDS int* ownl = omap + kMaxEnt;                           // owner entries in order
+    MOE_LDS int* dmisc = ownl + kMaxEnt;                          // [16]
+    MOE_LDS float* ybuf = (MOE_LDS float*)(dmisc + 16);           // [owner][rpd] first tile's Y rows
+    constexpr int kPoll = 64 * kDnWaves;   // a thread of a wave that streams no down chunks
+
+    // (a) this workgroup's q8_1 rows of h have reached device scope: count it
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    if (tid == 0) __hip_atomic_fetch_add(&a.ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // (b) the call in LDS: per group its first entry and down pointer, per entry its destination,
+    //     weight and whether it was computed
+    for (int g = wave; g < ng; g += kGuWaves) {
+      int l, b, a0, cnt;
+      uint64_t tm;
+      find_expert(g, l, b);
+      entries_of(l, b, a0, cnt, tm);
+      const int e = 32 * l + b;
+      const bool ok = uni64(ptab[e].x) != 0;
+      if (lane == 0) {
+        pl.gstart[g] = a0;
+        gptr[3 * g + 2] = ok ? ptabd[e] : 0ull;
+      }
+      if ((tm >> lane) & 1ull) {   // lane = token
+        const int ent = a0 + __popcll(tm & lt);
+        int r = 0;
+        while (r < a.k - 1 && pl.rid[lane * a.k + r] != e) ++r;
+        pl.edst[ent] = pl.dtok[lane];
+        pl.ew[ent] = pl.rw[lane * a.k + r];
+        pl.elive[ent] = ok ? 1 : 0;
+      }
+    }
+    if (tid == 0) pl.gstart[ng] = n;
+    lds_barrier();
+
+    // (c) this workgroup's down tiles (tile t goes to workgroup grid - 1 - t % grid, so the
+    //     workgroups without a block take the extra tiles); waves 0..kDnWaves-1 take the groups
+    //     g = w, w + kDnWaves, ...; their first chunks go out now, into the ring
+    const int ntiles = (a.A.n_embd + Gd.rp - 1) / Gd.rp;
+    const int rev = (int)gridDim.x - 1 - (int)blockIdx.x;
+    const int ntw = rev < ntiles ? (ntiles - rev + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+    const int cpt = (wave < kDnWaves && wave < ng) ? (ng - wave + kDnWaves - 1) / kDnWaves : 0;
+    const int nchd = ntw * cpt;
+    const int Md = a.Sd.M, NSd = a.Sd.NS;
+    MOE_LDS uint8_t* dring = ring + (wave < kDnWaves ? wave : 0) * NSd * Md * 1024;
+    auto dissue = [&](int kc, MOE_LDS uint8_t* slot) {
+      const int kt = kc / cpt, q = kc - kt * cpt;
+      const int t = rev + kt * (int)gridDim.x, g = wave + q * kDnWaves;
+      const int r0 = t * Gd.rp, nr = min(Gd.rp, a.A.n_embd - r0);
+      const uint64_t w = uni64(gptr[3 * g + 2]);
+      if (w)
+        issue_chunk(slot, Md, (const uint8_t*)(uintptr_t)(w + (uint64_t)r0 * Gd.rb), (uint32_t)(nr * Gd.rb),
+                    nullptr, 0, 0);
+      else   // a skipped group keeps the count of loads
+        issue_chunk(slot, Md, (const uint8_t*)a.P.err, 1, nullptr, 0, 0);
+    };
+    const int pred = min(NSd, nchd);
+    for (int kc = 0; kc < pred; ++kc) dissue(kc, dring + kc * Md * 1024);
+    int dissued = pred;
+
+    // (d) entries' destinations and owners (the first live entry naming a destination sums it)
+    if (tid < n) {
+      int g = 0;
+      while (g + 1 < ng && pl.gstart[g + 1] <= tid) ++g;
+      const int d = pl.edst[tid];
+      int live = pl.elive[tid] && gptr[3 * g + 2] != 0;
+      if (live && (d < 0 || d >= a.n_rows)) {
+        set_err(a.P.err, MOE_ERR_DST);
+        live = 0;
+      }
+      mdst[tid] = live ? d : -1;
+      mw[tid] = pl.ew[tid];
+    }
+    lds_barrier();
+    if (wave == 0) {   // n <= 64: one lane per entry
+      int owner = 0;
+      if (lane < n) {
+        const int d = mdst[lane];
+        owner = d >= 0;
+        for (int q = 0; q < lane && owner; ++q) owner = mdst[q] != d;
+        mown[lane] = owner;
+      }
+      const uint64_t om = __ballot(owner);
+      if (owner) {
+        const int o = __popcll(om & lt);
+        omap[lane] = o;
+        ownl[o] = lane;
+      }
+      if (lane == 0) dmisc[8] = __popcll(om);
+    }
+
+    // (e) every workgroup's q8_1 rows of h are in memory once the count reaches the grid (a wave
+    //     with no down chunks in flight polls; the wait is bounded)
+    if (tid == kPoll) {
+      int it = 0;
+      uint32_t v;
+      while ((v = __hip_atomic_load(&a.ctr[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < gridDim.x &&
+             ++it < a.spin_limit)
+        __builtin_amdgcn_s_sleep(2);
+      dmisc[9] = v >= gridDim.x;
+      if (v < gridDim.x) set_err(a.P.err, MOE_ERR_WAIT);
+    }
+    lds_barrier();
+    const bool go = uni(dmisc[9]) != 0;
+    const int nown = uni(dmisc[8]);
+
+    // (f) the waves with no down chunks read every entry's q8_1 rows of h (device scope) and the
+    //     first tile's destination rows of Y into LDS
+    const int r00 = rev * Gd.rp, nr0 = min(Gd.rp, a.A.n_embd - r00);
+    if (go && wave >= kDnWaves) {
+      const int dw = wave - kDnWaves, ndw = kGuWaves - kDnWaves;
+      const uint32_t qb = (uint32_t)(n * Ud * 16), db = (uint32_t)((n * Ud * 4 + 15) & ~15);
+      dma_span<true>((const uint8_t*)a.hq_lo, qb, (MOE_LDS uint8_t*)actd.lo, dw, ndw);
+      dma_span<true>((const uint8_t*)a.hq_hi, qb, (MOE_LDS uint8_t*)actd.hi, (dw + 3) % ndw, ndw);
+      dma_span<true>((const uint8_t*)a.hq_d, db, (MOE_LDS uint8_t*)actd.d, (dw + 6) % ndw, ndw);
+      if (ntw > 0 && wave == kDnWaves) {   // one float per lane
+        for (int p = 0; p * 64 < nown * nr0; ++p) {
+          const int l = p * 64 + lane;
+          if (l < nown * nr0) {
+            const int o = l / nr0, m = l - o * nr0;
+            const float* src = a.Y + (size_t)mdst[ownl[o]] * a.ldy + r00 + m;
+            __builtin_amdgcn_global_load_lds((const void*)src, (MOE_LDS void*)(ybuf + 64 * p), 4, 0, 0);
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(MOE_VM(0));   // these waves stream no down chunks
+    }
+    lds_barrier();
+
+    // (g) tiles: each down wave dots its groups' rows of the tile with the group's h rows; then
+    //     every destination row is summed in ascending entry order and written once
+    int kc = 0;
+    for (int kt = 0; go && kt < ntw; ++kt) {
+      const int t = rev + kt * (int)gridDim.x;
+      const int r0 = t * Gd.rp, nr = min(Gd.rp, a.A.n_embd - r0);
+      for (int q = 0; q < cpt; ++q, ++kc) {
+        const int g = wave + q * kDnWaves;
+        wait_vm((dissued - 1 - kc) * Md);
+        MOE_LDS uint8_t* slot = dring + (kc % NSd) * Md * 1024;
+        const uint64_t w = uni64(gptr[3 * g + 2]);
+        if (w) {
+          const uint32_t ra = (uint32_t)(slot - ring) + (uint32_t)((w + (uint64_t)r0 * Gd.rb) & 15);
+          const int a0 = uni(pl.gstart[g]), a1 = uni(pl.gstart[g + 1]);
+          for (int c0 = a0; c0 < a1; c0 += kSlots) {
+            const int ne = min(kSlots, a1 - c0);
+            int sidx[kSlots];
+#pragma unroll
+            for (int e = 0; e < kSlots; ++e) sidx[e] = e < ne ? c0 + e : 0;
+            dot_pass<FD>((const MOE_LDS uint32_t*)ring, ra, ra, nr, nr, Gd, tb, actd, sidx, ne,
+                         [&](int i, int e, float v) { ores[(c0 + e) * Gd.rp + i] = v; });
+          }
+        }
+        if (kc + NSd < nchd) {
+          MOE_WAIT_LGKM0;
+          dissue(kc + NSd, slot);
+          ++dissued;
+        }
+      }
+      lds_barrier();
+      for (int idx = tid; idx < n * nr; idx += kGuThreads) {
+        const int i = idx / nr, m = idx - i * nr;
+        if (!mown[i]) continue;
+        const int d = mdst[i];
+        float* y = a.Y + (size_t)d * a.ldy + r0 + m;
+        float acc = kt == 0 ? ybuf[omap[i] * nr + m] : *y;
+        for (int q = i; q < n; ++q)
+          if (mdst[q] == d) acc = acc + mw[q] * ores[q * Gd.rp + m];
+        *y = acc;
+      }
+      lds_barrier();
+    }
+    // a workgroup that gave up waiting still drains the chunks it issued
+    __builtin_amdgcn_s_waitcnt(MOE_VM(0));
+
+    // (h) the last workgroup out clears the counts for the next call
+    if (tid == 0) {
+      const uint32_t d = __hip_atomic_fetch_add(&a.ctr[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == gridDim.x - 1) {
+        __hip_atomic_store(&a.ctr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.ctr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 
@@ -1835,17 +2074,24 @@ hipError_t allow_smem(K kern, int bytes) {
   return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-hipError_t launch_gu(int fmt, int mode, const GuArgs& ga, int grid, int bytes, hipStream_t st) {
+hipError_t launch_gu(int fmt, int fmt_down, int mode, const GuArgs& ga, int grid, int bytes, hipStream_t st) {
   auto go = [&](auto kern) -> hipError_t {
     hipError_t e = allow_smem(kern, bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kGuThreads), bytes, st, ga);
     return hipGetLastError();
   };
-#define MOE_GU(F)                                              \
-  case F:                                                      \
-    return mode == GU_COMPOSED ? go(k_gate_up<F, GU_COMPOSED>) \
-           : mode == GU_FUSED  ? go(k_gate_up<F, GU_FUSED>)    \
+#define MOE_LY(F, D) \
+  case D:            \
+    return go(k_gate_up<F, GU_LAYER, D>);
+#define MOE_GU(F)                                                            \
+  case F:                                                                    \
+    if (mode == GU_LAYER) {                                                  \
+      switch (fmt_down) { MOE_LY(F, Q8_0) MOE_LY(F, NL4) MOE_LY(F, CB2) MOE_LY(F, CB3) } \
+      return hipErrorInvalidValue;                                           \
+    }                                                                        \
+    return mode == GU_COMPOSED ? go(k_gate_up<F, GU_COMPOSED>)               \
+           : mode == GU_FUSED  ? go(k_gate_up<F, GU_FUSED>)                  \
                                : go(k_gate_up<F, GU_ROUTED>);
   switch (fmt) {
     MOE_GU(Q8_0)
@@ -1854,6 +2100,7 @@ hipError_t launch_gu(int fmt, int mode, const GuArgs& ga, int grid, int bytes, h
     MOE_GU(CB3)
   }
 #undef MOE_GU
+#undef MOE_LY
   return hipErrorInvalidValue;
 }
 
@@ -1879,28 +2126,36 @@ hipError_t launch_dn(int fmt, int mode, const DnArgs& da, int grid, int bytes, h
 
 // LDS the gate/up kernel needs for n_tokens activation rows, its stream and how many of its waves
 // stream (all 16 when the slots fit, fewer for long rows), or -1 if it does not fit.
-int gu_lds(const moe_layer* L, int n_tokens, int mode, Stream* S, int* sw, int* ring, int* actb, int* tailb) {
+int gu_lds(const moe_layer* L, const moe_plan* P, int n_tokens, int mode, Stream* S, int* sw, int* ring,
+           int* actb, int* tailb, int* downb) {
   const Geom G = make_geom(L->fmt_gate_up, L->n_embd, true);
   *actb = act_bytes(n_tokens, G.U);
   if (*actb > kGuActMax) return -1;
   // the prologue uses the ring before the stream: routed, the routing waves' scratch; fused, at
-  // least one float row of x
+  // least one float row of x; layer mode, after the blocks, the down chunks of kDnWaves waves
   int lg = 0;
   *tailb = 0;
-  if (mode == GU_ROUTED) {
+  *downb = 0;
+  if (mode == GU_ROUTED || mode == GU_LAYER) {
     lg = std::min(n_tokens, kRtWaves) * route_scr_words(L->n_experts) * 4;
     *tailb = gu_tail_bytes(L->n_experts, n_tokens);
   } else if (mode == GU_FUSED) {
     lg = L->n_embd * 4;
   }
-  const int avail = kLdsMax - gu_smem_bytes(0, *actb, *tailb);
+  if (mode == GU_LAYER) {
+    const Geom Gd = make_geom(L->fmt_down, L->n_ff, false);
+    if (act_bytes_kb(P->cap_entries, Gd.U) > kDnActMax) return -1;
+    *downb = ly_down_bytes(P->cap_entries, Gd.U, Gd.rp);
+    lg = std::max(lg, kDnWaves * dn_stream(Gd, 1).M * 1024);
+  }
+  const int avail = kLdsMax - gu_smem_bytes(0, *actb, *tailb + *downb);
   for (int ns = 2; ns >= 1; --ns) {
     *S = gu_stream(G, ns);
     const int per_wave = S->NS * S->M * 1024;
     *sw = std::min(kGuWaves, avail / per_wave);
     if (*sw >= (ns == 2 ? kGuWaves : 1)) {
       *ring = std::max(*sw * per_wave, lg);
-      const int b = gu_smem_bytes(*ring, *actb, *tailb);
+      const int b = gu_smem_bytes(*ring, *actb, *tailb + *downb);
       if (b <= kLdsMax) return b;
     }
   }
@@ -1926,11 +2181,12 @@ int dn_lds(const moe_layer* L, const moe_plan* P, Stream* S, int* ring, int* act
 // The gate/up kernel of `mode`.
 int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, const void* act,
                 int n_tokens, float* g, float* u, int ld, uint8_t* ws, const float* logits, int T, int k,
-                const int32_t* dst_of_token, int entry_base, int grid_limit) {
+                const int32_t* dst_of_token, int entry_base, int grid_limit, float* Y = nullptr,
+                int n_rows = 0, int ldy = 0) {
   const Geom G = make_geom(L->fmt_gate_up, L->n_embd, true);
-  int ring = 0, actb = 0, sw = 0, tailb = 0;
+  int ring = 0, actb = 0, sw = 0, tailb = 0, downb = 0;
   Stream S{};
-  const int bytes = gu_lds(L, n_tokens, mode, &S, &sw, &ring, &actb, &tailb);
+  const int bytes = gu_lds(L, P, n_tokens, mode, &S, &sw, &ring, &actb, &tailb, &downb);
   if (bytes < 0) return MOE_E_SHAPE;
   GuArgs ga{};
   ga.A = layer_args(L);
@@ -1959,9 +2215,24 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
   ga.lds_ring = ring;
   ga.lds_act = actb;
   ga.sw = sw;
+  ga.lds_tail = tailb;
   const int items = P->cap_groups * (L->n_ff / 32);
-  const int grid = grid_for(items, bytes, grid_limit);
-  const hipError_t e = launch_gu(L->fmt_gate_up, mode, ga, grid, bytes, st);
+  int grid = grid_for(items, bytes, grid_limit);
+  if (mode == GU_LAYER) {
+    // every workgroup waits for all the others: at most what the CUs hold at once (LDS-limited)
+    const Geom Gd = make_geom(L->fmt_down, L->n_ff, false);
+    ga.Gd = Gd;
+    const int md = dn_stream(Gd, 1).M;
+    ga.Sd = dn_stream(Gd, std::max(1, std::min(3, ring / (kDnWaves * md * 1024))));
+    ga.Y = Y;
+    ga.n_rows = n_rows;
+    ga.ldy = ldy;
+    ga.ctr = (uint32_t*)(ws + kCtrOff);
+    ga.spin_limit = 1 << 22;
+    const int resident = num_cus() * std::max(1, std::min(8, kLdsMax / bytes));
+    grid = std::min(grid_limit ? grid_limit : num_cus(), resident);
+  }
+  const hipError_t e = launch_gu(L->fmt_gate_up, L->fmt_down, mode, ga, grid, bytes, st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "gate/up kernel");
 }
 
@@ -2144,6 +2415,22 @@ int moe_layer_decode(void* stream, const moe_layer* L, const moe_plan* P, const 
                                    grid_limit);
   if (rc) return rc;
   return moe_layer_down(stream, L, P, ws, ws_bytes, n_tokens, Y, n_rows, ldy, grid_limit);
+}
+
+int moe_layer_step(void* stream, const moe_layer* L, const moe_plan* P, const float* logits, int T, int k,
+                   const int32_t* dst_of_token, int entry_base, const float* x, float* Y, int n_rows, int ldy,
+                   void* ws, size_t ws_bytes, int grid_limit) {
+  int rc = check_layer(L, true);
+  if (rc) return rc;
+  if ((rc = check_plan(P))) return rc;
+  if (!logits || !x || !Y || n_rows < 0 || ldy < L->n_embd || grid_limit < 0) return MOE_E_ARG;
+  if ((uintptr_t)x & 15) return MOE_E_ARG;
+  if (T < 1 || k < 1 || k > 32 || k > L->n_experts || L->n_experts > 1024 || entry_base < 0) return MOE_E_ARG;
+  if (T * k > P->cap_entries || T * k > P->cap_groups || T * k > 64) return MOE_E_ARG;
+  const WsLayout wl = ws_layout(L, P);
+  if (!ws || ws_bytes < wl.total || ((uintptr_t)ws & 255)) return MOE_E_WS;
+  return run_gate_up((hipStream_t)stream, L, P, GU_LAYER, x, T, nullptr, nullptr, 0, (uint8_t*)ws, logits, T,
+                     k, dst_of_token, entry_base, grid_limit, Y, n_rows, ldy);
 }
 
 int moe_layer_decode_routed(void* stream, const moe_layer* L, const moe_plan* P, const float* logits,

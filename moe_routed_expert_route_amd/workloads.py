@@ -141,6 +141,16 @@ class Workload:
             self.gate_up(l, stream)
             self.down(l, stream)
 
+    def layer_step(self, l, stream=None):
+        """Layer l in one launch: route, group, q8_1(x), gate/up, SwiGLU + q8_1, down, scatter."""
+        B.moe_layer_step(self.layers[l], self.plans[l], self.d_logits[l], self.k, self.d_x[l], self.Y[l],
+                         self.ws[l], stream=stream)
+
+    def step_one_launch(self, stream=None):
+        """One pass of the whole hot path over every layer, one launch per layer."""
+        for l in range(self.L):
+            self.layer_step(l, stream)
+
     def step_separate(self, stream=None):
         """The same pass with routing and grouping as launches of their own."""
         for l in range(self.L):

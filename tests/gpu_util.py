@@ -99,17 +99,25 @@ def run_composed(c, plan, x_np, Y0_np, n_rows, grid_limit=0):
                 hq=hq.cpu().numpy(), Y=Y.cpu().numpy(), err=plan.errors())
 
 
-def run_routed(c, x_np, Y0_np, entry_base=0, dst_of_token=None, grid_limit=0, split=False):
+def run_routed(c, x_np, Y0_np, entry_base=0, dst_of_token=None, grid_limit=0, split=False, step=False,
+               ws=None, reps=1):
     """Routing, grouping and the layer step from the logits in two launches (one call, or with
-    split=True the two half-step calls); returns the plan it published and Y."""
+    split=True the two half-step calls, or with step=True the one-launch step, `reps` times on the
+    same workspace); returns the plan it published and Y."""
     d = dev()
     T, k = c.T, c.k
     plan = B.Plan(T * k, T * k, entry_capacity=entry_base + T * k, device=d)
     Y = torch.from_numpy(Y0_np.copy()).to(d)
-    ws = B.workspace(c.layer, plan, device=d)
+    if ws is None:
+        ws = B.workspace(c.layer, plan, device=d)
     dst = None if dst_of_token is None else torch.as_tensor(dst_of_token, dtype=torch.int32, device=d)
     lg, x = torch.from_numpy(c.logits).to(d), torch.from_numpy(x_np).to(d)
-    if split:
+    if step:
+        for _ in range(reps):
+            Y.copy_(torch.from_numpy(Y0_np))
+            B.moe_layer_step(c.layer, plan, lg, k, x, Y, ws, dst_of_token=dst, entry_base=entry_base,
+                             grid_limit=grid_limit)
+    elif split:
         B.moe_layer_gate_up(c.layer, plan, x, ws, logits=lg, k=k, dst_of_token=dst,
                             entry_base=entry_base, grid_limit=grid_limit)
         B.moe_layer_down(c.layer, plan, ws, T, Y, grid_limit=grid_limit)

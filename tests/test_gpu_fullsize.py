@@ -1,5 +1,8 @@
 """Full-size GPU parity: the benchmark's own workloads and launch configuration against the oracle.
 
+Both forms of the step are covered: two launches per layer, and one launch per layer (the
+workgroups meet through counts in the workspace); they must agree bit for bit.
+
 The workloads are the benchmark's (``moe_routed_expert_route_amd.workloads``): 2560 x 768 NL4
 experts, 128 per layer, top-8, T = 1; the same geometry with CB2 gate/up, NL4 down and a T = 4
 Zipf window; 2560 x 640 CB3 gate/up + Q8_0 down, 256 experts, uniform routing at T = 4. A few
@@ -114,12 +117,13 @@ def _check_layer(wl, l, Y_np, Y0_np):
     return U.check_close(Y_np, Yr, SY, f"Y layer {l}"), nflip
 
 
+@pytest.mark.parametrize("one_launch", [False, True], ids=["two_launches", "one_launch"])
 @pytest.mark.parametrize("name,T,routing", [
     ("nl4_2560x768_t1", 1, None),
     ("cb2nl4_2560x768_t4_zipf", 4, "zipf"),
     ("cb3q8_2560x640", 4, "uniform"),
 ])
-def test_fullsize_graph_step(name, T, routing):
+def test_fullsize_graph_step(name, T, routing, one_launch):
     wl = Workload(name, device="cuda", T=T, routing=routing, layers=LAYERS, key=0)
     Y0 = [np.random.default_rng([7, l]).standard_normal((wl.T, wl.n_embd)).astype(np.float32)
           for l in range(wl.L)]
@@ -128,16 +132,18 @@ def test_fullsize_graph_step(name, T, routing):
         for l in range(wl.L):
             wl.Y[l].copy_(torch.from_numpy(Y0[l]))
 
-    # eager first (as the benchmark does before capturing), then the captured step
+    # eager first (as the benchmark does before capturing), then the captured step; the one-launch
+    # step must give the two-launch step's bits
     reset()
     wl.step()
     torch.cuda.synchronize()
     eager = [wl.Y[l].cpu().numpy() for l in range(wl.L)]
+    step = wl.step_one_launch if one_launch else wl.step
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        wl.step()
+        step()
     torch.cuda.synchronize()
     worst = 0.0
     for rep in range(3):

@@ -153,6 +153,13 @@ def test_layer_stages(name):
     assert np.array_equal(U.bits(r["Y"]), U.bits(comp["Y"]))
     r2 = U.run_routed(c, c.x, Y0, entry_base=base, dst_of_token=dst, split=True)
     assert r2["err"] == 0 and np.array_equal(U.bits(r2["Y"]), U.bits(comp["Y"]))
+    # the whole step in one launch (workgroups meet through counts in the workspace), twice on one
+    # workspace: the counts are back to zero after each call
+    r3 = U.run_routed(c, c.x, Y0, entry_base=base, dst_of_token=dst, step=True, reps=2)
+    assert r3["err"] == 0
+    for key in ("n_groups", "grp_expert", "grp_start", "ent_src", "ent_dst"):
+        assert np.array_equal(np.asarray(r3["plan"][key]), np.asarray(ph[key])), key
+    assert np.array_equal(U.bits(r3["Y"]), U.bits(comp["Y"]))
 
 
 @pytest.mark.parametrize("name", ["nl4_t1", "cb2_nl4_t4_zipf"])
@@ -171,6 +178,8 @@ def test_grid_invariance(name):
         assert np.array_equal(U.bits(y2), U.bits(ref)), gl
         y3 = U.run_routed(c, c.x, Y0, grid_limit=gl)["Y"]
         assert np.array_equal(U.bits(y3), U.bits(ref)), gl
+        r4 = U.run_routed(c, c.x, Y0, grid_limit=gl, step=True)
+        assert r4["err"] == 0 and np.array_equal(U.bits(r4["Y"]), U.bits(ref)), gl
 
 
 # ------------------------------------------------------------------ edge matrix ---------------
