@@ -177,9 +177,9 @@ int moe_layer_decode_routed(void* stream, const moe_layer* L, const moe_plan* P,
  * moe_layer_decode_routed): every workgroup routes and groups, runs its gate/up blocks with SwiGLU
  * and q8_1 ("#363 ...", "What changes"), then, once every workgroup of the launch has finished its
  * blocks, the grouped down projection and the weighted scatter ("#2058 ...", "Why"; "#363 ...",
- * "Exactness"). The workgroups meet through two 32-bit counts inside the workspace: they must be
- * zero before the first call on a workspace (a zero-filled allocation), and every call leaves them
- * zero. The launch uses at most one workgroup per CU and needs all of them resident at once (the
+ * "Exactness"). The workgroups meet through device-scope counts inside the workspace: they must
+ * be zero before the first call on a workspace (a zero-filled allocation), and every call leaves
+ * them zero. The launch uses at most one workgroup per CU and needs all of them resident at once (the
  * device not shared with other work that holds CUs); a workgroup that has not seen the others
  * within a bounded wait sets MOE_ERR_WAIT and leaves its rows of Y unwritten. Calls that overlap on
  * one workspace race. Limits as moe_layer_gate_up and moe_layer_down together. */

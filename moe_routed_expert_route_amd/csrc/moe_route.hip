@@ -51,6 +51,7 @@ constexpr int kSlots = kMaxSlots;                         // entries per dot pas
 constexpr int kMaxEnt = MOE_MAX_CALL_ENTRIES;             // 64
 constexpr int kMaxGrp = MOE_MAX_GROUPS;                   // 64
 constexpr int kChunkCap = 8192;          // weight bytes per streamed chunk (target)
+constexpr int kDnTileMax = 16;           // down: most rows of Y in one tile
 constexpr int kGuActMax = 48 * 1024;     // LDS for the call's token activations (q8_1)
 constexpr int kDnActMax = 64 * 1024;     // LDS for the call's h rows (q8_1)
 constexpr int kLdsMax = 160 * 1024;      // LDS per workgroup on gfx950
@@ -106,9 +107,15 @@ constexpr int kDescLive = kDescW + kMaxEnt;   // [kMaxEnt] 1 = compute and scatt
 constexpr int kDescPtrByte = 4 * (kDescLive + kMaxEnt);   // [kMaxGrp] down pointers (u64)
 constexpr int kDescBytes = kDescPtrByte + 8 * kMaxGrp;
 constexpr int kDescReserve = 2048;            // workspace bytes reserved for it
-constexpr int kCtrOff = kDescReserve - 64;    // layer mode: two device-scope counts (zero between calls)
+// Layer mode: device-scope counts in the workspace after the descriptor (zero between calls), one
+// per kCtrLine bytes (atomics on one line are served one after another): the arrival count in two
+// levels (kCtrGroups group counts, then a top count of complete groups), then the same for done.
+constexpr int kCtrGroups = 16;
+constexpr int kCtrLine = 256;
+constexpr int kCtrOff = kDescReserve;
+constexpr int kCtrBytes = 2 * (kCtrGroups + 1) * kCtrLine;
 static_assert(kDescPtrByte % 16 == 0 && kDescBytes % 16 == 0 && kDescBytes <= kDescReserve, "desc");
-static_assert(kDescBytes <= kCtrOff && kCtrOff % 64 == 0, "counts");
+static_assert(kDescBytes <= kCtrOff && kCtrOff % kCtrLine == 0, "counts");
 
 // ------------------------------------------------------------------ small helpers -----------
 
@@ -124,6 +131,48 @@ __device__ __forceinline__ uint64_t uni64(uint64_t v) {
 
 __device__ __forceinline__ void set_err(uint32_t* err, uint32_t bit) {
   if (err) atomicOr(err, bit);
+}
+
+// Layer mode: count this workgroup into a two-level count starting at count `base` (group
+// blockIdx % kCtrGroups, then the top count of complete groups). True for the workgroup that
+// completes the top count. One thread calls it.
+__device__ __forceinline__ bool count_in(uint32_t* ctr, int base) {
+  constexpr int kW = kCtrLine / 4;
+  const int gi = (int)blockIdx.x % kCtrGroups;
+  const int ngrp = min((int)gridDim.x, kCtrGroups);
+  const uint32_t gsz = (gridDim.x - (uint32_t)gi + kCtrGroups - 1) / kCtrGroups;
+  const uint32_t c = __hip_atomic_fetch_add(ctr + (base + gi) * kW, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (c != gsz - 1) return false;
+  const uint32_t t =
+      __hip_atomic_fetch_add(ctr + (base + kCtrGroups) * kW, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return t == (uint32_t)ngrp - 1;
+}
+
+// The launch's argument block, every 64-byte line requested at once. The compiler reads the
+// fields where they are first used, and at the start of a launch each such read is a trip to
+// memory that the next one waits behind; after this they hit the scalar cache.
+template <typename Args>
+__device__ __forceinline__ void warm_args() {
+  typedef const __attribute__((address_space(4))) uint32_t* KP;
+  const KP k = (KP)__builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t s = 0u;
+#pragma unroll
+  for (int o = 0; o < (int)sizeof(Args); o += 64) s ^= k[o / 4];
+  asm volatile("" ::"s"(s));
+}
+
+// The 16-byte NL4 table with vector loads (a scalar load would hold up every later wait on the
+// scalar counter, which the argument reads also use, until it returns from memory).
+__device__ __forceinline__ void load_nl4(const int8_t* p, uint32_t t[4]) {
+  t[0] = t[1] = t[2] = t[3] = 0u;
+  if (!p) return;
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));   // an offset the compiler cannot see is uniform
+  const uint32_t* q = (const uint32_t*)(p + z);
+  t[0] = q[0];
+  t[1] = q[1];
+  t[2] = q[2];
+  t[3] = q[3];
 }
 
 // LDS written by some lanes of a wave, then read by other lanes of the same wave: a wave's LDS
@@ -160,31 +209,25 @@ __device__ __forceinline__ void wait_vm(int n) {
 // lgkmcnt(0) only: this wave's LDS reads have returned
 #define MOE_WAIT_LGKM0 __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4))
 
-// Issue exactly M 1-KB direct-to-LDS load instructions of this wave into `slot`: span a lands at
-// slot offset (a & 15) (whole aligned 16-byte chunks), span b at chunk index cb (16-byte units),
-// every other lane reloads span a's first chunk into the unused tail of the slot. Reading whole
-// aligned 16-byte chunks never leaves the pages that hold a span.
-__device__ __forceinline__ void issue_chunk(MOE_LDS uint8_t* slot, int M, const uint8_t* a, uint32_t na,
-                                            const uint8_t* b, uint32_t nb, uint32_t cb) {
-  const uint32_t lane = threadIdx.x & 63;
-  const uintptr_t a0 = (uintptr_t)a & ~(uintptr_t)15;
-  const uint32_t ca = ((uint32_t)((uintptr_t)a & 15) + na + 15) >> 4;
-  const uintptr_t b0 = (uintptr_t)b & ~(uintptr_t)15;
-  const uint32_t cbn = nb ? (((uint32_t)((uintptr_t)b & 15) + nb + 15) >> 4) : 0u;
-  for (int i = 0; i < M; ++i) {
-    const uint32_t c = (uint32_t)i * 64 + lane;
-    uintptr_t src = a0;
-    if (c < ca)
-      src = a0 + 16ull * c;
-    else if (c >= cb && c < cb + cbn)
-      src = b0 + 16ull * (c - cb);
-    __builtin_amdgcn_global_load_lds((const void*)src, (MOE_LDS void*)(slot + i * 1024), 16, 0, 0);
-  }
-}
+// Cache policy of the weight stream: non-temporal (each weight byte is read once per call), so the
+// stream does not push the launch's code, arguments and small tables out of L2.
+constexpr int kAuxStream = 2;
 
-// 16-byte chunk index where span b of a two-span chunk starts: after span a, one chunk of gap.
-__device__ __forceinline__ uint32_t span_b_chunk(uint64_t a, uint32_t na) {
-  return (((uint32_t)(a & 15) + na + 15) >> 4) + 1;
+// Issue exactly n 1-KB direct-to-LDS load instructions of this wave into `dst`: the span of na
+// bytes at `a` lands at dst offset (a & 15) as whole aligned 16-byte pieces (reading whole aligned
+// pieces never leaves the pages that hold the span); lanes past the span reload its first piece
+// into the rest of the n KB. Each instruction takes one uniform base and a 32-bit offset per lane.
+__device__ __forceinline__ void issue_span(MOE_LDS uint8_t* dst, int n, const uint8_t* a, uint32_t na) {
+  const uint32_t lane = threadIdx.x & 63;
+  // the same in every lane: scalar registers (the compiler cannot tell by itself)
+  const uint8_t* a0 = (const uint8_t*)(uintptr_t)uni64((uint64_t)(uintptr_t)a & ~15ull);
+  const uint32_t ca = (uint32_t)uni((int)((((uint32_t)(uintptr_t)a & 15u) + na + 15u) >> 4));
+  MOE_LDS uint8_t* d0 = (MOE_LDS uint8_t*)(uintptr_t)(uint32_t)uni((int)(uint32_t)(uintptr_t)dst);
+  for (int i = 0; i < n; ++i) {
+    const uint32_t c = (uint32_t)i * 64 + lane;
+    __builtin_amdgcn_global_load_lds((const void*)(a0 + (c < ca ? 16u * c : 0u)), (MOE_LDS void*)(d0 + i * 1024),
+                                     16, 0, kAuxStream);
+  }
 }
 
 // Copy `bytes` (a multiple of 16) from a 16-byte aligned global span into LDS with direct-to-LDS
@@ -615,19 +658,22 @@ __device__ __forceinline__ void issue_logits(const float* row, int E, MOE_LDS fl
 }
 __host__ __device__ inline int logits_pad(int E) { return (E + 63) & ~63; }
 
-// LDS words of one routing wave's scratch: the logits, the candidate (key, id) pairs plus two pad
-// pairs, 64 group maxima, 32 selected logits.
-__host__ __device__ inline int route_scr_words(int E) { return 3 * logits_pad(E) + 100; }
+// LDS words of one routing wave's scratch: the logits, the candidates' (key, id) pairs plus the
+// words a candidate batch may read past them, 64 group maxima, 32 selected logits.
+__host__ __device__ inline int route_scr_words(int E) { return 3 * logits_pad(E) + 32 + 64 + 32; }
 
 // Top-k (k <= min(E, 32)) of one token's logits by one wave, by (logit descending, expert id
 // ascending), then the router weights over the k chosen ("#363 ...", opening paragraph: each
-// token of the window picks its top-k experts):
+// token of the window picks its top-k experts). Lane l holds experts e = 64 j + l, j < V. The
+// steps are data-parallel over the lanes (every lane compares against values read from LDS by
+// broadcast), so the wave runs short dependent chains:
 //  1. threshold: the lanes form G groups (G a power of two, at least 2k and enough that k groups
 //     hold experts); the k-th largest of the G group maxima is a key that at least k keys reach,
 //     so every key among the top k reaches it;
 //  2. the keys that reach it are the candidates (typically a little over k); an expert's rank is
-//     the number of candidates that beat it (larger key, or equal key and lower id), which equals
-//     its rank among all E since whatever beats a candidate is a candidate;
+//     the number of candidates that beat it (larger key, or equal key and lower id: one 64-bit
+//     comparison of (key, ~id)), which equals its rank among all E since whatever beats a
+//     candidate is a candidate;
 //  3. weights in rank order: ex_j = exp(l_j - l_0), w_j = ex_j / (((ex_0 + ex_1) + ex_2) + ...).
 // scr: route_scr_words(E) words holding the logits (issue_logits into its start). Writes ids[0..k)
 // and w[0..k) in rank order and this token's selection as a bitmap bits[0..ceil(E / 32)) (bit e of
@@ -639,16 +685,19 @@ __device__ __forceinline__ void route_token_v(MOE_LDS uint32_t* scr, int E, int 
   const uint64_t lt = (1ull << lane) - 1ull;
   const int Epad = logits_pad(E);
   const MOE_LDS float* lg = (const MOE_LDS float*)scr;
-  MOE_LDS uint32_t* cand = scr + Epad;
-  MOE_LDS uint32_t* gmx = cand + 2 * Epad + 4;
-  MOE_LDS float* lsel = (MOE_LDS float*)(gmx + 64);
+  MOE_LDS uint32_t* cand = scr + Epad;          // [2 Epad + 32] candidates' (key, ~id) pairs
+  MOE_LDS uint32_t* gmx = cand + 2 * Epad + 32; // [64] group maxima
+  MOE_LDS float* lsel = (MOE_LDS float*)(gmx + 64);   // [32] chosen logits in rank order
   uint32_t key[V];
   uint32_t m = 0u;
 #pragma unroll
   for (int j = 0; j < V; ++j) {
-    key[j] = (64 * j + lane < E) ? fkey(lg[64 * j + lane]) : 0u;   // 0: no expert
+    const int e = 64 * j + lane;
+    key[j] = e < E ? fkey(lg[64 * j + lane]) : 0u;   // 0: no expert (past E the word is ignored)
     m = max(m, key[j]);
   }
+  // (key, ~id) of slot j: larger means ranked higher
+  auto K = [&](int j) { return ((uint64_t)key[j] << 32) | (uint32_t)~(uint32_t)(64 * j + lane); };
   // 1. threshold
   int G = 4;
   while (G < 64 && (G < 2 * k || E * G < 64 * k)) G <<= 1;
@@ -659,66 +708,74 @@ __device__ __forceinline__ void route_token_v(MOE_LDS uint32_t* scr, int E, int 
   if (gsz >= 16) m = max(m, dppu<0x140>(m));  // row_mirror
   if ((lane & (gsz - 1)) == 0) gmx[lane / gsz] = m;
   wave_lds_sync();
-  uint32_t thr = 0xFFFFFFFFu;
-  if (lane < G) {
-    const uint32_t mine = gmx[lane];
-    int r = 0;
-    for (int o = 0; o < G; o += 4) {
-      const u32x4 v = *(const MOE_LDS u32x4*)(gmx + o);
-      r += (int)(v.x > mine) + (int)(v.y > mine) + (int)(v.z > mine) + (int)(v.w > mine);
-    }
-    if (r < k) thr = mine;
+  // how many group maxima exceed this lane's (broadcast reads, G <= 16 or G <= 64)
+  int above = 0;
+  for (int g0 = 0; g0 < G; g0 += 16) {   // 16 maxima a batch: 4 broadcast reads, one wait
+    u32x4 v[4];
+#pragma unroll
+    for (int o = 0; o < 4; ++o) v[o] = *(const MOE_LDS u32x4*)(gmx + g0 + 4 * o);
+#pragma unroll
+    for (int o = 0; o < 4; ++o)
+      above += (g0 + 4 * o < G) ? (int)(v[o].x > m) + (int)(v[o].y > m) + (int)(v[o].z > m) + (int)(v[o].w > m) : 0;
   }
+  uint32_t thr = above < k ? m : 0xFFFFFFFFu;
   thr = min(thr, dppu<0xB1>(thr));
   thr = min(thr, dppu<0x4E>(thr));
   thr = min(thr, dppu<0x141>(thr));
   thr = min(thr, dppu<0x140>(thr));
   thr = min(min((uint32_t)__builtin_amdgcn_readlane((int)thr, 0), (uint32_t)__builtin_amdgcn_readlane((int)thr, 16)),
             min((uint32_t)__builtin_amdgcn_readlane((int)thr, 32), (uint32_t)__builtin_amdgcn_readlane((int)thr, 48)));
-  // 2. candidates, then exact ranks among them
+  // 2. candidates, packed in LDS in (j, lane) order, then each counts the candidates beating it
+  bool cnd[V];
   int C = 0;
 #pragma unroll
   for (int j = 0; j < V; ++j) {
-    const bool c = key[j] >= thr;   // thr is a real key, so key 0 never qualifies
-    const uint64_t bm = __ballot(c);
-    if (c) {
+    cnd[j] = key[j] != 0u && key[j] >= thr;
+    const uint64_t bm = __ballot(cnd[j]);
+    if (cnd[j]) {
       const int pos = C + __popcll(bm & lt);
-      cand[2 * pos] = key[j];
-      cand[2 * pos + 1] = (uint32_t)(64 * j + lane);
+      cand[2 * pos] = (uint32_t)K(j);
+      cand[2 * pos + 1] = key[j];
     }
     C += __popcll(bm);
   }
-  if (lane < 4) cand[2 * C + lane] = (lane & 1) ? 0xFFFFFFFFu : 0u;   // pad pairs: key 0 beats nothing
   wave_lds_sync();
-  for (int c0 = 0; c0 < C; c0 += 64) {
-    const int c = c0 + lane;
-    const bool live = c < C;
-    const uint32_t kc = live ? cand[2 * c] : 0u;
-    const uint32_t ic = live ? cand[2 * c + 1] : 0u;
-    int r = 0;
-    for (int o = 0; o < C; o += 2) {
-      const u32x4 v = *(const MOE_LDS u32x4*)(cand + 2 * o);
-      r += (int)((v.x > kc) | ((v.x == kc) & (v.y < ic)));
-      r += (int)((v.z > kc) | ((v.z == kc) & (v.w < ic)));
-    }
-    if (live && r < k) {
-      ids[r] = (int)ic;
-      lsel[r] = unkey(kc);
+  int r[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) r[j] = 0;
+  constexpr int kB = V <= 4 ? 8 : 2;   // candidate pairs a batch (fewer registers for wide V)
+  for (int c0 = 0; c0 < C; c0 += 2 * kB) {   // broadcast reads, one wait a batch
+    u32x4 v[kB];
+#pragma unroll
+    for (int o = 0; o < kB; ++o) v[o] = *(const MOE_LDS u32x4*)(cand + 2 * c0 + 4 * o);
+#pragma unroll
+    for (int o = 0; o < kB; ++o) {
+      const uint64_t ka = ((uint64_t)v[o].y << 32) | v[o].x, kb = ((uint64_t)v[o].w << 32) | v[o].z;
+      const bool va = c0 + 2 * o < C, vb = c0 + 2 * o + 1 < C;
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const uint64_t kj = K(j);
+        r[j] += (int)(va && ka > kj) + (int)(vb && kb > kj);
+      }
     }
   }
-  wave_lds_sync();
-  // this token's selection as a bitmap (word = lane)
+  // the chosen experts in rank order, and this token's selection as a bitmap (word = lane)
+  uint32_t bw = 0u;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const bool sel = cnd[j] && r[j] < k;
+    if (sel) {
+      ids[r[j]] = 64 * j + lane;
+      lsel[r[j]] = unkey(key[j]);
+    }
+    const uint64_t sm = __ballot(sel);
+    if ((lane >> 1) == j) bw = (lane & 1) ? (uint32_t)(sm >> 32) : (uint32_t)sm;
+  }
   const int nW = (E + 31) >> 5;
-  if (lane < nW) {
-    uint32_t bw = 0u;
-    for (int r = 0; r < k; ++r) {
-      const int e = ids[r];
-      bw |= ((e >> 5) == lane) ? (1u << (e & 31)) : 0u;
-    }
-    bits[lane] = bw;
-  }
+  if (lane < nW) bits[lane] = bw;
   // 3. weights
   if (!need_w) return;
+  wave_lds_sync();
   float ex = 0.0f;
   if (lane < k) ex = expf(lsel[lane] - lsel[0]);
   float sum = 0.0f;
@@ -930,6 +987,8 @@ struct GuArgs {
   // layer mode: the down half
   Geom Gd;              // down row geometry (rows of n_ff columns)
   Stream Sd;            // down stream: kDnWaves waves, NS slots of M KB each, in the ring
+  int trd;              // rows of Y per down tile (<= kDnTileMax)
+  int rcd;              // rows per streamed down chunk
   float* Y;
   int n_rows, ldy;
   int lds_tail;         // bytes of the routed tail (the down region follows it)
@@ -955,9 +1014,9 @@ __host__ __device__ inline int gu_smem_bytes(int lds_ring, int lds_act, int lds_
 // Layer mode, after the tail: the q8_1 rows of h (split form, KB-padded regions), the per-entry
 // outputs of a down tile, the entries' metadata and the first tile's destination rows of Y.
 constexpr int kLyMeta = 4 * (5 * kMaxEnt + 16);
-constexpr int kLyYBuf = 4 * kMaxEnt * 16;
-__host__ __device__ inline int ly_down_bytes(int cap_entries, int Ud, int rpd) {
-  return act_bytes_kb(cap_entries, Ud) + 4 * kMaxEnt * rpd + kLyMeta + kLyYBuf;
+constexpr int kLyYBuf = 4 * kMaxEnt * kDnTileMax;
+__host__ __device__ inline int ly_down_bytes(int cap_entries, int Ud) {
+  return act_bytes_kb(cap_entries, Ud) + 4 * kMaxEnt * kDnTileMax + kLyMeta + kLyYBuf;
 }
 
 // Work item = one 32-row block of h of one group (so SwiGLU and the q8_1 quantization of the block
@@ -998,33 +1057,40 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   const int nW = (a.E + 31) >> 5;
   MOE_LDS uint32_t* selT = (MOE_LDS uint32_t*)(tail + 24 * a.E);     // routed: [T][nW]
 
-  // ---- 1. every load that depends on nothing, at once
-  uint32_t t_nl4[4] = {0u, 0u, 0u, 0u};
-  if (a.A.nl4) {
-    const uint32_t* t = (const uint32_t*)a.A.nl4;
-    t_nl4[0] = t[0];
-    t_nl4[1] = t[1];
-    t_nl4[2] = t[2];
-    t_nl4[3] = t[3];
+  // ---- 1. every load that depends on nothing, at once. Routed: the routing waves (the first
+  //         kRtWaves) send their first logits rows before anything else and load nothing more
+  //         until they have routed (their wait then covers the logits alone); the other waves take
+  //         the tables, the expert pointers and the destinations.
+  warm_args<GuArgs>();
+  const bool rw = RT && wave < kRtWaves;   // a routing wave
+  const int q0 = RT ? tid - 64 * kRtWaves : tid;   // thread index among the waves that load tables
+  MOE_LDS uint32_t* rscr = (MOE_LDS uint32_t*)ring + wave * route_scr_words(a.E);
+  if constexpr (RT) {
+    if (rw) {
+      __builtin_amdgcn_s_setprio(2);   // the launch waits on the routing: it goes first on its SIMD
+      if (wave < a.T) issue_logits(a.logits + (size_t)wave * a.E, a.E, (MOE_LDS float*)rscr);
+    }
   }
+  uint32_t t_nl4[4] = {0u, 0u, 0u, 0u};
+  if (!rw) load_nl4(a.A.nl4, t_nl4);
   uint32_t t_cb = 0;
   if constexpr (FMT == CB2 || FMT == CB3) {
     const uint32_t* src = (const uint32_t*)(FMT == CB2 ? a.A.cb2 : a.A.cb3);
-    if (tid < 512) t_cb = src[tid];
+    if (q0 >= 0 && q0 < 512) t_cb = src[q0];
   }
   uint32_t t_cbd = 0;   // layer mode: the down format's grid, when it differs
   if constexpr (MODE == GU_LAYER && FD != FMT && (FD == CB2 || FD == CB3)) {
     const uint32_t* src = (const uint32_t*)(FD == CB2 ? a.A.cb2 : a.A.cb3);
-    if (tid < 512) t_cbd = src[tid];
+    if (q0 >= 0 && q0 < 512) t_cbd = src[q0];
   }
   int r_dt = 0, r_gs = 0, r_ge = 0, r_ng = 0;
-  uint64_t pg = 0, pu = 0, pd = 0;
+  uint64_t pg = 0, pu = 0, pd = 0;   // routed: expert q0's pointers (experts past kGuQThreads later)
   if constexpr (RT) {
-    if (tid < a.T) r_dt = a.dst_of_token ? a.dst_of_token[tid] : tid;
-    if (tid < a.E) {
-      pg = (uint64_t)(uintptr_t)a.A.gate[tid];
-      pu = (uint64_t)(uintptr_t)a.A.up[tid];
-      pd = (uint64_t)(uintptr_t)a.A.down[tid];
+    if (q0 >= 0 && q0 < a.T) r_dt = a.dst_of_token ? a.dst_of_token[q0] : q0;
+    if (q0 >= 0 && q0 < a.E) {
+      pg = (uint64_t)(uintptr_t)a.A.gate[q0];
+      pu = (uint64_t)(uintptr_t)a.A.up[q0];
+      pd = (uint64_t)(uintptr_t)a.A.down[q0];
     }
   } else {
     if (tid == 0) r_ng = *a.P.n_groups;
@@ -1034,15 +1100,16 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
 
   // ---- 2. routing and the activations' q8_1 blocks
   if constexpr (RT) {
-    if (wave < kRtWaves) {
-      MOE_LDS uint32_t* rscr = (MOE_LDS uint32_t*)ring + wave * route_scr_words(a.E);
+    if (rw) {
       for (int t = wave; t < a.T; t += kRtWaves) {
-        issue_logits(a.logits + (size_t)t * a.E, a.E, (MOE_LDS float*)rscr);
+        if (t != wave) issue_logits(a.logits + (size_t)t * a.E, a.E, (MOE_LDS float*)rscr);
         __builtin_amdgcn_s_waitcnt(MOE_VM(0));
         // routed: only workgroup 0 writes the plan, so only it needs the router weights
         route_token(rscr, a.E, a.k, pl.rid + t * a.k, pl.rw + t * a.k, selT + t * nW,
                     MODE == GU_LAYER || blockIdx.x == 0);
       }
+      __builtin_amdgcn_s_setprio(0);
+      load_nl4(a.A.nl4, t_nl4);
     } else {
       // two register passes cover one 4096-wide row; eight cover four (more: plain loads after)
       const int q = tid - 64 * kRtWaves, nblk = a.n_tokens * G.U;
@@ -1055,12 +1122,19 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
         if (nblk > nreg) act_rest_f<kGuQThreads>(a.x, a.A.n_embd, nreg, nblk, G.U, q, act);
       }
     }
-    if (tid < a.E) {
+    if (q0 >= 0 && q0 < a.E) {
       const bool ok = ptr_ok(pg | pu, a.P.err);
-      ptab[tid] = u64x2{ok ? pg : 0ull, ok ? pu : 0ull};
-      ptabd[tid] = ptr_ok(pd, a.P.err) ? pd : 0ull;
+      ptab[q0] = u64x2{ok ? pg : 0ull, ok ? pu : 0ull};
+      ptabd[q0] = ptr_ok(pd, a.P.err) ? pd : 0ull;
     }
-    if (tid < a.T) pl.dtok[tid] = r_dt;
+    for (int e = q0 + kGuQThreads; q0 >= 0 && e < a.E; e += kGuQThreads) {
+      const uint64_t g = (uint64_t)(uintptr_t)a.A.gate[e], u = (uint64_t)(uintptr_t)a.A.up[e];
+      const uint64_t d = (uint64_t)(uintptr_t)a.A.down[e];
+      const bool ok = ptr_ok(g | u, a.P.err);
+      ptab[e] = u64x2{ok ? g : 0ull, ok ? u : 0ull};
+      ptabd[e] = ptr_ok(d, a.P.err) ? d : 0ull;
+    }
+    if (q0 >= 0 && q0 < a.T) pl.dtok[q0] = r_dt;
   } else if constexpr (MODE == GU_COMPOSED) {
     act_stage_q<kGuThreads, kGuXPass>(a.xq, a.n_tokens * G.U, act, [](int) {});
   } else {
@@ -1110,9 +1184,9 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     }
   }
   if constexpr (FMT == CB2 || FMT == CB3)
-    if (tid < 512) (FMT == CB2 ? g2 : g3)[tid] = t_cb;
+    if (q0 >= 0 && q0 < 512) (FMT == CB2 ? g2 : g3)[q0] = t_cb;
   if constexpr (MODE == GU_LAYER && FD != FMT && (FD == CB2 || FD == CB3))
-    if (tid < 512) (FD == CB2 ? g2 : g3)[tid] = t_cbd;
+    if (q0 >= 0 && q0 < 512) (FD == CB2 ? g2 : g3)[q0] = t_cbd;
   if constexpr (!RT) {
     if (tid == 0) pl.misc[3] = r_ng;
     if (tid <= a.P.cap_groups) pl.gstart[tid] = r_gs;
@@ -1235,17 +1309,21 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     const int g = it / nb, blk = it - g * nb;
     uint64_t wg, wu;
     group_ptrs(g, wg, wu);
-    if (wg) {
+    if (wg) {   // the gate rows in the slot's first half, the up rows in its second
       const uint64_t off = (uint64_t)(blk * 32 + (wave + q * a.sw) * half) * (uint64_t)G.rb;
-      issue_chunk(slot, M, (const uint8_t*)(uintptr_t)(wg + off), nspan,
-                  (const uint8_t*)(uintptr_t)(wu + off), nspan, span_b_chunk(wg + off, nspan));
-    } else {   // a skipped group keeps the count of loads: one 16-byte chunk every lane reloads
-      issue_chunk(slot, M, (const uint8_t*)a.P.grp_start, 1, nullptr, 0, 0);
+      issue_span(slot, M / 2, (const uint8_t*)(uintptr_t)(wg + off), nspan);
+      issue_span(slot + (M / 2) * 1024, M / 2, (const uint8_t*)(uintptr_t)(wu + off), nspan);
+    } else {   // a skipped group keeps the count of loads: one 16-byte piece every lane reloads
+      issue_span(slot, M, (const uint8_t*)a.P.grp_start, 1);
     }
   };
   __builtin_amdgcn_s_waitcnt(MOE_VM(0));   // nothing of ours in flight before the stream
   const int pre = min(NS, nch);
+  // the first chunks go out ahead of the dots of waves whose chunks have already landed: a wave
+  // issuing competes for its SIMD only with those, and its loads are what the stream waits on
+  __builtin_amdgcn_s_setprio(3);
   for (int kc = 0; kc < pre; ++kc) issue(kc, myring + kc * M * 1024);
+  __builtin_amdgcn_s_setprio(0);
   int issued = pre;
 
   // ---- 5. workgroup 0 leaves the plan (routed) and the call's descriptor (fused / routed)
@@ -1327,7 +1405,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
         const uint64_t off = (uint64_t)(blk * 32 + prow) * (uint64_t)G.rb;
         const uint32_t sb = (uint32_t)(slot - ring);
         const uint32_t ra = sb + (uint32_t)((wgv + off) & 15);
-        const uint32_t rb0 = sb + 16 * span_b_chunk(wgv + off, nspan) + (uint32_t)((wuv + off) & 15);
+        const uint32_t rb0 = sb + (M / 2) * 1024 + (uint32_t)((wuv + off) & 15);
         uint64_t rest = tm;   // routed: the group's tokens not yet dotted
         for (int c0 = 0; c0 < ne; c0 += kSlots) {
           const int nc = min(kSlots, ne - c0);
@@ -1386,20 +1464,21 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     const int Ud = Gd.U;
     MOE_LDS uint8_t* dreg = tail + a.lds_tail;
     const ActSplit actd = act_layout_kb(dreg, a.P.cap_entries, Ud);
-    MOE_LDS float* ores = (MOE_LDS float*)(dreg + act_bytes_kb(a.P.cap_entries, Ud));   // [kMaxEnt][rpd]
-    MOE_LDS int* mdst = (MOE_LDS int*)(ores + kMaxEnt * Gd.rp);   // [kMaxEnt] dst or -1
+    const int tr = a.trd;
+    MOE_LDS float* ores = (MOE_LDS float*)(dreg + act_bytes_kb(a.P.cap_entries, Ud));   // [kMaxEnt][tr]
+    MOE_LDS int* mdst = (MOE_LDS int*)(ores + kMaxEnt * kDnTileMax);   // [kMaxEnt] dst or -1
     MOE_LDS int* mown = mdst + kMaxEnt;                           // first live entry of its dst
     MOE_LDS float* mw = (MOE_LDS float*)(mown + kMaxEnt);
     MOE_LDS int* omap = (MOE_LDS int*)(mw + kMaxEnt);             // owner index of an owner entry
     MOE_LDS int* ownl = omap + kMaxEnt;                           // owner entries in order
     MOE_LDS int* dmisc = ownl + kMaxEnt;                          // [16]
-    MOE_LDS float* ybuf = (MOE_LDS float*)(dmisc + 16);           // [owner][rpd] first tile's Y rows
+    MOE_LDS float* ybuf = (MOE_LDS float*)(dmisc + 16);           // [owner][tr] first tile's Y rows
     constexpr int kPoll = 64 * kDnWaves;   // a thread of a wave that streams no down chunks
 
     // (a) this workgroup's q8_1 rows of h have reached device scope: count it
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
-    if (tid == 0) __hip_atomic_fetch_add(&a.ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) count_in(a.ctr, 0);
 
     // (b) the call in LDS: per group its first entry and down pointer, per entry its destination,
     //     weight and whether it was computed
@@ -1429,26 +1508,37 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     // (c) this workgroup's down tiles (tile t goes to workgroup grid - 1 - t % grid, so the
     //     workgroups without a block take the extra tiles); waves 0..kDnWaves-1 take the groups
     //     g = w, w + kDnWaves, ...; their first chunks go out now, into the ring
-    const int ntiles = (a.A.n_embd + Gd.rp - 1) / Gd.rp;
+    const int ntiles = (a.A.n_embd + tr - 1) / tr;
     const int rev = (int)gridDim.x - 1 - (int)blockIdx.x;
     const int ntw = rev < ntiles ? (ntiles - rev + (int)gridDim.x - 1) / (int)gridDim.x : 0;
-    const int cpt = (wave < kDnWaves && wave < ng) ? (ng - wave + kDnWaves - 1) / kDnWaves : 0;
+    const int rc = a.rcd, nsub = (tr + rc - 1) / rc;   // chunk q: group w + (q / nsub) kDnWaves
+    const int cpt = ((wave < kDnWaves && wave < ng) ? (ng - wave + kDnWaves - 1) / kDnWaves : 0) * nsub;
     const int nchd = ntw * cpt;
+    auto chunk_rows = [&](int t, int sub, int& r0, int& nr) {
+      const int te = min(t * tr + tr, a.A.n_embd);
+      r0 = t * tr + sub * rc;
+      nr = min(rc, te - r0);
+    };
     const int Md = a.Sd.M, NSd = a.Sd.NS;
     MOE_LDS uint8_t* dring = ring + (wave < kDnWaves ? wave : 0) * NSd * Md * 1024;
     auto dissue = [&](int kc, MOE_LDS uint8_t* slot) {
       const int kt = kc / cpt, q = kc - kt * cpt;
-      const int t = rev + kt * (int)gridDim.x, g = wave + q * kDnWaves;
-      const int r0 = t * Gd.rp, nr = min(Gd.rp, a.A.n_embd - r0);
+      const int t = rev + kt * (int)gridDim.x, g = wave + (q / nsub) * kDnWaves;
+      int r0, nr;
+      chunk_rows(t, q % nsub, r0, nr);
       const uint64_t w = uni64(gptr[3 * g + 2]);
-      if (w)
-        issue_chunk(slot, Md, (const uint8_t*)(uintptr_t)(w + (uint64_t)r0 * Gd.rb), (uint32_t)(nr * Gd.rb),
-                    nullptr, 0, 0);
-      else   // a skipped group keeps the count of loads
-        issue_chunk(slot, Md, (const uint8_t*)a.P.err, 1, nullptr, 0, 0);
+      if (w && nr > 0)
+        issue_span(slot, Md, (const uint8_t*)(uintptr_t)(w + (uint64_t)r0 * Gd.rb), (uint32_t)(nr * Gd.rb));
+      else   // a skipped group (or rows past the end) keeps the count of loads
+        issue_span(slot, Md, (const uint8_t*)a.P.err, 1);
     };
+    // a workgroup that had blocks sends its first chunks only once the count is complete: its
+    // polls go through the same memory queue and would wait behind them; one without blocks has
+    // the whole gate/up phase to spare and sends them now
+    const bool early = true;
     const int pred = min(NSd, nchd);
-    for (int kc = 0; kc < pred; ++kc) dissue(kc, dring + kc * Md * 1024);
+    if (early)
+      for (int kc = 0; kc < pred; ++kc) dissue(kc, dring + kc * Md * 1024);
     int dissued = pred;
 
     // (d) entries' destinations and owners (the first live entry naming a destination sums it)
@@ -1485,21 +1575,24 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     // (e) every workgroup's q8_1 rows of h are in memory once the count reaches the grid (a wave
     //     with no down chunks in flight polls; the wait is bounded)
     if (tid == kPoll) {
+      const uint32_t* top = a.ctr + kCtrGroups * (kCtrLine / 4);
+      const uint32_t ngrp = min(gridDim.x, (uint32_t)kCtrGroups);
       int it = 0;
       uint32_t v;
-      while ((v = __hip_atomic_load(&a.ctr[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < gridDim.x &&
-             ++it < a.spin_limit)
-        __builtin_amdgcn_s_sleep(2);
-      dmisc[9] = v >= gridDim.x;
-      if (v < gridDim.x) set_err(a.P.err, MOE_ERR_WAIT);
+      while ((v = __hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < ngrp && ++it < a.spin_limit)
+        __builtin_amdgcn_s_sleep(1);
+      dmisc[9] = v >= ngrp;
+      if (v < ngrp) set_err(a.P.err, MOE_ERR_WAIT);
     }
     lds_barrier();
     const bool go = uni(dmisc[9]) != 0;
     const int nown = uni(dmisc[8]);
+    if (!early && go)
+      for (int kc = 0; kc < pred; ++kc) dissue(kc, dring + kc * Md * 1024);
 
     // (f) the waves with no down chunks read every entry's q8_1 rows of h (device scope) and the
     //     first tile's destination rows of Y into LDS
-    const int r00 = rev * Gd.rp, nr0 = min(Gd.rp, a.A.n_embd - r00);
+    const int r00 = rev * tr, nr0 = min(tr, a.A.n_embd - r00);
     if (go && wave >= kDnWaves) {
       const int dw = wave - kDnWaves, ndw = kGuWaves - kDnWaves;
       const uint32_t qb = (uint32_t)(n * Ud * 16), db = (uint32_t)((n * Ud * 4 + 15) & ~15);
@@ -1525,22 +1618,29 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     int kc = 0;
     for (int kt = 0; go && kt < ntw; ++kt) {
       const int t = rev + kt * (int)gridDim.x;
-      const int r0 = t * Gd.rp, nr = min(Gd.rp, a.A.n_embd - r0);
+      const int r0 = t * tr, nr = min(tr, a.A.n_embd - r0);
       for (int q = 0; q < cpt; ++q, ++kc) {
-        const int g = wave + q * kDnWaves;
+        const int g = wave + (q / nsub) * kDnWaves;
         wait_vm((dissued - 1 - kc) * Md);
         MOE_LDS uint8_t* slot = dring + (kc % NSd) * Md * 1024;
         const uint64_t w = uni64(gptr[3 * g + 2]);
-        if (w) {
-          const uint32_t ra = (uint32_t)(slot - ring) + (uint32_t)((w + (uint64_t)r0 * Gd.rb) & 15);
+        int c_r0, c_nr;
+        chunk_rows(t, q % nsub, c_r0, c_nr);
+        if (w && c_nr > 0) {
+          const uint32_t ra = (uint32_t)(slot - ring) + (uint32_t)((w + (uint64_t)c_r0 * Gd.rb) & 15);
           const int a0 = uni(pl.gstart[g]), a1 = uni(pl.gstart[g + 1]);
-          for (int c0 = a0; c0 < a1; c0 += kSlots) {
-            const int ne = min(kSlots, a1 - c0);
-            int sidx[kSlots];
+          const int o0 = c_r0 - r0;   // the chunk's first row inside the tile
+          for (int p0 = 0; p0 < c_nr; p0 += Gd.rp) {   // the chunk's rows in wave passes
+            const int np = min(Gd.rp, c_nr - p0);
+            const uint32_t rp0 = ra + (uint32_t)(p0 * Gd.rb);
+            for (int c0 = a0; c0 < a1; c0 += kSlots) {
+              const int ne = min(kSlots, a1 - c0);
+              int sidx[kSlots];
 #pragma unroll
-            for (int e = 0; e < kSlots; ++e) sidx[e] = e < ne ? c0 + e : 0;
-            dot_pass<FD>((const MOE_LDS uint32_t*)ring, ra, ra, nr, nr, Gd, tb, actd, sidx, ne,
-                         [&](int i, int e, float v) { ores[(c0 + e) * Gd.rp + i] = v; });
+              for (int e = 0; e < kSlots; ++e) sidx[e] = e < ne ? c0 + e : 0;
+              dot_pass<FD>((const MOE_LDS uint32_t*)ring, rp0, rp0, np, np, Gd, tb, actd, sidx, ne,
+                           [&](int i, int e, float v) { ores[(c0 + e) * tr + o0 + p0 + i] = v; });
+            }
           }
         }
         if (kc + NSd < nchd) {
@@ -1557,7 +1657,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
         float* y = a.Y + (size_t)d * a.ldy + r0 + m;
         float acc = kt == 0 ? ybuf[omap[i] * nr + m] : *y;
         for (int q = i; q < n; ++q)
-          if (mdst[q] == d) acc = acc + mw[q] * ores[q * Gd.rp + m];
+          if (mdst[q] == d) acc = acc + mw[q] * ores[q * tr + m];
         *y = acc;
       }
       lds_barrier();
@@ -1565,14 +1665,11 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     // a workgroup that gave up waiting still drains the chunks it issued
     __builtin_amdgcn_s_waitcnt(MOE_VM(0));
 
-    // (h) the last workgroup out clears the counts for the next call
-    if (tid == 0) {
-      const uint32_t d = __hip_atomic_fetch_add(&a.ctr[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (d == gridDim.x - 1) {
-        __hip_atomic_store(&a.ctr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.ctr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+    // (h) the last workgroup out clears the counts for the next call (every other workgroup has
+    //     made both counts by then)
+    if (tid == 0 && count_in(a.ctr, kCtrGroups + 1))
+      for (int i = 0; i < 2 * (kCtrGroups + 1); ++i)
+        __hip_atomic_store(a.ctr + i * (kCtrLine / 4), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1593,17 +1690,20 @@ struct DnArgs {
   float* Y;
   int n_rows, ldy;
   int lds_ring, lds_act;
+  int tr;               // rows of Y per tile (<= kDnTileMax)
+  int rc;               // rows per streamed chunk (a tile's rows of one group: ceil(tr / rc) chunks)
 };
 
-constexpr int kDnYBuf = kMaxEnt * 16;   // floats: the first tile's destination rows, per owner
+constexpr int kDnYBuf = kMaxEnt * kDnTileMax;   // floats: the first tile's destination rows, per owner
 constexpr int kDnFixed = 4096 + kDescBytes + 4 * 5 * kMaxEnt + 256 + 4 * kDnYBuf;
 
-__host__ __device__ inline int dn_smem_bytes(int lds_ring, int lds_act, int rp) {
-  return lds_ring + lds_act + kMaxEnt * rp * 4 + kDnFixed;
+__host__ __device__ inline int dn_smem_bytes(int lds_ring, int lds_act) {
+  return lds_ring + lds_act + kMaxEnt * kDnTileMax * 4 + kDnFixed;
 }
 
-// One work item: rows [rp t, rp t + rp) of Y. Wave w takes the groups g = w, w + 8, ... in
-// order; a chunk is a group's down rows of the tile. Per-entry rows of o stay in LDS; at the end
+// One work item: rows [tr t, tr t + tr) of Y (tr is chosen so that the tiles spread evenly over
+// the CUs). Wave w takes the groups g = w, w + 8, ... in order; a chunk is a group's down rows of
+// the tile, dotted in wave passes of rp rows. Per-entry rows of o stay in LDS; at the end
 // every destination row is summed in ascending entry order: Y[d][r] = ((Y[d][r] + w_a o_a[r]) +
 // w_b o_b[r]) + ...
 template <int FMT, int MODE>
@@ -1614,8 +1714,9 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   MOE_LDS uint8_t* ring = (MOE_LDS uint8_t*)smem;
   const int U = G.U;
   MOE_LDS uint8_t* actp = ring + a.lds_ring;
-  MOE_LDS float* ores = (MOE_LDS float*)(actp + a.lds_act);   // [kMaxEnt][rp]
-  MOE_LDS uint32_t* g2 = (MOE_LDS uint32_t*)(ores + kMaxEnt * G.rp);
+  const int tr = a.tr;
+  MOE_LDS float* ores = (MOE_LDS float*)(actp + a.lds_act);   // [kMaxEnt][tr]
+  MOE_LDS uint32_t* g2 = (MOE_LDS uint32_t*)(ores + kMaxEnt * kDnTileMax);
   MOE_LDS uint32_t* g3 = g2 + 512;
   MOE_LDS int* dsc = (MOE_LDS int*)(g3 + 512);                 // the descriptor, as in memory
   MOE_LDS uint64_t* dptr = (MOE_LDS uint64_t*)((MOE_LDS uint8_t*)dsc + kDescPtrByte);
@@ -1625,17 +1726,12 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   MOE_LDS int* omap = (MOE_LDS int*)(mw + kMaxEnt);          // [kMaxEnt] owner index of an owner entry
   MOE_LDS int* ownl = omap + kMaxEnt;                        // [kMaxEnt] owner entries in order
   MOE_LDS int* misc = ownl + kMaxEnt;                        // [64]
-  MOE_LDS float* ybuf = (MOE_LDS float*)(misc + 64);         // [owner][rp] first tile's Y rows
+  MOE_LDS float* ybuf = (MOE_LDS float*)(misc + 64);         // [owner][tr] first tile's Y rows
 
   // ---- 1. tables and the call (descriptor: one read; caller's plan: validated, two reads)
-  uint32_t t_nl4[4] = {0u, 0u, 0u, 0u};
-  if (a.A.nl4) {
-    const uint32_t* t = (const uint32_t*)a.A.nl4;
-    t_nl4[0] = t[0];
-    t_nl4[1] = t[1];
-    t_nl4[2] = t[2];
-    t_nl4[3] = t[3];
-  }
+  warm_args<DnArgs>();
+  uint32_t t_nl4[4];
+  load_nl4(a.A.nl4, t_nl4);
   uint32_t t_cb = 0;
   if constexpr (FMT == CB2 || FMT == CB3) {
     const uint32_t* src = (const uint32_t*)(FMT == CB2 ? a.A.cb2 : a.A.cb3);
@@ -1699,22 +1795,29 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   const int ng = uni(dsc[kDescNg]), e0 = uni(dsc[kDescE0]), n = uni(dsc[kDescN]);
   if (ng == 0) return;
   const ActSplit act = MODE == DN_DESC ? act_layout_kb(actp, n, U) : act_layout(actp, n, U);
-  const int ntiles = (a.A.n_embd + G.rp - 1) / G.rp;
+  const int ntiles = (a.A.n_embd + tr - 1) / tr;
   const int ntw = (int)blockIdx.x < ntiles ? (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
-  const int cpt = wave < ng ? (ng - wave + kDnWaves - 1) / kDnWaves : 0;   // this wave's groups
+  // chunk q of a tile: group wave + (q / nsub) kDnWaves, rows [sub rc, sub rc + rc) of the tile
+  const int rc = a.rc, nsub = (tr + rc - 1) / rc;
+  const int cpt = (wave < ng ? (ng - wave + kDnWaves - 1) / kDnWaves : 0) * nsub;   // per tile
   const int nch = ntw * cpt;
   const int M = a.S.M, NS = a.S.NS;
   MOE_LDS uint8_t* myring = ring + wave * NS * M * 1024;
+  auto chunk_rows = [&](int t, int sub, int& r0, int& nr) {
+    const int te = min(t * tr + tr, a.A.n_embd);
+    r0 = t * tr + sub * rc;
+    nr = min(rc, te - r0);
+  };
   auto issue = [&](int kc, MOE_LDS uint8_t* slot) {
     const int kt = kc / cpt, q = kc - kt * cpt;
-    const int t = (int)blockIdx.x + kt * (int)gridDim.x, g = wave + q * kDnWaves;
-    const int r0 = t * G.rp, nr = min(G.rp, a.A.n_embd - r0);
+    const int t = (int)blockIdx.x + kt * (int)gridDim.x, g = wave + (q / nsub) * kDnWaves;
+    int r0, nr;
+    chunk_rows(t, q % nsub, r0, nr);
     const uint64_t w = uni64(dptr[g]);
-    if (w)
-      issue_chunk(slot, M, (const uint8_t*)(uintptr_t)(w + (uint64_t)r0 * G.rb), (uint32_t)(nr * G.rb),
-                  nullptr, 0, 0);
-    else   // a skipped group keeps the count of loads: one 16-byte chunk every lane reloads
-      issue_chunk(slot, M, (const uint8_t*)a.P.err, 1, nullptr, 0, 0);
+    if (w && nr > 0)
+      issue_span(slot, M, (const uint8_t*)(uintptr_t)(w + (uint64_t)r0 * G.rb), (uint32_t)(nr * G.rb));
+    else   // a skipped group (or rows past the end) keeps the count of loads: one 16-byte chunk
+      issue_span(slot, M, (const uint8_t*)a.P.err, 1);
   };
   const int pre = min(NS, nch);
   // ---- 2. descriptor path: the h rows and the first chunks of the stream go out at once; the
@@ -1761,7 +1864,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   const int nown = uni(misc[8]);
 
   // the first tile's rows of every destination (wave 0, one float per lane): ny loads
-  const int r00 = (int)blockIdx.x * G.rp, nr0 = min(G.rp, a.A.n_embd - r00);   // first tile
+  const int r00 = (int)blockIdx.x * tr, nr0 = min(tr, a.A.n_embd - r00);   // first tile
   auto stage_y = [&]() {
     int ny = 0;
     if (wave == 0 && ntw > 0) {
@@ -1796,22 +1899,29 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   int kc = 0;
   for (int kt = 0; kt < ntw; ++kt) {
     const int t = (int)blockIdx.x + kt * (int)gridDim.x;
-    const int r0 = t * G.rp, nr = min(G.rp, a.A.n_embd - r0);
+    const int r0 = t * tr, nr = min(tr, a.A.n_embd - r0);
     for (int q = 0; q < cpt; ++q, ++kc) {
-      const int g = wave + q * kDnWaves;
+      const int g = wave + (q / nsub) * kDnWaves;
       wait_vm((issued - 1 - kc) * M + (kc < pre ? ny : 0));
       MOE_LDS uint8_t* slot = myring + (kc % NS) * M * 1024;
       const uint64_t w = uni64(dptr[g]);
-      if (w) {
-        const uint32_t ra = (uint32_t)(slot - ring) + (uint32_t)((w + (uint64_t)r0 * G.rb) & 15);
+      int c_r0, c_nr;
+      chunk_rows(t, q % nsub, c_r0, c_nr);
+      if (w && c_nr > 0) {
+        const uint32_t ra = (uint32_t)(slot - ring) + (uint32_t)((w + (uint64_t)c_r0 * G.rb) & 15);
         const int a0 = uni(dsc[kDescGs + g]), a1 = uni(dsc[kDescGs + g + 1]);
-        for (int c0 = a0; c0 < a1; c0 += kSlots) {
-          const int ne = min(kSlots, a1 - c0);
-          int sidx[kSlots];
+        const int o0 = c_r0 - r0;   // the chunk's first row inside the tile
+        for (int p0 = 0; p0 < c_nr; p0 += G.rp) {   // the chunk's rows in wave passes
+          const int np = min(G.rp, c_nr - p0);
+          const uint32_t rp0 = ra + (uint32_t)(p0 * G.rb);
+          for (int c0 = a0; c0 < a1; c0 += kSlots) {
+            const int ne = min(kSlots, a1 - c0);
+            int sidx[kSlots];
 #pragma unroll
-          for (int e = 0; e < kSlots; ++e) sidx[e] = e < ne ? c0 + e : 0;
-          dot_pass<FMT>((const MOE_LDS uint32_t*)ring, ra, ra, nr, nr, G, tb, act, sidx, ne,
-                        [&](int i, int e, float v) { ores[(c0 + e) * G.rp + i] = v; });
+            for (int e = 0; e < kSlots; ++e) sidx[e] = e < ne ? c0 + e : 0;
+            dot_pass<FMT>((const MOE_LDS uint32_t*)ring, rp0, rp0, np, np, G, tb, act, sidx, ne,
+                          [&](int i, int e, float v) { ores[(c0 + e) * tr + o0 + p0 + i] = v; });
+          }
         }
       }
       if (kc + NS < nch) {
@@ -1830,7 +1940,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
       float* y = a.Y + (size_t)d * a.ldy + r0 + m;
       float acc = kt == 0 ? ybuf[omap[i] * nr + m] : *y;
       for (int q = i; q < n; ++q)
-        if (mdst[q] == d) acc = acc + mw[q] * ores[q * G.rp + m];
+        if (mdst[q] == d) acc = acc + mw[q] * ores[q * tr + m];
       *y = acc;
     }
     lds_barrier();
@@ -1866,7 +1976,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
 // One wave per token.
 __global__ __launch_bounds__(64) void k_route(const float* __restrict__ logits, int E, int k,
                                               int32_t* __restrict__ ids, float* __restrict__ w) {
-  __shared__ __align__(16) uint32_t s_scr[3 * 1024 + 100];
+  __shared__ __align__(16) uint32_t s_scr[3 * 1024 + 128];   // route_scr_words(kMaxE)
   __shared__ int s_ids[32];
   __shared__ float s_w[32];
   __shared__ uint32_t s_bits[32];
@@ -1980,20 +2090,28 @@ Geom make_geom(int fmt, int ncols, bool gate_up) {
   return G;
 }
 
-// Slot size in KB: the chunk plus alignment slack (each span's head offset and 16-byte tail, the
-// 16-byte gap between spans, and the dwords past the end an unaligned read may touch). Two slots
+// Slot size in KB: each span (gate rows, then up rows, each in whole KB) plus alignment slack (its
+// head offset and 16-byte tail, and the dwords past the end an unaligned read may touch). Two slots
 // per wave (the next item streams in while this one computes) where LDS allows, else one.
 Stream gu_stream(const Geom& G, int ns) {
   Stream S;
-  S.M = (G.rp * G.rb + 96 + 1023) / 1024;
+  S.M = 2 * (((G.rp / 2) * G.rb + 48 + 1023) / 1024);
   S.NS = ns;
   return S;
 }
-Stream dn_stream(const Geom& G, int ns) {
+Stream dn_stream(const Geom& G, int rc, int ns) {
   Stream S;
-  S.M = (G.rp * G.rb + 48 + 1023) / 1024;
+  S.M = (rc * G.rb + 48 + 1023) / 1024;
   S.NS = ns;
   return S;
+}
+
+// Down tiling: tr rows of Y per tile, the rows spread evenly over `grid` workgroups (at most
+// kDnTileMax; a workgroup then takes several tiles), streamed in chunks of rc rows of one group
+// (within kChunkCap bytes where a whole wave pass allows).
+void dn_tiling(const Geom& G, int n_embd, int grid, int& tr, int& rc) {
+  tr = std::min(kDnTileMax, std::max(1, (n_embd + grid - 1) / std::max(grid, 1)));
+  rc = std::min(tr, std::max(G.rp, kChunkCap / G.rb / G.rp * G.rp));
 }
 
 struct WsLayout {
@@ -2007,7 +2125,7 @@ size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 WsLayout ws_layout(const moe_layer* L, const moe_plan* P) {
   WsLayout w{};
   const size_t blocks = (size_t)P->cap_entries * (L->n_ff / 32);
-  w.lo = kDescReserve;
+  w.lo = kDescReserve + kCtrBytes;
   w.hi = w.lo + al256(blocks * 16);
   w.d = w.hi + al256(blocks * 16);
   w.total = w.d + al256(blocks * 4);
@@ -2145,8 +2263,10 @@ int gu_lds(const moe_layer* L, const moe_plan* P, int n_tokens, int mode, Stream
   if (mode == GU_LAYER) {
     const Geom Gd = make_geom(L->fmt_down, L->n_ff, false);
     if (act_bytes_kb(P->cap_entries, Gd.U) > kDnActMax) return -1;
-    *downb = ly_down_bytes(P->cap_entries, Gd.U, Gd.rp);
-    lg = std::max(lg, kDnWaves * dn_stream(Gd, 1).M * 1024);
+    *downb = ly_down_bytes(P->cap_entries, Gd.U);
+    int tr, rc;
+    dn_tiling(Gd, L->n_embd, num_cus(), tr, rc);
+    lg = std::max(lg, kDnWaves * dn_stream(Gd, rc, 1).M * 1024);
   }
   const int avail = kLdsMax - gu_smem_bytes(0, *actb, *tailb + *downb);
   for (int ns = 2; ns >= 1; --ns) {
@@ -2162,18 +2282,16 @@ int gu_lds(const moe_layer* L, const moe_plan* P, int n_tokens, int mode, Stream
   return -1;
 }
 
-int dn_lds(const moe_layer* L, const moe_plan* P, Stream* S, int* ring, int* actb) {
+// LDS of the down kernel for chunks of rc rows: two slots per wave where they fit, else one.
+int dn_lds(const moe_layer* L, const moe_plan* P, int rc, Stream* S, int* ring, int* actb) {
   const Geom G = make_geom(L->fmt_down, L->n_ff, false);
   *actb = act_bytes_kb(P->cap_entries, G.U);
   if (*actb > kDnActMax) return -1;
-  const int tiles = (L->n_embd + G.rp - 1) / G.rp;
-  // two slots per wave only while every tile still gets a workgroup of its own at once
   for (int ns = 2; ns >= 1; --ns) {
-    *S = dn_stream(G, ns);
+    *S = dn_stream(G, rc, ns);
     *ring = kDnWaves * S->NS * S->M * 1024;
-    const int b = dn_smem_bytes(*ring, *actb, G.rp);
-    if (b > kLdsMax) continue;
-    if (ns == 1 || (kLdsMax / b) * num_cus() >= tiles) return b;
+    const int b = dn_smem_bytes(*ring, *actb);
+    if (b <= kLdsMax) return b;
   }
   return -1;
 }
@@ -2222,15 +2340,17 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
     // every workgroup waits for all the others: at most what the CUs hold at once (LDS-limited)
     const Geom Gd = make_geom(L->fmt_down, L->n_ff, false);
     ga.Gd = Gd;
-    const int md = dn_stream(Gd, 1).M;
-    ga.Sd = dn_stream(Gd, std::max(1, std::min(3, ring / (kDnWaves * md * 1024))));
+    const int resident = num_cus() * std::max(1, std::min(8, kLdsMax / bytes));
+    grid = std::min(grid_limit ? grid_limit : num_cus(), resident);
+    // one down tile per CU (a smaller grid takes several each)
+    dn_tiling(Gd, L->n_embd, num_cus(), ga.trd, ga.rcd);
+    const int md = dn_stream(Gd, ga.rcd, 1).M;
+    ga.Sd = dn_stream(Gd, ga.rcd, std::max(1, std::min(3, ring / (kDnWaves * md * 1024))));
     ga.Y = Y;
     ga.n_rows = n_rows;
     ga.ldy = ldy;
     ga.ctr = (uint32_t*)(ws + kCtrOff);
     ga.spin_limit = 1 << 22;
-    const int resident = num_cus() * std::max(1, std::min(8, kLdsMax / bytes));
-    grid = std::min(grid_limit ? grid_limit : num_cus(), resident);
   }
   const hipError_t e = launch_gu(L->fmt_gate_up, L->fmt_down, mode, ga, grid, bytes, st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "gate/up kernel");
@@ -2239,9 +2359,12 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
 int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, const uint8_t* ws,
              const uint8_t* hq, float* Y, int n_rows, int ldy, int grid_limit) {
   const Geom G = make_geom(L->fmt_down, L->n_ff, false);
+  // one tile per CU: every CU streams the same share of the down rows
+  int tr, rc;
+  dn_tiling(G, L->n_embd, num_cus(), tr, rc);
   int ring = 0, actb = 0;
   Stream S{};
-  const int bytes = dn_lds(L, P, &S, &ring, &actb);
+  const int bytes = dn_lds(L, P, rc, &S, &ring, &actb);
   if (bytes < 0) return MOE_E_SHAPE;
   DnArgs da{};
   da.A = layer_args(L);
@@ -2261,7 +2384,9 @@ int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, co
   da.ldy = ldy;
   da.lds_ring = ring;
   da.lds_act = actb;
-  const int tiles = (L->n_embd + G.rp - 1) / G.rp;
+  da.tr = tr;
+  da.rc = rc;
+  const int tiles = (L->n_embd + tr - 1) / tr;
   const int grid = grid_for(tiles, bytes, grid_limit);
   const hipError_t e = launch_dn(L->fmt_down, mode, da, grid, bytes, st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "down kernel");
