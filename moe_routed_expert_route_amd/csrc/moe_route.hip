@@ -209,6 +209,11 @@ __device__ __forceinline__ void wait_vm(int n) {
 // lgkmcnt(0) only: this wave's LDS reads have returned
 #define MOE_WAIT_LGKM0 __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4))
 
+// Ring slot of chunk kc for ns slots per wave (one or two slots: no division).
+__device__ __forceinline__ int slot_of(int kc, int ns) {
+  return ns == 1 ? 0 : ns == 2 ? (kc & 1) : kc % ns;
+}
+
 // Cache policy of the weight stream: non-temporal (each weight byte is read once per call), so the
 // stream does not push the launch's code, arguments and small tables out of L2.
 constexpr int kAuxStream = 2;
@@ -563,6 +568,31 @@ __device__ __forceinline__ void dot_pass(const MOE_LDS uint32_t* W, uint32_t ra,
 template <int CTRL>
 __device__ __forceinline__ uint32_t dppu(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// ------------------------------------------------------------------ weighted scatter --------
+
+// Row m of destination d, summed by its owner entry i: acc (the row's value in Y) plus w_q o_q[m]
+// for the entries q >= i that name d, in ascending q ("#2058 ...", "Why": the down outputs of a
+// token's experts are weighted by its router weights and added up). The LDS reads go out eight
+// entries at a time, one wait per batch; the additions keep their order.
+__device__ __forceinline__ float dst_sum(float acc, int i, int n, int d, int m, int tr, const MOE_LDS int* mdst,
+                                         const MOE_LDS float* mw, const MOE_LDS float* ores) {
+  for (int q0 = i; q0 < n; q0 += 8) {
+    int dd[8];
+    float ww[8], oo[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = min(q0 + j, n - 1);
+      dd[j] = mdst[q];
+      ww[j] = mw[q];
+      oo[j] = ores[q * tr + m];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (q0 + j < n && dd[j] == d) acc = acc + ww[j] * oo[j];
+  }
+  return acc;
 }
 
 // ------------------------------------------------------------------ SwiGLU + q8_1 -----------
@@ -1303,10 +1333,29 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   const int M = a.S.M, NS = a.S.NS;
   MOE_LDS uint8_t* myring = ring + wave * NS * M * 1024;
   const uint32_t nspan = (uint32_t)(half * G.rb);
-  auto issue = [&](int kc, MOE_LDS uint8_t* slot) {
-    const int kk = kc / cw, q = kc - kk * cw;
-    const int it = (int)blockIdx.x + kk * (int)gridDim.x;
-    const int g = it / nb, blk = it - g * nb;
+  // a chunk's place: pass q of item kk, the item's group g and block blk (item bid + kk * grid),
+  // stepped forward one chunk at a time (no division per chunk)
+  struct Pos {
+    int q, g, blk;
+  };
+  const int gstep = (int)gridDim.x / nb, bstep = (int)gridDim.x - gstep * nb;
+  const Pos first{0, (int)blockIdx.x / nb, (int)blockIdx.x % nb};
+  auto next_item = [&](Pos& p) {
+    p.q = 0;
+    p.g += gstep;
+    p.blk += bstep;
+    if (p.blk >= nb) {
+      p.blk -= nb;
+      ++p.g;
+    }
+  };
+  auto step = [&](Pos& p) {
+    if (++p.q >= cw) next_item(p);
+  };
+  Pos ip = first;   // the next chunk to issue
+  auto issue = [&](MOE_LDS uint8_t* slot) {
+    const int q = ip.q, g = ip.g, blk = ip.blk;
+    step(ip);
     uint64_t wg, wu;
     group_ptrs(g, wg, wu);
     if (wg) {   // the gate rows in the slot's first half, the up rows in its second
@@ -1322,7 +1371,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   // the first chunks go out ahead of the dots of waves whose chunks have already landed: a wave
   // issuing competes for its SIMD only with those, and its loads are what the stream waits on
   __builtin_amdgcn_s_setprio(3);
-  for (int kc = 0; kc < pre; ++kc) issue(kc, myring + kc * M * 1024);
+  for (int kc = 0; kc < pre; ++kc) issue(myring + kc * M * 1024);
   __builtin_amdgcn_s_setprio(0);
   int issued = pre;
 
@@ -1382,9 +1431,10 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   }
 
   int kc = 0;
+  Pos cp = first;   // the item being computed
   for (int kk = 0; kk < nit; ++kk) {
-    const int it = (int)blockIdx.x + kk * (int)gridDim.x;
-    const int g = it / nb, blk = it - g * nb;
+    const int g = cp.g, blk = cp.blk;
+    next_item(cp);
     uint64_t wgv, wuv;
     group_ptrs(g, wgv, wuv);
     int a0 = 0, ne = 0;
@@ -1399,7 +1449,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     }
     for (int q = 0; q < cw; ++q, ++kc) {
       wait_vm((issued - 1 - kc) * M);
-      MOE_LDS uint8_t* slot = myring + (kc % NS) * M * 1024;
+      MOE_LDS uint8_t* slot = myring + slot_of(kc, NS) * M * 1024;
       if (wgv) {
         const int prow = (wave + q * a.sw) * half;   // first h row of the pass inside the block
         const uint64_t off = (uint64_t)(blk * 32 + prow) * (uint64_t)G.rb;
@@ -1429,7 +1479,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
       }
       if (kc + NS < nch) {
         MOE_WAIT_LGKM0;   // this wave's LDS reads of the slot have returned
-        issue(kc + NS, slot);
+        issue(slot);
         ++issued;
       }
     }
@@ -1511,9 +1561,10 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     const int ntiles = (a.A.n_embd + tr - 1) / tr;
     const int rev = (int)gridDim.x - 1 - (int)blockIdx.x;
     const int ntw = rev < ntiles ? (ntiles - rev + (int)gridDim.x - 1) / (int)gridDim.x : 0;
-    const int rc = a.rcd, nsub = (tr + rc - 1) / rc;   // chunk q: group w + (q / nsub) kDnWaves
-    const int cpt = ((wave < kDnWaves && wave < ng) ? (ng - wave + kDnWaves - 1) / kDnWaves : 0) * nsub;
-    const int nchd = ntw * cpt;
+    // per tile its groups g = wave + q kDnWaves, per group the tile's rows in nsub chunks of rc rows
+    const int rc = a.rcd, nsub = (tr + rc - 1) / rc;
+    const int qpt = (wave < kDnWaves && wave < ng) ? (ng - wave + kDnWaves - 1) / kDnWaves : 0;
+    const int nchd = ntw * qpt * nsub;
     auto chunk_rows = [&](int t, int sub, int& r0, int& nr) {
       const int te = min(t * tr + tr, a.A.n_embd);
       r0 = t * tr + sub * rc;
@@ -1521,11 +1572,22 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     };
     const int Md = a.Sd.M, NSd = a.Sd.NS;
     MOE_LDS uint8_t* dring = ring + (wave < kDnWaves ? wave : 0) * NSd * Md * 1024;
-    auto dissue = [&](int kc, MOE_LDS uint8_t* slot) {
-      const int kt = kc / cpt, q = kc - kt * cpt;
-      const int t = rev + kt * (int)gridDim.x, g = wave + (q / nsub) * kDnWaves;
+    struct Pos {
+      int t, q, s;
+    };
+    Pos ip{rev, 0, 0};   // the next chunk to issue, stepped one chunk at a time
+    auto dissue = [&](MOE_LDS uint8_t* slot) {
+      const Pos p = ip;
+      if (++ip.s == nsub) {
+        ip.s = 0;
+        if (++ip.q == qpt) {
+          ip.q = 0;
+          ip.t += (int)gridDim.x;
+        }
+      }
+      const int g = wave + p.q * kDnWaves;
       int r0, nr;
-      chunk_rows(t, q % nsub, r0, nr);
+      chunk_rows(p.t, p.s, r0, nr);
       const uint64_t w = uni64(gptr[3 * g + 2]);
       if (w && nr > 0)
         issue_span(slot, Md, (const uint8_t*)(uintptr_t)(w + (uint64_t)r0 * Gd.rb), (uint32_t)(nr * Gd.rb));
@@ -1538,7 +1600,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     const bool early = true;
     const int pred = min(NSd, nchd);
     if (early)
-      for (int kc = 0; kc < pred; ++kc) dissue(kc, dring + kc * Md * 1024);
+      for (int kc = 0; kc < pred; ++kc) dissue(dring + kc * Md * 1024);
     int dissued = pred;
 
     // (d) entries' destinations and owners (the first live entry naming a destination sums it)
@@ -1588,7 +1650,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     const bool go = uni(dmisc[9]) != 0;
     const int nown = uni(dmisc[8]);
     if (!early && go)
-      for (int kc = 0; kc < pred; ++kc) dissue(kc, dring + kc * Md * 1024);
+      for (int kc = 0; kc < pred; ++kc) dissue(dring + kc * Md * 1024);
 
     // (f) the waves with no down chunks read every entry's q8_1 rows of h (device scope) and the
     //     first tile's destination rows of Y into LDS
@@ -1619,13 +1681,13 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     for (int kt = 0; go && kt < ntw; ++kt) {
       const int t = rev + kt * (int)gridDim.x;
       const int r0 = t * tr, nr = min(tr, a.A.n_embd - r0);
-      for (int q = 0; q < cpt; ++q, ++kc) {
-        const int g = wave + (q / nsub) * kDnWaves;
+      for (int q = 0, sb = 0; q < qpt; ++kc, sb = sb + 1 < nsub ? sb + 1 : 0, q += sb == 0) {
+        const int g = wave + q * kDnWaves;
         wait_vm((dissued - 1 - kc) * Md);
-        MOE_LDS uint8_t* slot = dring + (kc % NSd) * Md * 1024;
+        MOE_LDS uint8_t* slot = dring + slot_of(kc, NSd) * Md * 1024;
         const uint64_t w = uni64(gptr[3 * g + 2]);
         int c_r0, c_nr;
-        chunk_rows(t, q % nsub, c_r0, c_nr);
+        chunk_rows(t, sb, c_r0, c_nr);
         if (w && c_nr > 0) {
           const uint32_t ra = (uint32_t)(slot - ring) + (uint32_t)((w + (uint64_t)c_r0 * Gd.rb) & 15);
           const int a0 = uni(pl.gstart[g]), a1 = uni(pl.gstart[g + 1]);
@@ -1645,7 +1707,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
         }
         if (kc + NSd < nchd) {
           MOE_WAIT_LGKM0;
-          dissue(kc + NSd, slot);
+          dissue(slot);
           ++dissued;
         }
       }
@@ -1656,9 +1718,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
         const int d = mdst[i];
         float* y = a.Y + (size_t)d * a.ldy + r0 + m;
         float acc = kt == 0 ? ybuf[omap[i] * nr + m] : *y;
-        for (int q = i; q < n; ++q)
-          if (mdst[q] == d) acc = acc + mw[q] * ores[q * tr + m];
-        *y = acc;
+        *y = dst_sum(acc, i, n, d, m, tr, mdst, mw, ores);
       }
       lds_barrier();
     }
@@ -1797,10 +1857,11 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   const ActSplit act = MODE == DN_DESC ? act_layout_kb(actp, n, U) : act_layout(actp, n, U);
   const int ntiles = (a.A.n_embd + tr - 1) / tr;
   const int ntw = (int)blockIdx.x < ntiles ? (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
-  // chunk q of a tile: group wave + (q / nsub) kDnWaves, rows [sub rc, sub rc + rc) of the tile
+  // this wave's chunks, in order: per tile (t = bid + kt grid) its groups g = wave + q kDnWaves,
+  // per group the tile's rows in nsub chunks of rc rows
   const int rc = a.rc, nsub = (tr + rc - 1) / rc;
-  const int cpt = (wave < ng ? (ng - wave + kDnWaves - 1) / kDnWaves : 0) * nsub;   // per tile
-  const int nch = ntw * cpt;
+  const int qpt = wave < ng ? (ng - wave + kDnWaves - 1) / kDnWaves : 0;   // groups per tile
+  const int nch = ntw * qpt * nsub;
   const int M = a.S.M, NS = a.S.NS;
   MOE_LDS uint8_t* myring = ring + wave * NS * M * 1024;
   auto chunk_rows = [&](int t, int sub, int& r0, int& nr) {
@@ -1808,11 +1869,22 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
     r0 = t * tr + sub * rc;
     nr = min(rc, te - r0);
   };
-  auto issue = [&](int kc, MOE_LDS uint8_t* slot) {
-    const int kt = kc / cpt, q = kc - kt * cpt;
-    const int t = (int)blockIdx.x + kt * (int)gridDim.x, g = wave + (q / nsub) * kDnWaves;
+  struct Pos {
+    int t, q, s;
+  };
+  Pos ip{(int)blockIdx.x, 0, 0};   // the next chunk to issue, stepped one chunk at a time
+  auto issue = [&](MOE_LDS uint8_t* slot) {
+    const Pos p = ip;
+    if (++ip.s == nsub) {
+      ip.s = 0;
+      if (++ip.q == qpt) {
+        ip.q = 0;
+        ip.t += (int)gridDim.x;
+      }
+    }
+    const int g = wave + p.q * kDnWaves;
     int r0, nr;
-    chunk_rows(t, q % nsub, r0, nr);
+    chunk_rows(p.t, p.s, r0, nr);
     const uint64_t w = uni64(dptr[g]);
     if (w && nr > 0)
       issue_span(slot, M, (const uint8_t*)(uintptr_t)(w + (uint64_t)r0 * G.rb), (uint32_t)(nr * G.rb));
@@ -1827,7 +1899,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
     dma_span(a.hq_lo, qb, (MOE_LDS uint8_t*)act.lo, wave, kDnWaves);
     dma_span(a.hq_hi, qb, (MOE_LDS uint8_t*)act.hi, (wave + 3) % kDnWaves, kDnWaves);
     dma_span(a.hq_d, db, (MOE_LDS uint8_t*)act.d, (wave + 6) % kDnWaves, kDnWaves);
-    for (int kc = 0; kc < pre; ++kc) issue(kc, myring + kc * M * 1024);
+    for (int kc = 0; kc < pre; ++kc) issue(myring + kc * M * 1024);
   }
   // entry metadata: destination (or -1), weight, owner = first live entry naming its dst
   if (tid < n) {
@@ -1887,7 +1959,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
     // the caller's plan: q8_1 rows of h by absolute entry, staged after the first chunks go out
     auto mid = [&](int) {
       stage_y();
-      for (int kc = 0; kc < pre; ++kc) issue(kc, myring + kc * M * 1024);
+      for (int kc = 0; kc < pre; ++kc) issue(myring + kc * M * 1024);
       wait_vm(pre * M);   // the Y rows, older than every chunk, have landed
     };
     act_stage_q<kDnThreads, 16>(a.hq + (size_t)e0 * U * 36, n * U, act, mid);
@@ -1900,13 +1972,13 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   for (int kt = 0; kt < ntw; ++kt) {
     const int t = (int)blockIdx.x + kt * (int)gridDim.x;
     const int r0 = t * tr, nr = min(tr, a.A.n_embd - r0);
-    for (int q = 0; q < cpt; ++q, ++kc) {
-      const int g = wave + (q / nsub) * kDnWaves;
+    for (int q = 0, sb = 0; q < qpt; ++kc, sb = sb + 1 < nsub ? sb + 1 : 0, q += sb == 0) {
+      const int g = wave + q * kDnWaves;
       wait_vm((issued - 1 - kc) * M + (kc < pre ? ny : 0));
-      MOE_LDS uint8_t* slot = myring + (kc % NS) * M * 1024;
+      MOE_LDS uint8_t* slot = myring + slot_of(kc, NS) * M * 1024;
       const uint64_t w = uni64(dptr[g]);
       int c_r0, c_nr;
-      chunk_rows(t, q % nsub, c_r0, c_nr);
+      chunk_rows(t, sb, c_r0, c_nr);
       if (w && c_nr > 0) {
         const uint32_t ra = (uint32_t)(slot - ring) + (uint32_t)((w + (uint64_t)c_r0 * G.rb) & 15);
         const int a0 = uni(dsc[kDescGs + g]), a1 = uni(dsc[kDescGs + g + 1]);
@@ -1926,7 +1998,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
       }
       if (kc + NS < nch) {
         MOE_WAIT_LGKM0;
-        issue(kc + NS, slot);
+        issue(slot);
         ++issued;
       }
     }
@@ -1939,9 +2011,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
       const int d = mdst[i];
       float* y = a.Y + (size_t)d * a.ldy + r0 + m;
       float acc = kt == 0 ? ybuf[omap[i] * nr + m] : *y;
-      for (int q = i; q < n; ++q)
-        if (mdst[q] == d) acc = acc + mw[q] * ores[q * tr + m];
-      *y = acc;
+      *y = dst_sum(acc, i, n, d, m, tr, mdst, mw, ores);
     }
     lds_barrier();
   }
