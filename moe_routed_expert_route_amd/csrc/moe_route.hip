@@ -107,13 +107,19 @@ constexpr int kDescLive = kDescW + kMaxEnt;   // [kMaxEnt] 1 = compute and scatt
 constexpr int kDescPtrByte = 4 * (kDescLive + kMaxEnt);   // [kMaxGrp] down pointers (u64)
 constexpr int kDescBytes = kDescPtrByte + 8 * kMaxGrp;
 constexpr int kDescReserve = 2048;            // workspace bytes reserved for it
-// Layer mode: device-scope counts in the workspace after the descriptor (zero between calls), one
-// per kCtrLine bytes (atomics on one line are served one after another): the arrival count in two
-// levels (kCtrGroups group counts, then a top count of complete groups), then the same for done.
+// Layer mode, in the workspace after the descriptor (all zero before the first call): one arrival
+// flag per workgroup (set to the call's tag once its q8_1 rows of h are in memory: plain stores,
+// no read-modify-write on a shared line), the tag of the last call on a line of its own, and the
+// done count in two levels (kCtrGroups group counts, then a top count of complete groups), one
+// count per kCtrLine bytes (atomics on one line are served one after another).
+constexpr int kLyMaxGrid = 1024;
 constexpr int kCtrGroups = 16;
 constexpr int kCtrLine = 256;
 constexpr int kCtrOff = kDescReserve;
-constexpr int kCtrBytes = 2 * (kCtrGroups + 1) * kCtrLine;
+constexpr int kCtrFlags = 0;                          // u32 index: [kLyMaxGrid] arrival flags
+constexpr int kCtrEpoch = kLyMaxGrid;                 // u32 index: tag of the last call
+constexpr int kCtrDone = kLyMaxGrid + kCtrLine / 4;   // u32 index: the done counts
+constexpr int kCtrBytes = 4 * kCtrDone + (kCtrGroups + 1) * kCtrLine;
 static_assert(kDescPtrByte % 16 == 0 && kDescBytes % 16 == 0 && kDescBytes <= kDescReserve, "desc");
 static_assert(kDescBytes <= kCtrOff && kCtrOff % kCtrLine == 0, "counts");
 
@@ -133,9 +139,9 @@ __device__ __forceinline__ void set_err(uint32_t* err, uint32_t bit) {
   if (err) atomicOr(err, bit);
 }
 
-// Layer mode: count this workgroup into a two-level count starting at count `base` (group
-// blockIdx % kCtrGroups, then the top count of complete groups). True for the workgroup that
-// completes the top count. One thread calls it.
+// Layer mode: count this workgroup into a two-level count at ctr + base lines (group blockIdx %
+// kCtrGroups, then the top count of complete groups). True for the workgroup that completes the
+// top count. One thread calls it.
 __device__ __forceinline__ bool count_in(uint32_t* ctr, int base) {
   constexpr int kW = kCtrLine / 4;
   const int gi = (int)blockIdx.x % kCtrGroups;
@@ -1071,7 +1077,8 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   constexpr bool RT = MODE == GU_ROUTED || MODE == GU_LAYER;
   extern __shared__ __align__(16) uint8_t smem[];
   const Geom& G = a.G;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index in a scalar register: everything derived from it is uniform over the wave
+  const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63;
   const uint64_t lt = (1ull << lane) - 1ull;
   MOE_LDS uint8_t* ring = (MOE_LDS uint8_t*)smem;
   const ActSplit act = act_layout(ring + a.lds_ring, a.n_tokens, G.U);
@@ -1114,9 +1121,12 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     if (q0 >= 0 && q0 < 512) t_cbd = src[q0];
   }
   int r_dt = 0, r_gs = 0, r_ge = 0, r_ng = 0;
+  uint32_t r_ep = 0;
   uint64_t pg = 0, pu = 0, pd = 0;   // routed: expert q0's pointers (experts past kGuQThreads later)
   if constexpr (RT) {
     if (q0 >= 0 && q0 < a.T) r_dt = a.dst_of_token ? a.dst_of_token[q0] : q0;
+    if (MODE == GU_LAYER && q0 == 0)   // the last call's tag (this call's is one more)
+      r_ep = __hip_atomic_load(a.ctr + kCtrEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (q0 >= 0 && q0 < a.E) {
       pg = (uint64_t)(uintptr_t)a.A.gate[q0];
       pu = (uint64_t)(uintptr_t)a.A.up[q0];
@@ -1165,6 +1175,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
       ptabd[e] = ptr_ok(d, a.P.err) ? d : 0ull;
     }
     if (q0 >= 0 && q0 < a.T) pl.dtok[q0] = r_dt;
+    if (MODE == GU_LAYER && q0 == 0) pl.misc[12] = (int)r_ep;
   } else if constexpr (MODE == GU_COMPOSED) {
     act_stage_q<kGuThreads, kGuXPass>(a.xq, a.n_tokens * G.U, act, [](int) {});
   } else {
@@ -1523,12 +1534,13 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     MOE_LDS int* ownl = omap + kMaxEnt;                           // owner entries in order
     MOE_LDS int* dmisc = ownl + kMaxEnt;                          // [16]
     MOE_LDS float* ybuf = (MOE_LDS float*)(dmisc + 16);           // [owner][tr] first tile's Y rows
-    constexpr int kPoll = 64 * kDnWaves;   // a thread of a wave that streams no down chunks
+    constexpr int kPollWave = kDnWaves;   // a wave that streams no down chunks
+    const uint32_t tag = (uint32_t)uni(pl.misc[12]) + 1u;
 
-    // (a) this workgroup's q8_1 rows of h have reached device scope: count it
+    // (a) this workgroup's q8_1 rows of h have reached device scope: raise its flag
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
-    if (tid == 0) count_in(a.ctr, 0);
+    if (tid == 0) __hip_atomic_store(a.ctr + kCtrFlags + blockIdx.x, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // (b) the call in LDS: per group its first entry and down pointer, per entry its destination,
     //     weight and whether it was computed
@@ -1634,17 +1646,23 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
       if (lane == 0) dmisc[8] = __popcll(om);
     }
 
-    // (e) every workgroup's q8_1 rows of h are in memory once the count reaches the grid (a wave
-    //     with no down chunks in flight polls; the wait is bounded)
-    if (tid == kPoll) {
-      const uint32_t* top = a.ctr + kCtrGroups * (kCtrLine / 4);
-      const uint32_t ngrp = min(gridDim.x, (uint32_t)kCtrGroups);
+    // (e) every workgroup's q8_1 rows of h are in memory once every flag holds this call's tag (a
+    //     wave with no down chunks in flight reads them all, a few per lane; the wait is bounded)
+    if (wave == kPollWave) {
       int it = 0;
-      uint32_t v;
-      while ((v = __hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < ngrp && ++it < a.spin_limit)
+      bool all = false;
+      do {
+        int seen = 0, want = 0;
+        for (int i = lane; i < (int)gridDim.x; i += 64, ++want)
+          seen += __hip_atomic_load(a.ctr + kCtrFlags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+        all = __ballot(seen != want) == 0ull;
+        if (all) break;
         __builtin_amdgcn_s_sleep(1);
-      dmisc[9] = v >= ngrp;
-      if (v < ngrp) set_err(a.P.err, MOE_ERR_WAIT);
+      } while (++it < a.spin_limit);
+      if (lane == 0) {
+        dmisc[9] = all;
+        if (!all) set_err(a.P.err, MOE_ERR_WAIT);
+      }
     }
     lds_barrier();
     const bool go = uni(dmisc[9]) != 0;
@@ -1725,11 +1743,13 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     // a workgroup that gave up waiting still drains the chunks it issued
     __builtin_amdgcn_s_waitcnt(MOE_VM(0));
 
-    // (h) the last workgroup out clears the counts for the next call (every other workgroup has
-    //     made both counts by then)
-    if (tid == 0 && count_in(a.ctr, kCtrGroups + 1))
-      for (int i = 0; i < 2 * (kCtrGroups + 1); ++i)
-        __hip_atomic_store(a.ctr + i * (kCtrLine / 4), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // (h) the last workgroup out records this call's tag and clears the done counts for the next
+    //     call (every other workgroup has read the old tag and made its count by then)
+    if (tid == 0 && count_in(a.ctr + kCtrDone, 0)) {
+      __hip_atomic_store(a.ctr + kCtrEpoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i <= kCtrGroups; ++i)
+        __hip_atomic_store(a.ctr + kCtrDone + i * (kCtrLine / 4), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -1751,7 +1771,9 @@ struct DnArgs {
   int n_rows, ldy;
   int lds_ring, lds_act;
   int tr;               // rows of Y per tile (<= kDnTileMax)
-  int rc;               // rows per streamed chunk (a tile's rows of one group: ceil(tr / rc) chunks)
+  int rc;               // rows per streamed chunk (a tile's rows of one group: nsub chunks)
+  int nsub;             // ceil(tr / rc)
+  int ntiles;           // ceil(n_embd / tr)
 };
 
 constexpr int kDnYBuf = kMaxEnt * kDnTileMax;   // floats: the first tile's destination rows, per owner
@@ -1770,7 +1792,7 @@ template <int FMT, int MODE>
 __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const Geom& G = a.G;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = uni(tid >> 6);   // a scalar register (uniform over the wave)
   MOE_LDS uint8_t* ring = (MOE_LDS uint8_t*)smem;
   const int U = G.U;
   MOE_LDS uint8_t* actp = ring + a.lds_ring;
@@ -1855,11 +1877,12 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   const int ng = uni(dsc[kDescNg]), e0 = uni(dsc[kDescE0]), n = uni(dsc[kDescN]);
   if (ng == 0) return;
   const ActSplit act = MODE == DN_DESC ? act_layout_kb(actp, n, U) : act_layout(actp, n, U);
-  const int ntiles = (a.A.n_embd + tr - 1) / tr;
-  const int ntw = (int)blockIdx.x < ntiles ? (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+  const int ntiles = a.ntiles;
+  const int bid = (int)blockIdx.x, grid = (int)gridDim.x;
+  const int ntw = bid >= ntiles ? 0 : ntiles <= grid ? 1 : (ntiles - bid + grid - 1) / grid;   // tiles here
   // this wave's chunks, in order: per tile (t = bid + kt grid) its groups g = wave + q kDnWaves,
   // per group the tile's rows in nsub chunks of rc rows
-  const int rc = a.rc, nsub = (tr + rc - 1) / rc;
+  const int rc = a.rc, nsub = a.nsub;
   const int qpt = wave < ng ? (ng - wave + kDnWaves - 1) / kDnWaves : 0;   // groups per tile
   const int nch = ntw * qpt * nsub;
   const int M = a.S.M, NS = a.S.NS;
@@ -2411,7 +2434,7 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
     const Geom Gd = make_geom(L->fmt_down, L->n_ff, false);
     ga.Gd = Gd;
     const int resident = num_cus() * std::max(1, std::min(8, kLdsMax / bytes));
-    grid = std::min(grid_limit ? grid_limit : num_cus(), resident);
+    grid = std::min(std::min(grid_limit ? grid_limit : num_cus(), resident), kLyMaxGrid);
     // one down tile per CU (a smaller grid takes several each)
     dn_tiling(Gd, L->n_embd, num_cus(), ga.trd, ga.rcd);
     const int md = dn_stream(Gd, ga.rcd, 1).M;
@@ -2456,6 +2479,8 @@ int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, co
   da.lds_act = actb;
   da.tr = tr;
   da.rc = rc;
+  da.nsub = (tr + rc - 1) / rc;
+  da.ntiles = (L->n_embd + tr - 1) / tr;
   const int tiles = (L->n_embd + tr - 1) / tr;
   const int grid = grid_for(tiles, bytes, grid_limit);
   const hipError_t e = launch_dn(L->fmt_down, mode, da, grid, bytes, st);
