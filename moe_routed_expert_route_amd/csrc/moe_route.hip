@@ -2155,25 +2155,30 @@ int ilog2(int v) {
   return l;
 }
 
-// Lanes per row from the shape alone: among the allowed L whose wave pass (64 / L rows) keeps a
-// chunk within kChunkCap bytes (the widest L always qualifies), the best lane utilisation
-// U / (L ceil(U / L)). Gate/up: L <= 32 (a pass holds gate and up rows of rp / 2 h rows), ties
-// to the smaller L (longer items); down: ties to the larger L (more, smaller row tiles).
-Geom make_geom(int fmt, int ncols, bool gate_up) {
+// Lanes per row: among the allowed L whose wave pass (64 / L rows) keeps a chunk within kChunkCap
+// bytes (the widest L always qualifies), the best lane utilisation U / (L ceil(U / L)). Gate/up:
+// L <= 32 (a pass holds gate and up rows of rp / 2 h rows), ties to the smaller L (longer items);
+// down: ties to the larger L (more, smaller row tiles), except that one whose pass holds a whole
+// tile of rows_hint rows is kept over those that need two passes.
+Geom make_geom(int fmt, int ncols, bool gate_up, int rows_hint = 0) {
   Geom G{};
   G.U = ncols / 32;
   G.rb = ncols / block_weights(fmt) * block_bytes(fmt);
   const int Lmax = gate_up ? 32 : 64;
   int bestL = Lmax;
   double best = -1.0;
+  bool best_one = false;
   for (int L = 4; L <= Lmax; L <<= 1) {
     const int rp = 64 / L;
     if (rp * G.rb > kChunkCap && L < Lmax) continue;
     const double util = (double)G.U / (double)(L * ((G.U + L - 1) / L));
-    const bool better = gate_up ? util > best + 1e-9 : util >= best - 1e-9;
+    const bool one = rows_hint > 0 && rp >= rows_hint;
+    const bool better = gate_up ? util > best + 1e-9
+                                : util > best + 1e-9 || (util >= best - 1e-9 && (one || !best_one));
     if (better) {
       best = util;
       bestL = L;
+      best_one = one;
     }
   }
   G.L = bestL;
@@ -2181,6 +2186,14 @@ Geom make_geom(int fmt, int ncols, bool gate_up) {
   G.upl = (G.U + G.L - 1) / G.L;
   G.rp = 64 / G.L;
   return G;
+}
+
+int num_cus();
+
+// The down geometry for this device: its tiles hold ceil(n_embd / CUs) rows (at most kDnTileMax).
+Geom down_geom(const moe_layer* L) {
+  const int tr = std::min(kDnTileMax, std::max(1, (L->n_embd + num_cus() - 1) / num_cus()));
+  return make_geom(L->fmt_down, L->n_ff, false, tr);
 }
 
 // Slot size in KB: each span (gate rows, then up rows, each in whole KB) plus alignment slack (its
@@ -2354,7 +2367,7 @@ int gu_lds(const moe_layer* L, const moe_plan* P, int n_tokens, int mode, Stream
     lg = L->n_embd * 4;
   }
   if (mode == GU_LAYER) {
-    const Geom Gd = make_geom(L->fmt_down, L->n_ff, false);
+    const Geom Gd = down_geom(L);
     if (act_bytes_kb(P->cap_entries, Gd.U) > kDnActMax) return -1;
     *downb = ly_down_bytes(P->cap_entries, Gd.U);
     int tr, rc;
@@ -2377,7 +2390,7 @@ int gu_lds(const moe_layer* L, const moe_plan* P, int n_tokens, int mode, Stream
 
 // LDS of the down kernel for chunks of rc rows: two slots per wave where they fit, else one.
 int dn_lds(const moe_layer* L, const moe_plan* P, int rc, Stream* S, int* ring, int* actb) {
-  const Geom G = make_geom(L->fmt_down, L->n_ff, false);
+  const Geom G = down_geom(L);
   *actb = act_bytes_kb(P->cap_entries, G.U);
   if (*actb > kDnActMax) return -1;
   for (int ns = 2; ns >= 1; --ns) {
@@ -2431,7 +2444,7 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
   int grid = grid_for(items, bytes, grid_limit);
   if (mode == GU_LAYER) {
     // every workgroup waits for all the others: at most what the CUs hold at once (LDS-limited)
-    const Geom Gd = make_geom(L->fmt_down, L->n_ff, false);
+    const Geom Gd = down_geom(L);
     ga.Gd = Gd;
     const int resident = num_cus() * std::max(1, std::min(8, kLdsMax / bytes));
     grid = std::min(std::min(grid_limit ? grid_limit : num_cus(), resident), kLyMaxGrid);
@@ -2451,7 +2464,7 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
 
 int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, const uint8_t* ws,
              const uint8_t* hq, float* Y, int n_rows, int ldy, int grid_limit) {
-  const Geom G = make_geom(L->fmt_down, L->n_ff, false);
+  const Geom G = down_geom(L);
   // one tile per CU: every CU streams the same share of the down rows
   int tr, rc;
   dn_tiling(G, L->n_embd, num_cus(), tr, rc);
