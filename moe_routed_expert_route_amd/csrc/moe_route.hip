@@ -632,6 +632,9 @@ __device__ __forceinline__ void swiglu_q81_lanes(float gv, float uv, int l32, bo
 // Each quad of lanes packs its four quants into a dword; the stores are device-scope (they reach
 // memory past this XCD's L2), so another workgroup of the same launch can read them once it has
 // seen this workgroup's count.
+// DEV: device-scope stores (the one-launch step reads them back in the same launch); otherwise
+// plain stores, which the end of the launch makes visible to the next one.
+template <bool DEV>
 __device__ __forceinline__ void swiglu_q81_split(float gv, float uv, int l32, bool live, uint32_t* lo,
                                                  uint32_t* hi, float* dq) {
   const float h = live ? swiglu(gv, uv) : 0.0f;
@@ -647,10 +650,15 @@ __device__ __forceinline__ void swiglu_q81_split(float gv, float uv, int l32, bo
   const uint32_t b = (uint32_t)q & 0xFFu;
   const uint32_t w = b | (dppu<0x55>(b) << 8) | (dppu<0xAA>(b) << 16) | (dppu<0xFF>(b) << 24);   // quad lanes 1, 2, 3
   if (live) {
-    if ((l32 & 3) == 0)
-      __hip_atomic_store((l32 < 16 ? lo : hi) + ((l32 >> 2) & 3), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (l32 == 0)
-      __hip_atomic_store((uint32_t*)dq, __float_as_uint(h2f(f2h(d))), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t* qw = (l32 < 16 ? lo : hi) + ((l32 >> 2) & 3);
+    const uint32_t dw = __float_as_uint(h2f(f2h(d)));
+    if constexpr (DEV) {
+      if ((l32 & 3) == 0) __hip_atomic_store(qw, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (l32 == 0) __hip_atomic_store((uint32_t*)dq, dw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if ((l32 & 3) == 0) *qw = w;
+      if (l32 == 0) *(uint32_t*)dq = dw;
+    }
   }
 }
 
@@ -1512,7 +1520,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
           const float gv = live ? stage[e * 64 + l32] : 0.0f;
           const float uv = live ? stage[e * 64 + 32 + l32] : 0.0f;
           const size_t bk = (size_t)(a0 + (live ? e : 0)) * nb + blk;
-          swiglu_q81_split(gv, uv, l32, live, a.hq_lo + 4 * bk, a.hq_hi + 4 * bk, a.hq_d + bk);
+          swiglu_q81_split<MODE == GU_LAYER>(gv, uv, l32, live, a.hq_lo + 4 * bk, a.hq_hi + 4 * bk, a.hq_d + bk);
         }
       }
     }
