@@ -1036,6 +1036,7 @@ struct GuArgs {
   float* Y;
   int n_rows, ldy;
   int lds_tail;         // bytes of the routed tail (the down region follows it)
+  uint32_t nb_magic;    // floor(2^32 / (n_ff / 32)) (all ones for 1): division by the blocks per group
   uint32_t* ctr;        // workspace: [0] workgroups done with their blocks, [1] workgroups done
   int spin_limit;       // bounded wait for the other workgroups (then MOE_ERR_WAIT)
 };
@@ -1253,16 +1254,23 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   int upc = 0, upre = 0, cpre = 0;
   int ng = 0, e0 = 0, n = 0;
   if constexpr (RT) {
-    int ucnt = 0;
-    if (lane < nW)
-      for (int t = 0; t < a.T; ++t) {
-        const uint32_t bw = selT[t * nW + lane];
-        uw |= bw;
-        ucnt += __popc(bw);
-      }
-    upc = __popc(uw);
-    upre = lane_prefix(upc, 6);
-    cpre = lane_prefix(ucnt, 7);   // at most 64 entries in all
+    if (a.T == 1) {   // one token: the union is its selection, each group holds one entry
+      if (lane < nW) uw = selT[lane];
+      upc = __popc(uw);
+      upre = lane_prefix(upc, 6);
+      cpre = upre;
+    } else {
+      int ucnt = 0;
+      if (lane < nW)
+        for (int t = 0; t < a.T; ++t) {
+          const uint32_t bw = selT[t * nW + lane];
+          uw |= bw;
+          ucnt += __popc(bw);
+        }
+      upc = __popc(uw);
+      upre = lane_prefix(upc, 6);
+      cpre = lane_prefix(ucnt, 7);   // at most 64 entries in all
+    }
     ng = __builtin_amdgcn_readlane(upre + upc, 63);
     e0 = a.entry_base;
     n = a.T * a.k;
@@ -1346,8 +1354,10 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   const int nb = a.A.n_ff / 32;          // blocks per group
   const int npass = 64 / G.rp;           // passes per block
   const int items = ng * nb;
-  const int nit = (int)blockIdx.x < items ? (items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
-  const int cw = wave < min(a.sw, npass) ? (npass - wave + a.sw - 1) / a.sw : 0;   // passes per block
+  const int bid = (int)blockIdx.x, grid = (int)gridDim.x;
+  // (the usual shapes need no division: at most one item per workgroup, one pass per wave)
+  const int nit = bid >= items ? 0 : items <= grid ? 1 : (items - bid + grid - 1) / grid;
+  const int cw = wave >= min(a.sw, npass) ? 0 : npass <= a.sw ? 1 : (npass - wave + a.sw - 1) / a.sw;
   const int nch = nit * cw;
   const int M = a.S.M, NS = a.S.NS;
   MOE_LDS uint8_t* myring = ring + wave * NS * M * 1024;
@@ -1357,8 +1367,14 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   struct Pos {
     int q, g, blk;
   };
-  const int gstep = (int)gridDim.x / nb, bstep = (int)gridDim.x - gstep * nb;
-  const Pos first{0, (int)blockIdx.x / nb, (int)blockIdx.x % nb};
+  auto div_nb = [&](int x) {   // x / nb from the host's reciprocal, one correction step
+    int q = (int)__umulhi((uint32_t)x, a.nb_magic);
+    if ((q + 1) * nb <= x) ++q;
+    return q;
+  };
+  const int gstep = div_nb(grid), bstep = grid - gstep * nb;
+  const int g0 = div_nb(bid);
+  const Pos first{0, g0, bid - g0 * nb};
   auto next_item = [&](Pos& p) {
     p.q = 0;
     p.g += gstep;
@@ -2448,6 +2464,10 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
   ga.lds_act = actb;
   ga.sw = sw;
   ga.lds_tail = tailb;
+  {
+    const uint32_t nbk = (uint32_t)(L->n_ff / 32);
+    ga.nb_magic = nbk <= 1 ? 0xFFFFFFFFu : (uint32_t)((1ull << 32) / nbk);
+  }
   const int items = P->cap_groups * (L->n_ff / 32);
   int grid = grid_for(items, bytes, grid_limit);
   if (mode == GU_LAYER) {
