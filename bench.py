@@ -273,7 +273,7 @@ def run_cpu_baseline(wl, seconds):
     log(f"cpu oracle for ~{seconds} s")
     cache = {}
     total, calls, l = 0.0, 0, 0
-    while total < seconds and calls < 4 * wl.L:
+    while total < seconds and calls < 16 * wl.L:
         if l not in cache:
             ids, w = oracle.route_topk(wl.logits[l], wl.k)
             ex = {int(e): wl.host_expert(l, int(e)) for e in np.unique(ids)}
