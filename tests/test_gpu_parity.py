@@ -100,6 +100,9 @@ ROUTED = {
     "q8_t4_shared_small": dict(n_embd=256, n_ff=128, E=8, k=2, T=4, fg=Q8_0, fd=Q8_0, ids="shared"),
     # 2 units per row: one or two lanes per row
     "nl4_t4_shared_tiny": dict(n_embd=64, n_ff=64, E=4, k=2, T=4, fg=NL4, fd=Q8_0, ids="shared"),
+    # many experts: 16 logits per lane in the routing wave, expert pointers past the first 512
+    # loaded in a second round, a 32-word selection bitmap
+    "q8_e1000_t3": dict(n_embd=256, n_ff=128, E=1000, k=8, T=3, fg=Q8_0, fd=Q8_0),
 }
 
 
