@@ -125,6 +125,77 @@ def measure(wl, steps, warmup, reps=5):
     return ms_step, ms_plain, ks
 
 
+def stream_read_gbs(gib=2, reps=5):
+    """A plain streaming read of `gib` GiB (torch's sum over float32) timed with HIP events: the
+    bandwidth a simple kernel gets from HBM on this device, reported beside the HBM peak."""
+    import torch
+    n = gib << 28
+    t = torch.ones(n, dtype=torch.float32, device="cuda")
+    t.sum()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        t.sum()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del t
+    torch.cuda.empty_cache()
+    return {"gbs": round(4.0 * n / (ms * 1e-3) / 1e9, 1), "bytes": 4 * n,
+            "kind": "torch sum over a float32 tensor, HIP events, mean of 5"}
+
+
+def empty_call_us(layers=48, reps=20):
+    """Cost of a call with no work (n_groups = 0) at the 4096 x 1536 Q8_0 edge geometry, 256
+    experts, plan capacity 32 entries from entry 7: a HIP graph of `layers` fused calls
+    (moe_layer_decode), timed with HIP events."""
+    import torch
+
+    from moe_routed_expert_route_amd import binding as B
+    from moe_routed_expert_route_amd import synth
+    n_embd, n_ff, E = 4096, 1536, 256
+    d = torch.device("cuda")
+    zg = torch.zeros(synth.row_bytes(synth.Q8_0, n_embd) * n_ff, dtype=torch.uint8, device=d)
+    zd = torch.zeros(synth.row_bytes(synth.Q8_0, n_ff) * n_embd, dtype=torch.uint8, device=d)
+    t64 = dict(dtype=torch.int64, device=d)
+    layer = B.Layer.from_pointers(n_embd, n_ff, synth.Q8_0, synth.Q8_0,
+                                  torch.full((E,), zg.data_ptr(), **t64), torch.full((E,), zg.data_ptr(), **t64),
+                                  torch.full((E,), zd.data_ptr(), **t64), keep=(zg, zd))
+    plan = B.Plan(32, 32, entry_capacity=7 + 32, device=d)
+    plan.set(synth.direct_plan(0, E, 4, 64, 7, 5, max_entries=32))
+    x = torch.zeros((4, n_embd), dtype=torch.float32, device=d)
+    Y = torch.zeros((64, n_embd), dtype=torch.float32, device=d)
+    ws = B.workspace(layer, plan)
+    B.moe_layer_decode(layer, plan, x, Y, ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(layers):
+            B.moe_layer_decode(layer, plan, x, Y, ws)
+    torch.cuda.synchronize()
+    g.replay()
+    ms = time_graph(g, reps)
+    assert plan.errors() == 0
+    del g
+    return {"us_per_call": round(ms * 1e3 / layers, 3), "calls": layers,
+            "config": "4096 x 1536 Q8_0, 256 experts, n_groups 0, cap 32 entries from entry 7, two launches"}
+
+
+def fit_groups_entries(lines):
+    """Least-squares t = a + b n_groups + c n_entries over the sweep lines (b: per expert, c: per
+    entry)."""
+    import numpy as np
+    A = np.array([[1.0, ln["distinct_experts_per_layer"], ln["T"] * 8] for ln in lines])
+    t = np.array([ln["us_per_layer_call"] for ln in lines])
+    coef, *_ = np.linalg.lstsq(A, t, rcond=None)
+    return {"us_fixed": round(float(coef[0]), 3), "us_per_group": round(float(coef[1]), 3),
+            "us_per_entry": round(float(coef[2]), 3), "lines": len(lines)}
+
+
 def traffic_for(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary of `workload`, or None
     when there is none or the kernel sources changed since the counters were taken."""
@@ -246,6 +317,13 @@ def main():
     del wl
     torch.cuda.empty_cache()
     if not args.no_sweep:
+        log("reference streaming read")
+        ref = stream_read_gbs()
+        res["reference_stream_read"] = ref
+        res["frac_of_stream_read"] = round(gbs / ref["gbs"], 4)
+        log("empty call")
+        res["empty_call"] = empty_call_us()
+    if not args.no_sweep:
         sweep = {"nl4_2560x768_shared": [], "cb3q8_2560x640_uniform": []}
         for T in (1, 2, 3, 4):
             log(f"sweep nl4 2560x768 shared experts T={T}")
@@ -259,6 +337,9 @@ def main():
         log("cb2/nl4 T=4 zipf")
         sweep["cb2nl4_2560x768_t4_zipf"] = [sweep_line("cb2nl4_2560x768_t4_zipf", 4, "zipf", 10, 3)]
         res["t_sweep"] = sweep
+        res["fit_nl4_groups_entries"] = fit_groups_entries(
+            sweep["nl4_2560x768_shared"] + sweep["cb2nl4_2560x768_t4_zipf"])
+        res["fit_cb3q8_groups_entries"] = fit_groups_entries(sweep["cb3q8_2560x640_uniform"])
     print(json.dumps(res), flush=True)
 
 

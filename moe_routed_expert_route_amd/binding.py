@@ -237,8 +237,8 @@ def moe_workspace_bytes(layer: Layer, plan: Plan) -> int:
 
 def workspace(layer: Layer, plan: Plan, device="cuda"):
     """Allocate a zero-filled workspace for this layer geometry and plan capacity (the one-launch
-    step needs its two counts zero before the first call; every other call reads only bytes it
-    wrote itself)."""
+    step needs its flags and counts zero before the first call; every other call reads only bytes
+    it wrote itself)."""
     nb = moe_workspace_bytes(layer, plan)
     if nb == 0:
         raise RuntimeError("moe_workspace_bytes: bad layer or plan")

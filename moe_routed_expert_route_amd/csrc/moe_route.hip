@@ -519,14 +519,17 @@ __device__ __forceinline__ void dot_pass_n(const MOE_LDS uint32_t* W, uint32_t r
       unit_decode<FMT>(r, u, tb, c, sc);
 #pragma unroll
       for (int e = 0; e < NE; ++e) {
-        int s = __builtin_amdgcn_sdot4((int)c[0], (int)q[e][0], 0, false);
-        s = __builtin_amdgcn_sdot4((int)c[1], (int)q[e][1], s, false);
-        s = __builtin_amdgcn_sdot4((int)c[2], (int)q[e][2], s, false);
-        s = __builtin_amdgcn_sdot4((int)c[3], (int)q[e][3], s, false);
-        s = __builtin_amdgcn_sdot4((int)c[4], (int)q[e][4], s, false);
-        s = __builtin_amdgcn_sdot4((int)c[5], (int)q[e][5], s, false);
-        s = __builtin_amdgcn_sdot4((int)c[6], (int)q[e][6], s, false);
-        s = __builtin_amdgcn_sdot4((int)c[7], (int)q[e][7], s, false);
+        // two independent chains (an integer sum: the order does not change it), so a wave
+        // alone on its SIMD is not held up by one chain of eight dependent dot instructions
+        int s0 = __builtin_amdgcn_sdot4((int)c[0], (int)q[e][0], 0, false);
+        int s1 = __builtin_amdgcn_sdot4((int)c[1], (int)q[e][1], 0, false);
+        s0 = __builtin_amdgcn_sdot4((int)c[2], (int)q[e][2], s0, false);
+        s1 = __builtin_amdgcn_sdot4((int)c[3], (int)q[e][3], s1, false);
+        s0 = __builtin_amdgcn_sdot4((int)c[4], (int)q[e][4], s0, false);
+        s1 = __builtin_amdgcn_sdot4((int)c[5], (int)q[e][5], s1, false);
+        s0 = __builtin_amdgcn_sdot4((int)c[6], (int)q[e][6], s0, false);
+        s1 = __builtin_amdgcn_sdot4((int)c[7], (int)q[e][7], s1, false);
+        const int s = s0 + s1;
         // a unit past the row's end adds +0.0f: acc never holds -0 (it starts at +0), so this
         // equals skipping the add
         const float prod = (sc * dx[e]) * (float)s;
