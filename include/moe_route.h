@@ -165,7 +165,7 @@ int moe_layer_decode(void* stream, const moe_layer* L, const moe_plan* P, const 
 
 /* Same step starting from the router logits [T][n_experts] (float32): every gate/up workgroup
  * routes the T tokens (top-k, as moe_route_topk) and groups the entries (as moe_build_plan with
- * entry_base and dst_of_token) itself, and workgroup 0 writes that plan into P for the down
+ * entry_base and dst_of_token) itself, and one workgroup writes that plan into P for the down
  * launch and for the caller. Bit-identical to route_topk -> build_plan -> moe_layer_decode.
  * Requires T*k <= cap_entries, T*k <= cap_groups, k <= 32, n_experts <= 1024. */
 int moe_layer_decode_routed(void* stream, const moe_layer* L, const moe_plan* P,

@@ -1076,7 +1076,8 @@ __host__ __device__ inline int ly_down_bytes(int cap_entries, int Ud) {
 // waves 8..15 quantize x into LDS; after one workgroup barrier every wave finds, from the tokens'
 // selection bitmaps, the expert of each group it streams (groups ascending by expert id; the g-th
 // set bit of the union of the bitmaps) and that group's entries (tokens ascending), so the weight
-// loads go out with no further barrier. Workgroup 0 then writes the plan and the descriptor.
+// loads go out with no further barrier. The last workgroup (which holds the fewest blocks) then
+// writes the plan and the descriptor.
 //
 // Layer mode: the grid is at most one workgroup per CU and every workgroup is resident. After its
 // blocks, a workgroup's q8_1 rows of h are in memory (device-scope stores) and it adds one to a
@@ -1156,9 +1157,9 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
       for (int t = wave; t < a.T; t += kRtWaves) {
         if (t != wave) issue_logits(a.logits + (size_t)t * a.E, a.E, (MOE_LDS float*)rscr);
         __builtin_amdgcn_s_waitcnt(MOE_VM(0));
-        // routed: only workgroup 0 writes the plan, so only it needs the router weights
+        // routed: only the last workgroup writes the plan, so only it needs the router weights
         route_token(rscr, a.E, a.k, pl.rid + t * a.k, pl.rw + t * a.k, selT + t * nW,
-                    MODE == GU_LAYER || blockIdx.x == 0);
+                    MODE == GU_LAYER || blockIdx.x == gridDim.x - 1);
       }
       __builtin_amdgcn_s_setprio(0);
       load_nl4(a.A.nl4, t_nl4);
@@ -1413,8 +1414,9 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   __builtin_amdgcn_s_setprio(0);
   int issued = pre;
 
-  // ---- 5. workgroup 0 leaves the plan (routed) and the call's descriptor (fused / routed)
-  if (MODE != GU_COMPOSED && blockIdx.x == 0) {
+  // ---- 5. the last workgroup (the fewest blocks: they are dealt in workgroup order) leaves the
+  //         plan (routed) and the call's descriptor (fused / routed)
+  if (MODE != GU_COMPOSED && blockIdx.x == gridDim.x - 1) {
     int* dw = (int*)a.desc;
     uint64_t* dp = (uint64_t*)(a.desc + kDescPtrByte);
     if constexpr (RT) {
@@ -2472,7 +2474,9 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
     ga.nb_magic = nbk <= 1 ? 0xFFFFFFFFu : (uint32_t)((1ull << 32) / nbk);
   }
   const int items = P->cap_groups * (L->n_ff / 32);
-  int grid = grid_for(items, bytes, grid_limit);
+  // one workgroup more than the blocks where the CUs allow: the last one, which writes the plan
+  // and the descriptor, then holds no block of its own
+  int grid = grid_for(mode == GU_COMPOSED ? items : items + 1, bytes, grid_limit);
   if (mode == GU_LAYER) {
     // every workgroup waits for all the others: at most what the CUs hold at once (LDS-limited)
     const Geom Gd = down_geom(L);
