@@ -185,6 +185,55 @@ def empty_call_us(layers=48, reps=20):
             "config": "4096 x 1536 Q8_0, 256 experts, n_groups 0, cap 32 entries from entry 7, two launches"}
 
 
+def two_calls_us(wl, reps=20):
+    """Each layer as two fused calls (moe_layer_decode) sharing the entry arrays and Y: the routed
+    plan of the layer split so that the groups of its two highest expert ids go to the second call
+    (entries past the first call's), against one fused call with the whole plan. HIP graphs of the
+    48 (or 96) calls, timed with HIP events."""
+    import torch
+
+    from moe_routed_expert_route_amd import binding as B
+    from moe_routed_expert_route_amd import synth
+    cap = wl.T * wl.k
+    d = torch.device("cuda")
+    one, first, second = [], [], []
+    n2 = []
+    for l in range(wl.L):
+        ph = wl.plans[l].get()
+        late = set(int(e) for e in ph["grp_expert"][-2:])
+        pa, pb = synth.split_plan(ph, lambda e: e not in late)
+        p1 = B.Plan(cap, cap, device=d)
+        p1.set(ph)
+        pa_d = B.Plan(cap, cap, device=d)
+        pb_d = B.Plan(cap, cap, device=d, entries_of=pa_d)
+        pa_d.set(pa)
+        pb_d.set(pb)
+        one.append(p1)
+        first.append(pa_d)
+        second.append(pb_d)
+        n2.append(pb["n_groups"])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    out = {}
+    for name, calls in (("one_call", [(one[l],) for l in range(wl.L)]),
+                        ("two_calls", [(first[l], second[l]) for l in range(wl.L)])):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for l in range(wl.L):
+                for p in calls[l]:
+                    B.moe_layer_decode(wl.layers[l], p, wl.d_x[l], wl.Y[l], wl.ws[l])
+        torch.cuda.synchronize()
+        g.replay()
+        out[name] = time_graph(g, reps) * 1e3 / wl.L
+        del g
+    assert not any(p.errors() for p in one + first)
+    return {"us_per_layer_one_call": round(out["one_call"], 3),
+            "us_per_layer_two_calls": round(out["two_calls"], 3),
+            "us_second_call": round(out["two_calls"] - out["one_call"], 3),
+            "groups_in_second_call": sorted(set(n2)),
+            "config": "plan given (routed once beforehand), moe_layer_decode per call, graph of all layers"}
+
+
 def fit_groups_entries(lines):
     """Least-squares t = a + b n_groups + c n_entries over the sweep lines (b: per expert, c: per
     entry)."""
@@ -312,6 +361,9 @@ def main():
                      "avg_launch_us": dk["avg_launch_us"]},
         "kernels": kernels,
     }
+    if not args.no_sweep:
+        log("two calls per layer")
+        res["two_calls_per_layer"] = two_calls_us(wl)
     if not args.no_cpu:
         res["cpu_baseline"] = run_cpu_baseline(wl, args.cpu_seconds)
     del wl

@@ -151,16 +151,22 @@ class Plan:
     """Device arrays of a call's plan. Entry arrays hold `entry_capacity` entries (absolute
     indices), so a plan may start past entry 0."""
 
-    def __init__(self, cap_groups, cap_entries, entry_capacity=None, device="cuda"):
+    def __init__(self, cap_groups, cap_entries, entry_capacity=None, device="cuda", entries_of=None):
+        """entries_of: another Plan whose entry arrays (and error word) this one shares, so that
+        two calls of one layer (each over its own groups) index one run of entries."""
         ec = entry_capacity if entry_capacity is not None else cap_entries
         i32 = dict(dtype=torch.int32, device=device)
         self.n_groups = torch.zeros(1, **i32)
         self.grp_expert = torch.zeros(cap_groups, **i32)
         self.grp_start = torch.zeros(cap_groups + 1, **i32)
-        self.ent_src = torch.zeros(ec, **i32)
-        self.ent_dst = torch.zeros(ec, **i32)
-        self.ent_w = torch.zeros(ec, dtype=torch.float32, device=device)
-        self.err = torch.zeros(1, **i32)
+        if entries_of is not None:
+            self.ent_src, self.ent_dst = entries_of.ent_src, entries_of.ent_dst
+            self.ent_w, self.err = entries_of.ent_w, entries_of.err
+        else:
+            self.ent_src = torch.zeros(ec, **i32)
+            self.ent_dst = torch.zeros(ec, **i32)
+            self.ent_w = torch.zeros(ec, dtype=torch.float32, device=device)
+            self.err = torch.zeros(1, **i32)
         self.cap_groups, self.cap_entries = cap_groups, cap_entries
         self.struct = MoePlan(cap_groups, cap_entries, self.n_groups.data_ptr(),
                               self.grp_expert.data_ptr(), self.grp_start.data_ptr(),

@@ -162,6 +162,33 @@ def direct_plan(n_groups: int, E: int, T: int, n_rows: int, entry_base: int, *ke
                 ent_w=g.uniform(0.05, 1.0, size=len(src)).astype(np.float32), T=T)
 
 
+def split_plan(plan: dict, first) -> tuple[dict, dict]:
+    """Two calls' plans from one: the groups whose expert satisfies first(e) go to the first call,
+    the rest to the second, each keeping its groups ascending by expert. The entries are laid out
+    again in one shared run of entry indices starting at plan["entry_base"]: the first call's
+    entries, then the second's, so the second call starts past the first's entries. Entry order
+    inside a group is kept."""
+    ng, base = int(plan["n_groups"]), int(plan["entry_base"])
+    gs = np.asarray(plan["grp_start"], np.int64)
+    parts = ([], [])
+    for g in range(ng):
+        parts[0 if first(int(plan["grp_expert"][g])) else 1].append(g)
+    out, at = [], base
+    for gl in parts:
+        starts, rows = [at], []
+        for g in gl:
+            rows.extend(range(int(gs[g]) - base, int(gs[g + 1]) - base))
+            starts.append(starts[-1] + int(gs[g + 1] - gs[g]))
+        rows = np.asarray(rows, np.int64)
+        out.append(dict(n_groups=len(gl), grp_expert=np.asarray([plan["grp_expert"][g] for g in gl], np.int32),
+                        grp_start=np.asarray(starts, np.int32), entry_base=at,
+                        ent_src=np.asarray(plan["ent_src"], np.int32)[rows],
+                        ent_dst=np.asarray(plan["ent_dst"], np.int32)[rows],
+                        ent_w=np.asarray(plan["ent_w"], np.float32)[rows]))
+        at = starts[-1]
+    return out[0], out[1]
+
+
 def nan_rows(n_rows: int, n: int) -> np.ndarray:
     """float32 [n_rows, n] filled with the quiet-NaN pattern 0x7FC0DEAD."""
     return np.full((n_rows, n), NAN_FILL, np.uint32).view(np.float32)

@@ -165,6 +165,55 @@ def test_layer_stages(name):
     assert np.array_equal(U.bits(r3["Y"]), U.bits(comp["Y"]))
 
 
+@pytest.mark.parametrize("name", ["q8_nl4_t3", "nl4_t1", "cb2_nl4_t4_zipf"])
+def test_two_calls_per_layer(name):
+    """One layer as two calls sharing the entry arrays and Y: the even experts' groups first, the
+    odd experts' groups second with entries past the first call's. Each call's stages against the
+    oracle (the second from the Y the first left); the fused calls give the composed bits, eagerly
+    and as a HIP graph of the pair replayed three times."""
+    c = _routed(name, key=4)
+    T, k = c.T, c.k
+    base, n_rows = 3, 8
+    dst = synth.rng(41, T).choice(n_rows, T, replace=False).astype(np.int32)
+    plan, _, _ = U.gpu_route_and_plan(c, T * k, T * k, entry_base=base, dst_of_token=dst)
+    pa, pb = synth.split_plan(plan.get(), lambda e: e % 2 == 0)
+    d = U.dev()
+    PA = B.Plan(T * k, T * k, entry_capacity=base + T * k, device=d)
+    PB = B.Plan(T * k, T * k, entry_capacity=base + T * k, device=d, entries_of=PA)
+    PA.set(pa)
+    PB.set(pb)
+    print(f"{name}: {pa['n_groups']} + {pb['n_groups']} groups", flush=True)
+    Y0 = U.y0_for(n_rows, c.n_embd, dst, 2)
+    ca = U.run_composed(c, PA, c.x, Y0, n_rows)
+    cb = U.run_composed(c, PB, c.x, ca["Y"], n_rows)
+    assert ca["err"] == 0 and cb["err"] == 0
+    U.check_stages(c, pa, ca, Y0)
+    U.check_stages(c, pb, cb, ca["Y"])
+    x = torch.from_numpy(c.x).to(d)
+    y0 = torch.from_numpy(Y0).to(d)
+    Y = y0.clone()
+    ws = B.workspace(c.layer, PA, device=d)
+    B.moe_layer_decode(c.layer, PA, x, Y, ws)
+    B.moe_layer_decode(c.layer, PB, x, Y, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(U.bits(Y.cpu().numpy()), U.bits(cb["Y"]))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        B.moe_layer_decode(c.layer, PA, x, Y, ws)
+        B.moe_layer_decode(c.layer, PB, x, Y, ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        Y.copy_(y0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(U.bits(Y.cpu().numpy()), U.bits(cb["Y"])), rep
+    assert PA.errors() == 0
+    del g
+
+
 @pytest.mark.parametrize("name", ["nl4_t1", "cb2_nl4_t4_zipf"])
 def test_grid_invariance(name):
     c = _routed(name, key=2)

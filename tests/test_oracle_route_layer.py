@@ -139,3 +139,37 @@ def test_layer_brute_force(orc, fmts):
     assert np.all(np.abs(res["Y"] - Y) <= 1e-12 * res["S"])
     untouched = [r for r in range(6) if r not in dst.tolist()]
     assert np.array_equal(res["Y"][untouched], Y0[untouched].astype(np.float64))
+
+
+def test_two_calls_split_plan(orc):
+    """Two calls of one layer over disjoint expert subsets, the second's entries past the first's
+    ("#363 experts: ...", "Exactness": a call covers only its own entries, which may start past
+    entry 0; both calls add into the same output rows), give the one-call result."""
+    n_embd, n_ff, E, T, k = 256, 128, 8, 3, 2
+    tb, gate, up, down, x, lg = _small_layer(2, Q8_0, Q8_0, n_embd, n_ff, E, T, k)
+    ids, w = orc.route_topk(lg, k)
+    dst = np.array([1, 4, 2], np.int32)
+    plan = orc.build_plan(ids, w.astype(np.float32), dst, E, 4)
+    pa, pb = synth.split_plan(plan, lambda e: e % 2 == 0)
+    assert pa["n_groups"] + pb["n_groups"] == plan["n_groups"] and pa["n_groups"] and pb["n_groups"]
+    assert pa["entry_base"] == 4 and pb["entry_base"] == pa["grp_start"][-1] == pb["grp_start"][0]
+    assert pb["grp_start"][-1] == plan["grp_start"][-1]
+    for p, par in ((pa, 0), (pb, 1)):
+        assert np.all(np.diff(p["grp_expert"]) > 0) and np.all(p["grp_expert"] % 2 == par)
+    # the same (expert, token, destination, weight) entries, each once
+    def triples(p):
+        out = []
+        for g in range(p["n_groups"]):
+            for a in range(p["grp_start"][g], p["grp_start"][g + 1]):
+                r = a - p["entry_base"]
+                out.append((int(p["grp_expert"][g]), int(p["ent_src"][r]), int(p["ent_dst"][r]),
+                            float(p["ent_w"][r])))
+        return sorted(out)
+    assert triples(plan) == sorted(triples(pa) + triples(pb))
+    Y0 = synth.rng(5).standard_normal((6, n_embd)).astype(np.float32)
+    one = orc.layer(x, plan, Q8_0, Q8_0, gate, up, down, n_embd, n_ff, Y0, tb)
+    ra = orc.layer(x, pa, Q8_0, Q8_0, gate, up, down, n_embd, n_ff, Y0, tb)
+    rb = orc.layer(x, pb, Q8_0, Q8_0, gate, up, down, n_embd, n_ff, ra["Y"], tb)
+    assert np.all(np.abs(rb["Y"] - one["Y"]) <= 1e-12 * one["S"])
+    untouched = [r for r in range(6) if r not in dst.tolist()]
+    assert np.array_equal(rb["Y"][untouched], Y0[untouched].astype(np.float64))
