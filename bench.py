@@ -364,6 +364,19 @@ def main():
     if not args.no_sweep:
         log("two calls per layer")
         res["two_calls_per_layer"] = two_calls_us(wl)
+    if not args.no_sweep:
+        log("planar layout: repack every pool, time the step again")
+        sec, nb = wl.to_planar()
+        ms_p, _, ks_p = measure(wl, args.steps, args.warmup)
+        res["planar_layout"] = {
+            "us_per_layer_call": round(ms_p * 1e3 / wl.L, 3),
+            "gate_up_avg_launch_us": round(ks_p["gate_up"], 3),
+            "down_avg_launch_us": round(ks_p["down"], 3),
+            "repack_gb": round(nb / 1e9, 3), "repack_s": round(sec, 4),
+            "repack_gbs_read_plus_write": round(2 * nb / sec / 1e9, 1),
+            "config": "the same workload after moe_repack of every pool (all 128 experts of all "
+                      "48 layers) into the planar layout; the same launches with the format fields "
+                      "flagged planar"}
     if not args.no_cpu:
         res["cpu_baseline"] = run_cpu_baseline(wl, args.cpu_seconds)
     del wl

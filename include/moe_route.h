@@ -44,6 +44,12 @@
  *         amax = max|x|, d = amax / 127 (float32), q = clamp(round-half-away(x / d), +-127)
  *         (0 if amax == 0), d16 = fp16(d), s16 = fp16(f(d16) * sum q), all IEEE float32.
  * A matrix of R rows x C columns is R consecutive rows of C / block_weights blocks.
+ * Planar layout (MOE_LAYOUT_PLANAR OR-ed into a moe_layer format field): the same bytes per row,
+ * reordered so that the codes of the row's n blocks come first, block after block (Q8_0 32 B,
+ * NL4 16 B, CB2 the 64 index and sign bytes, CB3 the 104 low-index, high-bit and sign bytes,
+ * each in its row-major order), then the scales, block after block (Q8_0 / NL4 the fp16 d; CB2 /
+ * CB3 the fp16 D followed by the 4 sub-scale bytes). A row keeps its size and a matrix its rows,
+ * so every pointer and size of the row-major layout holds; moe_repack converts either way.
  * Shapes: C must be a multiple of 64 for Q8_0 / NL4 and of 256 for CB2 / CB3; n_embd and n_ff
  * at most MOE_MAX_DIM.
  * Block contribution: c_b = scale_w * f(d_x) * sum_j code_j q_j (exact int32 sum); a row's dot
@@ -64,6 +70,7 @@ extern "C" {
 #define MOE_MAX_GROUPS 64         /* max cap_groups of one call */
 
 typedef enum { MOE_FMT_Q8_0 = 1, MOE_FMT_NL4 = 2, MOE_FMT_CB2 = 3, MOE_FMT_CB3 = 4 } moe_fmt;
+#define MOE_LAYOUT_PLANAR 0x100   /* OR-ed into moe_layer.fmt_gate_up / fmt_down: planar rows */
 
 typedef enum {
   MOE_OK = 0,
@@ -87,8 +94,8 @@ typedef enum {
 /* One MoE layer's experts. Host struct, read during the call only. */
 typedef struct moe_layer {
   int32_t n_embd, n_ff, n_experts;
-  int32_t fmt_gate_up;           /* format of gate and up (moe_fmt) */
-  int32_t fmt_down;              /* format of down */
+  int32_t fmt_gate_up;           /* format of gate and up (moe_fmt, | MOE_LAYOUT_PLANAR) */
+  int32_t fmt_down;              /* format of down (moe_fmt, | MOE_LAYOUT_PLANAR) */
   const void* const* gate;       /* device array [n_experts] of device pointers: n_ff x n_embd */
   const void* const* up;         /* same */
   const void* const* down;       /* device array [n_experts]: n_embd x n_ff */
@@ -109,6 +116,20 @@ typedef struct moe_plan {
   float* ent_w;                  /* router weight of each entry */
   uint32_t* err;                 /* device sticky error bits (MOE_ERR_*) */
 } moe_plan;
+
+/* One-time weight repack ("#2058 ...", "Risks / limits": the weight-side loads of the blocks were
+ * left as the next step; "#3455 [Engine] GP100 (sm_60): 4-bit slots ...", "Problem and result" and
+ * "Approach": resident experts are transcoded once at load into a layout the decode kernels read,
+ * with the arithmetic order unchanged so the outputs keep their bits, and the original blocks are
+ * rebuilt from it and compared byte for byte). Here the layout is the planar one above, of the same
+ * size. rows x cols weights of base format fmt (moe_fmt, without the layout flag) at src, row-major
+ * when to_planar = 1 (written planar to dst), planar when to_planar = 0 (written row-major);
+ * rows may span several matrices of one shape (a pool of experts). src and dst: device, 2-byte
+ * aligned, not overlapping, rows x row_bytes each. A planar matrix, named with MOE_LAYOUT_PLANAR in
+ * the layer, gives every entry point the same results, bit for bit, as its row-major source.
+ * Errors: MOE_E_ARG (null or misaligned pointer, overlap, rows < 0, to_planar not 0 / 1),
+ * MOE_E_FMT (unknown format or the layout flag set), MOE_E_SHAPE (cols as under "Shapes"). */
+int moe_repack(void* stream, int fmt, const void* src, int64_t rows, int cols, void* dst, int to_planar);
 
 /* Router ("#363 ...": the window's tokens each pick top-k experts). For each of T tokens:
  * softmax over E float32 logits [T][E], the k largest by (logit descending, expert id

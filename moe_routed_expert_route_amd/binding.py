@@ -20,7 +20,7 @@ BLOCK_WEIGHTS = {Q8_0: 32, NL4: 32, CB2: 256, CB3: 256}
 
 ERR_BITS = {1: "NGROUPS", 2: "ENTRIES", 4: "EXPERT", 8: "SRC", 16: "DST", 32: "ALIGN"}
 
-EXPORTS = ("moe_route_topk", "moe_build_plan", "moe_quantize_q8_1", "moe_gate_up",
+EXPORTS = ("moe_route_topk", "moe_build_plan", "moe_quantize_q8_1", "moe_repack", "moe_gate_up",
            "moe_swiglu_q8_1", "moe_down_scatter", "moe_workspace_bytes",
            "moe_layer_decode", "moe_layer_decode_routed", "moe_layer_step", "moe_layer_gate_up",
            "moe_layer_down",
@@ -54,6 +54,7 @@ def lib():
         L.moe_route_topk.argtypes = [_P, _P, _I, _I, _I, _P, _P]
         L.moe_build_plan.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.POINTER(MoePlan)]
         L.moe_quantize_q8_1.argtypes = [_P, _P, _I, _I, _P]
+        L.moe_repack.argtypes = [_P, _I, _P, ctypes.c_int64, _I, _P, _I]
         L.moe_gate_up.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan), _P, _I, _P,
                                   _P, _I, _I]
         L.moe_swiglu_q8_1.argtypes = [_P, ctypes.POINTER(MoePlan), _P, _P, _I, _I, _P, _P]
@@ -203,6 +204,18 @@ class Plan:
 
 
 # ------------------------------------------------------------------ entry points --------------
+
+LAYOUT_PLANAR = 0x100   # OR-ed into a layer's format field: planar rows (see moe_repack)
+
+
+def moe_repack(fmt, src, rows, cols, dst=None, to_planar=True, stream=None):
+    """rows x cols weights of base format `fmt` (uint8 device tensor `src`) into the planar layout
+    (to_planar) or back into the row-major one; returns dst (a new tensor unless given)."""
+    dst = dst if dst is not None else torch.empty_like(src)
+    _check(lib().moe_repack(_stream(stream), int(fmt), _ptr(src), int(rows), int(cols), _ptr(dst),
+                            1 if to_planar else 0), "moe_repack")
+    return dst
+
 
 def moe_route_topk(logits, k, ids=None, w=None, stream=None):
     T, E = logits.shape

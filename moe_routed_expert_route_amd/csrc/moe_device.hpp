@@ -193,6 +193,31 @@ __device__ __forceinline__ uint32_t apply_sign(uint32_t mag, uint32_t nib) {
 }
 
 
+// Where a row's fields sit: for block b of the row (b = u for Q8_0 / NL4, u / 8 for CB2 / CB3) the
+// fp16 scale at d_a b + d_b, the codes at c_a b + c_b and (CB2 / CB3) the packed sub-scales at
+// x_a b + x_b, byte offsets from the row's start. The row-major layout interleaves them block by
+// block; the planar layout (same bytes per row) puts every block's codes first, then the scales.
+struct Lay {
+  uint32_t d_a, d_b, c_a, c_b, x_a, x_b;
+};
+
+__host__ __device__ constexpr int block_bytes(int fmt) {
+  return fmt == Q8_0 ? 34 : fmt == NL4 ? 18 : fmt == CB2 ? 70 : fmt == CB3 ? 110 : 0;
+}
+__host__ __device__ constexpr int block_weights(int fmt) {
+  return (fmt == CB2 || fmt == CB3) ? 256 : 32;
+}
+// Code bytes of one block: the block minus its fp16 scale and (CB2 / CB3) its 4 sub-scale bytes.
+__host__ __device__ constexpr int code_bytes(int fmt) {
+  return (fmt == CB2 || fmt == CB3) ? block_bytes(fmt) - 6 : block_bytes(fmt) - 2;
+}
+// The field map of a row of nblk blocks in either layout.
+__host__ __device__ inline Lay make_lay(int fmt, int nblk, bool planar) {
+  const uint32_t B = (uint32_t)block_bytes(fmt), C = (uint32_t)code_bytes(fmt), n = (uint32_t)nblk;
+  if (!planar) return Lay{B, 0u, B, 2u, B, B - 4u};
+  return Lay{B - C, C * n, C, 0u, B - C, C * n + 2u};
+}
+
 // A weight unit (32 weights, u = 32-weight index inside its row) is read from LDS in two steps so
 // that the reads of the next unit can be in flight while this one is decoded: unit_load issues the
 // aligned dword reads covering the unit's fields, unit_decode turns them into codes. c[k] holds the
@@ -202,45 +227,45 @@ struct URaw {
   // Q8_0: scale pair, 9 quant dwords; NL4: scale pair, 5 nibble dwords; CB2: D, index, sign and
   // sub-scale pairs; CB3: D, two index pairs, high-bit, sign and sub-scale pairs
   uint32_t v[FMT == Q8_0 ? 11 : FMT == NL4 ? 7 : FMT == CB2 ? 8 : 12];
-  uint32_t o;   // byte offset of the unit (Q8_0, NL4) or of its 256-weight block (CB2, CB3)
+  uint32_t od, oc, ox;   // byte offsets of the block's scale, codes and (CB2 / CB3) sub-scales
 };
 
 template <int FMT>
-__device__ __forceinline__ void unit_load(const MOE_LDS uint32_t* W, uint32_t row, int u, URaw<FMT>& r) {
+__device__ __forceinline__ void unit_load(const MOE_LDS uint32_t* W, uint32_t row, int u, const Lay& ly,
+                                          URaw<FMT>& r) {
   auto pair = [&](int j, uint32_t off) {
     r.v[2 * j] = W[off >> 2];
     r.v[2 * j + 1] = W[(off >> 2) + 1];
   };
-  if constexpr (FMT == Q8_0) {
-    const uint32_t o = row + 34u * (uint32_t)u;
-    r.o = o;
-    pair(0, o);
-    const uint32_t b = (o + 2) >> 2;
+  if constexpr (FMT == Q8_0 || FMT == NL4) {
+    const uint32_t b = (uint32_t)u;
+    r.od = row + ly.d_a * b + ly.d_b;
+    r.oc = row + ly.c_a * b + ly.c_b;
+    r.ox = 0;
+    pair(0, r.od);
+    const uint32_t c = r.oc >> 2;
 #pragma unroll
-    for (int i = 0; i < 9; ++i) r.v[2 + i] = W[b + i];
-  } else if constexpr (FMT == NL4) {
-    const uint32_t o = row + 18u * (uint32_t)u;
-    r.o = o;
-    pair(0, o);
-    const uint32_t b = (o + 2) >> 2;
-#pragma unroll
-    for (int i = 0; i < 5; ++i) r.v[2 + i] = W[b + i];
+    for (int i = 0; i < (FMT == Q8_0 ? 9 : 5); ++i) r.v[2 + i] = W[c + i];
   } else if constexpr (FMT == CB2) {
-    const uint32_t so = row + 70u * (uint32_t)(u >> 3), su = (uint32_t)u & 7u;
-    r.o = so;
-    pair(0, so);
-    pair(1, so + 2 + 4 * su);
-    pair(2, so + 34 + 4 * su);
-    pair(3, so + 66);
+    const uint32_t b = (uint32_t)u >> 3, su = (uint32_t)u & 7u;
+    r.od = row + ly.d_a * b + ly.d_b;
+    r.oc = row + ly.c_a * b + ly.c_b;
+    r.ox = row + ly.x_a * b + ly.x_b;
+    pair(0, r.od);
+    pair(1, r.oc + 4 * su);
+    pair(2, r.oc + 32 + 4 * su);
+    pair(3, r.ox);
   } else {  // CB3
-    const uint32_t so = row + 110u * (uint32_t)(u >> 3), su = (uint32_t)u & 7u;
-    r.o = so;
-    pair(0, so);
-    pair(1, so + 2 + 8 * su);
-    pair(2, so + 6 + 8 * su);
-    pair(3, so + 66 + su);
-    pair(4, so + 74 + 4 * su);
-    pair(5, so + 106);
+    const uint32_t b = (uint32_t)u >> 3, su = (uint32_t)u & 7u;
+    r.od = row + ly.d_a * b + ly.d_b;
+    r.oc = row + ly.c_a * b + ly.c_b;
+    r.ox = row + ly.x_a * b + ly.x_b;
+    pair(0, r.od);
+    pair(1, r.oc + 8 * su);
+    pair(2, r.oc + 4 + 8 * su);
+    pair(3, r.oc + 64 + su);
+    pair(4, r.oc + 72 + 4 * su);
+    pair(5, r.ox);
   }
 }
 
@@ -249,13 +274,13 @@ __device__ __forceinline__ void unit_decode(const URaw<FMT>& r, int u, const Tab
   // the dword at byte offset off of a pair read from off & ~3
   auto at = [&](int j, uint32_t off) { return __builtin_amdgcn_alignbyte(r.v[2 * j + 1], r.v[2 * j], off & 3u); };
   if constexpr (FMT == Q8_0) {
-    sc = h2f(at(0, r.o) & 0xFFFFu);
-    const uint32_t sh = (r.o + 2) & 3u;
+    sc = h2f(at(0, r.od) & 0xFFFFu);
+    const uint32_t sh = r.oc & 3u;
 #pragma unroll
     for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_alignbyte(r.v[3 + k], r.v[2 + k], sh);
   } else if constexpr (FMT == NL4) {
-    sc = h2f(at(0, r.o) & 0xFFFFu);
-    const uint32_t sh = (r.o + 2) & 3u;
+    sc = h2f(at(0, r.od) & 0xFFFFu);
+    const uint32_t sh = r.oc & 3u;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t n = __builtin_amdgcn_alignbyte(r.v[3 + k], r.v[2 + k], sh);
@@ -263,11 +288,11 @@ __device__ __forceinline__ void unit_decode(const URaw<FMT>& r, int u, const Tab
       c[k + 4] = lut16(n >> 4, tb);   // weights 16+4k..16+4k+3 (high nibbles)
     }
   } else if constexpr (FMT == CB2) {
-    const uint32_t so = r.o, su = (uint32_t)u & 7u;
-    const float D = h2f(at(0, so) & 0xFFFFu);
-    const uint32_t idx4 = at(1, so + 2);
-    const uint32_t sg4 = at(2, so + 34);
-    const uint32_t s = (at(3, so + 66) >> (4 * su)) & 15u;
+    const uint32_t su = (uint32_t)u & 7u;
+    const float D = h2f(at(0, r.od) & 0xFFFFu);
+    const uint32_t idx4 = at(1, r.oc + 4 * su);
+    const uint32_t sg4 = at(2, r.oc + 32 + 4 * su);
+    const uint32_t s = (at(3, r.ox) >> (4 * su)) & 15u;
     sc = D * (float)(2 * s + 1);
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
@@ -277,13 +302,13 @@ __device__ __forceinline__ void unit_decode(const URaw<FMT>& r, int u, const Tab
       c[2 * gq + 1] = apply_sign(tb.cb2[2 * idx + 1], sg >> 4);
     }
   } else {  // CB3
-    const uint32_t so = r.o, su = (uint32_t)u & 7u;
-    const float D = h2f(at(0, so) & 0xFFFFu);
-    const uint32_t lo0 = at(1, so + 2);
-    const uint32_t lo1 = at(2, so + 6);
-    const uint32_t hib = at(3, so + 66 + su);
-    const uint32_t sg4 = at(4, so + 74);
-    const uint32_t s = (at(5, so + 106) >> (4 * su)) & 15u;
+    const uint32_t su = (uint32_t)u & 7u;
+    const float D = h2f(at(0, r.od) & 0xFFFFu);
+    const uint32_t lo0 = at(1, r.oc + 8 * su);
+    const uint32_t lo1 = at(2, r.oc + 4 + 8 * su);
+    const uint32_t hib = at(3, r.oc + 64 + su);
+    const uint32_t sg4 = at(4, r.oc + 72 + 4 * su);
+    const uint32_t s = (at(5, r.ox) >> (4 * su)) & 15u;
     sc = D * (float)(2 * s + 1);
 #pragma unroll
     for (int gq = 0; gq < 8; ++gq) {
@@ -292,13 +317,6 @@ __device__ __forceinline__ void unit_decode(const URaw<FMT>& r, int u, const Tab
       c[gq] = apply_sign(tb.cb3[idx], (sg4 >> (4 * gq)) & 15u);
     }
   }
-}
-
-__host__ __device__ constexpr int block_bytes(int fmt) {
-  return fmt == Q8_0 ? 34 : fmt == NL4 ? 18 : fmt == CB2 ? 70 : fmt == CB3 ? 110 : 0;
-}
-__host__ __device__ constexpr int block_weights(int fmt) {
-  return (fmt == CB2 || fmt == CB3) ? 256 : 32;
 }
 
 }  // namespace moe

@@ -90,6 +90,7 @@ struct Geom {
   int upl;    // units per lane, ceil(U / L)
   int rb;     // bytes per row
   int rp;     // rows per wave pass (64 / L)
+  Lay ly;     // where a row's scales and codes sit (row-major or planar)
 };
 
 // Per-wave stream: NS slots of M KB each.
@@ -537,16 +538,16 @@ __device__ __forceinline__ void dot_pass_n(const MOE_LDS uint32_t* W, uint32_t r
       }
     };
     URaw<FMT> r0, r1;
-    unit_load<FMT>(W, row, unit_at(0), r0);
+    unit_load<FMT>(W, row, unit_at(0), G.ly, r0);
     // (landed before the loop: the loop is entered with no read of r0 in flight, as it leaves
     // each trip, so the waits inside it count only the reads issued in the trip)
     MOE_WAIT_LGKM0;
     for (int k = 0; k < G.upl; k += 2) {
-      unit_load<FMT>(W, row, unit_at(k + 1), r1);
+      unit_load<FMT>(W, row, unit_at(k + 1), G.ly, r1);
       __builtin_amdgcn_sched_barrier(0);
       step(r0, k);
       if (k + 1 < G.upl) {
-        unit_load<FMT>(W, row, unit_at(k + 2), r0);
+        unit_load<FMT>(W, row, unit_at(k + 2), G.ly, r0);
         __builtin_amdgcn_sched_barrier(0);
         step(r1, k + 1);
       }
@@ -2162,6 +2163,48 @@ __global__ __launch_bounds__(kThreads) void k_swiglu(PlanArgs P, const float* __
   }
 }
 
+// ------------------------------------------------------------------ weight repack -----------
+
+// Byte offset in a row-major row of the byte at offset p of the same row in planar layout (p even:
+// every field of both layouts starts at an even offset and has an even length).
+template <int FMT>
+__device__ __forceinline__ uint32_t planar_src(uint32_t nblk, uint32_t p) {
+  constexpr uint32_t B = block_bytes(FMT), C = code_bytes(FMT), S = B - C;
+  if (p < C * nblk) {
+    const uint32_t b = p / C;
+    return B * b + 2u + (p - C * b);
+  }
+  const uint32_t q = p - C * nblk, b = q / S, r = q - S * b;
+  return r < 2u ? B * b + r : B * b + (B - 4u) + (r - 2u);
+}
+// The inverse: offset in the planar row of byte p of the row-major row.
+template <int FMT>
+__device__ __forceinline__ uint32_t rowmajor_src(uint32_t nblk, uint32_t p) {
+  constexpr uint32_t B = block_bytes(FMT), C = code_bytes(FMT);
+  const uint32_t b = p / B, r = p - B * b;
+  if (r < 2u) return C * nblk + (B - C) * b + r;
+  if (B - C == 6u && r >= B - 4u) return C * nblk + 6u * b + 2u + (r - (B - 4u));
+  return C * b + (r - 2u);
+}
+
+// One row per workgroup at a time, two bytes per lane: every output half-word is gathered from
+// its place in the source row (the row, at most 8.5 KB, stays in cache while its workgroup
+// reads it).
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_repack(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                     long rows, int rb, int nblk, int to_planar) {
+  const int nh = rb >> 1;
+  for (long r = blockIdx.x; r < rows; r += gridDim.x) {
+    const uint16_t* s = src + r * nh;
+    uint16_t* d = dst + r * nh;
+    for (int i = threadIdx.x; i < nh; i += kThreads) {
+      const uint32_t p = 2u * (uint32_t)i;
+      const uint32_t q = to_planar ? planar_src<FMT>((uint32_t)nblk, p) : rowmajor_src<FMT>((uint32_t)nblk, p);
+      d[i] = s[q >> 1];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host side ---------------
 
 thread_local std::string t_last_error;
@@ -2171,9 +2214,13 @@ int hip_fail(hipError_t e, const char* what) {
   return MOE_E_HIP;
 }
 
-bool fmt_ok(int f) { return f >= Q8_0 && f <= CB3; }
+// A layer's format field: the encoding (moe_fmt) with MOE_LAYOUT_PLANAR optionally OR-ed in.
+int base_fmt(int f) { return f & ~MOE_LAYOUT_PLANAR; }
+bool is_planar(int f) { return (f & MOE_LAYOUT_PLANAR) != 0; }
+bool fmt_ok(int f) { return base_fmt(f) >= Q8_0 && base_fmt(f) <= CB3; }
 
 bool cols_ok(int fmt, int n) {
+  fmt = base_fmt(fmt);
   if (n <= 0 || n > MOE_MAX_DIM) return false;
   return (fmt == CB2 || fmt == CB3) ? n % 256 == 0 : n % 64 == 0;
 }
@@ -2189,10 +2236,12 @@ int ilog2(int v) {
 // L <= 32 (a pass holds gate and up rows of rp / 2 h rows), ties to the smaller L (longer items);
 // down: ties to the larger L (more, smaller row tiles), except that one whose pass holds a whole
 // tile of rows_hint rows is kept over those that need two passes.
-Geom make_geom(int fmt, int ncols, bool gate_up, int rows_hint = 0) {
+Geom make_geom(int fmt_field, int ncols, bool gate_up, int rows_hint = 0) {
+  const int fmt = base_fmt(fmt_field);
   Geom G{};
   G.U = ncols / 32;
   G.rb = ncols / block_weights(fmt) * block_bytes(fmt);
+  G.ly = make_lay(fmt, ncols / block_weights(fmt), is_planar(fmt_field));
   const int Lmax = gate_up ? 32 : 64;
   int bestL = Lmax;
   double best = -1.0;
@@ -2272,9 +2321,10 @@ int check_layer(const moe_layer* L, bool need_down) {
   if (!fmt_ok(L->fmt_gate_up) || !fmt_ok(L->fmt_down)) return MOE_E_FMT;
   if (L->n_experts <= 0) return MOE_E_ARG;
   if (!cols_ok(L->fmt_gate_up, L->n_embd) || !cols_ok(L->fmt_down, L->n_ff)) return MOE_E_SHAPE;
-  const bool nl4 = L->fmt_gate_up == NL4 || L->fmt_down == NL4;
-  const bool cb2 = L->fmt_gate_up == CB2 || L->fmt_down == CB2;
-  const bool cb3 = L->fmt_gate_up == CB3 || L->fmt_down == CB3;
+  const int fg = base_fmt(L->fmt_gate_up), fd = base_fmt(L->fmt_down);
+  const bool nl4 = fg == NL4 || fd == NL4;
+  const bool cb2 = fg == CB2 || fd == CB2;
+  const bool cb3 = fg == CB3 || fd == CB3;
   if ((nl4 && !L->nl4_table) || (cb2 && !L->cb2_grid) || (cb3 && !L->cb3_grid)) return MOE_E_ARG;
   return MOE_OK;
 }
@@ -2493,7 +2543,7 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
     ga.ctr = (uint32_t*)(ws + kCtrOff);
     ga.spin_limit = 1 << 22;
   }
-  const hipError_t e = launch_gu(L->fmt_gate_up, L->fmt_down, mode, ga, grid, bytes, st);
+  const hipError_t e = launch_gu(base_fmt(L->fmt_gate_up), base_fmt(L->fmt_down), mode, ga, grid, bytes, st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "gate/up kernel");
 }
 
@@ -2531,7 +2581,7 @@ int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, co
   da.ntiles = (L->n_embd + tr - 1) / tr;
   const int tiles = (L->n_embd + tr - 1) / tr;
   const int grid = grid_for(tiles, bytes, grid_limit);
-  const hipError_t e = launch_dn(L->fmt_down, mode, da, grid, bytes, st);
+  const hipError_t e = launch_dn(base_fmt(L->fmt_down), mode, da, grid, bytes, st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "down kernel");
 }
 
@@ -2567,6 +2617,30 @@ int moe_quantize_q8_1(void* stream, const float* x, int rows, int n, void* q) {
                      (uint8_t*)q);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_quantize_q8_1");
+}
+
+int moe_repack(void* stream, int fmt, const void* src, int64_t rows, int cols, void* dst, int to_planar) {
+  if (!src || !dst || rows < 0 || (to_planar != 0 && to_planar != 1)) return MOE_E_ARG;
+  if (!fmt_ok(fmt) || is_planar(fmt)) return MOE_E_FMT;
+  if (!cols_ok(fmt, cols)) return MOE_E_SHAPE;
+  if (((uintptr_t)src & 1) || ((uintptr_t)dst & 1)) return MOE_E_ARG;
+  const int rb = cols / block_weights(fmt) * block_bytes(fmt);
+  const uintptr_t a0 = (uintptr_t)src, b0 = (uintptr_t)dst, n = (uintptr_t)rows * (uintptr_t)rb;
+  if (rows && a0 < b0 + n && b0 < a0 + n) return MOE_E_ARG;   // the two must not overlap
+  if (rows == 0) return MOE_OK;
+  const int grid = (int)std::min<int64_t>(rows, 8192);
+  const int nblk = cols / block_weights(fmt);
+  const hipStream_t st = (hipStream_t)stream;
+  const uint16_t* s = (const uint16_t*)src;
+  uint16_t* d = (uint16_t*)dst;
+  switch (fmt) {
+    case Q8_0: hipLaunchKernelGGL(k_repack<Q8_0>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
+    case NL4: hipLaunchKernelGGL(k_repack<NL4>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
+    case CB2: hipLaunchKernelGGL(k_repack<CB2>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
+    default: hipLaunchKernelGGL(k_repack<CB3>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
+  }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_repack");
 }
 
 int moe_route_topk(void* stream, const float* logits, int T, int E, int k, int32_t* ids, float* w) {

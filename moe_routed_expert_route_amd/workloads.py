@@ -110,6 +110,38 @@ class Workload:
         self.ws = [B.workspace(self.layers[l], self.plans[l], device=d) for l in range(L)]
         self.pool_bytes = L * E * (2 * self.sz_g + self.sz_d)
 
+    def to_planar(self):
+        """Repack every pool (all experts of every layer) into the planar layout with moe_repack,
+        one pool at a time, and point the layers at the repacked pools with their format fields
+        flagged planar. Returns (seconds of repack kernels, bytes read)."""
+        d = self.pool_g[0].device
+        nl4, cb2, cb3 = self._tabs
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ms, nbytes = 0.0, 0
+        for l in range(self.L):
+            pools = []
+            for pool, fmt, rows, cols in ((self.pool_g, self.fg, self.E * self.n_ff, self.n_embd),
+                                          (self.pool_u, self.fg, self.E * self.n_ff, self.n_embd),
+                                          (self.pool_d, self.fd, self.E * self.n_embd, self.n_ff)):
+                dst = torch.empty_like(pool[l])
+                ev0.record()
+                B.moe_repack(fmt, pool[l], rows, cols, dst=dst, to_planar=True)
+                ev1.record()
+                torch.cuda.synchronize()
+                ms += ev0.elapsed_time(ev1)
+                nbytes += pool[l].numel()
+                pool[l] = dst
+                pools.append(dst)
+            pg, pu, pd = pools
+            i64 = dict(dtype=torch.int64, device=d)
+            ptr_g = torch.tensor([pg.data_ptr() + e * self.sz_g for e in range(self.E)], **i64)
+            ptr_u = torch.tensor([pu.data_ptr() + e * self.sz_g for e in range(self.E)], **i64)
+            ptr_d = torch.tensor([pd.data_ptr() + e * self.sz_d for e in range(self.E)], **i64)
+            self.layers[l] = B.Layer.from_pointers(
+                self.n_embd, self.n_ff, self.fg | B.LAYOUT_PLANAR, self.fd | B.LAYOUT_PLANAR,
+                ptr_g, ptr_u, ptr_d, nl4=nl4, cb2=cb2, cb3=cb3, keep=(pg, pu, pd))
+        return ms * 1e-3, nbytes
+
     # ---------------------------------------------------------------- the step ----------------
     def route_plan(self, l, stream=None):
         B.moe_route_topk(self.d_logits[l], self.k, ids=self.ids[l], w=self.w[l], stream=stream)

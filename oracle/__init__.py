@@ -113,6 +113,32 @@ def row_bytes(fmt: int, ncols: int) -> int:
 
 # ------------------------------------------------------------------ quantizers ----------------
 
+def repack(fmt: int, mat, rows: int, ncols: int, to_planar: bool = True) -> np.ndarray:
+    """The planar layout of a weight matrix, or back ("#3455 [Engine] GP100 (sm_60): 4-bit slots
+    ...", "Approach": a load-time rewrite of the resident blocks that the decode reads, rebuilt and
+    compared byte for byte). Per row: the row-major row is its blocks one after another; each block
+    is its fp16 scale (2 bytes), its code bytes, and for CB2 / CB3 the 4 sub-scale bytes at its end.
+    The planar row is every block's code bytes in block order, then every block's scale bytes (the
+    fp16 scale, then for CB2 / CB3 the sub-scale bytes) in block order. Same bytes, same size."""
+    B, W = _BLOCK_BYTES[fmt], _BLOCK_W[fmt]
+    tail = 4 if fmt in (CB2, CB3) else 0   # sub-scale bytes at the end of a block
+    nb = ncols // W
+    m = np.asarray(mat, np.uint8).reshape(rows, nb * B)
+    out = np.empty_like(m)
+    ncode = B - 2 - tail
+    for r in range(rows):
+        if to_planar:
+            blocks = m[r].reshape(nb, B)
+            codes = blocks[:, 2:2 + ncode]
+            scales = np.concatenate([blocks[:, :2], blocks[:, 2 + ncode:]], axis=1)
+            out[r] = np.concatenate([codes.reshape(-1), scales.reshape(-1)])
+        else:
+            codes = m[r, :nb * ncode].reshape(nb, ncode)
+            scales = m[r, nb * ncode:].reshape(nb, 2 + tail)
+            out[r] = np.concatenate([scales[:, :2], codes, scales[:, 2:]], axis=1).reshape(-1)
+    return out.reshape(-1)
+
+
 def quantize_q8_1(x) -> np.ndarray:
     """q8_1 blocks of the last axis (length a multiple of 32); returns uint8 [..., n/32*36]."""
     x = _c(x, np.float32)

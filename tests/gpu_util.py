@@ -58,6 +58,29 @@ class Case:
             keep=(zg, zd, self.dg, self.du, self.dd))
 
 
+def planar_twin(c):
+    """The same case with every expert matrix repacked on the device (moe_repack) into the planar
+    layout and the layer's format fields flagged planar; host weights stay row-major."""
+    import copy
+    p = copy.copy(c)
+    d = dev()
+    zg = torch.zeros(synth.row_bytes(c.fmt_gu, c.n_embd) * c.n_ff, dtype=torch.uint8, device=d)
+    zd = torch.zeros(synth.row_bytes(c.fmt_dn, c.n_ff) * c.n_embd, dtype=torch.uint8, device=d)
+    p.dg = {e: B.moe_repack(c.fmt_gu, t, c.n_ff, c.n_embd) for e, t in c.dg.items()}
+    p.du = {e: B.moe_repack(c.fmt_gu, t, c.n_ff, c.n_embd) for e, t in c.du.items()}
+    p.dd = {e: B.moe_repack(c.fmt_dn, t, c.n_embd, c.n_ff) for e, t in c.dd.items()}
+    pg = [p.dg[e].data_ptr() if e in p.dg else zg.data_ptr() for e in range(c.E)]
+    pu = [p.du[e].data_ptr() if e in p.du else zg.data_ptr() for e in range(c.E)]
+    pd = [p.dd[e].data_ptr() if e in p.dd else zd.data_ptr() for e in range(c.E)]
+    t64 = dict(dtype=torch.int64, device=d)
+    L = c.layer
+    p.layer = B.Layer.from_pointers(
+        c.n_embd, c.n_ff, c.fmt_gu | B.LAYOUT_PLANAR, c.fmt_dn | B.LAYOUT_PLANAR,
+        torch.tensor(pg, **t64), torch.tensor(pu, **t64), torch.tensor(pd, **t64),
+        nl4=L.nl4, cb2=L.cb2, cb3=L.cb3, keep=(zg, zd, p.dg, p.du, p.dd))
+    return p
+
+
 def routed_case(name, n_embd, n_ff, E, k, T, fmt_gu, fmt_dn, key, ids=None):
     """Logits routed on the host by the oracle only to know which experts to generate."""
     if ids is None:

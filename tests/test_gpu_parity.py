@@ -214,6 +214,46 @@ def test_two_calls_per_layer(name):
     del g
 
 
+@pytest.mark.parametrize("fmt,ncols", [(Q8_0, 256), (NL4, 192), (CB2, 768), (CB3, 512), (NL4, 2560)])
+def test_repack_bytes(fmt, ncols):
+    """moe_repack against the oracle's planar layout, byte for byte, and back."""
+    rows = 37
+    rb = synth.row_bytes(fmt, ncols)
+    m = synth.rng(62, fmt, ncols).integers(0, 256, size=rows * rb, dtype=np.uint8)
+    src = torch.from_numpy(m).to(U.dev())
+    p = B.moe_repack(fmt, src, rows, ncols, to_planar=True)
+    back = B.moe_repack(fmt, p, rows, ncols, to_planar=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(p.cpu().numpy(), oracle.repack(fmt, m, rows, ncols, True))
+    assert np.array_equal(back.cpu().numpy(), m)
+
+
+@pytest.mark.parametrize("name", ["small_q8", "nl4_t1", "cb2_nl4_t4_zipf", "cb3_q8_t2", "nl4_cb2_t2",
+                                  "cb2_cb3_t4"])
+def test_planar_layer_same_bits(name):
+    """Experts repacked into the planar layout give the row-major layer's bits on every path:
+    composed (g, u, h, q8_1 of h, Y), fused, routed in two launches, and the one-launch step."""
+    c = _routed(name, key=6)
+    pc = U.planar_twin(c)
+    T, k = c.T, c.k
+    base, n_rows = 2, 8
+    dst = synth.rng(42, T).choice(n_rows, T, replace=False).astype(np.int32)
+    plan, _, _ = U.gpu_route_and_plan(c, T * k, T * k, entry_base=base, dst_of_token=dst)
+    Y0 = U.y0_for(n_rows, c.n_embd, dst, 3)
+    ref = U.run_composed(c, plan, c.x, Y0, n_rows)
+    got = U.run_composed(pc, plan, c.x, Y0, n_rows)
+    assert ref["err"] == 0 and got["err"] == 0
+    for key in ("g", "u", "h", "Y"):
+        assert np.array_equal(U.bits(got[key]), U.bits(ref[key])), key
+    assert np.array_equal(got["hq"], ref["hq"])
+    f = U.run_fused(pc, plan, c.x, Y0)
+    assert f["err"] == 0 and np.array_equal(U.bits(f["Y"]), U.bits(ref["Y"]))
+    r = U.run_routed(pc, c.x, Y0, entry_base=base, dst_of_token=dst)
+    assert r["err"] == 0 and np.array_equal(U.bits(r["Y"]), U.bits(ref["Y"]))
+    r3 = U.run_routed(pc, c.x, Y0, entry_base=base, dst_of_token=dst, step=True)
+    assert r3["err"] == 0 and np.array_equal(U.bits(r3["Y"]), U.bits(ref["Y"]))
+
+
 @pytest.mark.parametrize("name", ["nl4_t1", "cb2_nl4_t4_zipf"])
 def test_grid_invariance(name):
     c = _routed(name, key=2)
