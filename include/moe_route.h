@@ -40,6 +40,10 @@
  *                       bits (group g: bit g%8 of byte g/8), [74:106] sign bits (weight i: bit i%8
  *                       of byte i/8), [106:110] sub-scales as CB2; code = +-G3[idx][j], G3 = 512 x 4
  *                       uint8 grid (cb3_grid); w = D (2 s_b + 1) code.
+ *   Q5_1  24 B / 32 w : [0:2] fp16 d, [2:4] fp16 m, [4:8] high bits (bit i of the little-endian
+ *                       word = bit 4 of code i), [8:24] b[16]; code of w_i = (b[i] & 15) | high
+ *                       bit i, of w_(i+16) = (b[i] >> 4) | high bit i+16; w = d * code + m (an
+ *                       offset format; down matrices only: fmt_gate_up rejects it).
  *   q8_1  36 B / 32 values (activations): [0:2] fp16 d, [2:4] fp16 s, [4:36] int8 q[32], with
  *         amax = max|x|, d = amax / 127 (float32), q = clamp(round-half-away(x / d), +-127)
  *         (0 if amax == 0), d16 = fp16(d), s16 = fp16(f(d16) * sum q), all IEEE float32.
@@ -47,13 +51,15 @@
  * Planar layout (MOE_LAYOUT_PLANAR OR-ed into a moe_layer format field): the same bytes per row,
  * reordered so that the codes of the row's n blocks come first, block after block (Q8_0 32 B,
  * NL4 16 B, CB2 the 64 index and sign bytes, CB3 the 104 low-index, high-bit and sign bytes,
- * each in its row-major order), then the scales, block after block (Q8_0 / NL4 the fp16 d; CB2 /
- * CB3 the fp16 D followed by the 4 sub-scale bytes). A row keeps its size and a matrix its rows,
+ * Q5_1 the 20 high-bit and nibble bytes, each in its row-major order), then the scales, block
+ * after block (Q8_0 / NL4 the fp16 d; Q5_1 d then m; CB2 / CB3 the fp16 D followed by the 4
+ * sub-scale bytes). A row keeps its size and a matrix its rows,
  * so every pointer and size of the row-major layout holds; moe_repack converts either way.
  * Shapes: C must be a multiple of 64 for Q8_0 / NL4 and of 256 for CB2 / CB3; n_embd and n_ff
  * at most MOE_MAX_DIM.
- * Block contribution: c_b = scale_w * f(d_x) * sum_j code_j q_j (exact int32 sum); a row's dot
- * product is the sum of its c_b.
+ * Block contribution: c_b = scale_w * f(d_x) * sum_j code_j q_j (exact int32 sum), plus for Q5_1
+ * m * f(s_x): the offset times the block's activation sum, read from the q8_1 sum field (the one
+ * consumer of that field); a row's dot product is the sum of its c_b.
  */
 #ifndef MOE_ROUTE_H
 #define MOE_ROUTE_H
@@ -69,7 +75,10 @@ extern "C" {
 #define MOE_MAX_CALL_ENTRIES 64   /* max cap_entries (T x k) of one call */
 #define MOE_MAX_GROUPS 64         /* max cap_groups of one call */
 
-typedef enum { MOE_FMT_Q8_0 = 1, MOE_FMT_NL4 = 2, MOE_FMT_CB2 = 3, MOE_FMT_CB3 = 4 } moe_fmt;
+typedef enum {
+  MOE_FMT_Q8_0 = 1, MOE_FMT_NL4 = 2, MOE_FMT_CB2 = 3, MOE_FMT_CB3 = 4,
+  MOE_FMT_Q5_1 = 5   /* down only */
+} moe_fmt;
 #define MOE_LAYOUT_PLANAR 0x100   /* OR-ed into moe_layer.fmt_gate_up / fmt_down: planar rows */
 
 typedef enum {
@@ -227,7 +236,8 @@ int moe_layer_down(void* stream, const moe_layer* L, const moe_plan* P, const vo
 /* Host: where the last single-call step left the q8_1 rows of h inside the workspace, in split
  * form (row = entry - grp_start[0], n_ff/32 blocks per row, cap_entries rows): off[0] the 16-byte
  * low halves of the blocks' quants (quants 0-15), off[1] the high halves (16-31), off[2] the
- * blocks' scales as float32 (the fp16 d widened exactly). */
+ * blocks' scales as float32 (the fp16 d widened exactly). When the down format is Q5_1 the
+ * blocks' sum fields (fp16 s widened) follow the scales, 256-byte aligned. */
 int moe_workspace_layout(const moe_layer* L, const moe_plan* P, size_t off[3]);
 
 const char* moe_status_string(int status);   /* host, static string */

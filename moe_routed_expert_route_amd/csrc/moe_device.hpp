@@ -24,7 +24,7 @@ namespace moe {
 constexpr int kThreads = 256;          // every kernel runs 4 waves of 64
 constexpr int kMaxSlots = 4;           // entries staged at once (a group's rows of the window)
 
-enum Fmt : int { Q8_0 = 1, NL4 = 2, CB2 = 3, CB3 = 4 };
+enum Fmt : int { Q8_0 = 1, NL4 = 2, CB2 = 3, CB3 = 4, Q5_1 = 5 };
 
 // ------------------------------------------------------------------ binary16 ----------------
 
@@ -202,20 +202,24 @@ struct Lay {
 };
 
 __host__ __device__ constexpr int block_bytes(int fmt) {
-  return fmt == Q8_0 ? 34 : fmt == NL4 ? 18 : fmt == CB2 ? 70 : fmt == CB3 ? 110 : 0;
+  return fmt == Q8_0 ? 34 : fmt == NL4 ? 18 : fmt == CB2 ? 70 : fmt == CB3 ? 110 : fmt == Q5_1 ? 24 : 0;
 }
 __host__ __device__ constexpr int block_weights(int fmt) {
   return (fmt == CB2 || fmt == CB3) ? 256 : 32;
 }
-// Code bytes of one block: the block minus its fp16 scale and (CB2 / CB3) its 4 sub-scale bytes.
+// Header bytes of a block before its codes: the fp16 scale (Q5_1: scale and offset).
+__host__ __device__ constexpr int head_bytes(int fmt) { return fmt == Q5_1 ? 4 : 2; }
+// Code bytes of one block: the block minus its header and (CB2 / CB3) its 4 trailing sub-scale
+// bytes.
 __host__ __device__ constexpr int code_bytes(int fmt) {
-  return (fmt == CB2 || fmt == CB3) ? block_bytes(fmt) - 6 : block_bytes(fmt) - 2;
+  return block_bytes(fmt) - head_bytes(fmt) - ((fmt == CB2 || fmt == CB3) ? 4 : 0);
 }
 // The field map of a row of nblk blocks in either layout.
 __host__ __device__ inline Lay make_lay(int fmt, int nblk, bool planar) {
   const uint32_t B = (uint32_t)block_bytes(fmt), C = (uint32_t)code_bytes(fmt), n = (uint32_t)nblk;
-  if (!planar) return Lay{B, 0u, B, 2u, B, B - 4u};
-  return Lay{B - C, C * n, C, 0u, B - C, C * n + 2u};
+  const uint32_t H = (uint32_t)head_bytes(fmt);
+  if (!planar) return Lay{B, 0u, B, H, B, B - 4u};
+  return Lay{B - C, C * n, C, 0u, B - C, C * n + H};
 }
 
 // A weight unit (32 weights, u = 32-weight index inside its row) is read from LDS in two steps so
@@ -226,7 +230,8 @@ template <int FMT>
 struct URaw {
   // Q8_0: scale pair, 9 quant dwords; NL4: scale pair, 5 nibble dwords; CB2: D, index, sign and
   // sub-scale pairs; CB3: D, two index pairs, high-bit, sign and sub-scale pairs
-  uint32_t v[FMT == Q8_0 ? 11 : FMT == NL4 ? 7 : FMT == CB2 ? 8 : 12];
+  // Q5_1: scale and offset pair, 6 dwords of high bits and nibbles
+  uint32_t v[FMT == Q8_0 ? 11 : FMT == NL4 ? 7 : FMT == CB2 ? 8 : FMT == Q5_1 ? 8 : 12];
   uint32_t od, oc, ox;   // byte offsets of the block's scale, codes and (CB2 / CB3) sub-scales
 };
 
@@ -237,7 +242,7 @@ __device__ __forceinline__ void unit_load(const MOE_LDS uint32_t* W, uint32_t ro
     r.v[2 * j] = W[off >> 2];
     r.v[2 * j + 1] = W[(off >> 2) + 1];
   };
-  if constexpr (FMT == Q8_0 || FMT == NL4) {
+  if constexpr (FMT == Q8_0 || FMT == NL4 || FMT == Q5_1) {
     const uint32_t b = (uint32_t)u;
     r.od = row + ly.d_a * b + ly.d_b;
     r.oc = row + ly.c_a * b + ly.c_b;
@@ -245,7 +250,7 @@ __device__ __forceinline__ void unit_load(const MOE_LDS uint32_t* W, uint32_t ro
     pair(0, r.od);
     const uint32_t c = r.oc >> 2;
 #pragma unroll
-    for (int i = 0; i < (FMT == Q8_0 ? 9 : 5); ++i) r.v[2 + i] = W[c + i];
+    for (int i = 0; i < (FMT == Q8_0 ? 9 : FMT == NL4 ? 5 : 6); ++i) r.v[2 + i] = W[c + i];
   } else if constexpr (FMT == CB2) {
     const uint32_t b = (uint32_t)u >> 3, su = (uint32_t)u & 7u;
     r.od = row + ly.d_a * b + ly.d_b;
@@ -269,11 +274,28 @@ __device__ __forceinline__ void unit_load(const MOE_LDS uint32_t* W, uint32_t ro
   }
 }
 
+// mo: the block's additive offset (Q5_1; 0 for the other formats): weight = sc * code + mo.
 template <int FMT>
-__device__ __forceinline__ void unit_decode(const URaw<FMT>& r, int u, const Tables& tb, uint32_t c[8], float& sc) {
+__device__ __forceinline__ void unit_decode(const URaw<FMT>& r, int u, const Tables& tb, uint32_t c[8], float& sc,
+                                            float& mo) {
   // the dword at byte offset off of a pair read from off & ~3
   auto at = [&](int j, uint32_t off) { return __builtin_amdgcn_alignbyte(r.v[2 * j + 1], r.v[2 * j], off & 3u); };
-  if constexpr (FMT == Q8_0) {
+  mo = 0.0f;
+  if constexpr (FMT == Q5_1) {
+    const uint32_t dm = at(0, r.od);
+    sc = h2f(dm & 0xFFFFu);
+    mo = h2f(dm >> 16);
+    const uint32_t sh = r.oc & 3u;
+    const uint32_t qh = __builtin_amdgcn_alignbyte(r.v[3], r.v[2], sh);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t n = __builtin_amdgcn_alignbyte(r.v[4 + k], r.v[3 + k], sh);   // nibbles of weights 4k.., 16+4k..
+      const uint32_t hl = (((qh >> (4 * k)) & 15u) * 0x00204081u) & 0x01010101u;       // bit j -> bit 0 of byte j
+      const uint32_t hh = (((qh >> (16 + 4 * k)) & 15u) * 0x00204081u) & 0x01010101u;
+      c[k] = (n & 0x0F0F0F0Fu) | (hl << 4);              // weights 4k..4k+3
+      c[k + 4] = ((n >> 4) & 0x0F0F0F0Fu) | (hh << 4);   // weights 16+4k..16+4k+3
+    }
+  } else if constexpr (FMT == Q8_0) {
     sc = h2f(at(0, r.od) & 0xFFFFu);
     const uint32_t sh = r.oc & 3u;
 #pragma unroll

@@ -267,6 +267,7 @@ struct ActSplit {
   MOE_LDS u32x4* lo;
   MOE_LDS u32x4* hi;
   MOE_LDS float* d;
+  MOE_LDS float* s;   // the blocks' sum fields f(s16), staged only for a Q5_1 matrix (else null)
   int U;
   __device__ __forceinline__ void get(int r, int u, uint32_t q[8], float& dx) const {
     const u32x4 a = lo[r * U + u], b = hi[r * U + u];
@@ -276,29 +277,34 @@ struct ActSplit {
   }
 };
 
-__device__ __forceinline__ ActSplit act_layout(MOE_LDS uint8_t* p, int rows, int U) {
+// with_s: also a region for the blocks' sum fields (the Q5_1 offset term reads them)
+__device__ __forceinline__ ActSplit act_layout(MOE_LDS uint8_t* p, int rows, int U, bool with_s = false) {
   ActSplit a;
   a.lo = (MOE_LDS u32x4*)p;
   a.hi = a.lo + rows * U;
   a.d = (MOE_LDS float*)(a.hi + rows * U);
+  a.s = with_s ? a.d + rows * U : nullptr;
   a.U = U;
   return a;
 }
-__host__ __device__ inline int act_bytes(int rows, int U) { return (rows * U * 36 + 15) & ~15; }
+__host__ __device__ inline int act_bytes(int rows, int U, bool with_s = false) {
+  return (rows * U * (with_s ? 40 : 36) + 15) & ~15;
+}
 
 // The same split form with each of its three regions padded to whole KB, so that whole-KB
 // direct-to-LDS pieces land inside it.
 __host__ __device__ inline int kb_pad(int b) { return (b + 1023) & ~1023; }
-__device__ __forceinline__ ActSplit act_layout_kb(MOE_LDS uint8_t* p, int rows, int U) {
+__device__ __forceinline__ ActSplit act_layout_kb(MOE_LDS uint8_t* p, int rows, int U, bool with_s = false) {
   ActSplit a;
   a.lo = (MOE_LDS u32x4*)p;
   a.hi = (MOE_LDS u32x4*)(p + kb_pad(rows * U * 16));
   a.d = (MOE_LDS float*)(p + 2 * kb_pad(rows * U * 16));
+  a.s = with_s ? (MOE_LDS float*)(p + 2 * kb_pad(rows * U * 16) + kb_pad(rows * U * 4)) : nullptr;
   a.U = U;
   return a;
 }
-__host__ __device__ inline int act_bytes_kb(int rows, int U) {
-  return 2 * kb_pad(rows * U * 16) + kb_pad(rows * U * 4);
+__host__ __device__ inline int act_bytes_kb(int rows, int U, bool with_s = false) {
+  return 2 * kb_pad(rows * U * 16) + (with_s ? 2 : 1) * kb_pad(rows * U * 4);
 }
 
 // Activation rows are staged in a fixed unrolled shape (constant register indices, no scratch):
@@ -401,9 +407,10 @@ __device__ __forceinline__ void act_store_q(const uint32_t (&qr)[NP], int nblk, 
     const int f = (int)threadIdx.x + p * NT;
     if (f < nblk * 9) {
       const int b = f / 9, k = f - b * 9;
-      if (k == 0)
+      if (k == 0) {
         act.d[b] = h2f(qr[p] & 0xFFFFu);
-      else if (k <= 4)
+        if (act.s) act.s[b] = h2f(qr[p] >> 16);
+      } else if (k <= 4)
         lo32[b * 4 + k - 1] = qr[p];
       else
         hi32[b * 4 + k - 5] = qr[p];
@@ -421,6 +428,7 @@ __device__ void act_rest_q(const uint8_t* base, int b0, int nblk, ActSplit act) 
     act.lo[b] = u32x4{qq[1], qq[2], qq[3], qq[4]};
     act.hi[b] = u32x4{qq[5], qq[6], qq[7], qq[8]};
     act.d[b] = h2f(qq[0] & 0xFFFFu);
+    if (act.s) act.s[b] = h2f(qq[0] >> 16);
   }
 }
 
@@ -511,13 +519,16 @@ __device__ __forceinline__ void dot_pass_n(const MOE_LDS uint32_t* W, uint32_t r
       const bool valid = li + (k << G.lgL) < G.U;
       const int u = unit_at(k);
       uint32_t q[NE][8];
-      float dx[NE];
+      float dx[NE], sx[NE];
 #pragma unroll
-      for (int e = 0; e < NE; ++e) act.get(sidx[e], u, q[e], dx[e]);
+      for (int e = 0; e < NE; ++e) {
+        act.get(sidx[e], u, q[e], dx[e]);
+        sx[e] = FMT == Q5_1 ? act.s[sidx[e] * act.U + u] : 0.0f;
+      }
       __builtin_amdgcn_sched_barrier(0);   // keep the reads above ahead of the decode
       uint32_t c[8];
-      float sc;
-      unit_decode<FMT>(r, u, tb, c, sc);
+      float sc, mo;
+      unit_decode<FMT>(r, u, tb, c, sc, mo);
 #pragma unroll
       for (int e = 0; e < NE; ++e) {
         // two independent chains (an integer sum: the order does not change it), so a wave
@@ -533,7 +544,9 @@ __device__ __forceinline__ void dot_pass_n(const MOE_LDS uint32_t* W, uint32_t r
         const int s = s0 + s1;
         // a unit past the row's end adds +0.0f: acc never holds -0 (it starts at +0), so this
         // equals skipping the add
-        const float prod = (sc * dx[e]) * (float)s;
+        float prod = (sc * dx[e]) * (float)s;
+        // Q5_1: the block's offset times the activations' sum field, added after the product
+        if constexpr (FMT == Q5_1) prod = prod + mo * sx[e];
         acc[e] = acc[e] + (valid ? prod : 0.0f);
       }
     };
@@ -639,8 +652,9 @@ __device__ __forceinline__ void swiglu_q81_lanes(float gv, float uv, int l32, bo
 // DEV: device-scope stores (the one-launch step reads them back in the same launch); otherwise
 // plain stores, which the end of the launch makes visible to the next one.
 template <bool DEV>
+// ds (null, or a place per block): also the block's sum field f(s16), for a Q5_1 down matrix.
 __device__ __forceinline__ void swiglu_q81_split(float gv, float uv, int l32, bool live, uint32_t* lo,
-                                                 uint32_t* hi, float* dq) {
+                                                 uint32_t* hi, float* dq, float* ds) {
   const float h = live ? swiglu(gv, uv) : 0.0f;
   const float amax = wave_max32(__builtin_fabsf(h));
   const float d = amax / 127.0f;
@@ -653,15 +667,22 @@ __device__ __forceinline__ void swiglu_q81_split(float gv, float uv, int l32, bo
   }
   const uint32_t b = (uint32_t)q & 0xFFu;
   const uint32_t w = b | (dppu<0x55>(b) << 8) | (dppu<0xAA>(b) << 16) | (dppu<0xFF>(b) << 24);   // quad lanes 1, 2, 3
+  uint32_t sw = 0u;
+  if (ds) {   // (uniform) every lane of the 32 takes part in the sum
+    const int isum = wave_sum32(q);
+    sw = __float_as_uint(h2f(sum_field(f2h(d), isum)));
+  }
   if (live) {
     uint32_t* qw = (l32 < 16 ? lo : hi) + ((l32 >> 2) & 3);
     const uint32_t dw = __float_as_uint(h2f(f2h(d)));
     if constexpr (DEV) {
       if ((l32 & 3) == 0) __hip_atomic_store(qw, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (l32 == 0) __hip_atomic_store((uint32_t*)dq, dw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (ds && l32 == 0) __hip_atomic_store((uint32_t*)ds, sw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       if ((l32 & 3) == 0) *qw = w;
       if (l32 == 0) *(uint32_t*)dq = dw;
+      if (ds && l32 == 0) *(uint32_t*)ds = sw;
     }
   }
 }
@@ -1025,6 +1046,7 @@ struct GuArgs {
   uint32_t* hq_lo;      // fused / routed: workspace q8_1 rows of h in split form (relative entry):
   uint32_t* hq_hi;      //   16-byte low and high halves of each block's quants, float scales
   float* hq_d;
+  float* hq_s;          //   and (a Q5_1 down matrix only, else null) the blocks' sum fields
   uint8_t* desc;        // fused / routed: the call's descriptor for the down launch
   const float* logits;  // routed: [T][E] router logits
   int T, E, k;
@@ -1064,8 +1086,8 @@ __host__ __device__ inline int gu_smem_bytes(int lds_ring, int lds_act, int lds_
 // outputs of a down tile, the entries' metadata and the first tile's destination rows of Y.
 constexpr int kLyMeta = 4 * (5 * kMaxEnt + 16);
 constexpr int kLyYBuf = 4 * kMaxEnt * kDnTileMax;
-__host__ __device__ inline int ly_down_bytes(int cap_entries, int Ud) {
-  return act_bytes_kb(cap_entries, Ud) + 4 * kMaxEnt * kDnTileMax + kLyMeta + kLyYBuf;
+__host__ __device__ inline int ly_down_bytes(int cap_entries, int Ud, bool with_s) {
+  return act_bytes_kb(cap_entries, Ud, with_s) + 4 * kMaxEnt * kDnTileMax + kLyMeta + kLyYBuf;
 }
 
 // Work item = one 32-row block of h of one group (so SwiGLU and the q8_1 quantization of the block
@@ -1542,7 +1564,8 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
           const float gv = live ? stage[e * 64 + l32] : 0.0f;
           const float uv = live ? stage[e * 64 + 32 + l32] : 0.0f;
           const size_t bk = (size_t)(a0 + (live ? e : 0)) * nb + blk;
-          swiglu_q81_split<MODE == GU_LAYER>(gv, uv, l32, live, a.hq_lo + 4 * bk, a.hq_hi + 4 * bk, a.hq_d + bk);
+          swiglu_q81_split<MODE == GU_LAYER>(gv, uv, l32, live, a.hq_lo + 4 * bk, a.hq_hi + 4 * bk, a.hq_d + bk,
+                                              a.hq_s ? a.hq_s + bk : nullptr);
         }
       }
     }
@@ -1554,9 +1577,9 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
     const Geom& Gd = a.Gd;
     const int Ud = Gd.U;
     MOE_LDS uint8_t* dreg = tail + a.lds_tail;
-    const ActSplit actd = act_layout_kb(dreg, a.P.cap_entries, Ud);
+    const ActSplit actd = act_layout_kb(dreg, a.P.cap_entries, Ud, FD == Q5_1);
     const int tr = a.trd;
-    MOE_LDS float* ores = (MOE_LDS float*)(dreg + act_bytes_kb(a.P.cap_entries, Ud));   // [kMaxEnt][tr]
+    MOE_LDS float* ores = (MOE_LDS float*)(dreg + act_bytes_kb(a.P.cap_entries, Ud, FD == Q5_1));   // [kMaxEnt][tr]
     MOE_LDS int* mdst = (MOE_LDS int*)(ores + kMaxEnt * kDnTileMax);   // [kMaxEnt] dst or -1
     MOE_LDS int* mown = mdst + kMaxEnt;                           // first live entry of its dst
     MOE_LDS float* mw = (MOE_LDS float*)(mown + kMaxEnt);
@@ -1709,6 +1732,8 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
       dma_span<true>((const uint8_t*)a.hq_lo, qb, (MOE_LDS uint8_t*)actd.lo, dw, ndw);
       dma_span<true>((const uint8_t*)a.hq_hi, qb, (MOE_LDS uint8_t*)actd.hi, (dw + 3) % ndw, ndw);
       dma_span<true>((const uint8_t*)a.hq_d, db, (MOE_LDS uint8_t*)actd.d, (dw + 6) % ndw, ndw);
+      if constexpr (FD == Q5_1)
+        dma_span<true>((const uint8_t*)a.hq_s, db, (MOE_LDS uint8_t*)actd.s, (dw + 7) % ndw, ndw);
       if (ntw > 0 && wave == kDnWaves) {   // one float per lane
         for (int p = 0; p * 64 < nown * nr0; ++p) {
           const int l = p * 64 + lane;
@@ -1797,6 +1822,7 @@ struct DnArgs {
   const uint8_t* hq_lo; // DN_DESC: the workspace's split q8_1 rows of h (entry - e0)
   const uint8_t* hq_hi;
   const uint8_t* hq_d;
+  const uint8_t* hq_s;  // DN_DESC, Q5_1 only: the blocks' sum fields
   float* Y;
   int n_rows, ldy;
   int lds_ring, lds_act;
@@ -1906,7 +1932,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   }
   const int ng = uni(dsc[kDescNg]), e0 = uni(dsc[kDescE0]), n = uni(dsc[kDescN]);
   if (ng == 0) return;
-  const ActSplit act = MODE == DN_DESC ? act_layout_kb(actp, n, U) : act_layout(actp, n, U);
+  const ActSplit act = MODE == DN_DESC ? act_layout_kb(actp, n, U, FMT == Q5_1) : act_layout(actp, n, U, FMT == Q5_1);
   const int ntiles = a.ntiles;
   const int bid = (int)blockIdx.x, grid = (int)gridDim.x;
   const int ntw = bid >= ntiles ? 0 : ntiles <= grid ? 1 : (ntiles - bid + grid - 1) / grid;   // tiles here
@@ -1952,6 +1978,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
     dma_span(a.hq_lo, qb, (MOE_LDS uint8_t*)act.lo, wave, kDnWaves);
     dma_span(a.hq_hi, qb, (MOE_LDS uint8_t*)act.hi, (wave + 3) % kDnWaves, kDnWaves);
     dma_span(a.hq_d, db, (MOE_LDS uint8_t*)act.d, (wave + 6) % kDnWaves, kDnWaves);
+    if constexpr (FMT == Q5_1) dma_span(a.hq_s, db, (MOE_LDS uint8_t*)act.s, (wave + 7) % kDnWaves, kDnWaves);
     for (int kc = 0; kc < pre; ++kc) issue(myring + kc * M * 1024);
   }
   // entry metadata: destination (or -1), weight, owner = first live entry naming its dst
@@ -2169,22 +2196,22 @@ __global__ __launch_bounds__(kThreads) void k_swiglu(PlanArgs P, const float* __
 // every field of both layouts starts at an even offset and has an even length).
 template <int FMT>
 __device__ __forceinline__ uint32_t planar_src(uint32_t nblk, uint32_t p) {
-  constexpr uint32_t B = block_bytes(FMT), C = code_bytes(FMT), S = B - C;
+  constexpr uint32_t B = block_bytes(FMT), C = code_bytes(FMT), H = head_bytes(FMT), S = B - C;
   if (p < C * nblk) {
     const uint32_t b = p / C;
-    return B * b + 2u + (p - C * b);
+    return B * b + H + (p - C * b);
   }
   const uint32_t q = p - C * nblk, b = q / S, r = q - S * b;
-  return r < 2u ? B * b + r : B * b + (B - 4u) + (r - 2u);
+  return r < H ? B * b + r : B * b + H + C + (r - H);   // the header, then (CB2 / CB3) the sub-scales
 }
 // The inverse: offset in the planar row of byte p of the row-major row.
 template <int FMT>
 __device__ __forceinline__ uint32_t rowmajor_src(uint32_t nblk, uint32_t p) {
-  constexpr uint32_t B = block_bytes(FMT), C = code_bytes(FMT);
+  constexpr uint32_t B = block_bytes(FMT), C = code_bytes(FMT), H = head_bytes(FMT), S = B - C;
   const uint32_t b = p / B, r = p - B * b;
-  if (r < 2u) return C * nblk + (B - C) * b + r;
-  if (B - C == 6u && r >= B - 4u) return C * nblk + 6u * b + 2u + (r - (B - 4u));
-  return C * b + (r - 2u);
+  if (r < H) return C * nblk + S * b + r;
+  if (r >= H + C) return C * nblk + S * b + H + (r - H - C);
+  return C * b + (r - H);
 }
 
 // One row per workgroup at a time, two bytes per lane: every output half-word is gathered from
@@ -2217,7 +2244,9 @@ int hip_fail(hipError_t e, const char* what) {
 // A layer's format field: the encoding (moe_fmt) with MOE_LAYOUT_PLANAR optionally OR-ed in.
 int base_fmt(int f) { return f & ~MOE_LAYOUT_PLANAR; }
 bool is_planar(int f) { return (f & MOE_LAYOUT_PLANAR) != 0; }
-bool fmt_ok(int f) { return base_fmt(f) >= Q8_0 && base_fmt(f) <= CB3; }
+bool fmt_ok(int f) { return base_fmt(f) >= Q8_0 && base_fmt(f) <= Q5_1; }
+// Q5_1 (an offset format: its dot product needs the activations' sum fields) is a down format only
+bool fmt_ok_gate_up(int f) { return fmt_ok(f) && base_fmt(f) != Q5_1; }
 
 bool cols_ok(int fmt, int n) {
   fmt = base_fmt(fmt);
@@ -2299,7 +2328,7 @@ void dn_tiling(const Geom& G, int n_embd, int grid, int& tr, int& rc) {
 }
 
 struct WsLayout {
-  size_t lo, hi, d, total;
+  size_t lo, hi, d, s, total;
 };
 
 size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -2312,13 +2341,14 @@ WsLayout ws_layout(const moe_layer* L, const moe_plan* P) {
   w.lo = kDescReserve + kCtrBytes;
   w.hi = w.lo + al256(blocks * 16);
   w.d = w.hi + al256(blocks * 16);
-  w.total = w.d + al256(blocks * 4);
+  w.s = w.d + al256(blocks * 4);   // the blocks' sum fields (written only for a Q5_1 down matrix)
+  w.total = w.s + al256(blocks * 4);
   return w;
 }
 
 int check_layer(const moe_layer* L, bool need_down) {
   if (!L || !L->gate || !L->up || (need_down && !L->down)) return MOE_E_ARG;
-  if (!fmt_ok(L->fmt_gate_up) || !fmt_ok(L->fmt_down)) return MOE_E_FMT;
+  if (!fmt_ok_gate_up(L->fmt_gate_up) || !fmt_ok(L->fmt_down)) return MOE_E_FMT;
   if (L->n_experts <= 0) return MOE_E_ARG;
   if (!cols_ok(L->fmt_gate_up, L->n_embd) || !cols_ok(L->fmt_down, L->n_ff)) return MOE_E_SHAPE;
   const int fg = base_fmt(L->fmt_gate_up), fd = base_fmt(L->fmt_down);
@@ -2390,7 +2420,7 @@ hipError_t launch_gu(int fmt, int fmt_down, int mode, const GuArgs& ga, int grid
 #define MOE_GU(F)                                                            \
   case F:                                                                    \
     if (mode == GU_LAYER) {                                                  \
-      switch (fmt_down) { MOE_LY(F, Q8_0) MOE_LY(F, NL4) MOE_LY(F, CB2) MOE_LY(F, CB3) } \
+      switch (fmt_down) { MOE_LY(F, Q8_0) MOE_LY(F, NL4) MOE_LY(F, CB2) MOE_LY(F, CB3) MOE_LY(F, Q5_1) } \
       return hipErrorInvalidValue;                                           \
     }                                                                        \
     return mode == GU_COMPOSED ? go(k_gate_up<F, GU_COMPOSED>)               \
@@ -2422,6 +2452,7 @@ hipError_t launch_dn(int fmt, int mode, const DnArgs& da, int grid, int bytes, h
     MOE_DN(NL4)
     MOE_DN(CB2)
     MOE_DN(CB3)
+    MOE_DN(Q5_1)
   }
 #undef MOE_DN
   return hipErrorInvalidValue;
@@ -2447,8 +2478,9 @@ int gu_lds(const moe_layer* L, const moe_plan* P, int n_tokens, int mode, Stream
   }
   if (mode == GU_LAYER) {
     const Geom Gd = down_geom(L);
-    if (act_bytes_kb(P->cap_entries, Gd.U) > kDnActMax) return -1;
-    *downb = ly_down_bytes(P->cap_entries, Gd.U);
+    const bool q51 = base_fmt(L->fmt_down) == Q5_1;
+    if (act_bytes_kb(P->cap_entries, Gd.U, q51) > kDnActMax) return -1;
+    *downb = ly_down_bytes(P->cap_entries, Gd.U, q51);
     int tr, rc;
     dn_tiling(Gd, L->n_embd, num_cus(), tr, rc);
     lg = std::max(lg, kDnWaves * dn_stream(Gd, rc, 1).M * 1024);
@@ -2470,7 +2502,7 @@ int gu_lds(const moe_layer* L, const moe_plan* P, int n_tokens, int mode, Stream
 // LDS of the down kernel for chunks of rc rows: two slots per wave where they fit, else one.
 int dn_lds(const moe_layer* L, const moe_plan* P, int rc, Stream* S, int* ring, int* actb) {
   const Geom G = down_geom(L);
-  *actb = act_bytes_kb(P->cap_entries, G.U);
+  *actb = act_bytes_kb(P->cap_entries, G.U, base_fmt(L->fmt_down) == Q5_1);
   if (*actb > kDnActMax) return -1;
   for (int ns = 2; ns >= 1; --ns) {
     *S = dn_stream(G, rc, ns);
@@ -2507,6 +2539,7 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
     ga.hq_lo = (uint32_t*)(ws + wl.lo);
     ga.hq_hi = (uint32_t*)(ws + wl.hi);
     ga.hq_d = (float*)(ws + wl.d);
+    ga.hq_s = base_fmt(L->fmt_down) == Q5_1 ? (float*)(ws + wl.s) : nullptr;
   }
   ga.desc = ws;
   ga.logits = logits;
@@ -2569,6 +2602,7 @@ int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, co
     da.hq_lo = ws + wl.lo;
     da.hq_hi = ws + wl.hi;
     da.hq_d = ws + wl.d;
+    da.hq_s = ws + wl.s;
   }
   da.Y = Y;
   da.n_rows = n_rows;
@@ -2637,7 +2671,8 @@ int moe_repack(void* stream, int fmt, const void* src, int64_t rows, int cols, v
     case Q8_0: hipLaunchKernelGGL(k_repack<Q8_0>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
     case NL4: hipLaunchKernelGGL(k_repack<NL4>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
     case CB2: hipLaunchKernelGGL(k_repack<CB2>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
-    default: hipLaunchKernelGGL(k_repack<CB3>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
+    case CB3: hipLaunchKernelGGL(k_repack<CB3>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
+    default: hipLaunchKernelGGL(k_repack<Q5_1>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
   }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_repack");

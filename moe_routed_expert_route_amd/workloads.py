@@ -28,6 +28,9 @@ CONFIGS = {
     # (48 layers: a pass reads >= 0.6 GB, well above the 256 MB last-level cache)
     "cb3q8_2560x640": dict(layers=48, E=256, n_embd=2560, n_ff=640, k=8, T=1,
                            fg=synth.CB3, fd=synth.Q8_0, routing="uniform"),
+    # the headline geometry with an offset down format (Q5_1, one of the pages' down formats)
+    "nl4q51_2560x768_t1": dict(layers=48, E=128, n_embd=2560, n_ff=768, k=8, T=1,
+                               fg=synth.NL4, fd=synth.Q5_1, routing="logits"),
 }
 
 

@@ -36,9 +36,10 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-Q8_0, NL4, CB2, CB3 = 1, 2, 3, 4
-_BLOCK_BYTES = {Q8_0: 34, NL4: 18, CB2: 70, CB3: 110}
-_BLOCK_W = {Q8_0: 32, NL4: 32, CB2: 256, CB3: 256}
+Q8_0, NL4, CB2, CB3, Q5_1 = 1, 2, 3, 4, 5
+_BLOCK_BYTES = {Q8_0: 34, NL4: 18, CB2: 70, CB3: 110, Q5_1: 24}
+_BLOCK_W = {Q8_0: 32, NL4: 32, CB2: 256, CB3: 256, Q5_1: 32}
+_HEAD = {Q8_0: 2, NL4: 2, CB2: 2, CB3: 2, Q5_1: 4}   # block bytes before the codes
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -68,7 +69,7 @@ def lib():
         L.orc_block_weights.argtypes = [_I]
         L.orc_quantize_q8_1.argtypes = [_P, _I, _P]
         L.orc_quantize_q8_0.argtypes = [_P, _I, _P]
-        L.orc_decode_row.argtypes = [_I, _P, _I, _P, _P, _P, _P, _P]
+        L.orc_decode_row.argtypes = [_I, _P, _I, _P, _P, _P, _P, _P, _P]
         L.orc_matvec.argtypes = [_I, _P, _I, _I, _P, _P, _P, _P, _P, _P]
         L.orc_swiglu.argtypes = [_P, _P, _I, _P]
         L.orc_route_topk.argtypes = [_P, _I, _I, _I, _P, _P]
@@ -119,23 +120,24 @@ def repack(fmt: int, mat, rows: int, ncols: int, to_planar: bool = True) -> np.n
     compared byte for byte). Per row: the row-major row is its blocks one after another; each block
     is its fp16 scale (2 bytes), its code bytes, and for CB2 / CB3 the 4 sub-scale bytes at its end.
     The planar row is every block's code bytes in block order, then every block's scale bytes (the
-    fp16 scale, then for CB2 / CB3 the sub-scale bytes) in block order. Same bytes, same size."""
-    B, W = _BLOCK_BYTES[fmt], _BLOCK_W[fmt]
+    header: fp16 scale, for Q5_1 also the fp16 offset; then for CB2 / CB3 the sub-scale bytes) in
+    block order. Same bytes, same size."""
+    B, W, H = _BLOCK_BYTES[fmt], _BLOCK_W[fmt], _HEAD[fmt]
     tail = 4 if fmt in (CB2, CB3) else 0   # sub-scale bytes at the end of a block
     nb = ncols // W
     m = np.asarray(mat, np.uint8).reshape(rows, nb * B)
     out = np.empty_like(m)
-    ncode = B - 2 - tail
+    ncode = B - H - tail
     for r in range(rows):
         if to_planar:
             blocks = m[r].reshape(nb, B)
-            codes = blocks[:, 2:2 + ncode]
-            scales = np.concatenate([blocks[:, :2], blocks[:, 2 + ncode:]], axis=1)
+            codes = blocks[:, H:H + ncode]
+            scales = np.concatenate([blocks[:, :H], blocks[:, H + ncode:]], axis=1)
             out[r] = np.concatenate([codes.reshape(-1), scales.reshape(-1)])
         else:
             codes = m[r, :nb * ncode].reshape(nb, ncode)
-            scales = m[r, nb * ncode:].reshape(nb, 2 + tail)
-            out[r] = np.concatenate([scales[:, :2], codes, scales[:, 2:]], axis=1).reshape(-1)
+            scales = m[r, nb * ncode:].reshape(nb, H + tail)
+            out[r] = np.concatenate([scales[:, :H], codes, scales[:, H:]], axis=1).reshape(-1)
     return out.reshape(-1)
 
 
@@ -166,24 +168,33 @@ def quantize_q8_0(x) -> np.ndarray:
 
 # ------------------------------------------------------------------ decoders ------------------
 
-def decode_row(fmt: int, row, ncols: int, tables: Tables):
-    """(codes int32 [ncols], scales float64 [ncols/32]) of one weight row."""
+def decode_row_offsets(fmt: int, row, ncols: int, tables: Tables):
+    """(codes int32 [ncols], scales float64 [ncols/32], offsets float64 [ncols/32]) of one weight
+    row: weight j = scales[j // 32] * codes[j] + offsets[j // 32] (offsets are 0 but for Q5_1)."""
     row = _c(row, np.uint8)
     codes = np.empty(ncols, np.int32)
     scales = np.empty(ncols // 32, np.float64)
-    rc = lib().orc_decode_row(fmt, _ptr(row), ncols, *tables.ptrs(), _ptr(codes), _ptr(scales))
+    offsets = np.empty(ncols // 32, np.float64)
+    rc = lib().orc_decode_row(fmt, _ptr(row), ncols, *tables.ptrs(), _ptr(codes), _ptr(scales),
+                              _ptr(offsets))
     if rc != 0:
         raise ValueError("bad format or shape")
+    return codes, scales, offsets
+
+
+def decode_row(fmt: int, row, ncols: int, tables: Tables):
+    """(codes int32 [ncols], scales float64 [ncols/32]) of one weight row."""
+    codes, scales, _ = decode_row_offsets(fmt, row, ncols, tables)
     return codes, scales
 
 
 def dequantize(fmt: int, mat, rows: int, ncols: int, tables: Tables) -> np.ndarray:
-    """float64 [rows, ncols] weight values (scale * code) of a row-major block matrix."""
+    """float64 [rows, ncols] weight values (scale * code + offset) of a row-major block matrix."""
     mat = _c(mat, np.uint8).reshape(rows, row_bytes(fmt, ncols))
     out = np.empty((rows, ncols), np.float64)
     for r in range(rows):
-        codes, scales = decode_row(fmt, mat[r], ncols, tables)
-        out[r] = codes.astype(np.float64) * np.repeat(scales, 32)
+        codes, scales, offsets = decode_row_offsets(fmt, mat[r], ncols, tables)
+        out[r] = codes.astype(np.float64) * np.repeat(scales, 32) + np.repeat(offsets, 32)
     return out
 
 

@@ -56,13 +56,14 @@ int orc_block_bytes(int fmt) {
     case ORC_NL4: return 18;
     case ORC_CB2: return 70;
     case ORC_CB3: return 110;
+    case ORC_Q5_1: return 24;
     default: return 0;
   }
 }
 
 int orc_block_weights(int fmt) {
   switch (fmt) {
-    case ORC_Q8_0: case ORC_NL4: return 32;
+    case ORC_Q8_0: case ORC_NL4: case ORC_Q5_1: return 32;
     case ORC_CB2: case ORC_CB3: return 256;
     default: return 0;
   }
@@ -74,11 +75,23 @@ static int sub_scale(const uint8_t* nibbles, int sub) {
   return (nibbles[sub / 2] >> (4 * (sub % 2))) & 15;
 }
 
-/* Decode weights [32*sb32, 32*sb32+32) of a row: integer codes and the sub-block's scale. */
+/* Decode weights [32*sb32, 32*sb32+32) of a row: integer codes, the sub-block's scale and its
+ * additive offset (weight = scale * code + offset; the offset is 0 except for Q5_1). */
 static void decode_sub32(int fmt, const uint8_t* row, int sb32, const int8_t* nl4_table,
                          const uint8_t* cb2_grid, const uint8_t* cb3_grid, int32_t code[32],
-                         double* scale) {
-  if (fmt == ORC_Q8_0) {
+                         double* scale, double* offset) {
+  *offset = 0.0;
+  if (fmt == ORC_Q5_1) {
+    const uint8_t* blk = row + 24 * sb32;
+    *scale = (double)orc_h2f(rd16(blk));
+    *offset = (double)orc_h2f(rd16(blk + 2));
+    uint32_t qh = (uint32_t)blk[4] | ((uint32_t)blk[5] << 8) | ((uint32_t)blk[6] << 16) |
+                  ((uint32_t)blk[7] << 24);
+    for (int i = 0; i < 16; ++i) {
+      code[i] = (blk[8 + i] & 15) | (int)(((qh >> i) & 1u) << 4);              /* weight i */
+      code[i + 16] = (blk[8 + i] >> 4) | (int)(((qh >> (i + 16)) & 1u) << 4);  /* weight i+16 */
+    }
+  } else if (fmt == ORC_Q8_0) {
     const uint8_t* blk = row + 34 * sb32;
     *scale = (double)orc_h2f(rd16(blk));
     for (int j = 0; j < 32; ++j) code[j] = (int8_t)blk[2 + j];
@@ -123,10 +136,14 @@ static int shape_ok(int fmt, int ncols) {
 }
 
 int orc_decode_row(int fmt, const uint8_t* row, int ncols, const int8_t* nl4_table,
-                   const uint8_t* cb2_grid, const uint8_t* cb3_grid, int32_t* codes, double* scales) {
+                   const uint8_t* cb2_grid, const uint8_t* cb3_grid, int32_t* codes, double* scales,
+                   double* offsets) {
   if (!shape_ok(fmt, ncols)) return -1;
-  for (int b = 0; b < ncols / 32; ++b)
-    decode_sub32(fmt, row, b, nl4_table, cb2_grid, cb3_grid, codes + 32 * b, scales + b);
+  for (int b = 0; b < ncols / 32; ++b) {
+    double off;
+    decode_sub32(fmt, row, b, nl4_table, cb2_grid, cb3_grid, codes + 32 * b, scales + b, &off);
+    if (offsets) offsets[b] = off;
+  }
   return 0;
 }
 
@@ -197,15 +214,18 @@ int orc_matvec(int fmt, const uint8_t* mat, int rows, int ncols, const uint8_t* 
     const uint8_t* row = mat + (size_t)r * row_bytes;
     double acc = 0.0, sabs = 0.0;
     for (int b = 0; b < ncols / 32; ++b) {
-      double scale;
-      decode_sub32(fmt, row, b, nl4_table, cb2_grid, cb3_grid, code, &scale);
+      double scale, offset;
+      decode_sub32(fmt, row, b, nl4_table, cb2_grid, cb3_grid, code, &scale, &offset);
       const uint8_t* xb = xq + 36 * b;
       double dx = (double)orc_h2f(rd16(xb));
       long isum = 0;
       for (int j = 0; j < 32; ++j) isum += (long)code[j] * (long)(int8_t)xb[4 + j];
       double c = scale * dx * (double)isum;
-      acc += c;
-      sabs += fabs(c);
+      /* an offset weight adds offset * sum of the block's activations, taken from the q8_1 sum
+       * field s = fp16(f(d) * sum q) */
+      double co = offset * (double)orc_h2f(rd16(xb + 2));
+      acc += c + co;
+      sabs += fabs(c) + fabs(co);
     }
     out[r] = acc;
     if (S) S[r] = sabs;

@@ -24,7 +24,7 @@
 #include <stdint.h>
 #include <stddef.h>
 
-enum { ORC_Q8_0 = 1, ORC_NL4 = 2, ORC_CB2 = 3, ORC_CB3 = 4 };
+enum { ORC_Q8_0 = 1, ORC_NL4 = 2, ORC_CB2 = 3, ORC_CB3 = 4, ORC_Q5_1 = 5 };
 
 /* IEEE binary16 <-> binary32 (round to nearest even, subnormals kept). */
 float    orc_h2f(uint16_t h);
@@ -39,13 +39,17 @@ void orc_quantize_q8_1(const float* x, int n, uint8_t* out);
 /* Q8_0 (34 B per 32: fp16 d, int8 q[32]); used only for round-trip invariants. */
 void orc_quantize_q8_0(const float* x, int n, uint8_t* out);
 
-/* Decode one row of `ncols` weights: integer code per weight and scale per 32-weight sub-block
- * (weight value = scale[j/32] * code[j]). Returns 0, or -1 for a bad format / shape. */
+/* Decode one row of `ncols` weights: integer code per weight, scale and offset per 32-weight
+ * sub-block (weight value = scale[j/32] * code[j] + offset[j/32]; offsets may be NULL, and are 0
+ * except for Q5_1). Returns 0, or -1 for a bad format / shape. */
 int orc_decode_row(int fmt, const uint8_t* row, int ncols, const int8_t* nl4_table,
-                   const uint8_t* cb2_grid, const uint8_t* cb3_grid, int32_t* codes, double* scales);
+                   const uint8_t* cb2_grid, const uint8_t* cb3_grid, int32_t* codes, double* scales,
+                   double* offsets);
 
-/* out[r] = sum over 32-blocks b of c_b, c_b = scale_w * f(d_x) * sum_j code_j * q_j (double),
- * S[r] = sum_b |c_b|. mat: rows x ncols weights, row-major blocks. xq: ncols/32 q8_1 blocks. */
+/* out[r] = sum over 32-blocks b of c_b, c_b = scale_w * f(d_x) * sum_j code_j * q_j
+ * + offset_w * f(s_x) (double; the second term only for Q5_1, whose offset multiplies the block's
+ * activation sum, read from the q8_1 sum field s), S[r] = sum_b of the terms' absolute values.
+ * mat: rows x ncols weights, row-major blocks. xq: ncols/32 q8_1 blocks. */
 int orc_matvec(int fmt, const uint8_t* mat, int rows, int ncols, const uint8_t* xq,
                const int8_t* nl4_table, const uint8_t* cb2_grid, const uint8_t* cb3_grid,
                double* out, double* S);

@@ -19,7 +19,7 @@ from . import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-Q8_0, NL4, CB2, CB3 = 1, 2, 3, 4
+Q8_0, NL4, CB2, CB3, Q5_1 = 1, 2, 3, 4, 5
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -103,6 +103,10 @@ ROUTED = {
     # many experts: 16 logits per lane in the routing wave, expert pointers past the first 512
     # loaded in a second round, a 32-word selection bitmap
     "q8_e1000_t3": dict(n_embd=256, n_ff=128, E=1000, k=8, T=3, fg=Q8_0, fd=Q8_0),
+    # an offset down format: the q8_1 sum field of h enters the down dot product
+    "nl4_q51_t1": dict(n_embd=2560, n_ff=768, E=128, k=8, T=1, fg=NL4, fd=Q5_1),
+    "cb3_q51_t4_shared": dict(n_embd=512, n_ff=256, E=16, k=4, T=4, fg=CB3, fd=Q5_1, ids="shared"),
+    "q8_q51_t3": dict(n_embd=256, n_ff=192, E=8, k=2, T=3, fg=Q8_0, fd=Q5_1),
 }
 
 
@@ -147,6 +151,11 @@ def test_layer_stages(name):
     assert np.array_equal(lo, ref[:, :, 4:20]) and np.array_equal(hi, ref[:, :, 20:36])
     d16 = ref[:, :, 0].astype(np.uint16) | (ref[:, :, 1].astype(np.uint16) << 8)
     assert np.array_equal(U.bits(dq), U.bits(d16.view(np.float16).astype(np.float32)))
+    if c.fmt_dn == Q5_1:   # the sum fields follow the scales (256-byte aligned)
+        so = off[2] + (T * k * nb * 4 + 255) // 256 * 256
+        sq = ws[so:so + ne * nb * 4].view(np.float32).reshape(ne, nb)
+        s16 = ref[:, :, 2].astype(np.uint16) | (ref[:, :, 3].astype(np.uint16) << 8)
+        assert np.array_equal(U.bits(sq), U.bits(s16.view(np.float16).astype(np.float32)))
     # routing + grouping inside the gate/up launch: same plan, same bits
     r = U.run_routed(c, c.x, Y0, entry_base=base, dst_of_token=dst)
     assert r["err"] == 0
@@ -214,7 +223,8 @@ def test_two_calls_per_layer(name):
     del g
 
 
-@pytest.mark.parametrize("fmt,ncols", [(Q8_0, 256), (NL4, 192), (CB2, 768), (CB3, 512), (NL4, 2560)])
+@pytest.mark.parametrize("fmt,ncols", [(Q8_0, 256), (NL4, 192), (CB2, 768), (CB3, 512), (NL4, 2560),
+                                      (Q5_1, 768)])
 def test_repack_bytes(fmt, ncols):
     """moe_repack against the oracle's planar layout, byte for byte, and back."""
     rows = 37
@@ -229,7 +239,7 @@ def test_repack_bytes(fmt, ncols):
 
 
 @pytest.mark.parametrize("name", ["small_q8", "nl4_t1", "cb2_nl4_t4_zipf", "cb3_q8_t2", "nl4_cb2_t2",
-                                  "cb2_cb3_t4"])
+                                  "cb2_cb3_t4", "q8_q51_t3"])
 def test_planar_layer_same_bits(name):
     """Experts repacked into the planar layout give the row-major layer's bits on every path:
     composed (g, u, h, q8_1 of h, Y), fused, routed in two launches, and the one-launch step."""
@@ -324,6 +334,18 @@ def test_negative_corrupted_weight_is_caught():
     c.gate[e] = bad
     with pytest.raises(AssertionError):
         U.check_stages(c, ph, comp, Y0)
+
+
+def test_offset_format_rejected_for_gate_up():
+    """Q5_1 is a down format only: a layer naming it for gate/up is refused on the host."""
+    c = _routed("q8_q51_t3", key=7)
+    L = c.layer
+    bad = B.Layer.from_pointers(c.n_embd, c.n_ff, Q5_1, Q5_1, L.ptr_gate, L.ptr_up, L.ptr_down)
+    plan, _, _ = U.gpu_route_and_plan(c, c.T * c.k, c.T * c.k)
+    xq = B.moe_quantize_q8_1(torch.from_numpy(c.x).to(U.dev()))
+    g = torch.empty((c.T * c.k, c.n_ff), dtype=torch.float32, device=U.dev())
+    with pytest.raises(RuntimeError, match="unknown weight format"):
+        B.moe_gate_up(bad, plan, xq, g, g.clone())
 
 
 def test_device_errors_reported():

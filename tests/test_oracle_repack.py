@@ -11,7 +11,7 @@ import pytest
 import oracle
 from moe_routed_expert_route_amd import synth
 
-Q8_0, NL4, CB2, CB3 = 1, 2, 3, 4
+Q8_0, NL4, CB2, CB3, Q5_1 = 1, 2, 3, 4, 5
 
 
 def _r(a, b):
@@ -23,6 +23,8 @@ def _r(a, b):
     (Q8_0, 64, _r(2, 34) + _r(36, 68) + [0, 1, 34, 35]),
     # two NL4 blocks of 18 bytes
     (NL4, 64, _r(2, 18) + _r(20, 36) + [0, 1, 18, 19]),
+    # two Q5_1 blocks of 24 bytes: high bits and nibbles 4..23, 28..47, then d, m of each
+    (Q5_1, 64, _r(4, 24) + _r(28, 48) + [0, 1, 2, 3, 24, 25, 26, 27]),
     # one CB2 super-block: index and sign bytes 2..65, then D 0,1 and sub-scales 66..69
     (CB2, 256, _r(2, 66) + [0, 1] + _r(66, 70)),
     # one CB3 super-block: low-index, high-bit and sign bytes 2..105, then D and sub-scales
@@ -43,7 +45,7 @@ def test_planar_two_cb3_blocks():
     assert got == _r(2, 106) + _r(112, 216) + [0, 1] + _r(106, 110) + [110, 111] + _r(216, 220)
 
 
-@pytest.mark.parametrize("fmt,ncols", [(Q8_0, 256), (NL4, 192), (CB2, 768), (CB3, 512)])
+@pytest.mark.parametrize("fmt,ncols", [(Q8_0, 256), (NL4, 192), (CB2, 768), (CB3, 512), (Q5_1, 128)])
 def test_planar_round_trip_and_permutation(fmt, ncols):
     rows = 5
     m = synth.rng(61, fmt).integers(0, 256, size=rows * oracle.row_bytes(fmt, ncols), dtype=np.uint8)
