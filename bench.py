@@ -403,6 +403,8 @@ def main():
         sweep["cb2nl4_2560x768_t4_zipf"] = [sweep_line("cb2nl4_2560x768_t4_zipf", 4, "zipf", 10, 3)]
         log("nl4/q5_1 T=1")
         sweep["nl4q51_2560x768_t1"] = [sweep_line("nl4q51_2560x768_t1", 1, "logits", 10, 3)]
+        log("nl4x T=1")
+        sweep["nl4x_2560x768_t1"] = [sweep_line("nl4x_2560x768_t1", 1, "logits", 10, 3)]
         res["t_sweep"] = sweep
         res["fit_nl4_groups_entries"] = fit_groups_entries(
             sweep["nl4_2560x768_shared"] + sweep["cb2nl4_2560x768_t4_zipf"])

@@ -44,6 +44,11 @@
  *                       word = bit 4 of code i), [8:24] b[16]; code of w_i = (b[i] & 15) | high
  *                       bit i, of w_(i+16) = (b[i] >> 4) | high bit i+16; w = d * code + m (an
  *                       offset format; down matrices only: fmt_gate_up rejects it).
+ *   NL4X 136 B / 256 w: [0:2] fp16 D, [2:4] 16-bit word of the sub-scales' high bits (sub-block b:
+ *                       bits 2b, 2b+1), [4:8] their low nibbles (sub-block b: byte 4 + b/2, low
+ *                       nibble for even b), [8:136] eight 16-byte nibble groups in the NL4 order
+ *                       (sub-block b = weights 32b..32b+31); l_b = low | high << 4 (0..63);
+ *                       w = D (l_b - 32) T[nibble] with the NL4 table.
  *   q8_1  36 B / 32 values (activations): [0:2] fp16 d, [2:4] fp16 s, [4:36] int8 q[32], with
  *         amax = max|x|, d = amax / 127 (float32), q = clamp(round-half-away(x / d), +-127)
  *         (0 if amax == 0), d16 = fp16(d), s16 = fp16(f(d16) * sum q), all IEEE float32.
@@ -51,11 +56,11 @@
  * Planar layout (MOE_LAYOUT_PLANAR OR-ed into a moe_layer format field): the same bytes per row,
  * reordered so that the codes of the row's n blocks come first, block after block (Q8_0 32 B,
  * NL4 16 B, CB2 the 64 index and sign bytes, CB3 the 104 low-index, high-bit and sign bytes,
- * Q5_1 the 20 high-bit and nibble bytes, each in its row-major order), then the scales, block
- * after block (Q8_0 / NL4 the fp16 d; Q5_1 d then m; CB2 / CB3 the fp16 D followed by the 4
- * sub-scale bytes). A row keeps its size and a matrix its rows,
+ * Q5_1 the 20 high-bit and nibble bytes, NL4X the 128 nibble bytes, each in its row-major
+ * order), then the scales, block after block (Q8_0 / NL4 the fp16 d; Q5_1 d then m; NL4X its 8
+ * header bytes; CB2 / CB3 the fp16 D followed by the 4 sub-scale bytes). A row keeps its size and a matrix its rows,
  * so every pointer and size of the row-major layout holds; moe_repack converts either way.
- * Shapes: C must be a multiple of 64 for Q8_0 / NL4 and of 256 for CB2 / CB3; n_embd and n_ff
+ * Shapes: C must be a multiple of 64 for Q8_0 / NL4 / Q5_1 and of 256 for CB2 / CB3 / NL4X; n_embd and n_ff
  * at most MOE_MAX_DIM.
  * Block contribution: c_b = scale_w * f(d_x) * sum_j code_j q_j (exact int32 sum), plus for Q5_1
  * m * f(s_x): the offset times the block's activation sum, read from the q8_1 sum field (the one
@@ -77,7 +82,8 @@ extern "C" {
 
 typedef enum {
   MOE_FMT_Q8_0 = 1, MOE_FMT_NL4 = 2, MOE_FMT_CB2 = 3, MOE_FMT_CB3 = 4,
-  MOE_FMT_Q5_1 = 5   /* down only */
+  MOE_FMT_Q5_1 = 5,  /* down only */
+  MOE_FMT_NL4X = 6
 } moe_fmt;
 #define MOE_LAYOUT_PLANAR 0x100   /* OR-ed into moe_layer.fmt_gate_up / fmt_down: planar rows */
 
@@ -108,7 +114,7 @@ typedef struct moe_layer {
   const void* const* gate;       /* device array [n_experts] of device pointers: n_ff x n_embd */
   const void* const* up;         /* same */
   const void* const* down;       /* device array [n_experts]: n_embd x n_ff */
-  const int8_t* nl4_table;       /* 16 B, needed if a format is NL4 (else may be NULL) */
+  const int8_t* nl4_table;       /* 16 B, needed if a format is NL4 or NL4X (else may be NULL) */
   const uint8_t* cb2_grid;       /* 256 x 8 B, needed if a format is CB2 */
   const uint8_t* cb3_grid;       /* 512 x 4 B, needed if a format is CB3 */
 } moe_layer;

@@ -14,9 +14,9 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_route.so")
 
-Q8_0, NL4, CB2, CB3, Q5_1 = 1, 2, 3, 4, 5
-BLOCK_BYTES = {Q8_0: 34, NL4: 18, CB2: 70, CB3: 110, Q5_1: 24}
-BLOCK_WEIGHTS = {Q8_0: 32, NL4: 32, CB2: 256, CB3: 256, Q5_1: 32}
+Q8_0, NL4, CB2, CB3, Q5_1, NL4X = 1, 2, 3, 4, 5, 6
+BLOCK_BYTES = {Q8_0: 34, NL4: 18, CB2: 70, CB3: 110, Q5_1: 24, NL4X: 136}
+BLOCK_WEIGHTS = {Q8_0: 32, NL4: 32, CB2: 256, CB3: 256, Q5_1: 32, NL4X: 256}
 
 ERR_BITS = {1: "NGROUPS", 2: "ENTRIES", 4: "EXPERT", 8: "SRC", 16: "DST", 32: "ALIGN"}
 

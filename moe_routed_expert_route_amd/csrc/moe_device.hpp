@@ -24,7 +24,7 @@ namespace moe {
 constexpr int kThreads = 256;          // every kernel runs 4 waves of 64
 constexpr int kMaxSlots = 4;           // entries staged at once (a group's rows of the window)
 
-enum Fmt : int { Q8_0 = 1, NL4 = 2, CB2 = 3, CB3 = 4, Q5_1 = 5 };
+enum Fmt : int { Q8_0 = 1, NL4 = 2, CB2 = 3, CB3 = 4, Q5_1 = 5, NL4X = 6 };
 
 // ------------------------------------------------------------------ binary16 ----------------
 
@@ -202,13 +202,15 @@ struct Lay {
 };
 
 __host__ __device__ constexpr int block_bytes(int fmt) {
-  return fmt == Q8_0 ? 34 : fmt == NL4 ? 18 : fmt == CB2 ? 70 : fmt == CB3 ? 110 : fmt == Q5_1 ? 24 : 0;
+  return fmt == Q8_0 ? 34 : fmt == NL4 ? 18 : fmt == CB2 ? 70 : fmt == CB3 ? 110 : fmt == Q5_1 ? 24
+         : fmt == NL4X ? 136 : 0;
 }
 __host__ __device__ constexpr int block_weights(int fmt) {
-  return (fmt == CB2 || fmt == CB3) ? 256 : 32;
+  return (fmt == CB2 || fmt == CB3 || fmt == NL4X) ? 256 : 32;
 }
-// Header bytes of a block before its codes: the fp16 scale (Q5_1: scale and offset).
-__host__ __device__ constexpr int head_bytes(int fmt) { return fmt == Q5_1 ? 4 : 2; }
+// Header bytes of a block before its codes: the fp16 scale (Q5_1: scale and offset; NL4X: scale,
+// then the 16-bit and 32-bit words of its sub-block scales).
+__host__ __device__ constexpr int head_bytes(int fmt) { return fmt == Q5_1 ? 4 : fmt == NL4X ? 8 : 2; }
 // Code bytes of one block: the block minus its header and (CB2 / CB3) its 4 trailing sub-scale
 // bytes.
 __host__ __device__ constexpr int code_bytes(int fmt) {
@@ -230,8 +232,9 @@ template <int FMT>
 struct URaw {
   // Q8_0: scale pair, 9 quant dwords; NL4: scale pair, 5 nibble dwords; CB2: D, index, sign and
   // sub-scale pairs; CB3: D, two index pairs, high-bit, sign and sub-scale pairs
-  // Q5_1: scale and offset pair, 6 dwords of high bits and nibbles
-  uint32_t v[FMT == Q8_0 ? 11 : FMT == NL4 ? 7 : FMT == CB2 ? 8 : FMT == Q5_1 ? 8 : 12];
+  // Q5_1: scale and offset pair, 6 dwords of high bits and nibbles; NL4X: 3 header dwords, 5 of
+  // the sub-block's nibbles
+  uint32_t v[FMT == Q8_0 ? 11 : FMT == NL4 ? 7 : FMT == CB2 ? 8 : FMT == Q5_1 ? 8 : FMT == NL4X ? 8 : 12];
   uint32_t od, oc, ox;   // byte offsets of the block's scale, codes and (CB2 / CB3) sub-scales
 };
 
@@ -251,6 +254,17 @@ __device__ __forceinline__ void unit_load(const MOE_LDS uint32_t* W, uint32_t ro
     const uint32_t c = r.oc >> 2;
 #pragma unroll
     for (int i = 0; i < (FMT == Q8_0 ? 9 : FMT == NL4 ? 5 : 6); ++i) r.v[2 + i] = W[c + i];
+  } else if constexpr (FMT == NL4X) {
+    const uint32_t b = (uint32_t)u >> 3, su = (uint32_t)u & 7u;
+    r.od = row + ly.d_a * b + ly.d_b;
+    r.oc = row + ly.c_a * b + ly.c_b + 16u * su;   // this sub-block's 16 nibble bytes
+    r.ox = 0;
+    const uint32_t h = r.od >> 2;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) r.v[i] = W[h + i];
+    const uint32_t c = r.oc >> 2;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) r.v[3 + i] = W[c + i];
   } else if constexpr (FMT == CB2) {
     const uint32_t b = (uint32_t)u >> 3, su = (uint32_t)u & 7u;
     r.od = row + ly.d_a * b + ly.d_b;
@@ -294,6 +308,22 @@ __device__ __forceinline__ void unit_decode(const URaw<FMT>& r, int u, const Tab
       const uint32_t hh = (((qh >> (16 + 4 * k)) & 15u) * 0x00204081u) & 0x01010101u;
       c[k] = (n & 0x0F0F0F0Fu) | (hl << 4);              // weights 4k..4k+3
       c[k + 4] = ((n >> 4) & 0x0F0F0F0Fu) | (hh << 4);   // weights 16+4k..16+4k+3
+    }
+  } else if constexpr (FMT == NL4X) {
+    // header: fp16 D, 16-bit word of the sub-scales' high bit pairs, 32-bit word of their low
+    // nibbles; sub-block su's 6-bit scale l gives D (l - 32)
+    const uint32_t ha = r.od & 3u;
+    const uint32_t w0 = __builtin_amdgcn_alignbyte(r.v[1], r.v[0], ha);   // D | high pairs << 16
+    const uint32_t w1 = __builtin_amdgcn_alignbyte(r.v[2], r.v[1], ha);   // low nibbles
+    const uint32_t su = (uint32_t)u & 7u;
+    const int l = (int)(((w1 >> (4u * su)) & 15u) | (((w0 >> (16u + 2u * su)) & 3u) << 4));
+    sc = h2f(w0 & 0xFFFFu) * (float)(l - 32);
+    const uint32_t sh = r.oc & 3u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t n = __builtin_amdgcn_alignbyte(r.v[4 + k], r.v[3 + k], sh);
+      c[k] = lut16(n, tb);            // weights 4k..4k+3 of the sub-block (low nibbles)
+      c[k + 4] = lut16(n >> 4, tb);   // weights 16+4k..16+4k+3 (high nibbles)
     }
   } else if constexpr (FMT == Q8_0) {
     sc = h2f(at(0, r.od) & 0xFFFFu);

@@ -2244,14 +2244,14 @@ int hip_fail(hipError_t e, const char* what) {
 // A layer's format field: the encoding (moe_fmt) with MOE_LAYOUT_PLANAR optionally OR-ed in.
 int base_fmt(int f) { return f & ~MOE_LAYOUT_PLANAR; }
 bool is_planar(int f) { return (f & MOE_LAYOUT_PLANAR) != 0; }
-bool fmt_ok(int f) { return base_fmt(f) >= Q8_0 && base_fmt(f) <= Q5_1; }
+bool fmt_ok(int f) { return base_fmt(f) >= Q8_0 && base_fmt(f) <= NL4X; }
 // Q5_1 (an offset format: its dot product needs the activations' sum fields) is a down format only
 bool fmt_ok_gate_up(int f) { return fmt_ok(f) && base_fmt(f) != Q5_1; }
 
 bool cols_ok(int fmt, int n) {
   fmt = base_fmt(fmt);
   if (n <= 0 || n > MOE_MAX_DIM) return false;
-  return (fmt == CB2 || fmt == CB3) ? n % 256 == 0 : n % 64 == 0;
+  return (fmt == CB2 || fmt == CB3 || fmt == NL4X) ? n % 256 == 0 : n % 64 == 0;
 }
 
 int ilog2(int v) {
@@ -2352,7 +2352,7 @@ int check_layer(const moe_layer* L, bool need_down) {
   if (L->n_experts <= 0) return MOE_E_ARG;
   if (!cols_ok(L->fmt_gate_up, L->n_embd) || !cols_ok(L->fmt_down, L->n_ff)) return MOE_E_SHAPE;
   const int fg = base_fmt(L->fmt_gate_up), fd = base_fmt(L->fmt_down);
-  const bool nl4 = fg == NL4 || fd == NL4;
+  const bool nl4 = fg == NL4 || fd == NL4 || fg == NL4X || fd == NL4X;
   const bool cb2 = fg == CB2 || fd == CB2;
   const bool cb3 = fg == CB3 || fd == CB3;
   if ((nl4 && !L->nl4_table) || (cb2 && !L->cb2_grid) || (cb3 && !L->cb3_grid)) return MOE_E_ARG;
@@ -2420,7 +2420,7 @@ hipError_t launch_gu(int fmt, int fmt_down, int mode, const GuArgs& ga, int grid
 #define MOE_GU(F)                                                            \
   case F:                                                                    \
     if (mode == GU_LAYER) {                                                  \
-      switch (fmt_down) { MOE_LY(F, Q8_0) MOE_LY(F, NL4) MOE_LY(F, CB2) MOE_LY(F, CB3) MOE_LY(F, Q5_1) } \
+      switch (fmt_down) { MOE_LY(F, Q8_0) MOE_LY(F, NL4) MOE_LY(F, CB2) MOE_LY(F, CB3) MOE_LY(F, Q5_1) MOE_LY(F, NL4X) } \
       return hipErrorInvalidValue;                                           \
     }                                                                        \
     return mode == GU_COMPOSED ? go(k_gate_up<F, GU_COMPOSED>)               \
@@ -2431,6 +2431,7 @@ hipError_t launch_gu(int fmt, int fmt_down, int mode, const GuArgs& ga, int grid
     MOE_GU(NL4)
     MOE_GU(CB2)
     MOE_GU(CB3)
+    MOE_GU(NL4X)
   }
 #undef MOE_GU
 #undef MOE_LY
@@ -2453,6 +2454,7 @@ hipError_t launch_dn(int fmt, int mode, const DnArgs& da, int grid, int bytes, h
     MOE_DN(CB2)
     MOE_DN(CB3)
     MOE_DN(Q5_1)
+    MOE_DN(NL4X)
   }
 #undef MOE_DN
   return hipErrorInvalidValue;
@@ -2672,7 +2674,8 @@ int moe_repack(void* stream, int fmt, const void* src, int64_t rows, int cols, v
     case NL4: hipLaunchKernelGGL(k_repack<NL4>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
     case CB2: hipLaunchKernelGGL(k_repack<CB2>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
     case CB3: hipLaunchKernelGGL(k_repack<CB3>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
-    default: hipLaunchKernelGGL(k_repack<Q5_1>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
+    case Q5_1: hipLaunchKernelGGL(k_repack<Q5_1>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
+    default: hipLaunchKernelGGL(k_repack<NL4X>, dim3(grid), dim3(kThreads), 0, st, s, d, (long)rows, rb, nblk, to_planar); break;
   }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_repack");

@@ -17,10 +17,10 @@ import numpy as np
 
 BASE_SEED = 20261202
 
-Q8_0, NL4, CB2, CB3, Q5_1 = 1, 2, 3, 4, 5
+Q8_0, NL4, CB2, CB3, Q5_1, NL4X = 1, 2, 3, 4, 5, 6
 FMT_NAMES = {"q8_0": Q8_0, "nl4": NL4, "cb2": CB2, "cb3": CB3}
-BLOCK_BYTES = {Q8_0: 34, NL4: 18, CB2: 70, CB3: 110, Q5_1: 24}
-BLOCK_WEIGHTS = {Q8_0: 32, NL4: 32, CB2: 256, CB3: 256, Q5_1: 32}
+BLOCK_BYTES = {Q8_0: 34, NL4: 18, CB2: 70, CB3: 110, Q5_1: 24, NL4X: 136}
+BLOCK_WEIGHTS = {Q8_0: 32, NL4: 32, CB2: 256, CB3: 256, Q5_1: 32, NL4X: 256}
 
 NAN_FILL = np.uint32(0x7FC0DEAD)   # quiet-NaN pattern put in rows a call must not write
 
@@ -63,15 +63,18 @@ def weight_matrix(fmt: int, rows: int, cols: int, *key) -> np.ndarray:
     """Bytes of a rows x cols weight matrix in `fmt`, row-major blocks (uint8 [rows*row_bytes]).
 
     Codes are uniform over every bit pattern the format allows (Q8_0 quants U{-127..127});
-    the fp16 scale of each block is U[1e-3, 1e-2]; a Q5_1 block's fp16 offset is about -15.5
-    scales (times U[0.9, 1.1]), so its 32 code levels straddle zero."""
+    the fp16 scale of each block is U[1e-3, 1e-2] (NL4X: U[1e-4, 1e-3], times its 6-bit sub-block
+    scale minus 32); a Q5_1 block's fp16 offset is about -15.5 scales (times U[0.9, 1.1]), so its
+    32 code levels straddle zero."""
     g = rng(10, fmt, rows, cols, *key)
     bsz = BLOCK_BYTES[fmt]
     nblk = rows * cols // BLOCK_WEIGHTS[fmt]
     blocks = g.integers(0, 256, size=(nblk, bsz), dtype=np.uint8)
     if fmt == Q8_0:
         blocks[:, 2:] = g.integers(-127, 128, size=(nblk, 32), dtype=np.int8).view(np.uint8)
-    sc = fp16_scales(g, nblk)
+    # NL4X: the super-block scale is multiplied by l - 32 (|l - 32| about 16 on average), so it is
+    # drawn ten times smaller to keep the weights' magnitudes those of the other formats
+    sc = fp16_scales(g, nblk, 1e-4, 1e-3) if fmt == NL4X else fp16_scales(g, nblk)
     blocks[:, 0] = (sc & 0xFF).astype(np.uint8)
     blocks[:, 1] = (sc >> 8).astype(np.uint8)
     if fmt == Q5_1:

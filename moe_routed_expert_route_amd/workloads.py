@@ -31,6 +31,9 @@ CONFIGS = {
     # the headline geometry with an offset down format (Q5_1, one of the pages' down formats)
     "nl4q51_2560x768_t1": dict(layers=48, E=128, n_embd=2560, n_ff=768, k=8, T=1,
                                fg=synth.NL4, fd=synth.Q5_1, routing="logits"),
+    # the headline geometry in the super-block 4-bit format (4.25 bits per weight)
+    "nl4x_2560x768_t1": dict(layers=48, E=128, n_embd=2560, n_ff=768, k=8, T=1,
+                             fg=synth.NL4X, fd=synth.NL4X, routing="logits"),
 }
 
 

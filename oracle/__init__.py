@@ -36,10 +36,10 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-Q8_0, NL4, CB2, CB3, Q5_1 = 1, 2, 3, 4, 5
-_BLOCK_BYTES = {Q8_0: 34, NL4: 18, CB2: 70, CB3: 110, Q5_1: 24}
-_BLOCK_W = {Q8_0: 32, NL4: 32, CB2: 256, CB3: 256, Q5_1: 32}
-_HEAD = {Q8_0: 2, NL4: 2, CB2: 2, CB3: 2, Q5_1: 4}   # block bytes before the codes
+Q8_0, NL4, CB2, CB3, Q5_1, NL4X = 1, 2, 3, 4, 5, 6
+_BLOCK_BYTES = {Q8_0: 34, NL4: 18, CB2: 70, CB3: 110, Q5_1: 24, NL4X: 136}
+_BLOCK_W = {Q8_0: 32, NL4: 32, CB2: 256, CB3: 256, Q5_1: 32, NL4X: 256}
+_HEAD = {Q8_0: 2, NL4: 2, CB2: 2, CB3: 2, Q5_1: 4, NL4X: 8}   # block bytes before the codes
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int

@@ -57,6 +57,7 @@ int orc_block_bytes(int fmt) {
     case ORC_CB2: return 70;
     case ORC_CB3: return 110;
     case ORC_Q5_1: return 24;
+    case ORC_NL4X: return 136;
     default: return 0;
   }
 }
@@ -64,7 +65,7 @@ int orc_block_bytes(int fmt) {
 int orc_block_weights(int fmt) {
   switch (fmt) {
     case ORC_Q8_0: case ORC_NL4: case ORC_Q5_1: return 32;
-    case ORC_CB2: case ORC_CB3: return 256;
+    case ORC_CB2: case ORC_CB3: case ORC_NL4X: return 256;
     default: return 0;
   }
 }
@@ -90,6 +91,21 @@ static void decode_sub32(int fmt, const uint8_t* row, int sb32, const int8_t* nl
     for (int i = 0; i < 16; ++i) {
       code[i] = (blk[8 + i] & 15) | (int)(((qh >> i) & 1u) << 4);              /* weight i */
       code[i + 16] = (blk[8 + i] >> 4) | (int)(((qh >> (i + 16)) & 1u) << 4);  /* weight i+16 */
+    }
+  } else if (fmt == ORC_NL4X) {
+    const uint8_t* blk = row + 136 * (sb32 / 8);
+    int sub = sb32 % 8;
+    /* 6-bit sub-block scale: low 4 bits from the nibble bytes at [4:8] (sub-block 2j in the low
+     * nibble of byte 4 + j, 2j+1 in the high one), high 2 bits from the 16-bit word at [2:4]
+     * (bits 2 sub, 2 sub + 1); the sub-block's scale is D * (l - 32) */
+    int lo = (blk[4 + sub / 2] >> (4 * (sub % 2))) & 15;
+    int hi = (rd16(blk + 2) >> (2 * sub)) & 3;
+    int l = lo | (hi << 4);
+    *scale = (double)orc_h2f(rd16(blk)) * (double)(l - 32);
+    const uint8_t* q = blk + 8 + 16 * sub;
+    for (int i = 0; i < 16; ++i) {
+      code[i] = nl4_table[q[i] & 15];        /* low nibble: weight i of the sub-block */
+      code[i + 16] = nl4_table[q[i] >> 4];   /* high nibble: weight i + 16 */
     }
   } else if (fmt == ORC_Q8_0) {
     const uint8_t* blk = row + 34 * sb32;

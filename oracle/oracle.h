@@ -24,7 +24,7 @@
 #include <stdint.h>
 #include <stddef.h>
 
-enum { ORC_Q8_0 = 1, ORC_NL4 = 2, ORC_CB2 = 3, ORC_CB3 = 4, ORC_Q5_1 = 5 };
+enum { ORC_Q8_0 = 1, ORC_NL4 = 2, ORC_CB2 = 3, ORC_CB3 = 4, ORC_Q5_1 = 5, ORC_NL4X = 6 };
 
 /* IEEE binary16 <-> binary32 (round to nearest even, subnormals kept). */
 float    orc_h2f(uint16_t h);

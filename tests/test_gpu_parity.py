@@ -19,7 +19,7 @@ from . import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-Q8_0, NL4, CB2, CB3, Q5_1 = 1, 2, 3, 4, 5
+Q8_0, NL4, CB2, CB3, Q5_1, NL4X = 1, 2, 3, 4, 5, 6
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -107,6 +107,10 @@ ROUTED = {
     "nl4_q51_t1": dict(n_embd=2560, n_ff=768, E=128, k=8, T=1, fg=NL4, fd=Q5_1),
     "cb3_q51_t4_shared": dict(n_embd=512, n_ff=256, E=16, k=4, T=4, fg=CB3, fd=Q5_1, ids="shared"),
     "q8_q51_t3": dict(n_embd=256, n_ff=192, E=8, k=2, T=3, fg=Q8_0, fd=Q5_1),
+    # the super-block 4-bit format (NL4 codes, 6-bit sub-block scales)
+    "nl4x_t1": dict(n_embd=2560, n_ff=768, E=128, k=8, T=1, fg=NL4X, fd=NL4X),
+    "nl4x_q51_t4_zipf": dict(n_embd=512, n_ff=512, E=16, k=4, T=4, fg=NL4X, fd=Q5_1, ids="zipf"),
+    "cb2_nl4x_t2": dict(n_embd=768, n_ff=256, E=12, k=3, T=2, fg=CB2, fd=NL4X),
 }
 
 
@@ -224,7 +228,7 @@ def test_two_calls_per_layer(name):
 
 
 @pytest.mark.parametrize("fmt,ncols", [(Q8_0, 256), (NL4, 192), (CB2, 768), (CB3, 512), (NL4, 2560),
-                                      (Q5_1, 768)])
+                                      (Q5_1, 768), (NL4X, 1024)])
 def test_repack_bytes(fmt, ncols):
     """moe_repack against the oracle's planar layout, byte for byte, and back."""
     rows = 37
@@ -239,7 +243,7 @@ def test_repack_bytes(fmt, ncols):
 
 
 @pytest.mark.parametrize("name", ["small_q8", "nl4_t1", "cb2_nl4_t4_zipf", "cb3_q8_t2", "nl4_cb2_t2",
-                                  "cb2_cb3_t4", "q8_q51_t3"])
+                                  "cb2_cb3_t4", "q8_q51_t3", "nl4x_q51_t4_zipf"])
 def test_planar_layer_same_bits(name):
     """Experts repacked into the planar layout give the row-major layer's bits on every path:
     composed (g, u, h, q8_1 of h, Y), fused, routed in two launches, and the one-launch step."""

@@ -18,9 +18,9 @@ import pytest
 from moe_routed_expert_route_amd import synth
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
-Q8_0, NL4, CB2, CB3, Q5_1 = 1, 2, 3, 4, 5
-BB = {Q8_0: 34, NL4: 18, CB2: 70, CB3: 110, Q5_1: 24}
-BW = {Q8_0: 32, NL4: 32, CB2: 256, CB3: 256, Q5_1: 32}
+Q8_0, NL4, CB2, CB3, Q5_1, NL4X = 1, 2, 3, 4, 5, 6
+BB = {Q8_0: 34, NL4: 18, CB2: 70, CB3: 110, Q5_1: 24, NL4X: 136}
+BW = {Q8_0: 32, NL4: 32, CB2: 256, CB3: 256, Q5_1: 32, NL4X: 256}
 
 
 def np_dequant(fmt, mat, rows, cols, nl4, cb2, cb3):
@@ -36,6 +36,16 @@ def np_dequant(fmt, mat, rows, cols, nl4, cb2, cb3):
         return (d[..., None] * codes + m[..., None]).reshape(rows, cols)
     if fmt == Q8_0:
         return (d[..., None] * b[..., 2:].view(np.int8)).reshape(rows, cols)
+    if fmt == NL4X:
+        sh = b[..., 2].astype(np.int64) | (b[..., 3].astype(np.int64) << 8)
+        sl = b[..., 4:8].astype(np.int64)
+        j = np.arange(8)
+        low = (sl[..., j // 2] >> (4 * (j % 2))) & 15
+        high = (sh[..., None] >> (2 * j)) & 3
+        scale = d[..., None] * ((low | (high << 4)) - 32)                 # [rows, nb, 8]
+        q = b[..., 8:136].reshape(rows, nb, 8, 16)
+        codes = np.asarray(nl4, np.int64)[np.concatenate([q & 15, q >> 4], axis=-1)]
+        return (scale[..., None] * codes).reshape(rows, cols)
     if fmt == NL4:
         nib = b[..., 2:18]
         codes = np.concatenate([nib & 15, nib >> 4], axis=-1)
@@ -128,6 +138,17 @@ def test_golden_q5_1(orc):
         assert vals[int(i)] == v
 
 
+def test_golden_nl4x(orc):
+    g = json.load(open(os.path.join(GOLD, "decode_blocks.json")))["nl4x"]
+    blk = np.zeros(136, np.uint8)
+    blk[0:8] = _from_hex(g["bytes_hex"])
+    blk[8:24] = [i | (15 - i) << 4 for i in range(16)]
+    codes, scales = orc.decode_row(NL4X, blk, 256, orc.Tables(nl4=np.array(g["table"], np.int8)))
+    assert scales.tolist() == g["scales"]
+    assert codes[:32].tolist() == g["codes_sub0"]
+    assert codes[32:].tolist() == [g["table"][0]] * 224   # zero nibbles elsewhere
+
+
 def _enumerating_matrix(fmt, rows, cols, key):
     """Random matrix whose code fields run through every value the format has."""
     m = synth.weight_matrix(fmt, rows, cols, key).reshape(-1, BB[fmt]).copy()
@@ -137,6 +158,9 @@ def _enumerating_matrix(fmt, rows, cols, key):
     elif fmt == CB2:
         m[:, 2:34] = (np.arange(n * 32) % 256).reshape(n, 32)          # every grid row
         m[:, 66:70] = (np.arange(n * 4) * 0x11 % 256).reshape(n, 4)     # every sub-scale
+    elif fmt == NL4X:
+        m[:, 8:136] = (np.arange(n * 128) % 256).reshape(n, 128)       # every nibble pair
+        m[:, 2:8] = (np.arange(n * 6) * 41 % 256).reshape(n, 6)        # sub-scales, both words
     elif fmt == Q5_1:
         m[:, 8:24] = (np.arange(n * 16) % 256).reshape(n, 16)          # every nibble pair
         m[:, 4:8] = (np.arange(n * 4) * 37 % 256).reshape(n, 4)        # both high-bit values
@@ -147,7 +171,7 @@ def _enumerating_matrix(fmt, rows, cols, key):
     return m.reshape(-1)
 
 
-@pytest.mark.parametrize("fmt", [Q8_0, NL4, CB2, CB3, Q5_1])
+@pytest.mark.parametrize("fmt", [Q8_0, NL4, CB2, CB3, Q5_1, NL4X])
 def test_decoder_matches_numpy(orc, fmt):
     rows, cols = 24, 512
     tb = _tables(1)
@@ -157,7 +181,7 @@ def test_decoder_matches_numpy(orc, fmt):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("fmt", [Q8_0, NL4, CB2, CB3])
+@pytest.mark.parametrize("fmt", [Q8_0, NL4, CB2, CB3, NL4X])
 def test_matvec_dense_equivalence(orc, fmt):
     rows, cols = 40, 768
     tb = _tables(2)

@@ -11,7 +11,7 @@ import pytest
 import oracle
 from moe_routed_expert_route_amd import synth
 
-Q8_0, NL4, CB2, CB3, Q5_1 = 1, 2, 3, 4, 5
+Q8_0, NL4, CB2, CB3, Q5_1, NL4X = 1, 2, 3, 4, 5, 6
 
 
 def _r(a, b):
@@ -25,6 +25,8 @@ def _r(a, b):
     (NL4, 64, _r(2, 18) + _r(20, 36) + [0, 1, 18, 19]),
     # two Q5_1 blocks of 24 bytes: high bits and nibbles 4..23, 28..47, then d, m of each
     (Q5_1, 64, _r(4, 24) + _r(28, 48) + [0, 1, 2, 3, 24, 25, 26, 27]),
+    # one NL4X super-block: its 128 nibble bytes 8..135, then its 8 header bytes
+    (NL4X, 256, _r(8, 136) + _r(0, 8)),
     # one CB2 super-block: index and sign bytes 2..65, then D 0,1 and sub-scales 66..69
     (CB2, 256, _r(2, 66) + [0, 1] + _r(66, 70)),
     # one CB3 super-block: low-index, high-bit and sign bytes 2..105, then D and sub-scales
@@ -45,7 +47,7 @@ def test_planar_two_cb3_blocks():
     assert got == _r(2, 106) + _r(112, 216) + [0, 1] + _r(106, 110) + [110, 111] + _r(216, 220)
 
 
-@pytest.mark.parametrize("fmt,ncols", [(Q8_0, 256), (NL4, 192), (CB2, 768), (CB3, 512), (Q5_1, 128)])
+@pytest.mark.parametrize("fmt,ncols", [(Q8_0, 256), (NL4, 192), (CB2, 768), (CB3, 512), (Q5_1, 128), (NL4X, 512)])
 def test_planar_round_trip_and_permutation(fmt, ncols):
     rows = 5
     m = synth.rng(61, fmt).integers(0, 256, size=rows * oracle.row_bytes(fmt, ncols), dtype=np.uint8)
