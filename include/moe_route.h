@@ -79,6 +79,8 @@ extern "C" {
 #define MOE_MAX_DIM 8192          /* max n_embd / n_ff */
 #define MOE_MAX_CALL_ENTRIES 64   /* max cap_entries (T x k) of one call */
 #define MOE_MAX_GROUPS 64         /* max cap_groups of one call */
+#define MOE_MAX_PREFILL_ENTRIES 65535   /* max cap_entries of a prompt-path plan (moe_prefill_*) */
+#define MOE_MAX_PREFILL_GROUPS 1024     /* max cap_groups of a prompt-path plan */
 
 typedef enum {
   MOE_FMT_Q8_0 = 1, MOE_FMT_NL4 = 2, MOE_FMT_CB2 = 3, MOE_FMT_CB3 = 4,
@@ -145,6 +147,45 @@ typedef struct moe_plan {
  * Errors: MOE_E_ARG (null or misaligned pointer, overlap, rows < 0, to_planar not 0 / 1),
  * MOE_E_FMT (unknown format or the layout flag set), MOE_E_SHAPE (cols as under "Shapes"). */
 int moe_repack(void* stream, int fmt, const void* src, int64_t rows, int cols, void* dst, int to_planar);
+
+/* ---- Prompt path (many tokens at once): the same layer computation, grouped GEMMs on the matrix
+ * cores. "#2058 ...", "Summary", and "#3455 [Engine] GP100 (sm_60): 4-bit slots ...", "Approach":
+ * the prompt path is a separate set of kernels (an activation-gathering matrix-multiply path) that
+ * the decode changes leave alone. Sequence: moe_quantize_q8_1(x) -> moe_prefill_plan ->
+ * moe_prefill_gate_up -> moe_prefill_swiglu_q8_1 -> moe_prefill_down -> moe_prefill_scatter.
+ * Plans here may hold up to MOE_MAX_PREFILL_ENTRIES entries and MOE_MAX_PREFILL_GROUPS groups;
+ * otherwise the moe_plan rules above hold (entries from grp_start[0], device n_groups, error bits).
+ * Results match the oracle within the same tolerance as the decode path; the float summation
+ * order differs from the decode kernels', so the two paths are not bit-identical to each other.
+ * Row-major weights only (a planar layout flag gives MOE_E_FMT). */
+
+/* The plan of T tokens' top-k choices ids [T][k] (weights w [T][k], may be NULL: weights 0):
+ * groups ascending by expert, entries ascending by token from entry_base, as moe_build_plan, for
+ * T x k up to MOE_MAX_PREFILL_ENTRIES (one workgroup). ent_of [T][k] (device, may be NULL)
+ * receives each choice's entry index (-1 for an id outside [0, E), which is dropped with
+ * MOE_ERR_EXPERT). Needs cap_entries >= T k, cap_groups >= min(E, T k), E <= 1024, and entry
+ * arrays holding entry_base + T k entries. */
+int moe_prefill_plan(void* stream, const int32_t* ids, const float* w, const int32_t* dst_of_token,
+                     int T, int k, int E, int entry_base, const moe_plan* P, int32_t* ent_of);
+/* g, u [entry][ld] float32 (rows by absolute entry index; n_ff columns written) of every entry
+ * of the plan, from q8_1 rows xq [n_tokens][n_embd/32 x 36 B] indexed by ent_src. Per 32-row
+ * tile of a matrix and group: weights decoded once per 512-weight chunk into LDS, one
+ * v_mfma_i32_16x16x32_i8 per 32-weight block and 16 x 16 (row, entry) tile, the block's integer
+ * sums scaled by d_w f(d_x) in float32 and added block after block. */
+int moe_prefill_gate_up(void* stream, const moe_layer* L, const moe_plan* P, const void* xq, int n_tokens,
+                        float* g, float* u, int ld);
+/* SwiGLU + q8_1 of the plan's entries (as moe_swiglu_q8_1, for prompt-path plans). */
+int moe_prefill_swiglu_q8_1(void* stream, const moe_plan* P, const float* g, const float* u, int n_ff, int ld,
+                            float* h, void* hq);
+/* O [entry][ldo] float32 = ent_w[entry] x (down_e . hq[entry]) for every entry of the plan (n_embd
+ * columns), hq rows by absolute entry index ([entry][n_ff/32 x 36 B]). Same tiling as gate/up. */
+int moe_prefill_down(void* stream, const moe_layer* L, const moe_plan* P, const void* hq, float* O, int ldo);
+/* Y[dst(t)] += O[ent_of[t k + j]] for j = 0..k-1 in that order (dst(t) = dst_of_token[t], or t
+ * when NULL), one thread per element. Destinations must be distinct rows (a prompt's tokens);
+ * a destination outside [0, n_rows) skips its token (MOE_ERR_DST), an ent_of outside the plan's
+ * entries skips that term (MOE_ERR_ENTRIES), -1 is a dropped choice. */
+int moe_prefill_scatter(void* stream, const moe_plan* P, const int32_t* ent_of, const int32_t* dst_of_token,
+                        int T, int k, const float* O, int ldo, int n_embd, float* Y, int n_rows, int ldy);
 
 /* Router ("#363 ...": the window's tokens each pick top-k experts). For each of T tokens:
  * softmax over E float32 logits [T][E], the k largest by (logit descending, expert id

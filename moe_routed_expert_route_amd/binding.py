@@ -24,7 +24,8 @@ EXPORTS = ("moe_route_topk", "moe_build_plan", "moe_quantize_q8_1", "moe_repack"
            "moe_swiglu_q8_1", "moe_down_scatter", "moe_workspace_bytes",
            "moe_layer_decode", "moe_layer_decode_routed", "moe_layer_step", "moe_layer_gate_up",
            "moe_layer_down",
-           "moe_workspace_layout",
+           "moe_workspace_layout", "moe_prefill_plan", "moe_prefill_gate_up", "moe_prefill_swiglu_q8_1",
+           "moe_prefill_down", "moe_prefill_scatter",
            "moe_status_string", "moe_last_error")
 
 _lib = None
@@ -74,6 +75,12 @@ def lib():
         L.moe_layer_down.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan), _P,
                                      ctypes.c_size_t, _I, _P, _I, _I, _I]
         L.moe_workspace_layout.argtypes = [ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan), _P]
+        L.moe_prefill_plan.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, ctypes.POINTER(MoePlan), _P]
+        L.moe_prefill_gate_up.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan), _P, _I, _P,
+                                          _P, _I]
+        L.moe_prefill_swiglu_q8_1.argtypes = [_P, ctypes.POINTER(MoePlan), _P, _P, _I, _I, _P, _P]
+        L.moe_prefill_down.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan), _P, _P, _I]
+        L.moe_prefill_scatter.argtypes = [_P, ctypes.POINTER(MoePlan), _P, _P, _I, _I, _P, _I, _I, _P, _I, _I]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [_I]
         L.moe_last_error.restype = ctypes.c_char_p
@@ -215,6 +222,40 @@ def moe_repack(fmt, src, rows, cols, dst=None, to_planar=True, stream=None):
     _check(lib().moe_repack(_stream(stream), int(fmt), _ptr(src), int(rows), int(cols), _ptr(dst),
                             1 if to_planar else 0), "moe_repack")
     return dst
+
+
+# ------------------------------------------------------------------ prompt path ---------------
+
+def moe_prefill_plan(ids, w, plan: Plan, E, dst_of_token=None, entry_base=0, ent_of=None, stream=None):
+    """Plan of T x k choices (ids, w int32 / float32 [T, k] device tensors); returns ent_of [T, k]."""
+    T, k = ids.shape
+    ent_of = ent_of if ent_of is not None else torch.empty((T, k), dtype=torch.int32, device=ids.device)
+    _check(lib().moe_prefill_plan(_stream(stream), _ptr(ids), _ptr(w), _ptr(dst_of_token), T, k, E,
+                                  entry_base, ctypes.byref(plan.struct), _ptr(ent_of)), "moe_prefill_plan")
+    return ent_of
+
+
+def moe_prefill_gate_up(layer: Layer, plan: Plan, xq, g, u, stream=None):
+    _check(lib().moe_prefill_gate_up(_stream(stream), ctypes.byref(layer.struct), ctypes.byref(plan.struct),
+                                     _ptr(xq), xq.shape[0], _ptr(g), _ptr(u), g.stride(0)),
+           "moe_prefill_gate_up")
+
+
+def moe_prefill_swiglu_q8_1(plan: Plan, g, u, n_ff, hq, h=None, stream=None):
+    _check(lib().moe_prefill_swiglu_q8_1(_stream(stream), ctypes.byref(plan.struct), _ptr(g), _ptr(u), n_ff,
+                                         g.stride(0), _ptr(h), _ptr(hq)), "moe_prefill_swiglu_q8_1")
+
+
+def moe_prefill_down(layer: Layer, plan: Plan, hq, O, stream=None):
+    _check(lib().moe_prefill_down(_stream(stream), ctypes.byref(layer.struct), ctypes.byref(plan.struct),
+                                  _ptr(hq), _ptr(O), O.stride(0)), "moe_prefill_down")
+
+
+def moe_prefill_scatter(plan: Plan, ent_of, O, Y, n_embd, dst_of_token=None, stream=None):
+    T, k = ent_of.shape
+    _check(lib().moe_prefill_scatter(_stream(stream), ctypes.byref(plan.struct), _ptr(ent_of),
+                                     _ptr(dst_of_token), T, k, _ptr(O), O.stride(0), n_embd, _ptr(Y),
+                                     Y.shape[0], Y.stride(0)), "moe_prefill_scatter")
 
 
 def moe_route_topk(logits, k, ids=None, w=None, stream=None):

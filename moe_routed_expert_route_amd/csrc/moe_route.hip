@@ -2232,6 +2232,395 @@ __global__ __launch_bounds__(kThreads) void k_repack(const uint16_t* __restrict_
   }
 }
 
+// ------------------------------------------------------------------ prompt path (large T) ---
+
+// The plan of a prompt's T x k entries (T x k up to MOE_MAX_PREFILL_ENTRIES, E up to 1024), by
+// one workgroup: per-expert counts (LDS atomics: a count does not depend on their order), the
+// groups and their starts by a scan over the experts, then rounds of 256 entries in token-major
+// order where each entry's place inside its group is its expert's count so far plus the number
+// of same-expert entries before it in the round (a per-expert bitmap of the round, set with LDS
+// atomic ORs and read back by popcount): groups ascending by expert, entries ascending by token,
+// the same order as the decode path's plan. ent_of[t k + j] = the entry of token t's j-th choice
+// (-1 for an expert id out of range, which is dropped with MOE_ERR_EXPERT).
+constexpr int kPpThreads = 256;
+constexpr int kPpMaxE = 1024;
+__global__ __launch_bounds__(kPpThreads) void k_plan_large(const int32_t* __restrict__ ids, const float* __restrict__ w,
+                                                           const int32_t* __restrict__ dst_of_token, int T, int k,
+                                                           int E, int entry_base, PlanArgs P, int32_t* ent_of) {
+  __shared__ int s_cnt[kPpMaxE];     // entries per expert, then the running count in pass 2
+  __shared__ int s_start[kPpMaxE];   // first entry of the expert's group (relative)
+  __shared__ uint32_t s_bits[kPpMaxE * (kPpThreads / 32)];   // this round's entries per expert
+  __shared__ int s_part[kPpThreads];
+  __shared__ int s_tot[2];
+  const int tid = threadIdx.x, n = T * k;
+  for (int e = tid; e < E; e += kPpThreads) s_cnt[e] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kPpThreads) {
+    const int e = ids[i];
+    if (e >= 0 && e < E)
+      atomicAdd(&s_cnt[e], 1);
+    else
+      set_err(P.err, MOE_ERR_EXPERT);
+  }
+  __syncthreads();
+  // scan over the experts: each thread a run of 4 (E <= 1024), then the runs' totals
+  const int per = (E + kPpThreads - 1) / kPpThreads;
+  int c_ent = 0, c_grp = 0;
+  for (int q = 0; q < per; ++q) {
+    const int e = tid * per + q;
+    if (e < E) {
+      c_ent += s_cnt[e];
+      c_grp += s_cnt[e] > 0;
+    }
+  }
+  s_part[tid] = c_ent | (c_grp << 16);   // at most 65535 entries and 1024 groups
+  __syncthreads();
+  for (int off = 1; off < kPpThreads; off <<= 1) {   // inclusive scan of the packed pairs
+    const int v = tid >= off ? s_part[tid - off] : 0;
+    __syncthreads();
+    s_part[tid] += v;
+    __syncthreads();
+  }
+  int b_ent = (tid ? s_part[tid - 1] : 0) & 0xFFFF, b_grp = (tid ? s_part[tid - 1] : 0) >> 16;
+  for (int q = 0; q < per; ++q) {
+    const int e = tid * per + q;
+    if (e < E) {
+      s_start[e] = b_ent;
+      if (s_cnt[e] > 0) {
+        P.grp_expert[b_grp] = e;
+        P.grp_start[b_grp] = entry_base + b_ent;
+        ++b_grp;
+      }
+      b_ent += s_cnt[e];
+    }
+  }
+  if (tid == kPpThreads - 1) {
+    s_tot[0] = s_part[tid] & 0xFFFF;
+    s_tot[1] = s_part[tid] >> 16;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    P.grp_start[s_tot[1]] = entry_base + s_tot[0];
+    *P.n_groups = s_tot[1];
+  }
+  for (int e = tid; e < E; e += kPpThreads) s_cnt[e] = 0;
+  // pass 2: rounds of kPpThreads entries
+  constexpr int kW = kPpThreads / 32;
+  for (int r0 = 0; r0 < n; r0 += kPpThreads) {
+    for (int x = tid; x < E * kW; x += kPpThreads) s_bits[x] = 0u;
+    __syncthreads();
+    const int i = r0 + tid;
+    const int e = i < n ? ids[i] : -1;
+    const bool ok = e >= 0 && e < E;
+    if (ok) atomicOr(&s_bits[e * kW + (tid >> 5)], 1u << (tid & 31));
+    __syncthreads();
+    if (i < n) {
+      int pos = -1;
+      if (ok) {
+        int rank = s_cnt[e];
+        for (int q = 0; q < (tid >> 5); ++q) rank += __popc(s_bits[e * kW + q]);
+        rank += __popc(s_bits[e * kW + (tid >> 5)] & ((1u << (tid & 31)) - 1u));
+        pos = entry_base + s_start[e] + rank;
+        const int t = i / k;
+        P.ent_src[pos] = t;
+        P.ent_dst[pos] = dst_of_token ? dst_of_token[t] : t;
+        P.ent_w[pos] = w ? w[i] : 0.0f;
+      }
+      if (ent_of) ent_of[i] = pos;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += kPpThreads) {
+      int add = 0;
+      for (int q = 0; q < kW; ++q) add += __popc(s_bits[x * kW + q]);
+      s_cnt[x] += add;
+    }
+    __syncthreads();
+  }
+}
+
+// Grouped GEMM of the prompt path on the matrix cores: for group g (blockIdx.y) and a tile of
+// kPfRows rows of one of its matrices (blockIdx.x: gate tiles, then up tiles; or down), the rows'
+// dot products with every entry's q8_1 activation row, entries in passes of kPfEnt. Per K chunk
+// of kPfK weights the tile's raw rows come into LDS by direct-to-LDS loads, are decoded once into
+// int8 codes and per-block float scales (the decode path's decoders), the entries' quants and
+// scales are staged beside them, and each wave runs one 16 x 16 output tile with
+// v_mfma_i32_16x16x32_i8: one instruction per 32-weight block gives the exact integer sums of
+// 16 rows x 16 entries, which are scaled in float32 and added in block order, so every output
+// is one fixed sequence of float operations: (d_w f(d_x)) isum (+ m f(s_x) for Q5_1), summed
+// block after block. Both operands list their 32 weights in the same slot order, so the integer
+// sum is that of the block.
+constexpr int kPfRows = 32;            // rows of a workgroup tile (two 16-row MFMA tiles)
+constexpr int kPfEnt = 32;             // entries of a pass (two 16-column MFMA tiles)
+constexpr int kPfK = 512;              // weights of a K chunk (16 blocks of 32, two of 256)
+constexpr int kPfBlk = kPfK / 32;
+constexpr int kPfRaw = 1024;           // LDS bytes of a raw row slot (a chunk is at most 544 B)
+constexpr int kPfCS = kPfK + 16;       // LDS row stride of the int8 codes and quants
+constexpr int kPfThreads = 256;
+constexpr int kPfLds = kPfRows * kPfRaw + (kPfRows + kPfEnt) * kPfCS + 4 * kPfBlk * 2 * (kPfRows + kPfEnt) +
+                       4096 + 64;
+
+struct PfArgs {
+  LayerArgs A;
+  PlanArgs P;
+  int nmat;             // 2: gate and up (outputs out0, out1); 1: down (output out0, times ent_w)
+  int rows, K, rb;      // rows per matrix, weights per row, bytes per row
+  Lay ly;               // row-major field map (the chunk's local blocks)
+  const uint8_t* act;   // q8_1 rows: by token (gate / up, through ent_src) or by entry (down)
+  int act_by_entry, n_act;
+  float* out0;
+  float* out1;
+  long ld;
+};
+
+template <int FMT>
+__global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  MOE_LDS uint8_t* raw = (MOE_LDS uint8_t*)smem;
+  MOE_LDS uint8_t* codes = raw + kPfRows * kPfRaw;
+  MOE_LDS uint8_t* quant = codes + kPfRows * kPfCS;
+  MOE_LDS float* dws = (MOE_LDS float*)(quant + kPfEnt * kPfCS);   // [blk][row]
+  MOE_LDS float* mos = dws + kPfBlk * kPfRows;                      // [blk][row] (Q5_1 offsets)
+  MOE_LDS float* dxs = mos + kPfBlk * kPfRows;                      // [blk][entry]
+  MOE_LDS float* sxs = dxs + kPfBlk * kPfEnt;                       // [blk][entry] (sum fields)
+  MOE_LDS uint32_t* grid = (MOE_LDS uint32_t*)(sxs + kPfBlk * kPfEnt);   // CB2 / CB3 grid
+  MOE_LDS int* misc = (MOE_LDS int*)(grid + 1024);
+  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+  const int g = (int)blockIdx.y;
+  const int tpm = (a.rows + kPfRows - 1) / kPfRows;
+  const int mi = (int)blockIdx.x / tpm, r0 = ((int)blockIdx.x - mi * tpm) * kPfRows;
+  // the group, checked as every call checks its plan (one thread; the others wait)
+  if (tid == 0) {
+    int ok = 1, sb = 0, se = 0, e = -1;
+    const int ng = *a.P.n_groups;
+    if (ng < 0 || ng > a.P.cap_groups) {
+      set_err(a.P.err, MOE_ERR_NGROUPS);
+      ok = 0;
+    } else if (g >= ng) {
+      ok = 0;
+    } else {
+      const int s0 = a.P.grp_start[0];
+      sb = a.P.grp_start[g];
+      se = a.P.grp_start[g + 1];
+      if (s0 < 0 || sb < s0 || se < sb || se - s0 > a.P.cap_entries) {
+        set_err(a.P.err, MOE_ERR_ENTRIES);
+        ok = 0;
+      } else {
+        e = a.P.grp_expert[g];
+        if (e < 0 || e >= a.A.n_experts) {
+          set_err(a.P.err, MOE_ERR_EXPERT);
+          ok = 0;
+        }
+      }
+    }
+    misc[0] = ok;
+    misc[1] = sb;
+    misc[2] = se;
+    misc[3] = e;
+  }
+  uint32_t t_nl4[4];
+  load_nl4(a.A.nl4, t_nl4);
+  if constexpr (FMT == CB2 || FMT == CB3) {
+    const uint32_t* src = (const uint32_t*)(FMT == CB2 ? a.A.cb2 : a.A.cb3);
+    for (int i = tid; i < 512; i += kPfThreads) grid[i] = src[i];
+  }
+  __syncthreads();
+  if (!uni(misc[0])) return;
+  const int sb = uni(misc[1]), se = uni(misc[2]), e = uni(misc[3]);
+  const void* const* mats = mi == 0 ? (a.nmat == 2 ? a.A.gate : a.A.down) : a.A.up;
+  const uint64_t wp = uni64((uint64_t)(uintptr_t)mats[e]);
+  if (!ptr_ok(wp, a.P.err)) return;
+  Tables tb;
+  tables_init(tb, t_nl4, grid, grid);
+  float* out = mi == 0 ? a.out0 : a.out1;
+  const int mt = wave & 1, nt = wave >> 1, q = lane >> 4, l16 = lane & 15;
+  const int bw = block_weights(FMT), bb = block_bytes(FMT);
+  const uint32_t cbytes = (uint32_t)(kPfK / bw * bb);   // raw bytes of a row's chunk
+  for (int ep = sb; ep < se; ep += kPfEnt) {
+    const int ne = min(kPfEnt, se - ep);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kc = 0; kc < a.K; kc += kPfK) {
+      const int nblk = min(kPfBlk, (a.K - kc) / 32);   // blocks of this chunk (K is a multiple of 64)
+      const uint32_t nbytes = (uint32_t)(nblk * 32 / bw * bb);
+      __syncthreads();   // the previous chunk's reads of LDS are done
+      // (1) raw rows of the chunk: wave w takes rows w, w + 4, ...
+      for (int r = wave; r < kPfRows; r += kPfThreads / 64) {
+        if (r0 + r < a.rows) {
+          const uint8_t* src = (const uint8_t*)(uintptr_t)(wp + (uint64_t)(r0 + r) * (uint64_t)a.rb +
+                                                           (uint64_t)(kc / bw * bb));
+          issue_span(raw + r * kPfRaw, 1, src, nbytes);
+        }
+      }
+      // (2) the entries' quants of the chunk: (entry, block) pairs over the threads
+      for (int x = tid; x < kPfEnt * kPfBlk; x += kPfThreads) {
+        const int en = x / kPfBlk, bl = x - en * kPfBlk;
+        const int ent = ep + en;
+        uint32_t qq[9];
+#pragma unroll
+        for (int i = 0; i < 9; ++i) qq[i] = 0u;
+        bool live = en < ne && bl < nblk;
+        if (live) {
+          long row = ent;
+          if (!a.act_by_entry) {
+            row = a.P.ent_src[ent];
+            if (row < 0 || row >= a.n_act) {
+              set_err(a.P.err, MOE_ERR_SRC);
+              live = false;
+            }
+          }
+          if (live) {
+            const uint32_t* pq = (const uint32_t*)(a.act + (size_t)row * (size_t)(a.K / 32) * 36 +
+                                                   (size_t)(kc / 32 + bl) * 36);
+#pragma unroll
+            for (int i = 0; i < 9; ++i) qq[i] = pq[i];
+          }
+        }
+        MOE_LDS uint32_t* dq = (MOE_LDS uint32_t*)(quant + en * kPfCS + 32 * bl);
+        *(MOE_LDS u32x4*)dq = u32x4{qq[1], qq[2], qq[3], qq[4]};
+        *(MOE_LDS u32x4*)(dq + 4) = u32x4{qq[5], qq[6], qq[7], qq[8]};
+        dxs[bl * kPfEnt + en] = h2f(qq[0] & 0xFFFFu);
+        sxs[bl * kPfEnt + en] = h2f(qq[0] >> 16);
+      }
+      __builtin_amdgcn_s_waitcnt(MOE_VM(0));
+      __syncthreads();
+      // (3) decode the raw rows into codes and scales: (row, block) pairs over the threads
+      for (int x = tid; x < kPfRows * kPfBlk; x += kPfThreads) {
+        const int r = x / kPfBlk, bl = x - r * kPfBlk;
+        uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        float sc = 0.0f, mo = 0.0f;
+        if (r0 + r < a.rows && bl < nblk) {
+          const uint64_t src = wp + (uint64_t)(r0 + r) * (uint64_t)a.rb + (uint64_t)(kc / bw * bb);
+          const uint32_t row = (uint32_t)(r * kPfRaw) + (uint32_t)(src & 15u);   // from raw
+          URaw<FMT> rr;
+          unit_load<FMT>((const MOE_LDS uint32_t*)raw, row, bl, a.ly, rr);
+          MOE_WAIT_LGKM0;
+          unit_decode<FMT>(rr, bl, tb, c, sc, mo);
+        }
+        MOE_LDS uint32_t* dc = (MOE_LDS uint32_t*)(codes + r * kPfCS + 32 * bl);
+        *(MOE_LDS u32x4*)dc = u32x4{c[0], c[1], c[2], c[3]};
+        *(MOE_LDS u32x4*)(dc + 4) = u32x4{c[4], c[5], c[6], c[7]};
+        dws[bl * kPfRows + r] = sc;
+        mos[bl * kPfRows + r] = mo;
+      }
+      __syncthreads();
+      // (4) this wave's 16 x 16 tile, block after block
+      const MOE_LDS uint8_t* pa = codes + (16 * mt + l16) * kPfCS + 8 * q;
+      const MOE_LDS uint8_t* pb = quant + (16 * nt + l16) * kPfCS + 8 * q;
+      for (int bl = 0; bl < nblk; ++bl) {
+        const long av = *(const MOE_LDS long*)(pa + 32 * bl);
+        const long bv = *(const MOE_LDS long*)(pb + 32 * bl);
+        typedef int v4i __attribute__((ext_vector_type(4)));
+        const v4i z = {0, 0, 0, 0};
+        const v4i d = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, z, 0, 0, 0);
+        const f32x4 dw = *(const MOE_LDS f32x4*)(dws + bl * kPfRows + 16 * mt + 4 * q);
+        const float dx = dxs[bl * kPfEnt + 16 * nt + l16];
+        float mw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float sx = 0.0f;
+        if constexpr (FMT == Q5_1) {
+          const f32x4 m4 = *(const MOE_LDS f32x4*)(mos + bl * kPfRows + 16 * mt + 4 * q);
+          mw[0] = m4.x; mw[1] = m4.y; mw[2] = m4.z; mw[3] = m4.w;
+          sx = sxs[bl * kPfEnt + 16 * nt + l16];
+        }
+        const float dwv[4] = {dw.x, dw.y, dw.z, dw.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float prod = (dwv[i] * dx) * (float)d[i];
+          if constexpr (FMT == Q5_1) prod = prod + mw[i] * sx;
+          acc[i] = acc[i] + prod;
+        }
+      }
+    }
+    // outputs: lane holds rows 4 q + i of its row tile, entry l16 of its entry tile
+    const int en = 16 * nt + l16;
+    if (en < ne) {
+      const int ent = ep + en;
+      const float wv = a.nmat == 1 ? a.P.ent_w[ent] : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = r0 + 16 * mt + 4 * q + i;
+        if (row < a.rows) out[(size_t)ent * (size_t)a.ld + row] = a.nmat == 1 ? wv * acc[i] : acc[i];
+      }
+    }
+  }
+}
+
+// SwiGLU + q8_1 of the prompt's entries [grp_start[0], grp_start[n_groups]) (the group table is
+// trusted as far as its two ends; they are checked against the capacity).
+__global__ __launch_bounds__(kThreads) void k_pf_swiglu(PlanArgs P, const float* __restrict__ g,
+                                                        const float* __restrict__ u, int n_ff, long ld,
+                                                        float* h, uint8_t* hq) {
+  __shared__ int s_e[2];
+  if (threadIdx.x == 0) {
+    const int ng = *P.n_groups;
+    int e0 = 0, e1 = 0;
+    if (ng < 0 || ng > P.cap_groups) {
+      set_err(P.err, MOE_ERR_NGROUPS);
+    } else if (ng > 0) {
+      e0 = P.grp_start[0];
+      e1 = P.grp_start[ng];
+      if (e0 < 0 || e1 < e0 || e1 - e0 > P.cap_entries) {
+        set_err(P.err, MOE_ERR_ENTRIES);
+        e0 = e1 = 0;
+      }
+    }
+    s_e[0] = e0;
+    s_e[1] = e1;
+  }
+  __syncthreads();
+  const int e0 = uni(s_e[0]), e1 = uni(s_e[1]);
+  const int nb = n_ff / 32;
+  const long total = (long)(e1 - e0) * nb;
+  const int half = threadIdx.x >> 5, l32 = threadIdx.x & 31;
+  for (long base = (long)blockIdx.x * 8; base < total; base += (long)gridDim.x * 8) {
+    const long it = base + half;
+    const bool live = it < total;
+    const long ai = live ? e0 + it / nb : e0;
+    const int b = live ? (int)(it % nb) : 0;
+    const float gv = live ? g[ai * ld + 32 * b + l32] : 0.0f;
+    const float uv = live ? u[ai * ld + 32 * b + l32] : 0.0f;
+    swiglu_q81_lanes(gv, uv, l32, live, hq + (size_t)ai * nb * 36 + (size_t)b * 36,
+                     h ? h + ai * ld + 32 * b : nullptr);
+  }
+}
+
+// Y[dst(t)] += sum over j < k of O[ent_of[t k + j]], j ascending, one thread per output element
+// (a prompt's destinations are distinct rows, so no two threads add into one element).
+__global__ __launch_bounds__(kThreads) void k_pf_scatter(PlanArgs P, const int32_t* __restrict__ ent_of,
+                                                         const int32_t* __restrict__ dst_of_token, int k,
+                                                         const float* __restrict__ O, long ldo, int n_embd,
+                                                         float* Y, int n_rows, long ldy) {
+  __shared__ int s_e[2];
+  if (threadIdx.x == 0) {
+    const int ng = *P.n_groups;
+    int e0 = 0, e1 = 0;
+    if (ng > 0 && ng <= P.cap_groups) {
+      e0 = P.grp_start[0];
+      e1 = P.grp_start[ng];
+    }
+    s_e[0] = e0;
+    s_e[1] = e1;
+  }
+  __syncthreads();
+  const int t = (int)blockIdx.y, c = (int)blockIdx.x * kThreads + (int)threadIdx.x;
+  const int e0 = s_e[0], e1 = s_e[1];
+  const int dst = dst_of_token ? dst_of_token[t] : t;
+  if (dst < 0 || dst >= n_rows) {
+    if (c == 0) set_err(P.err, MOE_ERR_DST);
+    return;
+  }
+  if (c >= n_embd) return;
+  float acc = Y[(size_t)dst * ldy + c];
+  for (int j = 0; j < k; ++j) {
+    const int ent = ent_of[t * k + j];
+    if (ent < 0) continue;   // a choice the plan dropped
+    if (ent < e0 || ent >= e1) {
+      if (c == 0) set_err(P.err, MOE_ERR_ENTRIES);
+      continue;
+    }
+    acc = acc + O[(size_t)ent * ldo + c];
+  }
+  Y[(size_t)dst * ldy + c] = acc;
+}
+
 // ------------------------------------------------------------------ host side ---------------
 
 thread_local std::string t_last_error;
@@ -2621,6 +3010,55 @@ int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, co
   return e == hipSuccess ? MOE_OK : hip_fail(e, "down kernel");
 }
 
+// ------------------------------------------------------------------ prompt path (host) ------
+
+int check_plan_pf(const moe_plan* P) {
+  if (!P || !P->n_groups || !P->grp_expert || !P->grp_start || !P->ent_src || !P->ent_dst ||
+      !P->ent_w || !P->err)
+    return MOE_E_ARG;
+  if (P->cap_groups < 1 || P->cap_groups > MOE_MAX_PREFILL_GROUPS || P->cap_entries < 1 ||
+      P->cap_entries > MOE_MAX_PREFILL_ENTRIES)
+    return MOE_E_ARG;
+  return MOE_OK;
+}
+
+int run_pf_gemm(hipStream_t st, const moe_layer* L, const moe_plan* P, bool down, const void* act,
+                int n_act, float* out0, float* out1, long ld) {
+  const int fmt = base_fmt(down ? L->fmt_down : L->fmt_gate_up);
+  const int rows = down ? L->n_embd : L->n_ff, K = down ? L->n_ff : L->n_embd;
+  PfArgs pa{};
+  pa.A = layer_args(L);
+  pa.P = plan_args(P);
+  pa.nmat = down ? 1 : 2;
+  pa.rows = rows;
+  pa.K = K;
+  pa.rb = K / block_weights(fmt) * block_bytes(fmt);
+  pa.ly = make_lay(fmt, K / block_weights(fmt), false);
+  pa.act = (const uint8_t*)act;
+  pa.act_by_entry = down ? 1 : 0;
+  pa.n_act = n_act;
+  pa.out0 = out0;
+  pa.out1 = out1;
+  pa.ld = ld;
+  const dim3 grid((unsigned)(pa.nmat * ((rows + kPfRows - 1) / kPfRows)), (unsigned)P->cap_groups);
+  auto go = [&](auto kern) -> hipError_t {
+    hipError_t e = allow_smem(kern, kPfLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(kPfThreads), kPfLds, st, pa);
+    return hipGetLastError();
+  };
+  hipError_t e = hipErrorInvalidValue;
+  switch (fmt) {
+    case Q8_0: e = go(k_pf_gemm<Q8_0>); break;
+    case NL4: e = go(k_pf_gemm<NL4>); break;
+    case CB2: e = go(k_pf_gemm<CB2>); break;
+    case CB3: e = go(k_pf_gemm<CB3>); break;
+    case Q5_1: e = go(k_pf_gemm<Q5_1>); break;
+    case NL4X: e = go(k_pf_gemm<NL4X>); break;
+  }
+  return e == hipSuccess ? MOE_OK : hip_fail(e, down ? "prefill down kernel" : "prefill gate/up kernel");
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -2679,6 +3117,69 @@ int moe_repack(void* stream, int fmt, const void* src, int64_t rows, int cols, v
   }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_repack");
+}
+
+int moe_prefill_plan(void* stream, const int32_t* ids, const float* w, const int32_t* dst_of_token, int T,
+                     int k, int E, int entry_base, const moe_plan* P, int32_t* ent_of) {
+  int rc = check_plan_pf(P);
+  if (rc) return rc;
+  if (!ids || T < 0 || k < 1 || E < 1 || E > 1024 || entry_base < 0) return MOE_E_ARG;
+  const long n = (long)T * k;
+  if (n > P->cap_entries || std::min<long>(n, E) > P->cap_groups || n > MOE_MAX_PREFILL_ENTRIES)
+    return MOE_E_ARG;
+  hipLaunchKernelGGL(k_plan_large, dim3(1), dim3(kPpThreads), 0, (hipStream_t)stream, ids, w, dst_of_token, T,
+                     k, E, entry_base, plan_args(P), ent_of);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_prefill_plan");
+}
+
+int moe_prefill_gate_up(void* stream, const moe_layer* L, const moe_plan* P, const void* xq, int n_tokens,
+                        float* g, float* u, int ld) {
+  int rc = check_layer(L, false);
+  if (rc) return rc;
+  if ((rc = check_plan_pf(P))) return rc;
+  if (is_planar(L->fmt_gate_up)) return MOE_E_FMT;
+  if (!xq || !g || !u || ld < L->n_ff || n_tokens < 0) return MOE_E_ARG;
+  if ((uintptr_t)xq & 3) return MOE_E_ARG;
+  return run_pf_gemm((hipStream_t)stream, L, P, false, xq, n_tokens, g, u, ld);
+}
+
+int moe_prefill_swiglu_q8_1(void* stream, const moe_plan* P, const float* g, const float* u, int n_ff, int ld,
+                            float* h, void* hq) {
+  int rc = check_plan_pf(P);
+  if (rc) return rc;
+  if (!g || !u || !hq || n_ff <= 0 || n_ff % 32 || n_ff > MOE_MAX_DIM || ld < n_ff) return MOE_E_ARG;
+  if ((uintptr_t)hq & 3) return MOE_E_ARG;
+  const long total = (long)P->cap_entries * (n_ff / 32);
+  const int grid = (int)std::max<long>(1, std::min<long>((total + 7) / 8, 8192));
+  hipLaunchKernelGGL(k_pf_swiglu, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, plan_args(P), g, u, n_ff,
+                     (long)ld, h, (uint8_t*)hq);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_prefill_swiglu_q8_1");
+}
+
+int moe_prefill_down(void* stream, const moe_layer* L, const moe_plan* P, const void* hq, float* O, int ldo) {
+  int rc = check_layer(L, true);
+  if (rc) return rc;
+  if ((rc = check_plan_pf(P))) return rc;
+  if (is_planar(L->fmt_down)) return MOE_E_FMT;
+  if (!hq || !O || ldo < L->n_embd) return MOE_E_ARG;
+  if ((uintptr_t)hq & 3) return MOE_E_ARG;
+  return run_pf_gemm((hipStream_t)stream, L, P, true, hq, 0, O, nullptr, ldo);
+}
+
+int moe_prefill_scatter(void* stream, const moe_plan* P, const int32_t* ent_of, const int32_t* dst_of_token,
+                        int T, int k, const float* O, int ldo, int n_embd, float* Y, int n_rows, int ldy) {
+  int rc = check_plan_pf(P);
+  if (rc) return rc;
+  if (!ent_of || !O || !Y || T < 0 || k < 1 || n_embd <= 0 || ldo < n_embd || ldy < n_embd || n_rows < 0)
+    return MOE_E_ARG;
+  if (T == 0) return MOE_OK;
+  const dim3 grid((unsigned)((n_embd + kThreads - 1) / kThreads), (unsigned)T);
+  hipLaunchKernelGGL(k_pf_scatter, grid, dim3(kThreads), 0, (hipStream_t)stream, plan_args(P), ent_of,
+                     dst_of_token, k, O, (long)ldo, n_embd, Y, n_rows, (long)ldy);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_prefill_scatter");
 }
 
 int moe_route_topk(void* stream, const float* logits, int T, int E, int k, int32_t* ids, float* w) {
