@@ -234,6 +234,105 @@ def two_calls_us(wl, reps=20):
             "config": "plan given (routed once beforehand), moe_layer_decode per call, graph of all layers"}
 
 
+def prefill_line(T=512, layers=2, reps=10):
+    """The prompt path at T tokens on the headline geometry (NL4 2560 x 768, 128 experts, top-8):
+    per layer quantize, route, plan, gate/up and down on the matrix cores, SwiGLU + q8_1, scatter,
+    each layer's 128 experts in its own pool (every expert is routed at this T, so a layer reads
+    all 128 experts' 425 MB once). HIP graphs of `layers` layers; per-kernel graphs of the two
+    GEMM launches alone."""
+    import numpy as np
+    import torch
+
+    from moe_routed_expert_route_amd import binding as B
+    from moe_routed_expert_route_amd import synth
+    n_embd, n_ff, E, k, fmt = 2560, 768, 128, 8, synth.NL4
+    d = torch.device("cuda")
+    sz_g, sz_d = synth.row_bytes(fmt, n_embd) * n_ff, synth.row_bytes(fmt, n_ff) * n_embd
+    distinct = 16   # drawn experts, tiled over the 128 slots of each pool
+    base_g = [torch.from_numpy(synth.weight_matrix(fmt, n_ff, n_embd, 90, e, 0)).to(d) for e in range(distinct)]
+    base_u = [torch.from_numpy(synth.weight_matrix(fmt, n_ff, n_embd, 90, e, 1)).to(d) for e in range(distinct)]
+    base_d = [torch.from_numpy(synth.weight_matrix(fmt, n_embd, n_ff, 90, e, 2)).to(d) for e in range(distinct)]
+    nl4 = torch.from_numpy(synth.nl4_table(90)).to(d)
+    L = []
+    for l in range(layers):
+        pg = torch.empty(E * sz_g, dtype=torch.uint8, device=d)
+        pu = torch.empty(E * sz_g, dtype=torch.uint8, device=d)
+        pd = torch.empty(E * sz_d, dtype=torch.uint8, device=d)
+        for e in range(E):
+            pg[e * sz_g:(e + 1) * sz_g].copy_(base_g[(e + l) % distinct])
+            pu[e * sz_g:(e + 1) * sz_g].copy_(base_u[(e + l) % distinct])
+            pd[e * sz_d:(e + 1) * sz_d].copy_(base_d[(e + l) % distinct])
+        i64 = dict(dtype=torch.int64, device=d)
+        lay = B.Layer.from_pointers(n_embd, n_ff, fmt, fmt,
+                                    torch.tensor([pg.data_ptr() + e * sz_g for e in range(E)], **i64),
+                                    torch.tensor([pu.data_ptr() + e * sz_g for e in range(E)], **i64),
+                                    torch.tensor([pd.data_ptr() + e * sz_d for e in range(E)], **i64),
+                                    nl4=nl4, keep=(pg, pu, pd))
+        n = T * k
+        st = dict(lay=lay, plan=B.Plan(E, n, device=d),
+                  logits=torch.from_numpy(synth.router_logits(T, E, 91, l)).to(d),
+                  x=torch.from_numpy(synth.activations(T, n_embd, 92, l)).to(d),
+                  ids=torch.empty((T, k), dtype=torch.int32, device=d),
+                  w=torch.empty((T, k), dtype=torch.float32, device=d),
+                  ent_of=torch.empty((T, k), dtype=torch.int32, device=d),
+                  xq=torch.empty((T, n_embd // 32 * 36), dtype=torch.uint8, device=d),
+                  g=torch.empty((n, n_ff), dtype=torch.float32, device=d),
+                  u=torch.empty((n, n_ff), dtype=torch.float32, device=d),
+                  hq=torch.empty((n, n_ff // 32 * 36), dtype=torch.uint8, device=d),
+                  O=torch.empty((n, n_embd), dtype=torch.float32, device=d),
+                  Y=torch.zeros((T, n_embd), dtype=torch.float32, device=d))
+        L.append(st)
+    del base_g, base_u, base_d
+
+    def layer(st, part="all"):
+        if part in ("all", "pre"):
+            B.moe_quantize_q8_1(st["x"], q=st["xq"])
+            B.moe_route_topk(st["logits"], k, ids=st["ids"], w=st["w"])
+            B.moe_prefill_plan(st["ids"], st["w"], st["plan"], E, ent_of=st["ent_of"])
+        if part in ("all", "gate_up"):
+            B.moe_prefill_gate_up(st["lay"], st["plan"], st["xq"], st["g"], st["u"])
+        if part == "all":
+            B.moe_prefill_swiglu_q8_1(st["plan"], st["g"], st["u"], n_ff, st["hq"])
+        if part in ("all", "down"):
+            B.moe_prefill_down(st["lay"], st["plan"], st["hq"], st["O"])
+        if part == "all":
+            B.moe_prefill_scatter(st["plan"], st["ent_of"], st["O"], st["Y"], n_embd)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    out = {}
+    for part in ("all", "gate_up", "down"):
+        for st in L:   # a full pass first, so the per-kernel graphs run on real plans
+            layer(st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for st in L:
+                layer(st, part)
+        torch.cuda.synchronize()
+        g.replay()
+        out[part] = time_graph(g, reps) * 1e3 / layers
+        del g
+    assert not any(st["plan"].errors() for st in L)
+    ng = [int(st["plan"].n_groups.item()) for st in L]
+    wbytes = float(np.mean(ng)) * (2 * sz_g + sz_d)
+    macs = T * k * 3 * n_ff * n_embd
+    res = {"T": T, "layers": layers, "experts_touched_per_layer": float(np.mean(ng)),
+           "us_per_layer": round(out["all"], 2), "gate_up_us": round(out["gate_up"], 2),
+           "down_us": round(out["down"], 2),
+           "weight_gbs": round(wbytes / (out["all"] * 1e-6) / 1e9, 1),
+           "int8_tops": round(2 * macs / (out["all"] * 1e-6) / 1e12, 2)}
+    gu_bytes = float(np.mean(ng)) * 2 * sz_g
+    res["roofline_gate_up"] = {"bound": "hbm", "achieved": round(gu_bytes / (out["gate_up"] * 1e-6) / 1e9, 1),
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(gu_bytes / (out["gate_up"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                               "mfma_int8_tops": round(2 * T * k * 2 * n_ff * n_embd / (out["gate_up"] * 1e-6) / 1e12, 2),
+                               "mfma_peak_tops": 5000.0}
+    res["config"] = (f"prompt path: {T} tokens, top-{k} of {E} NL4 2560 x 768 experts, {layers} layers, "
+                     "every expert routed; weights 16 drawn experts tiled over each pool")
+    return res
+
+
 def fit_groups_entries(lines):
     """Least-squares t = a + b n_groups + c n_entries over the sweep lines (b: per expert, c: per
     entry)."""
@@ -405,6 +504,8 @@ def main():
         sweep["nl4q51_2560x768_t1"] = [sweep_line("nl4q51_2560x768_t1", 1, "logits", 10, 3)]
         log("nl4x T=1")
         sweep["nl4x_2560x768_t1"] = [sweep_line("nl4x_2560x768_t1", 1, "logits", 10, 3)]
+        log("prompt path T=512")
+        res["prefill"] = prefill_line()
         res["t_sweep"] = sweep
         res["fit_nl4_groups_entries"] = fit_groups_entries(
             sweep["nl4_2560x768_shared"] + sweep["cb2nl4_2560x768_t4_zipf"])

@@ -2353,7 +2353,8 @@ constexpr int kPfRows = 32;            // rows of a workgroup tile (two 16-row M
 constexpr int kPfEnt = 32;             // entries of a pass (two 16-column MFMA tiles)
 constexpr int kPfK = 512;              // weights of a K chunk (16 blocks of 32, two of 256)
 constexpr int kPfBlk = kPfK / 32;
-constexpr int kPfRaw = 1024;           // LDS bytes of a raw row slot (a chunk is at most 544 B)
+constexpr int kPfRaw = 1040;           // LDS stride of the raw row slots: 1 KB loaded (a chunk is at most
+                                       // 544 B) plus 16 B so that rows start on different banks
 constexpr int kPfCS = kPfK + 16;       // LDS row stride of the int8 codes and quants
 constexpr int kPfThreads = 256;
 constexpr int kPfLds = kPfRows * kPfRaw + (kPfRows + kPfEnt) * kPfCS + 4 * kPfBlk * 2 * (kPfRows + kPfEnt) +
@@ -2435,52 +2436,71 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
   const int mt = wave & 1, nt = wave >> 1, q = lane >> 4, l16 = lane & 15;
   const int bw = block_weights(FMT), bb = block_bytes(FMT);
   const uint32_t cbytes = (uint32_t)(kPfK / bw * bb);   // raw bytes of a row's chunk
+  const int nkc = (a.K + kPfK - 1) / kPfK;
+  // the memory traffic of a chunk: its raw rows (direct to LDS) and the entries' q8_1 blocks (to
+  // registers, kPfEnt * kPfBlk / kPfThreads blocks per thread), issued together
+  constexpr int kQ = kPfEnt * kPfBlk / kPfThreads;
+  uint32_t qq[kQ][9];
+  long arow[kQ];   // the activation row of this thread's entries in the pass, or -1
+  auto issue_chunk = [&](int ep, int ne, int kc) {
+    const int nblk = min(kPfBlk, (a.K - kc) / 32);
+    const uint32_t nbytes = (uint32_t)(nblk * 32 / bw * bb);
+    for (int r = wave; r < kPfRows; r += kPfThreads / 64) {   // wave w takes rows w, w + 4, ...
+      if (r0 + r < a.rows) {
+        const uint8_t* src = (const uint8_t*)(uintptr_t)(wp + (uint64_t)(r0 + r) * (uint64_t)a.rb +
+                                                         (uint64_t)(kc / bw * bb));
+        issue_span(raw + r * kPfRaw, 1, src, nbytes);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+      const int x = tid + j * kPfThreads, en = x / kPfBlk, bl = x - en * kPfBlk;
+#pragma unroll
+      for (int i = 0; i < 9; ++i) qq[j][i] = 0u;
+      if (arow[j] >= 0 && bl < nblk) {
+        const uint32_t* pq = (const uint32_t*)(a.act + (size_t)arow[j] * (size_t)(a.K / 32) * 36 +
+                                               (size_t)(kc / 32 + bl) * 36);
+#pragma unroll
+        for (int i = 0; i < 9; ++i) qq[j][i] = pq[i];
+      }
+    }
+  };
   for (int ep = sb; ep < se; ep += kPfEnt) {
     const int ne = min(kPfEnt, se - ep);
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int kc = 0; kc < a.K; kc += kPfK) {
+    // the pass's activation rows, read once (gate / up: the entries' tokens, checked)
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+      const int en = (tid + j * kPfThreads) / kPfBlk;
+      long row = -1;
+      if (en < ne) {
+        row = ep + en;
+        if (!a.act_by_entry) {
+          row = a.P.ent_src[ep + en];
+          if (row < 0 || row >= a.n_act) {
+            set_err(a.P.err, MOE_ERR_SRC);
+            row = -1;
+          }
+        }
+      }
+      arow[j] = row;
+    }
+    __syncthreads();   // the previous pass's reads of LDS are done
+    issue_chunk(ep, ne, 0);
+    for (int ck = 0; ck < nkc; ++ck) {
+      const int kc = ck * kPfK;
       const int nblk = min(kPfBlk, (a.K - kc) / 32);   // blocks of this chunk (K is a multiple of 64)
-      const uint32_t nbytes = (uint32_t)(nblk * 32 / bw * bb);
-      __syncthreads();   // the previous chunk's reads of LDS are done
-      // (1) raw rows of the chunk: wave w takes rows w, w + 4, ...
-      for (int r = wave; r < kPfRows; r += kPfThreads / 64) {
-        if (r0 + r < a.rows) {
-          const uint8_t* src = (const uint8_t*)(uintptr_t)(wp + (uint64_t)(r0 + r) * (uint64_t)a.rb +
-                                                           (uint64_t)(kc / bw * bb));
-          issue_span(raw + r * kPfRaw, 1, src, nbytes);
-        }
-      }
-      // (2) the entries' quants of the chunk: (entry, block) pairs over the threads
-      for (int x = tid; x < kPfEnt * kPfBlk; x += kPfThreads) {
-        const int en = x / kPfBlk, bl = x - en * kPfBlk;
-        const int ent = ep + en;
-        uint32_t qq[9];
+      __builtin_amdgcn_s_waitcnt(MOE_VM(0));   // this chunk's raw rows and quants have landed
+      // (2) the entries' quants into LDS
 #pragma unroll
-        for (int i = 0; i < 9; ++i) qq[i] = 0u;
-        bool live = en < ne && bl < nblk;
-        if (live) {
-          long row = ent;
-          if (!a.act_by_entry) {
-            row = a.P.ent_src[ent];
-            if (row < 0 || row >= a.n_act) {
-              set_err(a.P.err, MOE_ERR_SRC);
-              live = false;
-            }
-          }
-          if (live) {
-            const uint32_t* pq = (const uint32_t*)(a.act + (size_t)row * (size_t)(a.K / 32) * 36 +
-                                                   (size_t)(kc / 32 + bl) * 36);
-#pragma unroll
-            for (int i = 0; i < 9; ++i) qq[i] = pq[i];
-          }
-        }
+      for (int j = 0; j < kQ; ++j) {
+        const int x = tid + j * kPfThreads, en = x / kPfBlk, bl = x - en * kPfBlk;
         MOE_LDS uint32_t* dq = (MOE_LDS uint32_t*)(quant + en * kPfCS + 32 * bl);
-        *(MOE_LDS u32x4*)dq = u32x4{qq[1], qq[2], qq[3], qq[4]};
-        *(MOE_LDS u32x4*)(dq + 4) = u32x4{qq[5], qq[6], qq[7], qq[8]};
-        dxs[bl * kPfEnt + en] = h2f(qq[0] & 0xFFFFu);
-        sxs[bl * kPfEnt + en] = h2f(qq[0] >> 16);
+        *(MOE_LDS u32x4*)dq = u32x4{qq[j][1], qq[j][2], qq[j][3], qq[j][4]};
+        *(MOE_LDS u32x4*)(dq + 4) = u32x4{qq[j][5], qq[j][6], qq[j][7], qq[j][8]};
+        dxs[bl * kPfEnt + en] = h2f(qq[j][0] & 0xFFFFu);
+        sxs[bl * kPfEnt + en] = h2f(qq[j][0] >> 16);
       }
-      __builtin_amdgcn_s_waitcnt(MOE_VM(0));
       __syncthreads();
       // (3) decode the raw rows into codes and scales: (row, block) pairs over the threads
       for (int x = tid; x < kPfRows * kPfBlk; x += kPfThreads) {
@@ -2502,6 +2522,9 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
         mos[bl * kPfRows + r] = mo;
       }
       __syncthreads();
+      // the next chunk's loads go out now (raw is free, the quants are in LDS) and land while
+      // this chunk's products run
+      if (ck + 1 < nkc) issue_chunk(ep, ne, kc + kPfK);
       // (4) this wave's 16 x 16 tile, block after block
       const MOE_LDS uint8_t* pa = codes + (16 * mt + l16) * kPfCS + 8 * q;
       const MOE_LDS uint8_t* pb = quant + (16 * nt + l16) * kPfCS + 8 * q;
@@ -2528,6 +2551,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
           acc[i] = acc[i] + prod;
         }
       }
+      __syncthreads();   // the products' reads of codes and quants are done before they are rewritten
     }
     // outputs: lane holds rows 4 q + i of its row tile, entry l16 of its entry tile
     const int en = 16 * nt + l16;
