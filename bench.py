@@ -384,6 +384,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time to measure")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the T = 1..4 lines")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prompt-path line (512 tokens), printed as one JSON line")
     ap.add_argument("--calib", action="store_true",
                     help="first copy 256 MiB device to device (a known-size kernel for counter runs)")
     args = ap.parse_args()
@@ -400,6 +402,9 @@ def main():
 
     B.lib()
     torch.cuda.set_device(0)
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_line(reps=args.steps)}), flush=True)
+        return
     if args.calib:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

@@ -2502,24 +2502,38 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
         sxs[bl * kPfEnt + en] = h2f(qq[j][0] >> 16);
       }
       __syncthreads();
-      // (3) decode the raw rows into codes and scales: (row, block) pairs over the threads
-      for (int x = tid; x < kPfRows * kPfBlk; x += kPfThreads) {
-        const int r = x / kPfBlk, bl = x - r * kPfBlk;
-        uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-        float sc = 0.0f, mo = 0.0f;
-        if (r0 + r < a.rows && bl < nblk) {
+      // (3) decode the raw rows into codes and scales: (row, block) pairs over the threads, the
+      //     reads of both of a thread's units first
+      {
+        constexpr int kD = kPfRows * kPfBlk / kPfThreads;
+        URaw<FMT> rr[kD];
+        bool dl[kD];
+#pragma unroll
+        for (int j = 0; j < kD; ++j) {
+          const int x = tid + j * kPfThreads, r = x / kPfBlk, bl = x - r * kPfBlk;
+          dl[j] = r0 + r < a.rows && bl < nblk;
           const uint64_t src = wp + (uint64_t)(r0 + r) * (uint64_t)a.rb + (uint64_t)(kc / bw * bb);
           const uint32_t row = (uint32_t)(r * kPfRaw) + (uint32_t)(src & 15u);   // from raw
-          URaw<FMT> rr;
-          unit_load<FMT>((const MOE_LDS uint32_t*)raw, row, bl, a.ly, rr);
-          MOE_WAIT_LGKM0;
-          unit_decode<FMT>(rr, bl, tb, c, sc, mo);
+          unit_load<FMT>((const MOE_LDS uint32_t*)raw, row, dl[j] ? bl : 0, a.ly, rr[j]);
         }
-        MOE_LDS uint32_t* dc = (MOE_LDS uint32_t*)(codes + r * kPfCS + 32 * bl);
-        *(MOE_LDS u32x4*)dc = u32x4{c[0], c[1], c[2], c[3]};
-        *(MOE_LDS u32x4*)(dc + 4) = u32x4{c[4], c[5], c[6], c[7]};
-        dws[bl * kPfRows + r] = sc;
-        mos[bl * kPfRows + r] = mo;
+#pragma unroll
+        for (int j = 0; j < kD; ++j) {
+          const int x = tid + j * kPfThreads, r = x / kPfBlk, bl = x - r * kPfBlk;
+          uint32_t c[8];
+          float sc, mo;
+          unit_decode<FMT>(rr[j], bl, tb, c, sc, mo);
+          if (!dl[j]) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = 0u;
+            sc = 0.0f;
+            mo = 0.0f;
+          }
+          MOE_LDS uint32_t* dc = (MOE_LDS uint32_t*)(codes + r * kPfCS + 32 * bl);
+          *(MOE_LDS u32x4*)dc = u32x4{c[0], c[1], c[2], c[3]};
+          *(MOE_LDS u32x4*)(dc + 4) = u32x4{c[4], c[5], c[6], c[7]};
+          dws[bl * kPfRows + r] = sc;
+          mos[bl * kPfRows + r] = mo;
+        }
       }
       __syncthreads();
       // the next chunk's loads go out now (raw is free, the quants are in LDS) and land while
@@ -2528,6 +2542,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
       // (4) this wave's 16 x 16 tile, block after block
       const MOE_LDS uint8_t* pa = codes + (16 * mt + l16) * kPfCS + 8 * q;
       const MOE_LDS uint8_t* pb = quant + (16 * nt + l16) * kPfCS + 8 * q;
+#pragma unroll 4
       for (int bl = 0; bl < nblk; ++bl) {
         const long av = *(const MOE_LDS long*)(pa + 32 * bl);
         const long bv = *(const MOE_LDS long*)(pb + 32 * bl);
