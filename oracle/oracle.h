@@ -17,7 +17,10 @@
  *  [NIBBLE]  "#3455 GP100 (sm_60): 4-bit slots ..." -- "Validation" (gate, up, h, hq and the
  *            combined output compared stage by stage).
  * The pages give no byte layout for any weight format; the layouts implemented here are the
- * readings written down in the repository's design notes (header fp16 scale first).
+ * readings written down in the repository's design notes (header fp16 scale first). Q5_1 (named
+ * among the down formats on [GROUPED] "Exactness") is an offset format: its block contribution
+ * adds offset * f(s_x), the q8_1 sum field. NL4X (the IQ4_XS class on the same list) scales each
+ * 32-weight sub-block by D (l - 32) with a 6-bit l.
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
