@@ -122,18 +122,28 @@ __device__ __forceinline__ float group_sum(float v, int L) {
   return v;
 }
 
-__device__ __forceinline__ float wave_max32(float v) {   // max over aligned groups of 32 lanes
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) {
-    float o = __shfl_xor(v, m);
-    v = o > v ? o : v;
-  }
-  return v;
+// Max and integer sum over aligned groups of 32 lanes. Within a row of 16 lanes the partners come
+// from DPP moves (pairs, then pairs of pairs, then the mirrored half-row and row), which pair every
+// lane with every other lane of its row once; only the step across rows goes through a lane
+// shuffle. Both results do not depend on the order of the steps.
+__device__ __forceinline__ float wave_max32(float v) {
+  float o = dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = o > v ? o : v;
+  o = dpp<0x4E>(v);          // quad_perm [2,3,0,1]
+  v = o > v ? o : v;
+  o = dpp<0x141>(v);         // row_half_mirror
+  v = o > v ? o : v;
+  o = dpp<0x140>(v);         // row_mirror
+  v = o > v ? o : v;
+  o = __shfl_xor(v, 16);
+  return o > v ? o : v;
 }
 __device__ __forceinline__ int wave_sum32(int v) {
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m);
-  return v;
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  return v + __shfl_xor(v, 16);
 }
 
 // ------------------------------------------------------------------ LDS byte images ---------
