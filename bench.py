@@ -500,6 +500,12 @@ def main():
         t1 = sweep["nl4_2560x768_shared"][0]["us_per_layer_call"]
         for ln in sweep["nl4_2560x768_shared"][1:]:
             ln["per_extra_row_frac_of_t1"] = round((ln["us_per_layer_call"] - t1) / (ln["T"] - 1) / t1, 4)
+        # the least-squares slope of t(T) over T = 1..4, as a fraction of t(1)
+        import numpy as np
+        Ts = np.array([ln["T"] for ln in sweep["nl4_2560x768_shared"]], np.float64)
+        ts = np.array([ln["us_per_layer_call"] for ln in sweep["nl4_2560x768_shared"]], np.float64)
+        slope = float(((Ts - Ts.mean()) * (ts - ts.mean())).sum() / ((Ts - Ts.mean()) ** 2).sum())
+        res["per_extra_row_ls_slope_frac_of_t1"] = round(slope / t1, 4)
         for T in (1, 2, 3, 4):
             log(f"sweep cb3/q8 2560x640 uniform T={T}")
             sweep["cb3q8_2560x640_uniform"].append(sweep_line("cb3q8_2560x640", T, "uniform", 10, 3))
