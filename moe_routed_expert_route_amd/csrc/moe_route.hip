@@ -1131,20 +1131,23 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   MOE_LDS uint32_t* selT = (MOE_LDS uint32_t*)(tail + 24 * a.E);     // routed: [T][nW]
 
   // ---- 1. every load that depends on nothing, at once. Routed: the routing waves (the first
-  //         kRtWaves) send their first logits rows before anything else and load nothing more
-  //         until they have routed (their wait then covers the logits alone); the other waves take
-  //         the tables, the expert pointers and the destinations.
+  //         kRtWaves) send the NL4 table and their first logits rows before anything else and
+  //         load nothing more until they have routed (their wait then covers those alone); the
+  //         other waves take the tables, the expert pointers and the destinations.
   warm_args<GuArgs>();
   const bool rw = RT && wave < kRtWaves;   // a routing wave
   const int q0 = RT ? tid - 64 * kRtWaves : tid;   // thread index among the waves that load tables
   MOE_LDS uint32_t* rscr = (MOE_LDS uint32_t*)ring + wave * route_scr_words(a.E);
+  uint32_t t_nl4[4] = {0u, 0u, 0u, 0u};
   if constexpr (RT) {
     if (rw) {
       __builtin_amdgcn_s_setprio(2);   // the launch waits on the routing: it goes first on its SIMD
+      // the table (hot in L2) goes out just ahead of the logits, so the routing wave's one wait on
+      // the logits covers it and nothing is loaded after the routing
+      load_nl4(a.A.nl4, t_nl4);
       if (wave < a.T) issue_logits(a.logits + (size_t)wave * a.E, a.E, (MOE_LDS float*)rscr);
     }
   }
-  uint32_t t_nl4[4] = {0u, 0u, 0u, 0u};
   if (!rw) load_nl4(a.A.nl4, t_nl4);
   uint32_t t_cb = 0;
   if constexpr (FMT == CB2 || FMT == CB3) {
@@ -1185,7 +1188,6 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
                     MODE == GU_LAYER || blockIdx.x == gridDim.x - 1);
       }
       __builtin_amdgcn_s_setprio(0);
-      load_nl4(a.A.nl4, t_nl4);
     } else {
       // two register passes cover one 4096-wide row; eight cover four (more: plain loads after)
       const int q = tid - 64 * kRtWaves, nblk = a.n_tokens * G.U;
