@@ -30,8 +30,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# what the kernels' machine code follows from: the sources and the compiler flags
 KERNEL_SOURCES = ("moe_routed_expert_route_amd/csrc/moe_route.hip",
-                  "moe_routed_expert_route_amd/csrc/moe_device.hpp")
+                  "moe_routed_expert_route_amd/csrc/moe_device.hpp",
+                  "moe_routed_expert_route_amd/build.py")
 
 
 def log(msg):

@@ -15,6 +15,8 @@ HIPCC_FLAGS = [
     # IEEE float32 exactly as written: no FMA contraction, correctly rounded division, denormals
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
+    # leading scalar kernel arguments arrive preloaded in scalar registers (gfx950)
+    "-mllvm", "-amdgpu-kernarg-preload-count=4",
 ]
 
 

@@ -168,6 +168,25 @@ __device__ __forceinline__ void warm_args() {
   asm volatile("" ::"s"(s));
 }
 
+// The argument struct at byte `off` of the launch's argument block, read only after the code
+// before the call: the block's address goes through an empty asm the compiler cannot see into,
+// so no field read can be scheduled ahead of it (loads of launch arguments are otherwise hoisted
+// to the kernel's entry, with their waits). Every 64-byte line is requested at once first.
+template <typename Args>
+__device__ __forceinline__ Args args_after(uint32_t off) {
+  typedef const __attribute__((address_space(4))) uint32_t* KP;
+  uint64_t p = (uint64_t)(uintptr_t)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  const KP k = (KP)(p + off);
+  uint32_t s = 0u;
+#pragma unroll
+  for (int o = 0; o < (int)sizeof(Args); o += 64) s ^= k[o / 4];
+  asm volatile("" ::"s"(s));
+  Args r;
+  __builtin_memcpy(&r, (const void*)k, sizeof(Args));
+  return r;
+}
+
 // The 16-byte NL4 table with vector loads (a scalar load would hold up every later wait on the
 // scalar counter, which the argument reads also use, until it returns from memory).
 __device__ __forceinline__ void load_nl4(const int8_t* p, uint32_t t[4]) {
@@ -1069,6 +1088,11 @@ struct GuArgs {
 
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
+// Byte offset of the struct in k_gate_up's argument block: kernel arguments sit in order at their
+// natural alignment, after two pointers and two ints.
+constexpr uint32_t kGuArgsOff = 24;
+static_assert(alignof(GuArgs) <= 8, "GuArgs must start right after the leading arguments");
+
 constexpr int kGuStage = 64 * kMaxEnt;   // floats of output staging: a 32-row block of g and u per entry
 constexpr int kGuFixed = 4096 + kPlanLBytes + 8 * 3 * kMaxGrp + 4 * kGuStage;
 constexpr int kGuXPass = 8;    // float4 (or q8_1 dword) register passes: 1024 float blocks, 910 q8_1
@@ -1108,15 +1132,39 @@ __host__ __device__ inline int ly_down_bytes(int cap_entries, int Ud, bool with_
 // workgroups without a block take the extra tiles) go out at once; it waits until the count reaches
 // the grid (bounded), reads every entry's q8_1 rows of h and runs the down tiles and the scatter as
 // the down launch does. The last workgroup to finish clears the counts for the next call.
+// The routing waves' first loads need only the logits, the NL4 table, T and E: they come as the
+// leading scalar arguments (copies of the struct's fields), which the launch preloads into
+// scalar registers, so those loads go out before any read of the argument struct.
 template <int FMT, int MODE, int FD = FMT>
-__global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
+__global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict__ logits0,
+                                                        const int8_t* __restrict__ nl4_0, int T0,
+                                                        int E0, GuArgs a_) {
   constexpr bool RT = MODE == GU_ROUTED || MODE == GU_LAYER;
   extern __shared__ __align__(16) uint8_t smem[];
-  const Geom& G = a.G;
   // the wave index in a scalar register: everything derived from it is uniform over the wave
   const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63;
-  const uint64_t lt = (1ull << lane) - 1ull;
   MOE_LDS uint8_t* ring = (MOE_LDS uint8_t*)smem;
+  // ---- 1. every load that depends on nothing, at once. Routed: the routing waves (the first
+  //         kRtWaves) send the NL4 table and their first logits rows before anything else (from
+  //         the preloaded leading arguments) and load nothing more until they have routed (their
+  //         wait then covers those alone); the other waves take the tables, the expert pointers
+  //         and the destinations.
+  const bool rw = RT && wave < kRtWaves;   // a routing wave
+  MOE_LDS uint32_t* rscr = (MOE_LDS uint32_t*)ring + wave * route_scr_words(E0);
+  uint32_t t_nl4[4] = {0u, 0u, 0u, 0u};
+  if constexpr (RT) {
+    if (rw) {
+      __builtin_amdgcn_s_setprio(2);   // the launch waits on the routing: it goes first on its SIMD
+      // the table (hot in L2) goes out just ahead of the logits, so the routing wave's one wait on
+      // the logits covers it and nothing is loaded after the routing
+      load_nl4(nl4_0, t_nl4);
+      if (wave < T0) issue_logits(logits0 + (size_t)wave * E0, E0, (MOE_LDS float*)rscr);
+    }
+  }
+  (void)a_;
+  const GuArgs a = args_after<GuArgs>(kGuArgsOff);
+  const Geom& G = a.G;
+  const uint64_t lt = (1ull << lane) - 1ull;
   const ActSplit act = act_layout(ring + a.lds_ring, a.n_tokens, G.U);
   MOE_LDS uint8_t* p8 = ring + a.lds_ring + a.lds_act;
   MOE_LDS uint32_t* g2 = (MOE_LDS uint32_t*)p8;
@@ -1130,25 +1178,8 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(GuArgs a) {
   const int nW = (a.E + 31) >> 5;
   MOE_LDS uint32_t* selT = (MOE_LDS uint32_t*)(tail + 24 * a.E);     // routed: [T][nW]
 
-  // ---- 1. every load that depends on nothing, at once. Routed: the routing waves (the first
-  //         kRtWaves) send the NL4 table and their first logits rows before anything else and
-  //         load nothing more until they have routed (their wait then covers those alone); the
-  //         other waves take the tables, the expert pointers and the destinations.
-  warm_args<GuArgs>();
-  const bool rw = RT && wave < kRtWaves;   // a routing wave
   const int q0 = RT ? tid - 64 * kRtWaves : tid;   // thread index among the waves that load tables
-  MOE_LDS uint32_t* rscr = (MOE_LDS uint32_t*)ring + wave * route_scr_words(a.E);
-  uint32_t t_nl4[4] = {0u, 0u, 0u, 0u};
-  if constexpr (RT) {
-    if (rw) {
-      __builtin_amdgcn_s_setprio(2);   // the launch waits on the routing: it goes first on its SIMD
-      // the table (hot in L2) goes out just ahead of the logits, so the routing wave's one wait on
-      // the logits covers it and nothing is loaded after the routing
-      load_nl4(a.A.nl4, t_nl4);
-      if (wave < a.T) issue_logits(a.logits + (size_t)wave * a.E, a.E, (MOE_LDS float*)rscr);
-    }
-  }
-  if (!rw) load_nl4(a.A.nl4, t_nl4);
+  if (!rw) load_nl4(nl4_0, t_nl4);
   uint32_t t_cb = 0;
   if constexpr (FMT == CB2 || FMT == CB3) {
     const uint32_t* src = (const uint32_t*)(FMT == CB2 ? a.A.cb2 : a.A.cb3);
@@ -2841,7 +2872,7 @@ hipError_t launch_gu(int fmt, int fmt_down, int mode, const GuArgs& ga, int grid
   auto go = [&](auto kern) -> hipError_t {
     hipError_t e = allow_smem(kern, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGuThreads), bytes, st, ga);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGuThreads), bytes, st, ga.logits, ga.A.nl4, ga.T, ga.E, ga);
     return hipGetLastError();
   };
 #define MOE_LY(F, D) \
