@@ -2389,9 +2389,20 @@ constexpr int kPfBlk = kPfK / 32;
 constexpr int kPfRaw = 1040;           // LDS stride of the raw row slots: 1 KB loaded (a chunk is at most
                                        // 544 B) plus 16 B so that rows start on different banks
 constexpr int kPfCS = kPfK + 16;       // LDS row stride of the int8 codes and quants
+constexpr int kPfSS = 36;              // LDS block stride of the per-(block, row / entry) scales: a
+                                       // wave's stores (16 blocks x 4 rows) then meet every bank twice
 constexpr int kPfThreads = 256;
-constexpr int kPfLds = kPfRows * kPfRaw + (kPfRows + kPfEnt) * kPfCS + 4 * kPfBlk * 2 * (kPfRows + kPfEnt) +
+static_assert(kPfSS >= kPfRows && kPfSS >= kPfEnt && kPfSS % 4 == 0, "scale rows fit, float4 reads aligned");
+constexpr int kPfLds = kPfRows * kPfRaw + (kPfRows + kPfEnt) * kPfCS + 4 * kPfBlk * 4 * kPfSS +
                        4096 + 64;
+static_assert(2 * kPfLds <= 160 * 1024, "two prompt-path workgroups share a CU's LDS");
+// The (row, block) unit that decode slot x (0..511) of a chunk takes: each 64-slot wave pass
+// covers 8 rows x 8 blocks with the row fastest, so the 8 lanes that store their 32 codes to LDS
+// together write 8 different rows (row stride 132 dwords: distinct bank groups) rather than
+// blocks 32 bytes apart in one row.
+static_assert(kPfRows == 32 && kPfBlk == 16 && kPfRows * kPfBlk == 2 * kPfThreads, "decode slot map");
+__device__ __forceinline__ int pf_dec_row(int x) { return 8 * ((x >> 6) & 3) + (x & 7); }
+__device__ __forceinline__ int pf_dec_blk(int x) { return 8 * (x >> 8) + ((x >> 3) & 7); }
 
 struct PfArgs {
   LayerArgs A;
@@ -2413,10 +2424,10 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
   MOE_LDS uint8_t* codes = raw + kPfRows * kPfRaw;
   MOE_LDS uint8_t* quant = codes + kPfRows * kPfCS;
   MOE_LDS float* dws = (MOE_LDS float*)(quant + kPfEnt * kPfCS);   // [blk][row]
-  MOE_LDS float* mos = dws + kPfBlk * kPfRows;                      // [blk][row] (Q5_1 offsets)
-  MOE_LDS float* dxs = mos + kPfBlk * kPfRows;                      // [blk][entry]
-  MOE_LDS float* sxs = dxs + kPfBlk * kPfEnt;                       // [blk][entry] (sum fields)
-  MOE_LDS uint32_t* grid = (MOE_LDS uint32_t*)(sxs + kPfBlk * kPfEnt);   // CB2 / CB3 grid
+  MOE_LDS float* mos = dws + kPfBlk * kPfSS;                      // [blk][row] (Q5_1 offsets)
+  MOE_LDS float* dxs = mos + kPfBlk * kPfSS;                      // [blk][entry]
+  MOE_LDS float* sxs = dxs + kPfBlk * kPfSS;                       // [blk][entry] (sum fields)
+  MOE_LDS uint32_t* grid = (MOE_LDS uint32_t*)(sxs + kPfBlk * kPfSS);   // CB2 / CB3 grid
   MOE_LDS int* misc = (MOE_LDS int*)(grid + 1024);
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int g = (int)blockIdx.y;
@@ -2531,8 +2542,8 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
         MOE_LDS uint32_t* dq = (MOE_LDS uint32_t*)(quant + en * kPfCS + 32 * bl);
         *(MOE_LDS u32x4*)dq = u32x4{qq[j][1], qq[j][2], qq[j][3], qq[j][4]};
         *(MOE_LDS u32x4*)(dq + 4) = u32x4{qq[j][5], qq[j][6], qq[j][7], qq[j][8]};
-        dxs[bl * kPfEnt + en] = h2f(qq[j][0] & 0xFFFFu);
-        sxs[bl * kPfEnt + en] = h2f(qq[j][0] >> 16);
+        dxs[bl * kPfSS + en] = h2f(qq[j][0] & 0xFFFFu);
+        sxs[bl * kPfSS + en] = h2f(qq[j][0] >> 16);
       }
       __syncthreads();
       // (3) decode the raw rows into codes and scales: (row, block) pairs over the threads, the
@@ -2543,7 +2554,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
         bool dl[kD];
 #pragma unroll
         for (int j = 0; j < kD; ++j) {
-          const int x = tid + j * kPfThreads, r = x / kPfBlk, bl = x - r * kPfBlk;
+          const int x = tid + j * kPfThreads, r = pf_dec_row(x), bl = pf_dec_blk(x);
           dl[j] = r0 + r < a.rows && bl < nblk;
           const uint64_t src = wp + (uint64_t)(r0 + r) * (uint64_t)a.rb + (uint64_t)(kc / bw * bb);
           const uint32_t row = (uint32_t)(r * kPfRaw) + (uint32_t)(src & 15u);   // from raw
@@ -2551,7 +2562,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < kD; ++j) {
-          const int x = tid + j * kPfThreads, r = x / kPfBlk, bl = x - r * kPfBlk;
+          const int x = tid + j * kPfThreads, r = pf_dec_row(x), bl = pf_dec_blk(x);
           uint32_t c[8];
           float sc, mo;
           unit_decode<FMT>(rr[j], bl, tb, c, sc, mo);
@@ -2564,8 +2575,8 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
           MOE_LDS uint32_t* dc = (MOE_LDS uint32_t*)(codes + r * kPfCS + 32 * bl);
           *(MOE_LDS u32x4*)dc = u32x4{c[0], c[1], c[2], c[3]};
           *(MOE_LDS u32x4*)(dc + 4) = u32x4{c[4], c[5], c[6], c[7]};
-          dws[bl * kPfRows + r] = sc;
-          mos[bl * kPfRows + r] = mo;
+          dws[bl * kPfSS + r] = sc;
+          mos[bl * kPfSS + r] = mo;
         }
       }
       __syncthreads();
@@ -2582,14 +2593,14 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
         typedef int v4i __attribute__((ext_vector_type(4)));
         const v4i z = {0, 0, 0, 0};
         const v4i d = __builtin_amdgcn_mfma_i32_16x16x32_i8(av, bv, z, 0, 0, 0);
-        const f32x4 dw = *(const MOE_LDS f32x4*)(dws + bl * kPfRows + 16 * mt + 4 * q);
-        const float dx = dxs[bl * kPfEnt + 16 * nt + l16];
+        const f32x4 dw = *(const MOE_LDS f32x4*)(dws + bl * kPfSS + 16 * mt + 4 * q);
+        const float dx = dxs[bl * kPfSS + 16 * nt + l16];
         float mw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         float sx = 0.0f;
         if constexpr (FMT == Q5_1) {
-          const f32x4 m4 = *(const MOE_LDS f32x4*)(mos + bl * kPfRows + 16 * mt + 4 * q);
+          const f32x4 m4 = *(const MOE_LDS f32x4*)(mos + bl * kPfSS + 16 * mt + 4 * q);
           mw[0] = m4.x; mw[1] = m4.y; mw[2] = m4.z; mw[3] = m4.w;
-          sx = sxs[bl * kPfEnt + 16 * nt + l16];
+          sx = sxs[bl * kPfSS + 16 * nt + l16];
         }
         const float dwv[4] = {dw.x, dw.y, dw.z, dw.w};
 #pragma unroll
