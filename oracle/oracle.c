@@ -253,9 +253,12 @@ int orc_matvec(int fmt, const uint8_t* mat, int rows, int ncols, const uint8_t* 
 
 void orc_swiglu(const float* g, const float* u, int n, float* h) {
   for (int i = 0; i < n; ++i) {
-    double gd = (double)g[i];
-    double silu = gd / (1.0 + exp(-gd));
-    h[i] = (float)(silu * (double)u[i]);
+    /* float32 throughout, one rounding per operation in this order (no contraction: the file is
+     * built with -ffp-contract=off); expf is libm's single-precision exponential */
+    float e = expf(-g[i]);
+    float den = 1.0f + e;
+    float silu = g[i] / den;
+    h[i] = silu * u[i];
   }
 }
 

@@ -57,7 +57,10 @@ int orc_matvec(int fmt, const uint8_t* mat, int rows, int ncols, const uint8_t* 
                const int8_t* nl4_table, const uint8_t* cb2_grid, const uint8_t* cb3_grid,
                double* out, double* S);
 
-/* h = silu(g) * u = g / (1 + exp(-g)) * u, evaluated in double and rounded once to float32. */
+/* h = silu(g) * u, evaluated in float32 one operation at a time: e = expf(-g), den = 1 + e,
+ * s = g / den, h = s * u, each result rounded to float32 ([GROUPED] "What changes": the product
+ * is rounded on its own before the q8_1 block sums). expf overflows to +inf for g < -88.72, so h
+ * is then a signed zero. */
 void orc_swiglu(const float* g, const float* u, int n, float* h);
 
 /* Per token: top-k experts by (logit descending, id ascending); weights are the softmax over the
