@@ -33,6 +33,10 @@ PREFILL = {
     "nl4_2560x768_t24": dict(n_embd=2560, n_ff=768, E=128, k=8, T=24, fg=NL4, fd=NL4),
 }
 
+# the benchmarked prompt-path shape: 512 tokens, top-8 of 128 NL4 experts of 2560 x 768 (every
+# expert routed, about 32 entries per group: many 32-entry passes over five K chunks of 512)
+BENCH = dict(n_embd=2560, n_ff=768, E=128, k=8, T=512, fg=NL4, fd=NL4)
+
 
 def _case(name, key=0):
     p = PREFILL[name]
@@ -106,3 +110,67 @@ def test_prefill_plan_large():
     assert np.array_equal(np.sort(eo), np.arange(T * k))   # a bijection onto the entries
     assert np.array_equal(ph["ent_src"][eo], np.repeat(np.arange(T), k))
     assert plan.errors() == 0
+
+
+def test_prefill_bench_shape():
+    """The prompt path at the shape the benchmark times, launched as it launches it (entries from
+    0, each token its own destination row): the plan bit for bit, x's q8_1 bytes for every token,
+    and g, u, h, hq, the per-entry down rows O and Y element by element on a seeded sample of 48
+    tokens (their 384 entries), each against the oracle fed the GPU's upstream values."""
+    p = BENCH
+    c = U.routed_case("prefill_bench", p["n_embd"], p["n_ff"], p["E"], p["k"], p["T"], p["fg"], p["fd"], 5)
+    T, k, d, n = c.T, c.k, U.dev(), c.T * c.k
+    plan = B.Plan(c.E, n, device=d)
+    ids, w = B.moe_route_topk(torch.from_numpy(c.logits).to(d), k)
+    ent_of = B.moe_prefill_plan(ids, w, plan, c.E)
+    ph = plan.get()
+    ref = oracle.build_plan(ids.cpu().numpy(), w.cpu().numpy(), None, c.E, 0)
+    for key in ("n_groups", "grp_expert", "grp_start", "ent_src", "ent_dst"):
+        assert np.array_equal(np.asarray(ph[key]), np.asarray(ref[key])), key
+    assert np.array_equal(U.bits(ph["ent_w"]), U.bits(ref["ent_w"]))
+    sizes = np.diff(ph["grp_start"])
+    assert ph["n_groups"] == c.E and sizes.max() > 32, sizes
+    xq = B.moe_quantize_q8_1(torch.from_numpy(c.x).to(d))
+    g = torch.empty((n, c.n_ff), dtype=torch.float32, device=d)
+    u = torch.empty_like(g)
+    h = torch.empty_like(g)
+    hq = torch.empty((n, c.n_ff // 32 * 36), dtype=torch.uint8, device=d)
+    O = torch.empty((n, c.n_embd), dtype=torch.float32, device=d)
+    Y0 = synth.rng(78, T).standard_normal((T, c.n_embd)).astype(np.float32)
+    Y = torch.from_numpy(Y0.copy()).to(d)
+    B.moe_prefill_gate_up(c.layer, plan, xq, g, u)
+    B.moe_prefill_swiglu_q8_1(plan, g, u, c.n_ff, hq, h=h)
+    B.moe_prefill_down(c.layer, plan, hq, O)
+    B.moe_prefill_scatter(plan, ent_of, O, Y, c.n_embd)
+    torch.cuda.synchronize()
+    assert plan.errors() == 0
+    xq_h = xq.cpu().numpy()
+    U.assert_q81_equal(xq_h, oracle.quantize_q8_1(c.x), c.x, "xq")
+    g_h, u_h, h_h, hq_h = g.cpu().numpy(), u.cpu().numpy(), h.cpu().numpy(), hq.cpu().numpy()
+    O_h, Y_h, eo = O.cpu().numpy(), Y.cpu().numpy(), ent_of.cpu().numpy()
+    ids_h = ids.cpu().numpy()
+    group_of = np.searchsorted(ph["grp_start"], np.arange(n), "right") - 1
+    worst = 0.0
+    for t in sorted(synth.rng(79).choice(T, 48, replace=False)):
+        yr = Y0[t].astype(np.float64)
+        sy = np.abs(yr)
+        for j in range(k):
+            a = int(eo[t, j])
+            e = int(ph["grp_expert"][group_of[a]])
+            assert ph["ent_src"][a] == t and e == ids_h[t, j]
+            gr, Sg = oracle.matvec(c.fmt_gu, c.gate[e], c.n_ff, c.n_embd, xq_h[t], c.tables)
+            ur, Su = oracle.matvec(c.fmt_gu, c.up[e], c.n_ff, c.n_embd, xq_h[t], c.tables)
+            worst = max(worst, U.check_close(g_h[a], gr, Sg, f"g entry {a}"))
+            worst = max(worst, U.check_close(u_h[a], ur, Su, f"u entry {a}"))
+            hr = oracle.swiglu(g_h[a], u_h[a]).astype(np.float64)
+            ulp = np.spacing(np.abs(hr).astype(np.float32)).astype(np.float64)
+            assert np.all(np.abs(h_h[a].astype(np.float64) - hr) <= 4 * ulp + 1e-30), f"h entry {a}"
+            U.assert_q81_equal(hq_h[a], oracle.quantize_q8_1(h_h[a]), h_h[a], f"hq entry {a}")
+            o, So = oracle.matvec(c.fmt_dn, c.down[e], c.n_embd, c.n_ff, hq_h[a], c.tables)
+            wa = float(ph["ent_w"][a])
+            worst = max(worst, U.check_close(O_h[a], wa * o, abs(wa) * So, f"O entry {a}"))
+            yr = yr + wa * o
+            sy = sy + abs(wa) * So
+        worst = max(worst, U.check_close(Y_h[t], yr, sy, f"Y row {t}"))
+    print(f"prefill bench shape: {ph['n_groups']} groups, largest {sizes.max()} entries, "
+          f"worst err/S {worst:.3g}")
