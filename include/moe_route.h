@@ -207,32 +207,42 @@ int moe_build_plan(void* stream, const int32_t* ids, const float* w, const int32
  * 36 B (layout above), bit-exact IEEE float32 ("#363 ...", "What changes": the quantizer). */
 int moe_quantize_q8_1(void* stream, const float* x, int rows, int n, void* q);
 
-/* Grouped gate/up: for each entry a of the call (group g, expert e) and row r < n_ff,
+/* Grouped gate/up ("#2058 ...", "Why" and "What changed": each expert's gate and up weights are
+ * decoded once per group and dotted with the q8_1 rows of the group's 1-4 entries; "#363 ...",
+ * "What changes": the call covers its own entries, n_groups read on the device).
+ * For each entry a of the call (group g, expert e) and row r < n_ff,
  * g[a][r] = sum_b c_b(gate_e row r, xq row ent_src[a]) and the same for u with up_e.
  * xq: n_tokens rows of n_embd/32 q8_1 blocks. g, u: float32 rows of stride ld >= n_ff, indexed by
  * absolute entry; only the call's entries' rows are written. */
 int moe_gate_up(void* stream, const moe_layer* L, const moe_plan* P, const void* xq, int n_tokens,
                 float* g, float* u, int ld, int grid_limit);
 
-/* Fused SwiGLU + q8_1 over the call's entries: h = (g / (1 + exp(-g))) * u, each operation a
- * float32 rounding, then hq = q8_1(h). h may be NULL. hq rows: n_ff/32 blocks per absolute entry;
+/* Fused SwiGLU + q8_1 over the call's entries ("#363 ...", "What changes": one kernel over the
+ * call's own entries, the SwiGLU product rounded on its own before the q8_1 block sums; "Measured":
+ * the fused kernel against the two it replaces): e = expf(-g), h = (g / (1 + e)) * u, each
+ * operation a float32 rounding in that order, then hq = q8_1(h). h may be NULL. hq rows: n_ff/32 blocks per absolute entry;
  * h rows: stride ld. Only the call's entries are read or written. */
 int moe_swiglu_q8_1(void* stream, const moe_plan* P, const float* g, const float* u, int n_ff,
                     int ld, float* h, void* hq);
 
-/* Grouped down + weighted scatter: o_a[m] = sum_b c_b(down_e row m, hq row a) for m < n_embd, then
+/* Grouped down + weighted scatter ("#2058 ...", "Why": the down projection grouped by expert like
+ * gate/up, each token's expert outputs weighted by its router weights and added up; "#363 ...",
+ * "Exactness": scattered destinations, rows no entry names keep their contents, results
+ * independent of the grid): o_a[m] = sum_b c_b(down_e row m, hq row a) for m < n_embd, then
  * Y[ent_dst[a]][m] = Y + sum over the call's entries with that destination, in ascending entry
  * order, of ent_w[a] * o_a[m] (float32, each product and sum rounded). Y: n_rows rows of stride
  * ldy; rows no entry names are neither read nor written. hq: q8_1 rows by absolute entry. */
 int moe_down_scatter(void* stream, const moe_layer* L, const moe_plan* P, const void* hq,
                      float* Y, int n_rows, int ldy, int grid_limit);
 
-/* Host: bytes of workspace the single-call paths need for this layer and plan capacity (the
+/* Host: bytes of workspace the single-call paths need for this layer and plan capacity ("#363
+ * ...", "Exactness": stale scratch contents must not matter, which this workspace meets; the
  * call's descriptor for the down launch and the q8_1 rows of h). The workspace is 256-byte aligned and
  * needs no clearing: a call reads only bytes it wrote itself. */
 size_t moe_workspace_bytes(const moe_layer* L, const moe_plan* P);
 
-/* The whole step for the call's entries in two launches: q8_1(x rows) -> grouped gate/up ->
+/* The whole step for the call's entries in two launches ("#363 ...", opening paragraph and
+ * "What changes": fewer launches per call; "#2058 ...", "Why"): q8_1(x rows) -> grouped gate/up ->
  * SwiGLU + q8_1 -> grouped down -> weighted scatter into Y. x: n_tokens float32 rows of n_embd
  * (16-byte aligned). Bit-identical to the composed calls quantize -> gate_up -> swiglu ->
  * down_scatter. Calls that overlap on one workspace race; calls in one stream do not. */
@@ -250,7 +260,9 @@ int moe_layer_decode_routed(void* stream, const moe_layer* L, const moe_plan* P,
                             int entry_base, const float* x, float* Y, int n_rows, int ldy,
                             void* workspace, size_t ws_bytes, int grid_limit);
 
-/* The whole step from the router logits in ONE launch (same results, bit for bit, as
+/* EXPERIMENTAL, on no default path: slower than the two launches on MI355X (the cross-workgroup
+ * wait costs more than the launch it saves) and dependent on every workgroup being resident.
+ * The whole step from the router logits in ONE launch (same results, bit for bit, as
  * moe_layer_decode_routed): every workgroup routes and groups, runs its gate/up blocks with SwiGLU
  * and q8_1 ("#363 ...", "What changes"), then, once every workgroup of the launch has finished its
  * blocks, the grouped down projection and the weighted scatter ("#2058 ...", "Why"; "#363 ...",

@@ -18,7 +18,7 @@ Q8_0, NL4, CB2, CB3, Q5_1, NL4X = 1, 2, 3, 4, 5, 6
 BLOCK_BYTES = {Q8_0: 34, NL4: 18, CB2: 70, CB3: 110, Q5_1: 24, NL4X: 136}
 BLOCK_WEIGHTS = {Q8_0: 32, NL4: 32, CB2: 256, CB3: 256, Q5_1: 32, NL4X: 256}
 
-ERR_BITS = {1: "NGROUPS", 2: "ENTRIES", 4: "EXPERT", 8: "SRC", 16: "DST", 32: "ALIGN"}
+ERR_BITS = {1: "NGROUPS", 2: "ENTRIES", 4: "EXPERT", 8: "SRC", 16: "DST", 32: "ALIGN", 64: "WAIT"}
 
 EXPORTS = ("moe_route_topk", "moe_build_plan", "moe_quantize_q8_1", "moe_repack", "moe_gate_up",
            "moe_swiglu_q8_1", "moe_down_scatter", "moe_workspace_bytes",

@@ -21,7 +21,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace moe {
 
-constexpr int kThreads = 256;          // every kernel runs 4 waves of 64
+constexpr int kThreads = 256;          // the small kernels (quantize, SwiGLU, repack, scatter): 4 waves of 64
 constexpr int kMaxSlots = 4;           // entries staged at once (a group's rows of the window)
 
 enum Fmt : int { Q8_0 = 1, NL4 = 2, CB2 = 3, CB3 = 4, Q5_1 = 5, NL4X = 6 };
