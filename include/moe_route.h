@@ -276,6 +276,21 @@ int moe_layer_step(void* stream, const moe_layer* L, const moe_plan* P, const fl
                    int k, const int32_t* dst_of_token, int entry_base, const float* x, float* Y,
                    int n_rows, int ldy, void* workspace, size_t ws_bytes, int grid_limit);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): moe_layer_decode_routed with the workspace taken from
+ * a static device array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends; nothing is allocated or freed. Same arguments, results and limits
+ * as moe_layer_decode_routed (bit-identical), minus the workspace. A layer and plan whose
+ * workspace (moe_workspace_bytes) exceeds MOE_NOALLOC_SCRATCH_BYTES gives MOE_E_WS before
+ * anything is enqueued. Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (other streams, other threads) race; calls in one stream do not. The first call on a device
+ * looks the array's address up (hipGetSymbolAddress) with that device current. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)512 << 10)
+int moe_layer_decode_routed_noalloc(void* stream, const moe_layer* L, const moe_plan* P,
+                                    const float* logits, int T, int k, const int32_t* dst_of_token,
+                                    int entry_base, const float* x, float* Y, int n_rows, int ldy,
+                                    int grid_limit);
+
 /* The first of the two launches of moe_layer_decode (logits == NULL: the plan in P as built) or
  * of moe_layer_decode_routed (logits != NULL: route and group here, publish the plan into P;
  * then n_tokens must equal T). Leaves the call's descriptor and the q8_1 rows of h in the

@@ -22,7 +22,7 @@ ERR_BITS = {1: "NGROUPS", 2: "ENTRIES", 4: "EXPERT", 8: "SRC", 16: "DST", 32: "A
 
 EXPORTS = ("moe_route_topk", "moe_build_plan", "moe_quantize_q8_1", "moe_repack", "moe_gate_up",
            "moe_swiglu_q8_1", "moe_down_scatter", "moe_workspace_bytes",
-           "moe_layer_decode", "moe_layer_decode_routed", "moe_layer_step", "moe_layer_gate_up",
+           "moe_layer_decode", "moe_layer_decode_routed", "moe_layer_decode_routed_noalloc", "moe_layer_step", "moe_layer_gate_up",
            "moe_layer_down",
            "moe_workspace_layout", "moe_prefill_plan", "moe_prefill_gate_up", "moe_prefill_swiglu_q8_1",
            "moe_prefill_down", "moe_prefill_scatter",
@@ -68,6 +68,8 @@ def lib():
         L.moe_layer_decode_routed.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan),
                                               _P, _I, _I, _P, _I, _P, _P, _I, _I, _P,
                                               ctypes.c_size_t, _I]
+        L.moe_layer_decode_routed_noalloc.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan),
+                                                      _P, _I, _I, _P, _I, _P, _P, _I, _I, _I]
         L.moe_layer_step.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan),
                                      _P, _I, _I, _P, _I, _P, _P, _I, _I, _P, ctypes.c_size_t, _I]
         L.moe_layer_gate_up.argtypes = [_P, ctypes.POINTER(MoeLayer), ctypes.POINTER(MoePlan), _P, _I,
@@ -97,7 +99,7 @@ def _check(rc: int, what: str):
     if rc != 0:
         L = lib()
         msg = L.moe_status_string(rc).decode()
-        extra = L.moe_last_error().decode() if rc == -4 else ""
+        extra = L.moe_last_error().decode() if rc in (-4, -5) else ""
         raise RuntimeError(f"{what}: {msg} ({rc}) {extra}")
 
 
@@ -337,6 +339,18 @@ def moe_layer_decode_routed(layer: Layer, plan: Plan, logits, k, x, Y, ws, dst_o
                                          _ptr(dst_of_token), entry_base, _ptr(x), _ptr(Y), Y.shape[0],
                                          Y.stride(0), _ptr(ws), ws.numel(), grid_limit),
            "moe_layer_decode_routed")
+
+
+def moe_layer_decode_routed_noalloc(layer: Layer, plan: Plan, logits, k, x, Y, dst_of_token=None,
+                                    entry_base=0, grid_limit=0, stream=None):
+    """moe_layer_decode_routed with the library's static scratch as its workspace (nothing is
+    allocated); calls that overlap on one GPU race."""
+    T = logits.shape[0]
+    _check(lib().moe_layer_decode_routed_noalloc(_stream(stream), ctypes.byref(layer.struct),
+                                                 ctypes.byref(plan.struct), _ptr(logits), T, k,
+                                                 _ptr(dst_of_token), entry_base, _ptr(x), _ptr(Y), Y.shape[0],
+                                                 Y.stride(0), grid_limit),
+           "moe_layer_decode_routed_noalloc")
 
 
 def moe_layer_step(layer: Layer, plan: Plan, logits, k, x, Y, ws, dst_of_token=None, entry_base=0,

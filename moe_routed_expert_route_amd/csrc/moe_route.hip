@@ -38,6 +38,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe_route.h"
@@ -2708,9 +2709,47 @@ __global__ __launch_bounds__(kThreads) void k_pf_scatter(PlanArgs P, const int32
 
 thread_local std::string t_last_error;
 
+
 int hip_fail(hipError_t e, const char* what) {
   t_last_error = std::string(what) + ": " + hipGetErrorString(e);
   return MOE_E_HIP;
+}
+
+// ------------------------------------------------------------------ static scratch ----------
+
+// Workspace of moe_layer_decode_routed_noalloc, for callers that cannot allocate: one array per
+// device, held until the process ends. Host code never uses the array's name as an address (on
+// the host it is only a stand-in for the symbol); it asks the runtime for the device address once
+// per device and passes that pointer on.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kScratchDevices = 64;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call on each device).
+int scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices) {
+    t_last_error = "device index beyond the scratch table";
+    return MOE_E_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) {
+      t_last_error = "hipGetSymbolAddress(scratch) gave a null address";
+      return MOE_E_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 // A layer's format field: the encoding (moe_fmt) with MOE_LAYOUT_PLANAR optionally OR-ed in.
@@ -3405,6 +3444,25 @@ int moe_layer_decode_routed(void* stream, const moe_layer* L, const moe_plan* P,
                                    ws_bytes, grid_limit);
   if (rc) return rc;
   return moe_layer_down(stream, L, P, ws, ws_bytes, T, Y, n_rows, ldy, grid_limit);
+}
+
+int moe_layer_decode_routed_noalloc(void* stream, const moe_layer* L, const moe_plan* P, const float* logits,
+                                    int T, int k, const int32_t* dst_of_token, int entry_base, const float* x,
+                                    float* Y, int n_rows, int ldy, int grid_limit) {
+  int rc = check_layer(L, true);
+  if (rc) return rc;
+  if ((rc = check_plan(P))) return rc;
+  // the size check needs no device: an oversize layer is rejected before anything is enqueued
+  const size_t need = ws_layout(L, P).total;
+  if (need > kScratchBytes) {
+    t_last_error = "moe_layer_decode_routed_noalloc: the layer needs " + std::to_string(need) +
+                   " bytes of workspace, more than the " + std::to_string(kScratchBytes) + " of the static scratch";
+    return MOE_E_WS;
+  }
+  void* ws = nullptr;
+  if ((rc = scratch_ptr(&ws))) return rc;
+  return moe_layer_decode_routed(stream, L, P, logits, T, k, dst_of_token, entry_base, x, Y, n_rows, ldy, ws,
+                                 kScratchBytes, grid_limit);
 }
 
 }  // extern "C"
