@@ -11,16 +11,19 @@ routing of the layer's logits, grouping of the entries by expert, q8_1 of x, gro
 SwiGLU + q8_1 of h; (2) grouped down + weighted scatter into Y. Steps are replayed from a HIP
 graph.
 
-Printed: one JSON line. value = expert-weight GB/s (distinct routed experts' bytes per pass / time
-per pass); us_per_layer_call = time per layer; roofline = the dominant kernel alone (a HIP graph
-of its 48 launches replayed between HIP events on its stream); t_sweep = the same measurement
-at T = 1..4 (shared experts: the per-extra-row cost; the 256-expert CB3/Q8_0 geometry with
-uniform routing); cpu_baseline = the CPU oracle on a sample of layer calls.
+Printed: one JSON line. value = expert-weight GB/s (distinct routed experts' bytes per pass / the
+median time per pass over the timed replays, each replay bracketed by its own HIP events);
+us_per_layer_call = time per layer; roofline = the dominant kernel alone (a HIP graph of its 48
+launches, the median of several replays between HIP events on its stream), with the committed
+rocprofv3 trace's figure beside it when the kernel sources are the traced ones; in-line
+comparisons (planar vs row-major, one vs two calls) alternate their arms A B / B A; t_sweep = the
+same measurement at T = 1..4 (shared experts: the per-extra-row cost; the 256-expert CB3/Q8_0
+geometry with uniform routing); cpu_baseline = the CPU oracle on a sample of layer calls, on one
+thread and on all cores.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,10 +33,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# what the kernels' machine code follows from: the sources and the compiler flags
-KERNEL_SOURCES = ("moe_routed_expert_route_amd/csrc/moe_route.hip",
-                  "moe_routed_expert_route_amd/csrc/moe_device.hpp",
-                  "moe_routed_expert_route_amd/build.py")
 
 
 def log(msg):
@@ -41,11 +40,9 @@ def log(msg):
 
 
 def source_digest():
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
+    """SHA-256 of what the kernels' machine code follows from: the sources and the build flags."""
+    from moe_routed_expert_route_amd.profsum import source_digest as d
+    return d()
 
 
 def barrier():
@@ -54,27 +51,54 @@ def barrier():
         dist.barrier()
 
 
-def time_graph(graph, n):
-    """ms per replay of `graph` over n replays (HIP events on the replay stream), bracketed by a
-    barrier and a device synchronize on both sides."""
+def replay_ms(graph, n, stream=None):
+    """ms of each of n replays of `graph` (a HIP event after every replay, on the stream the
+    replays run on), bracketed by a barrier and a device synchronize on both sides."""
     import torch
     barrier()
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(n):
-        graph.replay()
-    ev1.record()
+    st = stream if stream is not None else torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    with torch.cuda.stream(st):
+        ev[0].record(st)
+        for i in range(n):
+            graph.replay()
+            ev[i + 1].record(st)
     torch.cuda.synchronize()
     barrier()
-    return ev0.elapsed_time(ev1) / n
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+
+
+def median(v):
+    import numpy as np
+    return float(np.median(np.asarray(v, dtype=np.float64)))
+
+
+def time_graph(graph, n):
+    """Median ms per replay of `graph` over n replays."""
+    return median(replay_ms(graph, n))
+
+
+def alternate(graphs, rounds=6, per=5):
+    """In-line A/B comparison: the graphs (name -> graph) replayed in turn, A B, B A, A B, ... for
+    `rounds` rounds of `per` replays each (so a clock change of the card falls on both arms), every
+    replay timed with its own HIP events. Returns name -> {median ms, per-visit medians}."""
+    names = list(graphs)
+    times = {k: [] for k in names}
+    visits = {k: [] for k in names}
+    for r in range(rounds):
+        for k in (names if r % 2 == 0 else names[::-1]):
+            t = replay_ms(graphs[k], per)
+            times[k] += t
+            visits[k].append(round(median(t), 4))
+    return {k: {"median_ms": median(times[k]), "visit_medians_ms": visits[k],
+                "replays": len(times[k])} for k in names}
 
 
 def kernel_us(wl, reps):
-    """Average duration of each launch kind (gate/up, down): a HIP graph of the kind's launches for
-    every layer, replayed `reps` times between HIP events on its stream, divided by the launch
-    count (kernels of one graph run back to back, so this is the kernels' own time)."""
+    """Duration of each launch kind (gate/up, down): a HIP graph of the kind's launches for every
+    layer, each of `reps` replays timed between HIP events on its stream; the median replay divided
+    by the launch count (kernels of one graph run back to back, so this is the kernels' own time)."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -87,21 +111,14 @@ def kernel_us(wl, reps):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(s)
-        with torch.cuda.stream(s):
-            for _ in range(reps):
-                g.replay()
-        b.record(s)
-        torch.cuda.synchronize()
-        out[kind] = a.elapsed_time(b) * 1e3 / (reps * wl.L)
+        out[kind] = median(replay_ms(g, reps, stream=s)) * 1e3 / wl.L
         del g
     return out
 
 
-def measure(wl, steps, warmup, reps=5):
-    """Graph-replayed step time, plain-stream step time and per-kernel launch times."""
+def measure(wl, steps, warmup, reps=9):
+    """Graph-replayed step time (median of `steps` replays), plain-stream step time and per-kernel
+    launch times."""
     import torch
     wl.step()
     torch.cuda.synchronize()
@@ -116,7 +133,9 @@ def measure(wl, steps, warmup, reps=5):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
-    ms_step = time_graph(g, steps)
+    per = replay_ms(g, steps)
+    ms_step = median(per)
+    wl.last_replays = per
     t0 = time.perf_counter()
     for _ in range(3):
         wl.step()
@@ -127,26 +146,60 @@ def measure(wl, steps, warmup, reps=5):
     return ms_step, ms_plain, ks
 
 
-def stream_read_gbs(gib=2, reps=5):
-    """A plain streaming read of `gib` GiB (torch's sum over float32) timed with HIP events: the
-    bandwidth a simple kernel gets from HBM on this device, reported beside the HBM peak."""
+def step_graph(wl):
+    """A HIP graph of one step of the workload (captured on a side stream), replayed once."""
     import torch
-    n = gib << 28
-    t = torch.ones(n, dtype=torch.float32, device="cuda")
-    t.sum()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        wl.step()
     torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        t.sum()
-    b.record()
+    g.replay()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
-    del t
+    return g
+
+
+def stream_read_gbs(gib=2, reps=7):
+    """The library's own streaming read (moe_stream_read: 16-byte non-temporal loads, eight in
+    flight per lane, every CU an equal share) over `gib` GiB, for a few grid sizes; each launch
+    timed with HIP events on its stream, the median of `reps` per grid, the best grid reported:
+    the bandwidth a plain read reaches from HBM on this device, beside the 8 TB/s peak."""
+    import numpy as np
+    import torch
+
+    from moe_routed_expert_route_amd import binding as B
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.view(torch.int32).copy_(torch.arange(n // 4, dtype=torch.int32, device="cuda"))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(64 * cus, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    res = {}
+    with torch.cuda.stream(s):
+        for m in (4, 8, 16, 32, 64):
+            grid = m * cus
+            B.moe_stream_read(buf, out, grid, stream=s)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            ev[0].record(s)
+            for i in range(reps):
+                B.moe_stream_read(buf, out, grid, stream=s)
+                ev[i + 1].record(s)
+            torch.cuda.synchronize()
+            res[grid] = median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+    # the XOR of the workgroups' words is the buffer's: words 0..n/4-1, so x ^ (x + 1) pairs cancel
+    got = int(np.bitwise_xor.reduce(out[:grid].cpu().numpy().astype(np.uint32)))
+    assert got == 0, f"stream read checksum {got:#x}"
+    best = min(res, key=res.get)
+    del buf
     torch.cuda.empty_cache()
-    return {"gbs": round(4.0 * n / (ms * 1e-3) / 1e9, 1), "bytes": 4 * n,
-            "kind": "torch sum over a float32 tensor, HIP events, mean of 5"}
+    return {"gbs": round(n / (res[best] * 1e-3) / 1e9, 1), "bytes": n, "grid": best,
+            "workgroup_threads": 256,
+            "gbs_by_grid": {str(g): round(n / (t * 1e-3) / 1e9, 1) for g, t in res.items()},
+            "kind": "moe_stream_read (this library's k_stream_read: 16-byte non-temporal loads, "
+                    "8 per lane in flight, every CU an equal share), HIP events, median of 7 "
+                    "launches per grid, best grid"}
 
 
 def empty_call_us(layers=48, reps=20):
@@ -216,7 +269,7 @@ def two_calls_us(wl, reps=20):
         n2.append(pb["n_groups"])
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    out = {}
+    graphs = {}
     for name, calls in (("one_call", [(one[l],) for l in range(wl.L)]),
                         ("two_calls", [(first[l], second[l]) for l in range(wl.L)])):
         g = torch.cuda.CUDAGraph()
@@ -226,14 +279,18 @@ def two_calls_us(wl, reps=20):
                     B.moe_layer_decode(wl.layers[l], p, wl.d_x[l], wl.Y[l], wl.ws[l])
         torch.cuda.synchronize()
         g.replay()
-        out[name] = time_graph(g, reps) * 1e3 / wl.L
-        del g
+        graphs[name] = g
+    ab = alternate(graphs, rounds=6, per=max(2, reps // 4))
+    out = {k: v["median_ms"] * 1e3 / wl.L for k, v in ab.items()}
+    del graphs
     assert not any(p.errors() for p in one + first)
     return {"us_per_layer_one_call": round(out["one_call"], 3),
             "us_per_layer_two_calls": round(out["two_calls"], 3),
             "us_second_call": round(out["two_calls"] - out["one_call"], 3),
             "groups_in_second_call": sorted(set(n2)),
-            "config": "plan given (routed once beforehand), moe_layer_decode per call, graph of all layers"}
+            "ab": {k: v["visit_medians_ms"] for k, v in ab.items()},
+            "config": "plan given (routed once beforehand), moe_layer_decode per call, graph of all "
+                      "layers; the two graphs alternated A B / B A over 6 rounds, medians"}
 
 
 def prefill_line(T=512, layers=2, reps=10):
@@ -346,6 +403,23 @@ def fit_groups_entries(lines):
             "us_per_entry": round(float(coef[2]), 3), "lines": len(lines)}
 
 
+def profile_for(workload, kind, bytes_per_launch):
+    """The committed rocprofv3 kernel-trace summary of `workload` for launch `kind`: its average
+    duration and the roofline fraction it gives for `bytes_per_launch`, or None when there is none
+    or the kernel sources changed since it was taken."""
+    p = os.path.join(ROOT, "profiles", f"kernels_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        doc = json.load(f)
+    if doc.get("source_sha256") != source_digest() or kind not in doc.get("kernels", {}):
+        return None
+    k = doc["kernels"][kind]
+    ach = bytes_per_launch / (k["avg_ns"] * 1e-9) / 1e9
+    return {"file": f"profiles/kernels_{workload}.md", "avg_launch_us": round(k["avg_ns"] / 1e3, 3),
+            "calls": k["calls"], "achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBS, 4)}
+
+
 def traffic_for(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary of `workload`, or None
     when there is none or the kernel sources changed since the counters were taken."""
@@ -360,18 +434,23 @@ def traffic_for(workload, kernel):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def sweep_line(name, T, routing, steps, warmup):
+def sweep_line(name, T, routing, steps, warmup, cpu_seconds=0.0, model=None):
+    """One workload's graph-replayed step and launch times; with cpu_seconds, the CPU oracle on a
+    sample of its layer calls too (one thread and all cores)."""
     import torch
 
     from moe_routed_expert_route_amd.workloads import Workload
     wl = Workload(name, device="cuda", T=T, routing=routing)
-    ms_step, _, ks = measure(wl, steps, warmup, reps=2)
+    ms_step, _, ks = measure(wl, steps, warmup, reps=5)
     bytes_pass = float(sum(wl.weight_bytes_per_layer()))
     us = ms_step * 1e3 / wl.L
     line = {"T": T, "routing": routing, "us_per_layer_call": round(us, 3),
             "gbs": round(bytes_pass / (ms_step * 1e-3) / 1e9, 1),
             "distinct_experts_per_layer": round(sum(wl.distinct_experts(l) for l in range(wl.L)) / wl.L, 2),
             "gate_up_us": round(ks["gate_up"], 3), "down_us": round(ks["down"], 3)}
+    if cpu_seconds > 0:
+        log(f"cpu oracle on {name} T={T}")
+        line["cpu_oracle"] = run_cpu_baseline(wl, cpu_seconds, model, layers=4)
     del wl
     torch.cuda.empty_cache()
     return line
@@ -396,6 +475,7 @@ def main():
               "runs on a single GPU (the path would shard by expert ownership, one rank per GPU)",
               file=sys.stderr)
         sys.exit(2)
+    model = cpu_model() if not args.no_cpu else None
 
     import torch
 
@@ -448,6 +528,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_replays": {"n": len(wl.last_replays), "median_ms": round(ms_step, 4),
+                         "mean_ms": round(sum(wl.last_replays) / len(wl.last_replays), 4),
+                         "min_ms": round(min(wl.last_replays), 4), "max_ms": round(max(wl.last_replays), 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -464,27 +547,37 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dk["kernel"], "achieved": dk["achieved_gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["frac"],
                      "traffic": traffic, "bytes_per_launch": dk["bytes_per_launch"],
-                     "avg_launch_us": dk["avg_launch_us"]},
+                     "avg_launch_us": dk["avg_launch_us"],
+                     "profile": profile_for(args.workload, dom, dk["bytes_per_launch"])},
         "kernels": kernels,
     }
     if not args.no_sweep:
         log("two calls per layer")
         res["two_calls_per_layer"] = two_calls_us(wl)
     if not args.no_sweep:
-        log("planar layout: repack every pool, time the step again")
-        sec, nb = wl.to_planar()
-        ms_p, _, ks_p = measure(wl, args.steps, args.warmup)
+        log("planar layout: repack every pool beside the row-major one, alternate the two")
+        sec, nb = wl.to_planar(keep_rowmajor=True)
+        _, _, ks_p = measure(wl, 3, 1)
+        graphs = {}
+        for name in ("rowmajor", "planar"):
+            wl.use_layout(name)
+            graphs[name] = step_graph(wl)
+        ab = alternate(graphs, rounds=6, per=5)
+        del graphs
+        wl.use_layout("rowmajor")
         res["planar_layout"] = {
-            "us_per_layer_call": round(ms_p * 1e3 / wl.L, 3),
+            "us_per_layer_call": round(ab["planar"]["median_ms"] * 1e3 / wl.L, 3),
+            "us_per_layer_call_rowmajor": round(ab["rowmajor"]["median_ms"] * 1e3 / wl.L, 3),
+            "ab": {k: v["visit_medians_ms"] for k, v in ab.items()},
             "gate_up_avg_launch_us": round(ks_p["gate_up"], 3),
             "down_avg_launch_us": round(ks_p["down"], 3),
             "repack_gb": round(nb / 1e9, 3), "repack_s": round(sec, 4),
             "repack_gbs_read_plus_write": round(2 * nb / sec / 1e9, 1),
             "config": "the same workload after moe_repack of every pool (all 128 experts of all "
-                      "48 layers) into the planar layout; the same launches with the format fields "
-                      "flagged planar"}
+                      "48 layers) into the planar layout, kept beside the row-major pools; step "
+                      "graphs of both alternated A B / B A over 6 rounds of 5 replays, medians"}
     if not args.no_cpu:
-        res["cpu_baseline"] = run_cpu_baseline(wl, args.cpu_seconds)
+        res["cpu_baseline"] = run_cpu_baseline(wl, args.cpu_seconds, model)
     del wl
     torch.cuda.empty_cache()
     if not args.no_sweep:
@@ -510,9 +603,14 @@ def main():
         res["per_extra_row_ls_slope_frac_of_t1"] = round(slope / t1, 4)
         for T in (1, 2, 3, 4):
             log(f"sweep cb3/q8 2560x640 uniform T={T}")
-            sweep["cb3q8_2560x640_uniform"].append(sweep_line("cb3q8_2560x640", T, "uniform", 10, 3))
+            sweep["cb3q8_2560x640_uniform"].append(
+                sweep_line("cb3q8_2560x640", T, "uniform", 10, 3,
+                           cpu_seconds=args.cpu_seconds / 2 if T == 4 and not args.no_cpu else 0.0,
+                           model=model))
         log("cb2/nl4 T=4 zipf")
-        sweep["cb2nl4_2560x768_t4_zipf"] = [sweep_line("cb2nl4_2560x768_t4_zipf", 4, "zipf", 10, 3)]
+        sweep["cb2nl4_2560x768_t4_zipf"] = [
+            sweep_line("cb2nl4_2560x768_t4_zipf", 4, "zipf", 10, 3,
+                       cpu_seconds=0.0 if args.no_cpu else args.cpu_seconds / 2, model=model)]
         log("nl4/q5_1 T=1")
         sweep["nl4q51_2560x768_t1"] = [sweep_line("nl4q51_2560x768_t1", 1, "logits", 10, 3)]
         log("nl4x T=1")
@@ -526,38 +624,111 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def run_cpu_baseline(wl, seconds):
-    """The CPU oracle, as it stands, on the same workload: whole layer calls (route, group,
-    quantize, gate/up, SwiGLU, q8_1, down, scatter), cycling over the layers until about
-    `seconds` of oracle time have been measured. Weight generation is outside the timed part."""
+def cpu_model():
+    """The host CPU's model name from lscpu (run before anything touches the GPU), else
+    /proc/cpuinfo."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads():
+    """Threads for the all-cores oracle run: the cores this process may use, at most
+    OMP_NUM_THREADS when that is set (the host's share of cores for this GPU)."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
+def oracle_calls(wl, layers):
+    """A function running the CPU oracle, as it stands, on one whole layer call of the workload
+    (route, group, quantize, gate/up, SwiGLU, q8_1, down, scatter) for layer l, with the layer's
+    routed experts regenerated on the host beforehand (outside any timing)."""
     import numpy as np
 
     import oracle
     tb = oracle.Tables(wl.tables["nl4"], wl.tables["cb2"], wl.tables["cb3"])
-    log(f"cpu oracle for ~{seconds} s")
-    cache = {}
-    total, calls, l = 0.0, 0, 0
-    while total < seconds and calls < 16 * wl.L:
-        if l not in cache:
-            ids, w = oracle.route_topk(wl.logits[l], wl.k)
-            ex = {int(e): wl.host_expert(l, int(e)) for e in np.unique(ids)}
-            cache[l] = ex
-        ex = cache[l]
-        t0 = time.perf_counter()
+    ex = {}
+    for l in layers:
+        ids, _ = oracle.route_topk(wl.logits[l], wl.k)
+        ex[l] = {int(e): wl.host_expert(l, int(e)) for e in np.unique(ids)}
+
+    def call(l):
         ids, w = oracle.route_topk(wl.logits[l], wl.k)
         plan = oracle.build_plan(ids, w.astype(np.float32), None, wl.E, 0)
-        oracle.layer(wl.x[l], plan, wl.fg, wl.fd, {e: v[0] for e, v in ex.items()},
-                     {e: v[1] for e, v in ex.items()}, {e: v[2] for e, v in ex.items()},
+        e = ex[l]
+        oracle.layer(wl.x[l], plan, wl.fg, wl.fd, {k: v[0] for k, v in e.items()},
+                     {k: v[1] for k, v in e.items()}, {k: v[2] for k, v in e.items()},
                      wl.n_embd, wl.n_ff, np.zeros((wl.T, wl.n_embd), np.float32), tb)
-        total += time.perf_counter() - t0
-        calls += 1
-        l = (l + 1) % wl.L
-    us = total / calls * 1e6
-    return {"value": round(us, 1), "unit": "us per layer call", "cores": 1, "kind": "oracle",
-            "sample": f"{calls} layer calls cycling over the {wl.L} layers of the same workload "
-                      f"(same weights, logits and x); single-threaded plain-C oracle, float64 "
-                      f"sums; {total:.1f} s measured, weight generation excluded",
-            "gbs": round(sum(wl.weight_bytes_per_layer()) / wl.L * calls / total / 1e9, 3)}
+    return call
+
+
+def time_oracle(call, layers, threads, seconds):
+    """(calls, wall seconds): `threads` threads each running layer calls (cycling over `layers`)
+    until `seconds` of wall time have passed. The oracle's C routines release the interpreter
+    lock, so the threads run on separate cores."""
+    import threading
+    stop = time.perf_counter() + seconds
+    counts = [0] * threads
+
+    def worker(i):
+        j = i
+        while time.perf_counter() < stop:
+            call(layers[j % len(layers)])
+            counts[i] += 1
+            j += threads
+    t0 = time.perf_counter()
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    return sum(counts), time.perf_counter() - t0
+
+
+def run_cpu_baseline(wl, seconds, model, layers=6, reps=3):
+    """The CPU oracle on a bounded sample of the same workload: whole layer calls over `layers`
+    of its layers, on one thread and on every core this process may use, each the median of
+    `reps` runs of about seconds / (2 reps) each. Weight generation is outside the timed part."""
+    lays = list(range(min(layers, wl.L)))
+    call = oracle_calls(wl, lays)
+    call(lays[0])   # first call: library load and page-in
+    n_all = cpu_threads()
+    per = seconds / (2 * reps)
+    out = {}
+    for name, th in (("one_thread", 1), ("all_cores", n_all)):
+        us = []
+        for _ in range(reps):
+            calls, wall = time_oracle(call, lays, th, per)
+            us.append(wall / calls * 1e6)
+        out[name] = {"us_per_layer_call": round(median(us), 1), "threads": th,
+                     "runs_us": [round(u, 1) for u in us]}
+    wb = sum(wl.weight_bytes_per_layer()[l] for l in lays) / len(lays)
+    return {"value": out["all_cores"]["us_per_layer_call"], "unit": "us per layer call",
+            "cores": n_all, "kind": "oracle", "cpu_model": model,
+            "one_thread_us_per_layer_call": out["one_thread"]["us_per_layer_call"],
+            "runs": out,
+            "gbs_all_cores": round(wb / (out["all_cores"]["us_per_layer_call"] * 1e-6) / 1e9, 3),
+            "sample": f"whole layer calls of the same workload (same weights, logits and x) over "
+                      f"its first {len(lays)} layers: plain-C oracle, float64 sums, as it stands; "
+                      f"value = wall time per call with {n_all} threads each running calls (the "
+                      f"aggregate rate); one_thread = one thread; each the median of {reps} runs "
+                      f"of {per:.1f} s; weight generation excluded"}
 
 
 if __name__ == "__main__":

@@ -23,7 +23,9 @@
  *    pointer, bad shape or format, a HIP launch error). Problems only the device can see (an
  *    expert id, token or destination out of range, n_groups above cap_groups, a bounded wait that
  *    ran out) make the device skip that group or entry and OR a bit into *plan->err
- *    (MOE_ERR_* below); nothing traps or prints.
+ *    (MOE_ERR_* below); nothing traps. Nothing prints either, unless MOE_ROUTE_VERBOSE is set in
+ *    the environment: then each distinct kernel choice of a launch (role, weight format and
+ *    layout, kernel instance, grid, LDS, stream shape) is noted once on stderr.
  *  - Results are bit-identical for every grid_limit (0 = automatic) and between
  *    moe_layer_decode and the composed calls quantize -> gate_up -> swiglu -> down_scatter.
  *
@@ -313,6 +315,14 @@ int moe_layer_down(void* stream, const moe_layer* L, const moe_plan* P, const vo
  * blocks' scales as float32 (the fp16 d widened exactly). When the down format is Q5_1 the
  * blocks' sum fields (fp16 s widened) follow the scales, 256-byte aligned. */
 int moe_workspace_layout(const moe_layer* L, const moe_plan* P, size_t off[3]);
+
+/* The achievable-bandwidth reference the decode launches are measured against (not a step of the
+ * method): one launch of `grid` workgroups of 256 threads reads the `bytes` at buf once with
+ * 16-byte non-temporal loads, eight in flight per lane, the workgroups striding over the whole
+ * buffer. out[b] (grid words, device) receives the XOR of the 32-bit words workgroup b read, so
+ * the XOR of out[0..grid) is that of the whole buffer. buf and bytes must be multiples of 16 and
+ * 1 <= grid <= 65535, else MOE_E_ARG. */
+int moe_stream_read(void* stream, const void* buf, uint64_t bytes, uint32_t* out, int grid);
 
 const char* moe_status_string(int status);   /* host, static string */
 const char* moe_last_error(void);            /* host, text of the last MOE_E_HIP on this thread */

@@ -26,7 +26,7 @@ EXPORTS = ("moe_route_topk", "moe_build_plan", "moe_quantize_q8_1", "moe_repack"
            "moe_layer_down",
            "moe_workspace_layout", "moe_prefill_plan", "moe_prefill_gate_up", "moe_prefill_swiglu_q8_1",
            "moe_prefill_down", "moe_prefill_scatter",
-           "moe_status_string", "moe_last_error")
+           "moe_stream_read", "moe_status_string", "moe_last_error")
 
 _lib = None
 _P = ctypes.c_void_p
@@ -86,6 +86,7 @@ def lib():
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [_I]
         L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_stream_read.argtypes = [_P, _P, ctypes.c_uint64, _P, _I]
         _lib = L
     return _lib
 
@@ -377,3 +378,12 @@ def moe_layer_down(layer: Layer, plan: Plan, ws, n_tokens, Y, grid_limit=0, stre
     _check(lib().moe_layer_down(_stream(stream), ctypes.byref(layer.struct), ctypes.byref(plan.struct),
                                 _ptr(ws), ws.numel(), n_tokens, _ptr(Y), Y.shape[0], Y.stride(0),
                                 grid_limit), "moe_layer_down")
+
+
+def moe_stream_read(buf, out, grid, stream=None):
+    """The achievable-bandwidth reference: one streaming read of `buf` (a contiguous device tensor
+    of a multiple of 16 bytes) by `grid` workgroups; out[b] (uint32 or int32, >= grid words) gets
+    the XOR of the 32-bit words workgroup b read."""
+    assert buf.is_contiguous() and out.numel() >= grid and out.element_size() == 4
+    _check(lib().moe_stream_read(_stream(stream), _ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                                 grid), "moe_stream_read")

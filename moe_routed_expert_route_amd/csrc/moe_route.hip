@@ -35,11 +35,14 @@
 //    kernel variant and every grid produces the same bits.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/moe_route.h"
 #include "moe_device.hpp"
@@ -2705,6 +2708,37 @@ __global__ __launch_bounds__(kThreads) void k_pf_scatter(PlanArgs P, const int32
   Y[(size_t)dst * ldy + c] = acc;
 }
 
+// ------------------------------------------------------------------ streaming read ----------
+
+// The achievable-bandwidth reference for the weight streams above: a plain read of a buffer, every
+// lane with eight independent 16-byte non-temporal loads in flight per trip, the blocks striding
+// over the whole buffer (so every CU reads an equal share). Block b writes the XOR of the 32-bit
+// words it read to out[b], which keeps the loads and lets a caller check them.
+constexpr int kSrThreads = 256;
+__global__ __launch_bounds__(kSrThreads) void k_stream_read(const u32x4* __restrict__ p, uint64_t n16,
+                                                            uint32_t* __restrict__ out) {
+  const uint64_t stride = (uint64_t)gridDim.x * kSrThreads;
+  uint64_t i = (uint64_t)blockIdx.x * kSrThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_nontemporal_load(p + i + j * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  // the block's XOR: a butterfly over the wave, then one word per wave through LDS
+  __shared__ uint32_t wx[kSrThreads / 64];
+  for (int m = 32; m >= 1; m >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m);
+  if ((threadIdx.x & 63) == 0) wx[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = wx[0] ^ wx[1] ^ wx[2] ^ wx[3];
+}
+
 // ------------------------------------------------------------------ host side ---------------
 
 thread_local std::string t_last_error;
@@ -2905,6 +2939,28 @@ int num_cus() {
 
 // Workgroups for `items` work items: every item gets its own workgroup up to what the CUs hold
 // at once (LDS-limited, 8 per CU at most); beyond that workgroups take several items.
+// On request (MOE_ROUTE_VERBOSE set in the environment), one line on stderr per distinct kernel
+// choice of a launch: its role, weight format and layout, the kernel instance and its launch shape.
+const char* fmt_str(int f) {
+  static const char* n[] = {"?", "Q8_0", "NL4", "CB2", "CB3", "Q5_1", "NL4X"};
+  return n[(f >= 1 && f <= 6) ? f : 0];
+}
+void note_choice(const char* role, int fmt_field, const char* kernel, const char* mode, int grid, int threads,
+                 int lds, const char* extra) {
+  static const bool on = getenv("MOE_ROUTE_VERBOSE") != nullptr;
+  if (!on) return;
+  static std::mutex mu;
+  static std::vector<std::string> seen;
+  char line[320];
+  snprintf(line, sizeof line, "moe_route: %s %s (%s layout) -> %s<%s, %s>: grid %d x %d threads, %d KB LDS%s%s",
+           role, fmt_str(base_fmt(fmt_field)), (fmt_field & MOE_LAYOUT_PLANAR) ? "planar" : "row-major", kernel,
+           fmt_str(base_fmt(fmt_field)), mode, grid, threads, (lds + 1023) / 1024, extra[0] ? ", " : "", extra);
+  std::lock_guard<std::mutex> g(mu);
+  if (std::find(seen.begin(), seen.end(), std::string(line)) != seen.end()) return;
+  seen.emplace_back(line);
+  fprintf(stderr, "%s\n", line);
+}
+
 int grid_for(int items, int lds_bytes, int grid_limit) {
   const int per_cu = std::max(1, std::min(8, kLdsMax / std::max(lds_bytes, 1)));
   int grid = std::min(items, num_cus() * per_cu);
@@ -3090,6 +3146,12 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
     ga.spin_limit = 1 << 22;
   }
   const hipError_t e = launch_gu(base_fmt(L->fmt_gate_up), base_fmt(L->fmt_down), mode, ga, grid, bytes, st);
+  {
+    static const char* mn[] = {"GU_COMPOSED", "GU_FUSED", "GU_ROUTED", "GU_LAYER"};
+    char ex[96];
+    snprintf(ex, sizeof ex, "%d streaming waves, %d-row passes, %d x %d KB ring slots", sw, G.rp, S.NS, S.M);
+    note_choice("gate/up", L->fmt_gate_up, "k_gate_up", mn[mode & 3], grid, kGuThreads, bytes, ex);
+  }
   return e == hipSuccess ? MOE_OK : hip_fail(e, "gate/up kernel");
 }
 
@@ -3129,6 +3191,11 @@ int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, co
   const int tiles = (L->n_embd + tr - 1) / tr;
   const int grid = grid_for(tiles, bytes, grid_limit);
   const hipError_t e = launch_dn(base_fmt(L->fmt_down), mode, da, grid, bytes, st);
+  {
+    char ex[96];
+    snprintf(ex, sizeof ex, "%d-row tiles, %d-row chunks", tr, rc);
+    note_choice("down", L->fmt_down, "k_down", mode == DN_DESC ? "DN_DESC" : "DN_PLAN", grid, kDnThreads, bytes, ex);
+  }
   return e == hipSuccess ? MOE_OK : hip_fail(e, "down kernel");
 }
 
@@ -3463,6 +3530,16 @@ int moe_layer_decode_routed_noalloc(void* stream, const moe_layer* L, const moe_
   if ((rc = scratch_ptr(&ws))) return rc;
   return moe_layer_decode_routed(stream, L, P, logits, T, k, dst_of_token, entry_base, x, Y, n_rows, ldy, ws,
                                  kScratchBytes, grid_limit);
+}
+
+int moe_stream_read(void* stream, const void* buf, uint64_t bytes, uint32_t* out, int grid) {
+  if (!buf || !out || grid < 1 || grid > 65535 || bytes == 0 || (bytes & 15) ||
+      ((uintptr_t)buf & 15))
+    return MOE_E_ARG;
+  hipLaunchKernelGGL(k_stream_read, dim3(grid), dim3(kSrThreads), 0, (hipStream_t)stream, (const u32x4*)buf,
+                     bytes >> 4, out);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "stream read kernel");
 }
 
 }  // extern "C"

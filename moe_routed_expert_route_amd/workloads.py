@@ -116,10 +116,14 @@ class Workload:
         self.ws = [B.workspace(self.layers[l], self.plans[l], device=d) for l in range(L)]
         self.pool_bytes = L * E * (2 * self.sz_g + self.sz_d)
 
-    def to_planar(self):
+    def to_planar(self, keep_rowmajor=False):
         """Repack every pool (all experts of every layer) into the planar layout with moe_repack,
         one pool at a time, and point the layers at the repacked pools with their format fields
-        flagged planar. Returns (seconds of repack kernels, bytes read)."""
+        flagged planar. keep_rowmajor: keep the row-major pools and layers too (use_layout switches
+        between the two sets). Returns (seconds of repack kernels, bytes read)."""
+        if keep_rowmajor:
+            self.layouts = {"rowmajor": (list(self.layers), list(self.pool_g), list(self.pool_u),
+                                         list(self.pool_d))}
         d = self.pool_g[0].device
         nl4, cb2, cb3 = self._tabs
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -146,7 +150,15 @@ class Workload:
             self.layers[l] = B.Layer.from_pointers(
                 self.n_embd, self.n_ff, self.fg | B.LAYOUT_PLANAR, self.fd | B.LAYOUT_PLANAR,
                 ptr_g, ptr_u, ptr_d, nl4=nl4, cb2=cb2, cb3=cb3, keep=(pg, pu, pd))
+        if keep_rowmajor:
+            self.layouts["planar"] = (list(self.layers), list(self.pool_g), list(self.pool_u),
+                                      list(self.pool_d))
         return ms * 1e-3, nbytes
+
+    def use_layout(self, name):
+        """Point the layers at the row-major or the planar pools (after to_planar(keep_rowmajor=True))."""
+        layers, pg, pu, pd = self.layouts[name]
+        self.layers, self.pool_g, self.pool_u, self.pool_d = list(layers), list(pg), list(pu), list(pd)
 
     # ---------------------------------------------------------------- the step ----------------
     def route_plan(self, l, stream=None):
@@ -206,16 +218,17 @@ class Workload:
 
     def launch_bytes(self, l):
         """Algorithmic HBM bytes of layer l's two launches: (gate/up, down). Gate/up reads the
-        distinct experts' gate and up matrices once, the logits and x once, writes the plan, g, u
-        and the q8_1 rows of h; down reads the distinct experts' down matrices once, the plan,
-        the q8_1 rows of h once and the destination rows of Y, and writes those rows."""
+        distinct experts' gate and up matrices once, the logits and x once, and writes the plan,
+        the call's descriptor and the q8_1 rows of h (g and u stay on chip); down reads the
+        distinct experts' down matrices once, the descriptor, the q8_1 rows of h once and the
+        destination rows of Y, and writes those rows."""
         ne = self.T * self.k
         nd = len(self.routed[l])
         hq = ne * (self.n_ff // 32) * 36
         plan = 4 * (2 * nd + 1 + 1 + 3 * ne)
-        gu = (nd * 2 * self.sz_g + self.T * self.E * 4 + self.T * self.n_embd * 4 + plan
-              + 2 * ne * self.n_ff * 4 + hq)
-        dn = nd * self.sz_d + plan + hq + 2 * self.T * self.n_embd * 4
+        desc = 4 * (3 + nd + 1 + 3 * ne) + 8 * nd
+        gu = nd * 2 * self.sz_g + self.T * self.E * 4 + self.T * self.n_embd * 4 + plan + desc + hq
+        dn = nd * self.sz_d + desc + hq + 2 * self.T * self.n_embd * 4
         return gu, dn
 
     def host_expert(self, l, e):

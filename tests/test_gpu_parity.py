@@ -178,6 +178,42 @@ def test_layer_stages(name):
     assert np.array_equal(U.bits(r3["Y"]), U.bits(comp["Y"]))
 
 
+@pytest.mark.parametrize("E,T,k", [(128, 1, 8), (16, 2, 4), (8, 1, 2)])
+def test_routed_ties(E, T, k):
+    """Exact ties in the logits through the routed step (the launch ranks the experts itself):
+    at the k-th place (the lower id is chosen), inside the chosen set, and a -0 / +0 pair; the
+    published plan equals the oracle's routing and grouping, and Y the composed calls' bits."""
+    lg = synth.router_logits(T, E, E, T, k, 9) - 3.0
+    for t in range(T):
+        top = synth.rng(44, E, t).permutation(E)
+        lg[t, top[:k + 2]] = np.float32(2.0)                 # k + 2 equal logits: ties at the k-th place
+        lg[t, top[0]] = lg[t, top[1]] = np.float32(5.0)      # a tie inside the chosen set
+        lg[t, top[2]] = np.float32(0.0)
+        lg[t, top[3]] = np.float32(-0.0)                     # equal to +0 (lower id first)
+        lg[t, top[4:k + 2]] = np.float32(0.0)
+    oids, ow = oracle.route_topk(lg, k)
+    need = set(int(e) for e in oids.reshape(-1))
+    c = U.Case(f"ties_{E}_{T}", 256, 128, E, Q8_0, Q8_0, 9, need)
+    c.logits, c.k, c.T = lg.astype(np.float32), k, T
+    c.x = synth.activations(T, 256, 9)
+    n_rows = 8
+    dst = np.arange(T, dtype=np.int32) + 2
+    plan, ids, w = U.gpu_route_and_plan(c, T * k, T * k, entry_base=1, dst_of_token=dst)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    ph = plan.get()
+    ref = oracle.build_plan(oids, ow.astype(np.float32), dst, E, 1)
+    for key in ("n_groups", "grp_expert", "grp_start", "ent_src", "ent_dst"):
+        assert np.array_equal(np.asarray(ph[key]), np.asarray(ref[key])), key
+    Y0 = U.y0_for(n_rows, 256, dst, 2)
+    comp = U.run_composed(c, plan, c.x, Y0, n_rows)
+    r = U.run_routed(c, c.x, Y0, entry_base=1, dst_of_token=dst)
+    assert r["err"] == 0 and comp["err"] == 0
+    for key in ("n_groups", "grp_expert", "grp_start", "ent_src", "ent_dst"):
+        assert np.array_equal(np.asarray(r["plan"][key]), np.asarray(ph[key])), key
+    assert np.array_equal(U.bits(r["plan"]["ent_w"]), U.bits(ph["ent_w"]))
+    assert np.array_equal(U.bits(r["Y"]), U.bits(comp["Y"]))
+
+
 @pytest.mark.parametrize("name", ["q8_nl4_t3", "nl4_t1", "cb2_nl4_t4_zipf"])
 def test_two_calls_per_layer(name):
     """One layer as two calls sharing the entry arrays and Y: the even experts' groups first, the
@@ -324,8 +360,19 @@ def test_edges_q8_4096(ng):
                               U.bits(comp["Y"])), gl
 
 
-def test_negative_corrupted_weight_is_caught():
-    """A byte flipped in the oracle's copy of one expert must fail the parity check."""
+# (matrix, byte offset in the expert's Q8_0 matrix, bits): Q8_0 block = fp16 d (bytes 0-1), 32 quants
+CORRUPT = {
+    "gate_quant": ("gate", 34 * 3 + 2, 0x40),     # row 0, block 3, quant 0
+    "gate_scale": ("gate", 34 * 3 + 1, 0x04),     # row 0, block 3, an exponent bit of d
+    "up_scale": ("up", 34 * 5 + 0, 0x80),         # row 0, block 5, a mantissa bit of d
+    "down_scale": ("down", 34 * 2 + 1, 0x08),     # row 0, block 2, an exponent bit of d
+}
+
+
+@pytest.mark.parametrize("where", list(CORRUPT))
+def test_negative_corrupted_weight_is_caught(where):
+    """A byte flipped in the oracle's copy of one expert (a quant or a scale of a gate, up or down
+    matrix) must fail the parity check of the GPU's unchanged results."""
     c = _routed("small_q8", key=3)
     plan, _, _ = U.gpu_route_and_plan(c, 2, 2)
     ph = plan.get()
@@ -333,9 +380,10 @@ def test_negative_corrupted_weight_is_caught():
     comp = U.run_composed(c, plan, c.x, Y0, 1)
     U.check_stages(c, ph, comp, Y0)
     e = int(ph["grp_expert"][0])
-    bad = c.gate[e].copy()
-    bad[2 + 34 * 3] ^= 0x40           # row 0, block 3, one quant
-    c.gate[e] = bad
+    mat, off, bit = CORRUPT[where]
+    bad = getattr(c, mat)[e].copy()
+    bad[off] ^= bit
+    getattr(c, mat)[e] = bad
     with pytest.raises(AssertionError):
         U.check_stages(c, ph, comp, Y0)
 

@@ -48,3 +48,15 @@ def test_binding_structs_follow_header():
             first = decl.split(",")[0].split()[-1].lstrip("*")
             fields += [first] + [n.strip().lstrip("*") for n in decl.split(",")[1:]]
         assert [f[0] for f in py._fields_] == fields, (cname, fields)
+
+
+def test_stream_read_rejects_bad_arguments():
+    """Argument checks happen on the host, before anything is enqueued (no GPU needed)."""
+    lib = ctypes.CDLL(LIB)
+    f = lib.moe_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int]
+    fake = 1 << 20   # never dereferenced: every call below fails its checks first
+    for args in ((None, fake, 15, fake, 1), (None, fake + 8, 16, fake, 1), (None, fake, 16, fake, 0),
+                 (None, fake, 16, fake, 65536), (None, None, 16, fake, 1), (None, fake, 16, None, 1),
+                 (None, fake, 0, fake, 1)):
+        assert f(*args) == -1, args   # MOE_E_ARG
