@@ -16,7 +16,7 @@ HIPCC_FLAGS = [
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
     # leading scalar kernel arguments arrive preloaded in scalar registers (gfx950)
-    "-mllvm", "-amdgpu-kernarg-preload-count=4",
+    "-mllvm", "-amdgpu-kernarg-preload-count=8",
 ]
 
 

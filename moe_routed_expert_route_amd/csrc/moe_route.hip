@@ -611,6 +611,108 @@ __device__ __forceinline__ void dot_pass(const MOE_LDS uint32_t* W, uint32_t ra,
   }
 }
 
+// ------------------------------------------------------------------ register-direct pass ---
+
+// The planar NL4 layout puts every unit's 16 code bytes on a 16-byte boundary (the row's code
+// plane first, then its fp16 scales), so a lane can load its own units straight into registers:
+// one 16-byte load per unit, no LDS on the code side. The scale planes of the wave's rows (2 U
+// bytes each, whole 16-byte pieces when U % 8 == 0) come in one direct-to-LDS instruction issued
+// first, so the wait for a lane's code loads covers them. The lane map is the LDS pass's (row
+// i = lane >> lgL, lane li takes units li, li + L, ... in order; past the row's end it reloads unit
+// 0 and drops the result), and so are the dot and the sums: the same bits.
+constexpr int kRegUnits = 5;   // most units per lane the register path holds (n_embd <= 2560 at 16 lanes a row)
+constexpr int kRegSlots = 2;   // entries per register pass (more would spill next to the held units)
+struct RegW {
+  u32x4 c[kRegUnits];   // the unit's 16 code bytes
+};
+
+// Issue the wave's loads (planar NL4): the scale planes of its rows into LDS at `sbuf` (row i's
+// at sbuf + 2 U i; lane j < rows * U / 8 takes piece j % (U / 8) of row j / (U / 8), whose first
+// byte is srow), then this lane's G.upl units of its row `row` into registers.
+__device__ __forceinline__ void reg_issue(RegW& w, const uint8_t* row, const uint8_t* srow, int sj,
+                                          MOE_LDS uint8_t* sbuf, const Geom& G, int li) {
+  const int lane = threadIdx.x & 63;
+  if (lane < G.rp * (G.U >> 3))
+    __builtin_amdgcn_global_load_lds((const void*)(srow + G.ly.d_b + 16u * (uint32_t)sj), (MOE_LDS void*)sbuf, 16, 0,
+                                     kAuxStream);
+#pragma unroll
+  for (int k = 0; k < kRegUnits; ++k) {
+    if (k < G.upl) {
+      int u = li + (k << G.lgL);
+      u = u < G.U ? u : 0;
+      w.c[k] = __builtin_nontemporal_load((const u32x4*)(row + G.ly.c_a * (uint32_t)u + G.ly.c_b));
+    }
+  }
+}
+
+// Dot the wave's rows (loaded by reg_issue) with NE <= 4 activation rows; out as dot_pass_n.
+template <int NE, class Out>
+__device__ __forceinline__ void dot_pass_reg_n(const RegW& w, const MOE_LDS uint16_t* sbuf, int nrows, const Geom& G,
+                                               const Tables& tb, const ActSplit& act, const int (&sidx)[kSlots],
+                                               Out& out) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane >> G.lgL, li = lane & (G.L - 1);
+  float acc[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = 0.0f;
+  if (i < nrows) {
+#pragma unroll
+    for (int k = 0; k < kRegUnits; ++k) {
+      if (k < G.upl) {
+        const bool valid = li + (k << G.lgL) < G.U;
+        const int u = valid ? li + (k << G.lgL) : 0;
+        uint32_t q[NE][8];
+        float dx[NE];
+        __builtin_amdgcn_sched_barrier(0);   // one unit at a time: its activation reads, then its dots
+#pragma unroll
+        for (int e = 0; e < NE; ++e) act.get(sidx[e], u, q[e], dx[e]);
+        uint32_t n[4] = {w.c[k].x, w.c[k].y, w.c[k].z, w.c[k].w};
+        uint32_t sw = sbuf[i * G.U + u];
+        // opaque to the optimiser: the decode stays here, per pass over the entries, instead of
+        // being hoisted for every unit at once (which would hold all the decoded units live)
+        asm volatile("" : "+v"(n[0]), "+v"(n[1]), "+v"(n[2]), "+v"(n[3]), "+v"(sw));
+        uint32_t c[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c[j] = lut16(n[j], tb);            // weights 4j..4j+3 (low nibbles)
+          c[j + 4] = lut16(n[j] >> 4, tb);   // weights 16+4j..16+4j+3 (high nibbles)
+        }
+        const float sc = h2f(sw & 0xFFFFu);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          int s0 = __builtin_amdgcn_sdot4((int)c[0], (int)q[e][0], 0, false);
+          int s1 = __builtin_amdgcn_sdot4((int)c[1], (int)q[e][1], 0, false);
+          s0 = __builtin_amdgcn_sdot4((int)c[2], (int)q[e][2], s0, false);
+          s1 = __builtin_amdgcn_sdot4((int)c[3], (int)q[e][3], s1, false);
+          s0 = __builtin_amdgcn_sdot4((int)c[4], (int)q[e][4], s0, false);
+          s1 = __builtin_amdgcn_sdot4((int)c[5], (int)q[e][5], s1, false);
+          s0 = __builtin_amdgcn_sdot4((int)c[6], (int)q[e][6], s0, false);
+          s1 = __builtin_amdgcn_sdot4((int)c[7], (int)q[e][7], s1, false);
+          const float prod = (sc * dx[e]) * (float)(s0 + s1);
+          acc[e] = acc[e] + (valid ? prod : 0.0f);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = group_sum(acc[e], G.L);
+  if (i < nrows) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      if ((e & (G.L - 1)) == li) out(i, e, acc[e]);
+  }
+}
+
+template <class Out>
+__device__ __forceinline__ void dot_pass_reg(const RegW& w, const MOE_LDS uint16_t* sbuf, int nrows, const Geom& G,
+                                             const Tables& tb, const ActSplit& act, const int (&sidx)[kSlots], int ne,
+                                             Out out) {
+  if (ne == 1)
+    dot_pass_reg_n<1>(w, sbuf, nrows, G, tb, act, sidx, out);
+  else
+    dot_pass_reg_n<2>(w, sbuf, nrows, G, tb, act, sidx, out);
+}
+
 template <int CTRL>
 __device__ __forceinline__ uint32_t dppu(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
@@ -876,6 +978,74 @@ __device__ __forceinline__ void route_token_v(MOE_LDS uint32_t* scr, int E, int 
   wave_lds_sync();
 }
 
+// Routing spread over the routing waves of a workgroup ("#363 ...", opening paragraph: each token
+// of the window picks its top-k experts), for T (rounded up to a power of two, Tp) tokens of E
+// experts (Ep: E rounded up to a power of two, at least 64) when Tp Ep <= nthreads: thread rt is
+// (token t, expert e, part p) with parts = nthreads / (Tp Ep) adjacent lanes per (t, e); it counts
+// the experts of its part of the row that beat e (a larger logit, or an equal one with a lower id),
+// the parts' counts are summed over the lanes, and e is chosen iff fewer than k beat it (its rank).
+// Exact, and the same selection as route_token.
+// Writes the selection bitmaps bits[t nW ..] (each wave its slice of one token's row) and, in rank
+// order, ids[t k + r] = e and lsel[t k + r] = the logit (the router weights follow from those).
+// lg(t): token t's logits in LDS (read by broadcast).
+__device__ __forceinline__ int pow2ceil(int v) { return v <= 1 ? 1 : 1 << (32 - __builtin_clz((uint32_t)(v - 1))); }
+__device__ __forceinline__ int route_parts(int T, int E, int nthreads) {
+  const int p = min(4, nthreads / (pow2ceil(T) * max(64, pow2ceil(E))));
+  return p == 4 ? p : 0;   // four parts of at least 16 experts (else one wave per token)
+}
+template <class LgOf>
+__device__ __forceinline__ void route_ranked(int rt, int T, int E, int k, int parts, LgOf lg, MOE_LDS int* ids,
+                                             MOE_LDS float* lsel, MOE_LDS uint32_t* bits) {
+  const int lane = threadIdx.x & 63;
+  const int Ep = max(64, pow2ceil(E));
+  const int lgP = __builtin_ctz((uint32_t)parts), lgE = __builtin_ctz((uint32_t)Ep);
+  const int part = rt & (parts - 1), e = (rt >> lgP) & (Ep - 1), t = rt >> (lgP + lgE);
+  const int chunk = Ep >> lgP;   // a multiple of 16
+  const bool live = t < T && e < E;
+  // (each row holds -inf from E to Ep: those never beat a logit)
+  const MOE_LDS float* row = lg(live ? t : 0);
+  // the floats order like their keys (fkey: -0 == +0), so a part counts the larger logits with one
+  // compare each, and the equal ones (a tie goes to the lower id) are looked at again only in a
+  // wave where some lane has one
+  const float le = live ? row[e] + 0.0f : __builtin_huge_valf();
+  const int j00 = part * chunk;
+  int gt = 0, eq = 0;
+  for (int i0 = 0; i0 < chunk; i0 += 16) {   // the same trip count in every lane
+    f32x4 v[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) v[b] = *(const MOE_LDS f32x4*)(row + j00 + i0 + 4 * b);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      gt += (int)(v[b].x > le) + (int)(v[b].y > le) + (int)(v[b].z > le) + (int)(v[b].w > le);
+      eq += (int)(v[b].x == le) + (int)(v[b].y == le) + (int)(v[b].z == le) + (int)(v[b].w == le);
+    }
+  }
+  const int self = (e >= j00 && e < j00 + chunk) ? 1 : 0;   // e itself is equal to le
+  int beats = gt;
+  if (__ballot(live && eq > self)) {   // (rare) the equal logits of lower id beat e as well
+    for (int i0 = 0; i0 < chunk; ++i0) {
+      const int j = j00 + i0;
+      beats += (j < e && row[j] + 0.0f == le) ? 1 : 0;
+    }
+  }
+  beats += __builtin_amdgcn_update_dpp(0, beats, 0xB1, 0xF, 0xF, false);   // xor 1
+  beats += __builtin_amdgcn_update_dpp(0, beats, 0x4E, 0xF, 0xF, false);   // xor 2
+  const bool sel = live && beats < k;
+  if (sel && part == 0) {
+    ids[t * k + beats] = e;
+    lsel[t * k + beats] = le;
+  }
+  // this wave's slice of the bitmap: its 16 experts e0.. of token t0 (lane i of the slice takes
+  // the selection of lane 4 i)
+  const int rt0 = rt - lane;
+  const int e0 = (rt0 >> lgP) & (Ep - 1), t0 = rt0 >> (lgP + lgE);
+  const int sv = __shfl(sel ? 1 : 0, (lane & 15) << 2);
+  const uint64_t m = __ballot(lane < 16 && sv);
+  const int nW = (E + 31) >> 5;
+  if (t0 < T && e0 < 32 * nW && lane == 0)
+    *((MOE_LDS uint16_t*)(bits + t0 * nW) + (e0 >> 4)) = (uint16_t)m;
+}
+
 // need_w: also the weights (a caller that only needs the selection skips them)
 __device__ __forceinline__ void route_token(MOE_LDS uint32_t* scr, int E, int k, MOE_LDS int* ids,
                                             MOE_LDS float* w, MOE_LDS uint32_t* bits, bool need_w = true) {
@@ -1077,6 +1247,7 @@ struct GuArgs {
   int entry_base;
   int lds_ring, lds_act;
   int sw;               // waves that stream items (the ring holds sw waves' slots)
+  int regw;             // planar NL4: each lane loads its weight units into registers (no ring)
   // layer mode: the down half
   Geom Gd;              // down row geometry (rows of n_ff columns)
   Stream Sd;            // down stream: kDnWaves waves, NS slots of M KB each, in the ring
@@ -1093,8 +1264,8 @@ struct GuArgs {
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 // Byte offset of the struct in k_gate_up's argument block: kernel arguments sit in order at their
-// natural alignment, after two pointers and two ints.
-constexpr uint32_t kGuArgsOff = 24;
+// natural alignment, after five pointers and three ints (then padding to 8 bytes).
+constexpr uint32_t kGuArgsOff = 56;
 static_assert(alignof(GuArgs) <= 8, "GuArgs must start right after the leading arguments");
 
 constexpr int kGuStage = 64 * kMaxEnt;   // floats of output staging: a 32-row block of g and u per entry
@@ -1136,13 +1307,17 @@ __host__ __device__ inline int ly_down_bytes(int cap_entries, int Ud, bool with_
 // workgroups without a block take the extra tiles) go out at once; it waits until the count reaches
 // the grid (bounded), reads every entry's q8_1 rows of h and runs the down tiles and the scatter as
 // the down launch does. The last workgroup to finish clears the counts for the next call.
-// The routing waves' first loads need only the logits, the NL4 table, T and E: they come as the
-// leading scalar arguments (copies of the struct's fields), which the launch preloads into
-// scalar registers, so those loads go out before any read of the argument struct.
-template <int FMT, int MODE, int FD = FMT>
+// The first loads of the launch need only the logits, the NL4 table, x, the gate and up pointer
+// arrays, T, E and n_embd: they come as the leading scalar arguments (copies of the struct's
+// fields), which the launch preloads into scalar registers, so those loads go out before any read
+// of the argument struct.
+template <int FMT, int MODE, int FD = FMT, bool RW = false>
 __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict__ logits0,
-                                                        const int8_t* __restrict__ nl4_0, int T0,
-                                                        int E0, GuArgs a_) {
+                                                        const int8_t* __restrict__ nl4_0,
+                                                        const float* __restrict__ x0,
+                                                        const void* const* __restrict__ gate0,
+                                                        const void* const* __restrict__ up0, int T0,
+                                                        int E0, int n_embd0, GuArgs a_) {
   constexpr bool RT = MODE == GU_ROUTED || MODE == GU_LAYER;
   extern __shared__ __align__(16) uint8_t smem[];
   // the wave index in a scalar register: everything derived from it is uniform over the wave
@@ -1155,14 +1330,35 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
   //         and the destinations.
   const bool rw = RT && wave < kRtWaves;   // a routing wave
   MOE_LDS uint32_t* rscr = (MOE_LDS uint32_t*)ring + wave * route_scr_words(E0);
+  // routed: the routing waves rank every token's experts together when the window is small
+  // enough (then all waves meet once the logits rows are in LDS); else one wave per token
+  const int rparts = MODE == GU_ROUTED ? route_parts(T0, E0, 64 * kRtWaves) : 0;
   uint32_t t_nl4[4] = {0u, 0u, 0u, 0u};
   if constexpr (RT) {
     if (rw) {
-      __builtin_amdgcn_s_setprio(2);   // the launch waits on the routing: it goes first on its SIMD
+      // the launch waits on the routing: a wave routing a token alone goes first on its SIMD (the
+      // ranking of a small window shares the work with the x staging, which the launch waits on too)
+      if (rparts == 0) __builtin_amdgcn_s_setprio(2);
       // the table (hot in L2) goes out just ahead of the logits, so the routing wave's one wait on
       // the logits covers it and nothing is loaded after the routing
       load_nl4(nl4_0, t_nl4);
       if (wave < T0) issue_logits(logits0 + (size_t)wave * E0, E0, (MOE_LDS float*)rscr);
+    }
+  }
+  // routed, the other waves: x's rows (when they fit two register passes) and the gate and up
+  // pointers of their experts, also from the preloaded arguments
+  const int U0 = n_embd0 >> 5;
+  const bool early_x = RT && T0 * U0 * 8 <= 2 * kGuQThreads;
+  float4 xr0[2];
+  uint64_t pg = 0, pu = 0, pd = 0;   // routed: expert q0's pointers (experts past kGuQThreads later)
+  if constexpr (RT) {
+    if (!rw) {
+      const int q = tid - 64 * kRtWaves;
+      if (early_x) act_issue_f<kGuQThreads, 2>(x0, n_embd0, T0 * U0, U0, q, xr0);
+      if (q < E0) {
+        pg = (uint64_t)(uintptr_t)gate0[q];
+        pu = (uint64_t)(uintptr_t)up0[q];
+      }
     }
   }
   (void)a_;
@@ -1196,16 +1392,14 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
   }
   int r_dt = 0, r_gs = 0, r_ge = 0, r_ng = 0;
   uint32_t r_ep = 0;
-  uint64_t pg = 0, pu = 0, pd = 0;   // routed: expert q0's pointers (experts past kGuQThreads later)
+  // the destinations and the down pointers serve only the workgroup that writes the plan and the
+  // descriptor (and layer mode, where every workgroup runs down tiles)
+  const bool writer = MODE == GU_LAYER || blockIdx.x == gridDim.x - 1;
   if constexpr (RT) {
     if (q0 >= 0 && q0 < a.T) r_dt = a.dst_of_token ? a.dst_of_token[q0] : q0;
     if (MODE == GU_LAYER && q0 == 0)   // the last call's tag (this call's is one more)
       r_ep = __hip_atomic_load(a.ctr + kCtrEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (q0 >= 0 && q0 < a.E) {
-      pg = (uint64_t)(uintptr_t)a.A.gate[q0];
-      pu = (uint64_t)(uintptr_t)a.A.up[q0];
-      pd = (uint64_t)(uintptr_t)a.A.down[q0];
-    }
+    if (writer && q0 >= 0 && q0 < a.E) pd = (uint64_t)(uintptr_t)a.A.down[q0];
   } else {
     if (tid == 0) r_ng = *a.P.n_groups;
     if (tid <= a.P.cap_groups) r_gs = a.P.grp_start[tid];
@@ -1214,7 +1408,19 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
 
   // ---- 2. routing and the activations' q8_1 blocks
   if constexpr (RT) {
-    if (rw) {
+    if (rw && rparts > 0) {
+      __builtin_amdgcn_s_waitcnt(MOE_VM(0));   // this wave's logits row (and the NL4 table)
+      if (wave < a.T) {   // its row from E to the power of two the ranking reads: -inf
+        const int Ep = max(64, pow2ceil(a.E));
+        for (int j = a.E + lane; j < Ep; j += 64) ((MOE_LDS float*)rscr)[j] = -__builtin_huge_valf();
+      }
+      lds_barrier();                           // every token's row is in LDS
+      // ranks and selections; the last workgroup turns the chosen logits into weights later
+      route_ranked(tid, a.T, a.E, a.k, rparts,
+                   [&](int t) { return (const MOE_LDS float*)((MOE_LDS uint32_t*)ring + t * route_scr_words(a.E)); },
+                   pl.rid, pl.rw, selT);
+      __builtin_amdgcn_s_setprio(0);
+    } else if (rw) {
       for (int t = wave; t < a.T; t += kRtWaves) {
         if (t != wave) issue_logits(a.logits + (size_t)t * a.E, a.E, (MOE_LDS float*)rscr);
         __builtin_amdgcn_s_waitcnt(MOE_VM(0));
@@ -1226,8 +1432,15 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
     } else {
       // two register passes cover one 4096-wide row; eight cover four (more: plain loads after)
       const int q = tid - 64 * kRtWaves, nblk = a.n_tokens * G.U;
-      auto none = [](int) {};
-      if (nblk * 8 <= 2 * kGuQThreads) {
+      // (with the routing waves' ranking, every wave meets them once the logits are in LDS, while
+      // the x loads are in flight)
+      auto none = [&](int) {
+        if (rparts > 0) lds_barrier();
+      };
+      if (early_x) {   // (the loads went out at the start)
+        none(2);
+        act_store_f<kGuQThreads, 2>(xr0, nblk, q, act);
+      } else if (nblk * 8 <= 2 * kGuQThreads) {
         act_stage_f_np<kGuQThreads, 2>(a.x, a.A.n_embd, nblk, G.U, q, act, none);
       } else {
         const int nreg = min(nblk, kGuQThreads * kGuXPass / 8);
@@ -1238,14 +1451,16 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
     if (q0 >= 0 && q0 < a.E) {
       const bool ok = ptr_ok(pg | pu, a.P.err);
       ptab[q0] = u64x2{ok ? pg : 0ull, ok ? pu : 0ull};
-      ptabd[q0] = ptr_ok(pd, a.P.err) ? pd : 0ull;
+      if (writer) ptabd[q0] = ptr_ok(pd, a.P.err) ? pd : 0ull;
     }
     for (int e = q0 + kGuQThreads; q0 >= 0 && e < a.E; e += kGuQThreads) {
       const uint64_t g = (uint64_t)(uintptr_t)a.A.gate[e], u = (uint64_t)(uintptr_t)a.A.up[e];
-      const uint64_t d = (uint64_t)(uintptr_t)a.A.down[e];
       const bool ok = ptr_ok(g | u, a.P.err);
       ptab[e] = u64x2{ok ? g : 0ull, ok ? u : 0ull};
-      ptabd[e] = ptr_ok(d, a.P.err) ? d : 0ull;
+      if (writer) {
+        const uint64_t d = (uint64_t)(uintptr_t)a.A.down[e];
+        ptabd[e] = ptr_ok(d, a.P.err) ? d : 0ull;
+      }
     }
     if (q0 >= 0 && q0 < a.T) pl.dtok[q0] = r_dt;
     if (MODE == GU_LAYER && q0 == 0) pl.misc[12] = (int)r_ep;
@@ -1465,12 +1680,36 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
       issue_span(slot, M, (const uint8_t*)a.P.grp_start, 1);
     }
   };
+  // register-direct (planar NL4): this lane's units of the chunk's rows straight into registers
+  constexpr bool regw = RW;
+  RegW rwt;
+  // the scale planes' lanes: lane j < rp U / 8 takes piece sj of the wave's row sri
+  const int s16 = G.U >> 3, sri = lane / max(s16, 1), sj = lane - sri * s16;
+  auto issue_reg = [&]() {
+    const int q = ip.q, g = ip.g, blk = ip.blk;
+    step(ip);
+    uint64_t wg, wu;
+    group_ptrs(g, wg, wu);
+    const int i = lane >> G.lgL;
+    if (wg) {
+      const int r0 = blk * 32 + (wave + q * a.sw) * half;
+      auto row_of = [&](int ii) {
+        return (const uint8_t*)(uintptr_t)((ii < half ? wg : wu) +
+                                           (uint64_t)(r0 + (ii < half ? ii : ii - half)) * (uint64_t)G.rb);
+      };
+      reg_issue(rwt, row_of(i < G.rp ? i : 0), row_of(sri < G.rp ? sri : 0), sj, myring, G, lane & (G.L - 1));
+    }
+  };
   __builtin_amdgcn_s_waitcnt(MOE_VM(0));   // nothing of ours in flight before the stream
-  const int pre = min(NS, nch);
+  const int pre = regw ? 0 : min(NS, nch);
   // the first chunks go out ahead of the dots of waves whose chunks have already landed: a wave
   // issuing competes for its SIMD only with those, and its loads are what the stream waits on
   __builtin_amdgcn_s_setprio(3);
-  for (int kc = 0; kc < pre; ++kc) issue(myring + kc * M * 1024);
+  if (regw) {
+    if (nch > 0) issue_reg();
+  } else {
+    for (int kc = 0; kc < pre; ++kc) issue(myring + kc * M * 1024);
+  }
   __builtin_amdgcn_s_setprio(0);
   int issued = pre;
 
@@ -1480,6 +1719,18 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
     int* dw = (int*)a.desc;
     uint64_t* dp = (uint64_t*)(a.desc + kDescPtrByte);
     if constexpr (RT) {
+      if (rparts > 0) {   // the ranking left each token's chosen logits: the router weights
+        if (wave < a.T) {
+          const int t = wave;
+          const float l0 = pl.rw[t * a.k];
+          float ex = 0.0f;
+          if (lane < a.k) ex = expf(pl.rw[t * a.k + lane] - l0);
+          float sum = 0.0f;
+          for (int j = 0; j < a.k; ++j) sum = sum + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+          if (lane < a.k) pl.rw[t * a.k + lane] = ex / sum;
+        }
+        lds_barrier();
+      }
       for (int g = wave; g < ng; g += kGuWaves) {
         int l, b, a0, cnt;
         uint64_t tm;
@@ -1548,9 +1799,36 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
       ne = uni(pl.gstart[g + 1]) - e0 - a0;
     }
     for (int q = 0; q < cw; ++q, ++kc) {
-      wait_vm((issued - 1 - kc) * M);
+      if (regw) {
+        if (kc > 0) issue_reg();   // one chunk at a time (the registers hold one)
+      } else {
+        wait_vm((issued - 1 - kc) * M);
+      }
       MOE_LDS uint8_t* slot = myring + slot_of(kc, NS) * M * 1024;
-      if (wgv) {
+      if (wgv && regw) {
+        const int prow = (wave + q * a.sw) * half;
+        uint64_t rest = tm;
+        for (int c0 = 0; c0 < ne; c0 += kRegSlots) {
+          const int nc = min(kRegSlots, ne - c0);
+          int sidx[kSlots];
+#pragma unroll
+          for (int e = 0; e < kSlots; ++e) {
+            if constexpr (RT) {
+              sidx[e] = 0;
+              if (e < nc) {
+                sidx[e] = (int)__builtin_ctzll(rest);
+                rest &= rest - 1ull;
+              }
+            } else {
+              sidx[e] = e < nc ? uni(pl.esrc[a0 + c0 + e]) : 0;
+            }
+          }
+          MOE_LDS float* st = stage + c0 * 64 + prow;
+          if (c0 == 0) wait_vm(G.upl);   // the scale planes (issued before this lane's code loads)
+          dot_pass_reg(rwt, (const MOE_LDS uint16_t*)myring, G.rp, G, tb, act, sidx, nc,
+                       [&](int i, int e, float v) { st[e * 64 + (i < half ? i : 32 + i - half)] = v; });
+        }
+      } else if (wgv) {
         const int prow = (wave + q * a.sw) * half;   // first h row of the pass inside the block
         const uint64_t off = (uint64_t)(blk * 32 + prow) * (uint64_t)G.rb;
         const uint32_t sb = (uint32_t)(slot - ring);
@@ -1577,7 +1855,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
                         [&](int i, int e, float v) { st[e * 64 + (i < half ? i : 32 + i - half)] = v; });
         }
       }
-      if (kc + NS < nch) {
+      if (!regw && kc + NS < nch) {
         MOE_WAIT_LGKM0;   // this wave's LDS reads of the slot have returned
         issue(slot);
         ++issued;
@@ -2978,7 +3256,8 @@ hipError_t launch_gu(int fmt, int fmt_down, int mode, const GuArgs& ga, int grid
   auto go = [&](auto kern) -> hipError_t {
     hipError_t e = allow_smem(kern, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGuThreads), bytes, st, ga.logits, ga.A.nl4, ga.T, ga.E, ga);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGuThreads), bytes, st, ga.logits, ga.A.nl4, ga.x, ga.A.gate, ga.A.up,
+                       ga.T, ga.E, ga.A.n_embd, ga);
     return hipGetLastError();
   };
 #define MOE_LY(F, D) \
@@ -2993,6 +3272,10 @@ hipError_t launch_gu(int fmt, int fmt_down, int mode, const GuArgs& ga, int grid
     return mode == GU_COMPOSED ? go(k_gate_up<F, GU_COMPOSED>)               \
            : mode == GU_FUSED  ? go(k_gate_up<F, GU_FUSED>)                  \
                                : go(k_gate_up<F, GU_ROUTED>);
+  if (ga.regw && fmt == NL4 && mode != GU_LAYER)
+    return mode == GU_COMPOSED ? go(k_gate_up<NL4, GU_COMPOSED, NL4, true>)
+           : mode == GU_FUSED  ? go(k_gate_up<NL4, GU_FUSED, NL4, true>)
+                               : go(k_gate_up<NL4, GU_ROUTED, NL4, true>);
   switch (fmt) {
     MOE_GU(Q8_0)
     MOE_GU(NL4)
@@ -3120,6 +3403,11 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
   ga.lds_ring = ring;
   ga.lds_act = actb;
   ga.sw = sw;
+  // register-direct weights: planar NL4 rows of at most kRegUnits units per lane, every wave of
+  // the workgroup streaming (the LDS ring then only serves the prologue)
+  ga.regw = base_fmt(L->fmt_gate_up) == NL4 && is_planar(L->fmt_gate_up) && G.upl <= kRegUnits &&
+            G.U % 8 == 0 && G.rp * 2 * G.U <= std::min(1024, S.NS * S.M * 1024) && sw == kGuWaves &&
+            mode != GU_LAYER;
   ga.lds_tail = tailb;
   {
     const uint32_t nbk = (uint32_t)(L->n_ff / 32);

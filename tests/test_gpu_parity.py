@@ -90,6 +90,8 @@ def test_build_plan(T, E, k, base):
 ROUTED = {
     "small_q8": dict(n_embd=256, n_ff=128, E=8, k=2, T=1, fg=Q8_0, fd=Q8_0),
     "nl4_t1": dict(n_embd=2560, n_ff=768, E=128, k=8, T=1, fg=NL4, fd=NL4),
+    # four tokens sharing their experts: groups of 4 entries on the headline geometry
+    "nl4_t4_shared": dict(n_embd=2560, n_ff=768, E=128, k=8, T=4, fg=NL4, fd=NL4, ids="shared"),
     "cb2_nl4_t4_zipf": dict(n_embd=2560, n_ff=768, E=128, k=8, T=4, fg=CB2, fd=NL4, ids="zipf"),
     "cb3_q8_t2": dict(n_embd=2560, n_ff=640, E=256, k=8, T=2, fg=CB3, fd=Q8_0, ids="uniform"),
     "cb3_q8_t4_shared": dict(n_embd=2560, n_ff=640, E=256, k=8, T=4, fg=CB3, fd=Q8_0, ids="shared"),
@@ -278,8 +280,9 @@ def test_repack_bytes(fmt, ncols):
     assert np.array_equal(back.cpu().numpy(), m)
 
 
-@pytest.mark.parametrize("name", ["small_q8", "nl4_t1", "cb2_nl4_t4_zipf", "cb3_q8_t2", "nl4_cb2_t2",
-                                  "cb2_cb3_t4", "q8_q51_t3", "nl4x_q51_t4_zipf"])
+@pytest.mark.parametrize("name", ["small_q8", "nl4_t1", "nl4_t4_shared", "cb2_nl4_t4_zipf", "cb3_q8_t2",
+                                  "nl4_cb2_t2", "cb2_cb3_t4", "q8_q51_t3", "nl4x_q51_t4_zipf",
+                                  "nl4_t4_shared_tiny"])
 def test_planar_layer_same_bits(name):
     """Experts repacked into the planar layout give the row-major layer's bits on every path:
     composed (g, u, h, q8_1 of h, Y), fused, routed in two launches, and the one-launch step."""
@@ -304,9 +307,14 @@ def test_planar_layer_same_bits(name):
     assert r3["err"] == 0 and np.array_equal(U.bits(r3["Y"]), U.bits(ref["Y"]))
 
 
-@pytest.mark.parametrize("name", ["nl4_t1", "cb2_nl4_t4_zipf"])
-def test_grid_invariance(name):
+@pytest.mark.parametrize("name,planar", [("nl4_t1", False), ("cb2_nl4_t4_zipf", False), ("nl4_t1", True),
+                                         ("nl4_t4_shared", True)])
+def test_grid_invariance(name, planar):
+    """Every path and every grid limit gives the same bits (planar NL4: each wave may take several
+    passes, each loaded into registers on its own)."""
     c = _routed(name, key=2)
+    if planar:
+        c = U.planar_twin(c)
     T, k = c.T, c.k
     plan, _, _ = U.gpu_route_and_plan(c, T * k, T * k)
     Y0 = U.y0_for(T, c.n_embd, range(T), 3)
