@@ -434,17 +434,20 @@ def traffic_for(workload, kernel):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
-def sweep_line(name, T, routing, steps, warmup, cpu_seconds=0.0, model=None):
-    """One workload's graph-replayed step and launch times; with cpu_seconds, the CPU oracle on a
-    sample of its layer calls too (one thread and all cores)."""
+def sweep_line(name, T, routing, steps, warmup, cpu_seconds=0.0, model=None, layout="planar"):
+    """One workload's graph-replayed step and launch times (its pools repacked into `layout`);
+    with cpu_seconds, the CPU oracle on a sample of its layer calls too (one thread and all
+    cores)."""
     import torch
 
     from moe_routed_expert_route_amd.workloads import Workload
     wl = Workload(name, device="cuda", T=T, routing=routing)
+    if layout == "planar":
+        wl.to_planar()
     ms_step, _, ks = measure(wl, steps, warmup, reps=5)
     bytes_pass = float(sum(wl.weight_bytes_per_layer()))
     us = ms_step * 1e3 / wl.L
-    line = {"T": T, "routing": routing, "us_per_layer_call": round(us, 3),
+    line = {"T": T, "routing": routing, "layout": layout, "us_per_layer_call": round(us, 3),
             "gbs": round(bytes_pass / (ms_step * 1e-3) / 1e9, 1),
             "distinct_experts_per_layer": round(sum(wl.distinct_experts(l) for l in range(wl.L)) / wl.L, 2),
             "gate_up_us": round(ks["gate_up"], 3), "down_us": round(ks["down"], 3)}
@@ -462,6 +465,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="nl4_2560x768_t1")
+    ap.add_argument("--layout", default="planar", choices=("planar", "rowmajor"),
+                    help="weight layout of the timed pools (planar: repacked once at load by moe_repack)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time to measure")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the T = 1..4 lines")
@@ -496,6 +501,11 @@ def main():
         log("calibration copy: 256 MiB read, 256 MiB written")
     log(f"building workload {args.workload}")
     wl = Workload(args.workload, device="cuda", log=log)
+    repack = None
+    if args.layout == "planar":
+        # the row-major pools stay for the alternated layout comparison
+        repack = wl.to_planar(keep_rowmajor=not args.no_sweep)
+        log(f"repacked every pool into the planar layout ({repack[1] / 1e9:.1f} GB in {repack[0]:.3f} s)")
     per_layer = wl.weight_bytes_per_layer()
     bytes_pass = float(sum(per_layer))
     log(f"pool {wl.pool_bytes / 1e9:.2f} GB, routed bytes per pass {bytes_pass / 1e9:.3f} GB")
@@ -507,8 +517,10 @@ def main():
     gbs = bytes_pass / (ms_step * 1e-3) / 1e9
     lb = [wl.launch_bytes(l) for l in range(wl.L)]
     kb = {"gate_up": sum(b[0] for b in lb) / wl.L, "down": sum(b[1] for b in lb) / wl.L}
-    fmt_names = {1: "Q8_0", 2: "NL4", 3: "CB2", 4: "CB3"}
-    kname = {"gate_up": f"k_gate_up<{fmt_names[wl.fg]}, GU_ROUTED>",
+    fmt_names = {1: "Q8_0", 2: "NL4", 3: "CB2", 4: "CB3", 5: "Q5_1", 6: "NL4X"}
+    regw = args.layout == "planar" and wl.fg == 2
+    kname = {"gate_up": f"k_gate_up<{fmt_names[wl.fg]}, GU_ROUTED" +
+                        (", NL4, true> (weights straight into registers)" if regw else ">"),
              "down": f"k_down<{fmt_names[wl.fd]}>"}
     kernels = {}
     for kind in ("gate_up", "down"):
@@ -538,7 +550,8 @@ def main():
         "data": "synthetic (seeded), random-init experts",
         "config": {"workload": f"{wl.L} layers x {wl.E} experts {args.workload}: n_embd {wl.n_embd}, "
                                f"n_ff {wl.n_ff}, top-{wl.k}, T={wl.T}, cold pool "
-                               f"{wl.pool_bytes / 1e9:.1f} GB",
+                               f"{wl.pool_bytes / 1e9:.1f} GB, {args.layout} weight layout",
+                   "layout": args.layout,
                    "layers": wl.L, "experts": wl.E, "n_embd": wl.n_embd, "n_ff": wl.n_ff,
                    "top_k": wl.k, "T": wl.T, "parallelism": "single GPU"},
         "us_per_layer_call": round(us_layer, 3),
@@ -555,27 +568,31 @@ def main():
         log("two calls per layer")
         res["two_calls_per_layer"] = two_calls_us(wl)
     if not args.no_sweep:
-        log("planar layout: repack every pool beside the row-major one, alternate the two")
-        sec, nb = wl.to_planar(keep_rowmajor=True)
-        _, _, ks_p = measure(wl, 3, 1)
+        log("layouts: the row-major and the planar pools alternated")
+        if repack is None:
+            repack = wl.to_planar(keep_rowmajor=True)
+        sec, nb = repack
+        wl.use_layout("rowmajor")
+        _, _, ks_r = measure(wl, 3, 1)
         graphs = {}
         for name in ("rowmajor", "planar"):
             wl.use_layout(name)
             graphs[name] = step_graph(wl)
         ab = alternate(graphs, rounds=6, per=5)
         del graphs
-        wl.use_layout("rowmajor")
+        wl.use_layout(args.layout)
         res["planar_layout"] = {
             "us_per_layer_call": round(ab["planar"]["median_ms"] * 1e3 / wl.L, 3),
             "us_per_layer_call_rowmajor": round(ab["rowmajor"]["median_ms"] * 1e3 / wl.L, 3),
             "ab": {k: v["visit_medians_ms"] for k, v in ab.items()},
-            "gate_up_avg_launch_us": round(ks_p["gate_up"], 3),
-            "down_avg_launch_us": round(ks_p["down"], 3),
+            "rowmajor_gate_up_avg_launch_us": round(ks_r["gate_up"], 3),
+            "rowmajor_down_avg_launch_us": round(ks_r["down"], 3),
             "repack_gb": round(nb / 1e9, 3), "repack_s": round(sec, 4),
             "repack_gbs_read_plus_write": round(2 * nb / sec / 1e9, 1),
-            "config": "the same workload after moe_repack of every pool (all 128 experts of all "
-                      "48 layers) into the planar layout, kept beside the row-major pools; step "
-                      "graphs of both alternated A B / B A over 6 rounds of 5 replays, medians"}
+            "config": "the same workload in both layouts: every pool (all 128 experts of all 48 "
+                      "layers) repacked by moe_repack into the planar layout beside the row-major "
+                      "pools; step graphs of both alternated A B / B A over 6 rounds of 5 "
+                      "replays, medians"}
     if not args.no_cpu:
         res["cpu_baseline"] = run_cpu_baseline(wl, args.cpu_seconds, model)
     del wl

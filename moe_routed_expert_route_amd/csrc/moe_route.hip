@@ -625,6 +625,9 @@ constexpr int kRegSlots = 2;   // entries per register pass (more would spill ne
 struct RegW {
   u32x4 c[kRegUnits];   // the unit's 16 code bytes
 };
+// (The down rows do not take this path: at their 4 lanes a row, one 16-byte load per lane and
+// unit touches every row's line in 64-byte halves, which streamed measurably slower than the
+// direct-to-LDS spans of whole contiguous chunks.)
 
 // Issue the wave's loads (planar NL4): the scale planes of its rows into LDS at `sbuf` (row i's
 // at sbuf + 2 U i; lane j < rows * U / 8 takes piece j % (U / 8) of row j / (U / 8), whose first
@@ -3404,10 +3407,11 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
   ga.lds_act = actb;
   ga.sw = sw;
   // register-direct weights: planar NL4 rows of at most kRegUnits units per lane, every wave of
-  // the workgroup streaming (the LDS ring then only serves the prologue)
+  // the workgroup streaming (the LDS ring then only serves the prologue), groups of at most
+  // kRegSlots entries (n_tokens bounds them; larger groups would decode every unit once per pass)
   ga.regw = base_fmt(L->fmt_gate_up) == NL4 && is_planar(L->fmt_gate_up) && G.upl <= kRegUnits &&
             G.U % 8 == 0 && G.rp * 2 * G.U <= std::min(1024, S.NS * S.M * 1024) && sw == kGuWaves &&
-            mode != GU_LAYER;
+            mode != GU_LAYER && n_tokens <= kRegSlots;
   ga.lds_tail = tailb;
   {
     const uint32_t nbk = (uint32_t)(L->n_ff / 32);

@@ -90,7 +90,9 @@ def test_build_plan(T, E, k, base):
 ROUTED = {
     "small_q8": dict(n_embd=256, n_ff=128, E=8, k=2, T=1, fg=Q8_0, fd=Q8_0),
     "nl4_t1": dict(n_embd=2560, n_ff=768, E=128, k=8, T=1, fg=NL4, fd=NL4),
-    # four tokens sharing their experts: groups of 4 entries on the headline geometry
+    # tokens sharing their experts: groups of 2 (the register path's largest) and 4 entries on the
+    # headline geometry
+    "nl4_t2_shared": dict(n_embd=2560, n_ff=768, E=128, k=8, T=2, fg=NL4, fd=NL4, ids="shared"),
     "nl4_t4_shared": dict(n_embd=2560, n_ff=768, E=128, k=8, T=4, fg=NL4, fd=NL4, ids="shared"),
     "cb2_nl4_t4_zipf": dict(n_embd=2560, n_ff=768, E=128, k=8, T=4, fg=CB2, fd=NL4, ids="zipf"),
     "cb3_q8_t2": dict(n_embd=2560, n_ff=640, E=256, k=8, T=2, fg=CB3, fd=Q8_0, ids="uniform"),
@@ -280,7 +282,7 @@ def test_repack_bytes(fmt, ncols):
     assert np.array_equal(back.cpu().numpy(), m)
 
 
-@pytest.mark.parametrize("name", ["small_q8", "nl4_t1", "nl4_t4_shared", "cb2_nl4_t4_zipf", "cb3_q8_t2",
+@pytest.mark.parametrize("name", ["small_q8", "nl4_t1", "nl4_t2_shared", "nl4_t4_shared", "cb2_nl4_t4_zipf", "cb3_q8_t2",
                                   "nl4_cb2_t2", "cb2_cb3_t4", "q8_q51_t3", "nl4x_q51_t4_zipf",
                                   "nl4_t4_shared_tiny"])
 def test_planar_layer_same_bits(name):
@@ -307,8 +309,30 @@ def test_planar_layer_same_bits(name):
     assert r3["err"] == 0 and np.array_equal(U.bits(r3["Y"]), U.bits(ref["Y"]))
 
 
+@pytest.mark.parametrize("name", ["nl4_t1", "nl4_t2_shared"])
+def test_planar_skipped_group_same_bits(name):
+    """A group whose expert is out of range is skipped (MOE_ERR_EXPERT) the same way on the planar
+    NL4 path (weights loaded into registers; a skipped group still issues its count of loads) as on
+    the row-major one: fused and composed Y equal bit for bit, rows it owned keep Y0."""
+    c = _routed(name, key=8)
+    pc = U.planar_twin(c)
+    T, k = c.T, c.k
+    plan, _, _ = U.gpu_route_and_plan(c, T * k, T * k)
+    Y0 = U.y0_for(T, c.n_embd, range(T), 6)
+    plan.grp_expert[1] = 100000                  # out of range: group 1 skipped in both launches
+    for run in (lambda cc: U.run_fused(cc, plan, c.x, Y0),
+                lambda cc: U.run_composed(cc, plan, c.x, Y0, T)):
+        plan.err.zero_()
+        ref = run(c)
+        assert ref["err"] & 4
+        plan.err.zero_()
+        got = run(pc)
+        assert got["err"] & 4
+        assert np.array_equal(U.bits(got["Y"]), U.bits(ref["Y"]))
+
+
 @pytest.mark.parametrize("name,planar", [("nl4_t1", False), ("cb2_nl4_t4_zipf", False), ("nl4_t1", True),
-                                         ("nl4_t4_shared", True)])
+                                         ("nl4_t2_shared", True), ("nl4_t4_shared", True)])
 def test_grid_invariance(name, planar):
     """Every path and every grid limit gives the same bits (planar NL4: each wave may take several
     passes, each loaded into registers on its own)."""
