@@ -8,31 +8,32 @@
 // destination rows with the router weights.
 //
 // Design for gfx950 (the pages' CUDA kernels are prior art, not the blueprint):
-//  * Two launches per layer and no cross-workgroup synchronisation inside a kernel (a grid-wide
-//    release/acquire costs more than the kernel boundary on this part):
-//      gate/up kernel: one work item = 2 rp consecutive h rows of one group (rp = weight rows per
-//        wave pass); wave w streams the gate and up rows of its rp / 2 h rows, dots them with the
-//        group's entries and writes SwiGLU(g, u) straight out, so items need no workgroup barrier;
-//      down kernel: one work item = rp rows of Y across every group of the call, so each output
-//        element is summed by one workgroup in ascending entry order (deterministic, no atomics);
-//        its prologue quantizes the call's h rows to q8_1 in LDS.
-//  * Latency first: a layer call moves tens of MB, so every dependent round trip to memory shows.
-//    Each kernel issues all independent loads of its prologue at once (logits, x, tables, plan or
-//    descriptor, expert pointers), routes with one wave per token (a ballot radix select) and
-//    groups with one wave; the gate/up launch leaves a one-read descriptor of the call (groups,
-//    entries, down pointers) for the down launch.
-//  * Each wave streams its weight rows HBM -> LDS with direct-to-LDS 16-byte loads
-//    (global_load_lds_dwordx4, fully coalesced for 18/34/70/110-byte blocks that do not align to
-//    16 bytes) through a private ring of slots. Every chunk costs exactly M load instructions, and
-//    loads complete in issue order, so "chunk k has landed" is a vmcnt wait on the number of
-//    loads issued after it: later chunks stay in flight while the wave computes. Stores issued
-//    between two waits only raise the count, so they can make a wait longer, never too short.
-//  * Weight units are decoded out of LDS at any byte alignment (v_alignbyte); activations sit in
-//    LDS as q8_1 split into 16-byte halves plus the float scale.
+//  * Two launches per layer. The gate/up kernel (16 waves, one workgroup per CU) routes the
+//    tokens, groups the entries, quantizes x, streams the routed experts' gate and up rows, and
+//    writes SwiGLU + q8_1 of h into the caller's workspace; its last workgroup also writes the
+//    plan and a one-read descriptor of the call. The down kernel (8 waves) reads the descriptor
+//    and the h rows and owns a tile of Y rows across every group, so each output element is
+//    summed by one workgroup in ascending entry order (deterministic, no atomics).
+//  * Work items: gate/up, one 32-row block of h of one group (SwiGLU and the block's q8_1 finish
+//    inside the workgroup); down, tr = ceil(n_embd / CUs) rows of Y.
+//  * Latency first: a layer call moves tens of MB, so every dependent round trip shows. The
+//    leading kernel arguments (logits, NL4 table, x, the gate / up pointer arrays, T, E, n_embd)
+//    arrive preloaded in scalar registers, so the first loads go out before the argument block
+//    is read. Every workgroup routes the window itself: one wave per token (group-maxima
+//    threshold, then exact ranks of the candidates), or for one-token windows all eight routing
+//    waves rank every expert at once; after one workgroup barrier each wave finds its item's
+//    expert and entries from the tokens' selection bitmaps and issues its weight loads.
+//  * Weight streams: row-major rows (any byte alignment) come HBM -> LDS by direct-to-LDS 16-byte
+//    loads (global_load_lds_dwordx4, one uniform base per span) through a private ring per wave;
+//    loads complete in issue order, so "chunk k has landed" is a vmcnt wait on the loads issued
+//    after it. Planar NL4 rows (codes on 16-byte boundaries) go straight into registers, one
+//    16-byte load per lane and unit, their scale planes by one direct-to-LDS instruction.
 //  * A row is split over L lanes (a power of two chosen from the shape only); lane l takes units
 //    l, l+L, ...; per unit v_dot4 (int8) per 4 weights, then scale * d_x * isum in float32; the L
 //    partial sums meet in a fixed DPP tree. The lane map depends only on the shape, so every
-//    kernel variant and every grid produces the same bits.
+//    kernel variant, layout and grid produces the same bits.
+//  * The prompt path (hundreds of tokens) runs the same per-entry computation as grouped GEMMs
+//    on the matrix cores (v_mfma_i32_16x16x32_i8, one instruction per 32-weight block).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -2671,16 +2672,26 @@ constexpr int kPfRows = 32;            // rows of a workgroup tile (two 16-row M
 constexpr int kPfEnt = 32;             // entries of a pass (two 16-column MFMA tiles)
 constexpr int kPfK = 512;              // weights of a K chunk (16 blocks of 32, two of 256)
 constexpr int kPfBlk = kPfK / 32;
-constexpr int kPfRaw = 1040;           // LDS stride of the raw row slots: 1 KB loaded (a chunk is at most
-                                       // 544 B) plus 16 B so that rows start on different banks
 constexpr int kPfCS = kPfK + 16;       // LDS row stride of the int8 codes and quants
 constexpr int kPfSS = 36;              // LDS block stride of the per-(block, row / entry) scales: a
                                        // wave's stores (16 blocks x 4 rows) then meet every bank twice
 constexpr int kPfThreads = 256;
 static_assert(kPfSS >= kPfRows && kPfSS >= kPfEnt && kPfSS % 4 == 0, "scale rows fit, float4 reads aligned");
-constexpr int kPfLds = kPfRows * kPfRaw + (kPfRows + kPfEnt) * kPfCS + 4 * kPfBlk * 4 * kPfSS +
-                       4096 + 64;
-static_assert(2 * kPfLds <= 160 * 1024, "two prompt-path workgroups share a CU's LDS");
+// Raw rows of a chunk, packed: row r's aligned 16-byte pieces at r * kPfP pieces (a chunk's bytes
+// plus its start's offset inside a piece), so one direct-to-LDS instruction (64 pieces) covers
+// several rows.
+template <int FMT>
+constexpr int pf_pieces() { return (kPfK / block_weights(FMT) * block_bytes(FMT) + 15) / 16 + 1; }
+// LDS of the prompt-path GEMM for format FMT: raw rows, codes and quants, the per-block scales
+// (weights and activations; offsets and sum fields for Q5_1 only), the CB grid (CB2 / CB3 only).
+template <int FMT>
+constexpr int pf_lds() {
+  return kPfRows * pf_pieces<FMT>() * 16 + (kPfRows + kPfEnt) * kPfCS + (FMT == Q5_1 ? 4 : 2) * kPfBlk * 4 * kPfSS +
+         ((FMT == CB2 || FMT == CB3) ? 4096 : 0) + 64;
+}
+static_assert(3 * pf_lds<NL4>() <= 160 * 1024, "three NL4 prompt-path workgroups share a CU's LDS");
+static_assert(2 * pf_lds<Q8_0>() <= 160 * 1024 && 2 * pf_lds<Q5_1>() <= 160 * 1024 &&
+              2 * pf_lds<CB3>() <= 160 * 1024, "two prompt-path workgroups share a CU's LDS");
 // The (row, block) unit that decode slot x (0..511) of a chunk takes: each 64-slot wave pass
 // covers 8 rows x 8 blocks with the row fastest, so the 8 lanes that store their 32 codes to LDS
 // together write 8 different rows (row stride 132 dwords: distinct bank groups) rather than
@@ -2705,15 +2716,16 @@ struct PfArgs {
 template <int FMT>
 __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int kP = pf_pieces<FMT>();
   MOE_LDS uint8_t* raw = (MOE_LDS uint8_t*)smem;
-  MOE_LDS uint8_t* codes = raw + kPfRows * kPfRaw;
+  MOE_LDS uint8_t* codes = raw + kPfRows * kP * 16;
   MOE_LDS uint8_t* quant = codes + kPfRows * kPfCS;
   MOE_LDS float* dws = (MOE_LDS float*)(quant + kPfEnt * kPfCS);   // [blk][row]
-  MOE_LDS float* mos = dws + kPfBlk * kPfSS;                      // [blk][row] (Q5_1 offsets)
-  MOE_LDS float* dxs = mos + kPfBlk * kPfSS;                      // [blk][entry]
-  MOE_LDS float* sxs = dxs + kPfBlk * kPfSS;                       // [blk][entry] (sum fields)
-  MOE_LDS uint32_t* grid = (MOE_LDS uint32_t*)(sxs + kPfBlk * kPfSS);   // CB2 / CB3 grid
-  MOE_LDS int* misc = (MOE_LDS int*)(grid + 1024);
+  MOE_LDS float* dxs = dws + kPfBlk * kPfSS;                      // [blk][entry]
+  MOE_LDS float* mos = dxs + kPfBlk * kPfSS;                      // [blk][row] (Q5_1 offsets)
+  MOE_LDS float* sxs = mos + kPfBlk * kPfSS;                      // [blk][entry] (Q5_1 sum fields)
+  MOE_LDS uint32_t* grid = (MOE_LDS uint32_t*)(dxs + (FMT == Q5_1 ? 3 : 1) * kPfBlk * kPfSS);   // CB2 / CB3
+  MOE_LDS int* misc = (MOE_LDS int*)(grid + ((FMT == CB2 || FMT == CB3) ? 1024 : 0));
   const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
   const int g = (int)blockIdx.y;
   const int tpm = (a.rows + kPfRows - 1) / kPfRows;
@@ -2774,12 +2786,18 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
   auto issue_chunk = [&](int ep, int ne, int kc) {
     const int nblk = min(kPfBlk, (a.K - kc) / 32);
     const uint32_t nbytes = (uint32_t)(nblk * 32 / bw * bb);
-    for (int r = wave; r < kPfRows; r += kPfThreads / 64) {   // wave w takes rows w, w + 4, ...
-      if (r0 + r < a.rows) {
-        const uint8_t* src = (const uint8_t*)(uintptr_t)(wp + (uint64_t)(r0 + r) * (uint64_t)a.rb +
-                                                         (uint64_t)(kc / bw * bb));
-        issue_span(raw + r * kPfRaw, 1, src, nbytes);
-      }
+    // piece i of the tile's chunk: row i / kP, piece i % kP of the row's span (from its aligned
+    // start); wave w issues the 64-piece instructions w, w + 4, ... (rows past the matrix and
+    // pieces past a row's span reload the row's first piece: never read)
+    for (int i0 = wave * 64; i0 < kPfRows * kP; i0 += kPfThreads) {
+      const int idx = i0 + lane, r = idx / kP, p = idx - r * kP;
+      const int rr = min(r0 + min(r, kPfRows - 1), a.rows - 1);
+      const uint64_t src = wp + (uint64_t)rr * (uint64_t)a.rb + (uint64_t)(kc / bw * bb);
+      const uint32_t need = ((uint32_t)(src & 15u) + nbytes + 15u) >> 4;
+      const uint64_t at = (src & ~15ull) + ((r0 + r < a.rows && (uint32_t)p < need) ? 16ull * p : 0ull);
+      if (idx < kPfRows * kP)   // (lanes past the tile would write past the raw rows)
+        __builtin_amdgcn_global_load_lds((const void*)(uintptr_t)at, (MOE_LDS void*)(raw + i0 * 16), 16, 0,
+                                         kAuxStream);
     }
 #pragma unroll
     for (int j = 0; j < kQ; ++j) {
@@ -2828,7 +2846,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
         *(MOE_LDS u32x4*)dq = u32x4{qq[j][1], qq[j][2], qq[j][3], qq[j][4]};
         *(MOE_LDS u32x4*)(dq + 4) = u32x4{qq[j][5], qq[j][6], qq[j][7], qq[j][8]};
         dxs[bl * kPfSS + en] = h2f(qq[j][0] & 0xFFFFu);
-        sxs[bl * kPfSS + en] = h2f(qq[j][0] >> 16);
+        if constexpr (FMT == Q5_1) sxs[bl * kPfSS + en] = h2f(qq[j][0] >> 16);
       }
       __syncthreads();
       // (3) decode the raw rows into codes and scales: (row, block) pairs over the threads, the
@@ -2842,7 +2860,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
           const int x = tid + j * kPfThreads, r = pf_dec_row(x), bl = pf_dec_blk(x);
           dl[j] = r0 + r < a.rows && bl < nblk;
           const uint64_t src = wp + (uint64_t)(r0 + r) * (uint64_t)a.rb + (uint64_t)(kc / bw * bb);
-          const uint32_t row = (uint32_t)(r * kPfRaw) + (uint32_t)(src & 15u);   // from raw
+          const uint32_t row = (uint32_t)(r * kP * 16) + (uint32_t)(src & 15u);   // from raw
           unit_load<FMT>((const MOE_LDS uint32_t*)raw, row, dl[j] ? bl : 0, a.ly, rr[j]);
         }
 #pragma unroll
@@ -2861,7 +2879,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
           *(MOE_LDS u32x4*)dc = u32x4{c[0], c[1], c[2], c[3]};
           *(MOE_LDS u32x4*)(dc + 4) = u32x4{c[4], c[5], c[6], c[7]};
           dws[bl * kPfSS + r] = sc;
-          mos[bl * kPfSS + r] = mo;
+          if constexpr (FMT == Q5_1) mos[bl * kPfSS + r] = mo;   // (the others have no offset plane)
         }
       }
       __syncthreads();
@@ -3291,6 +3309,35 @@ hipError_t launch_gu(int fmt, int fmt_down, int mode, const GuArgs& ga, int grid
   return hipErrorInvalidValue;
 }
 
+// Workgroups of the one-launch gate/up kernel (format fmt, down format fmt_down) that one CU holds
+// at once with `bytes` of dynamic LDS, as the runtime computes it (registers, LDS, waves); 0 if the
+// query fails.
+int gu_layer_occupancy(int fmt, int fmt_down, int bytes) {
+  int nb = 0;
+  auto q = [&](auto kern) {
+    if (allow_smem(kern, bytes) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kGuThreads, (size_t)bytes) != hipSuccess)
+      nb = 0;
+  };
+#define MOE_LQ(F, D) \
+  case D:            \
+    q(k_gate_up<F, GU_LAYER, D>); break;
+#define MOE_GQ(F)                                                                                            \
+  case F:                                                                                                    \
+    switch (fmt_down) { MOE_LQ(F, Q8_0) MOE_LQ(F, NL4) MOE_LQ(F, CB2) MOE_LQ(F, CB3) MOE_LQ(F, Q5_1) MOE_LQ(F, NL4X) } \
+    break;
+  switch (fmt) {
+    MOE_GQ(Q8_0)
+    MOE_GQ(NL4)
+    MOE_GQ(CB2)
+    MOE_GQ(CB3)
+    MOE_GQ(NL4X)
+  }
+#undef MOE_GQ
+#undef MOE_LQ
+  return nb;
+}
+
 hipError_t launch_dn(int fmt, int mode, const DnArgs& da, int grid, int bytes, hipStream_t st) {
   auto go = [&](auto kern) -> hipError_t {
     hipError_t e = allow_smem(kern, bytes);
@@ -3422,10 +3469,12 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
   // and the descriptor, then holds no block of its own
   int grid = grid_for(mode == GU_COMPOSED ? items : items + 1, bytes, grid_limit);
   if (mode == GU_LAYER) {
-    // every workgroup waits for all the others: at most what the CUs hold at once (LDS-limited)
+    // every workgroup waits for all the others: at most what the CUs hold at once (the runtime's
+    // occupancy for this kernel: registers, LDS and waves; at least one per CU)
     const Geom Gd = down_geom(L);
     ga.Gd = Gd;
-    const int resident = num_cus() * std::max(1, std::min(8, kLdsMax / bytes));
+    const int resident =
+        num_cus() * std::max(1, gu_layer_occupancy(base_fmt(L->fmt_gate_up), base_fmt(L->fmt_down), bytes));
     grid = std::min(std::min(grid_limit ? grid_limit : num_cus(), resident), kLyMaxGrid);
     // one down tile per CU (a smaller grid takes several each)
     dn_tiling(Gd, L->n_embd, num_cus(), ga.trd, ga.rcd);
@@ -3522,20 +3571,20 @@ int run_pf_gemm(hipStream_t st, const moe_layer* L, const moe_plan* P, bool down
   pa.out1 = out1;
   pa.ld = ld;
   const dim3 grid((unsigned)(pa.nmat * ((rows + kPfRows - 1) / kPfRows)), (unsigned)P->cap_groups);
-  auto go = [&](auto kern) -> hipError_t {
-    hipError_t e = allow_smem(kern, kPfLds);
+  auto go = [&](auto kern, int lds) -> hipError_t {
+    hipError_t e = allow_smem(kern, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, grid, dim3(kPfThreads), kPfLds, st, pa);
+    hipLaunchKernelGGL(kern, grid, dim3(kPfThreads), lds, st, pa);
     return hipGetLastError();
   };
   hipError_t e = hipErrorInvalidValue;
   switch (fmt) {
-    case Q8_0: e = go(k_pf_gemm<Q8_0>); break;
-    case NL4: e = go(k_pf_gemm<NL4>); break;
-    case CB2: e = go(k_pf_gemm<CB2>); break;
-    case CB3: e = go(k_pf_gemm<CB3>); break;
-    case Q5_1: e = go(k_pf_gemm<Q5_1>); break;
-    case NL4X: e = go(k_pf_gemm<NL4X>); break;
+    case Q8_0: e = go(k_pf_gemm<Q8_0>, pf_lds<Q8_0>()); break;
+    case NL4: e = go(k_pf_gemm<NL4>, pf_lds<NL4>()); break;
+    case CB2: e = go(k_pf_gemm<CB2>, pf_lds<CB2>()); break;
+    case CB3: e = go(k_pf_gemm<CB3>, pf_lds<CB3>()); break;
+    case Q5_1: e = go(k_pf_gemm<Q5_1>, pf_lds<Q5_1>()); break;
+    case NL4X: e = go(k_pf_gemm<NL4X>, pf_lds<NL4X>()); break;
   }
   return e == hipSuccess ? MOE_OK : hip_fail(e, down ? "prefill down kernel" : "prefill gate/up kernel");
 }
