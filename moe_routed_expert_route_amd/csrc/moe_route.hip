@@ -2670,11 +2670,12 @@ __global__ __launch_bounds__(kPpThreads) void k_plan_large(const int32_t* __rest
 // sum is that of the block.
 constexpr int kPfRows = 32;            // rows of a workgroup tile (two 16-row MFMA tiles)
 constexpr int kPfEnt = 32;             // entries of a pass (two 16-column MFMA tiles)
-constexpr int kPfK = 512;              // weights of a K chunk (16 blocks of 32, two of 256)
+constexpr int kPfK = 256;              // weights of a K chunk (8 blocks of 32, one of 256): small chunks
+                                       // keep the LDS small, so five or six workgroups share a CU
 constexpr int kPfBlk = kPfK / 32;
 constexpr int kPfCS = kPfK + 16;       // LDS row stride of the int8 codes and quants
 constexpr int kPfSS = 36;              // LDS block stride of the per-(block, row / entry) scales: a
-                                       // wave's stores (16 blocks x 4 rows) then meet every bank twice
+                                       // wave's stores (blocks x 4 rows) spread over the banks
 constexpr int kPfThreads = 256;
 static_assert(kPfSS >= kPfRows && kPfSS >= kPfEnt && kPfSS % 4 == 0, "scale rows fit, float4 reads aligned");
 // Raw rows of a chunk, packed: row r's aligned 16-byte pieces at r * kPfP pieces (a chunk's bytes
@@ -2689,14 +2690,14 @@ constexpr int pf_lds() {
   return kPfRows * pf_pieces<FMT>() * 16 + (kPfRows + kPfEnt) * kPfCS + (FMT == Q5_1 ? 4 : 2) * kPfBlk * 4 * kPfSS +
          ((FMT == CB2 || FMT == CB3) ? 4096 : 0) + 64;
 }
-static_assert(3 * pf_lds<NL4>() <= 160 * 1024, "three NL4 prompt-path workgroups share a CU's LDS");
+static_assert(5 * pf_lds<NL4>() <= 160 * 1024, "five NL4 prompt-path workgroups share a CU's LDS");
 static_assert(2 * pf_lds<Q8_0>() <= 160 * 1024 && 2 * pf_lds<Q5_1>() <= 160 * 1024 &&
               2 * pf_lds<CB3>() <= 160 * 1024, "two prompt-path workgroups share a CU's LDS");
 // The (row, block) unit that decode slot x (0..511) of a chunk takes: each 64-slot wave pass
 // covers 8 rows x 8 blocks with the row fastest, so the 8 lanes that store their 32 codes to LDS
 // together write 8 different rows (row stride 132 dwords: distinct bank groups) rather than
 // blocks 32 bytes apart in one row.
-static_assert(kPfRows == 32 && kPfBlk == 16 && kPfRows * kPfBlk == 2 * kPfThreads, "decode slot map");
+static_assert(kPfRows == 32 && kPfBlk <= 16 && kPfRows * kPfBlk % kPfThreads == 0, "decode slot map");
 __device__ __forceinline__ int pf_dec_row(int x) { return 8 * ((x >> 6) & 3) + (x & 7); }
 __device__ __forceinline__ int pf_dec_blk(int x) { return 8 * (x >> 8) + ((x >> 3) & 7); }
 
