@@ -31,6 +31,8 @@ PREFILL = {
     "nl4x_q8_t50": dict(n_embd=1024, n_ff=320, E=24, k=4, T=50, fg=NL4X, fd=Q8_0),
     # the decode geometry with a prompt's worth of tokens
     "nl4_2560x768_t24": dict(n_embd=2560, n_ff=768, E=128, k=8, T=24, fg=NL4, fd=NL4),
+    # about 80 entries per group: every group takes a second 64-entry pass over its rows
+    "nl4_t160_e4": dict(n_embd=512, n_ff=256, E=4, k=2, T=160, fg=NL4, fd=NL4),
 }
 
 # the benchmarked prompt-path shape: 512 tokens, top-8 of 128 NL4 experts of 2560 x 768 (every
