@@ -465,6 +465,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="nl4_2560x768_t1")
+    ap.add_argument("--T", type=int, default=None, help="tokens per window (default: the workload's)")
+    ap.add_argument("--routing", default=None, help="logits / zipf / uniform / shared (default: the workload's)")
     ap.add_argument("--layout", default="planar", choices=("planar", "rowmajor"),
                     help="weight layout of the timed pools (planar: repacked once at load by moe_repack)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time to measure")
@@ -500,7 +502,7 @@ def main():
         del src, dst
         log("calibration copy: 256 MiB read, 256 MiB written")
     log(f"building workload {args.workload}")
-    wl = Workload(args.workload, device="cuda", log=log)
+    wl = Workload(args.workload, device="cuda", T=args.T, routing=args.routing, log=log)
     repack = None
     if args.layout == "planar":
         # the row-major pools stay for the alternated layout comparison

@@ -26,8 +26,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ("moe_routed_expert_route_amd/csrc/moe_route.hip",
                   "moe_routed_expert_route_amd/csrc/moe_device.hpp",
                   "moe_routed_expert_route_amd/build.py")
-# the decode launches by their mangled-name prefix (template arguments: formats, mode)
+# the decode launches by their mangled-name prefix (template arguments: formats, mode); the prompt
+# path's GEMM (gate/up and down launches share the kernel)
 KINDS = {"gate_up": "void moe::k_gate_up<", "down": "void moe::k_down<"}
+PF_KIND = {"prefill_gemm": "void moe::k_pf_gemm<"}
 CALIB = "__amd_rocclr_copyBuffer"
 
 
@@ -108,14 +110,22 @@ def counter_per_dispatch(path, counter):
     return {n: (sum(v) / len(v), len(v)) for n, v in agg.items()}
 
 
+def dispatch_values(path, counter, prefix):
+    """Per-dispatch values of `counter` (summed over dimension rows) for kernels named `prefix`..."""
+    per = defaultdict(float)
+    for r in _rows(path):
+        if _col(r, "Counter_Name", "Counter-Name") == counter and \
+                _col(r, "Kernel_Name", "Kernel-Name").startswith(prefix):
+            per[_col(r, "Dispatch_Id", "Dispatch-Id")] += float(_col(r, "Counter_Value", "Counter-Value"))
+    return list(per.values())
+
+
 def write_traffic(fetch_csv, write_csv, workload, command, calib_kib=262144.0, algorithmic=None):
     fe = counter_per_dispatch(fetch_csv, "FETCH_SIZE")
     wr = counter_per_dispatch(write_csv, "WRITE_SIZE")
-    cal_f = [v for n, v in fe.items() if n.startswith(CALIB)]
-    cal_w = [v for n, v in wr.items() if n.startswith(CALIB)]
-    # the calibration copy is the largest copy of the run (256 MiB read, 256 MiB written)
-    f_cal = max(v[0] for v in cal_f)
-    w_cal = max(v[0] for v in cal_w)
+    # the calibration copy is the largest copy dispatch of the run (256 MiB read, 256 MiB written)
+    f_cal = max(dispatch_values(fetch_csv, "FETCH_SIZE", CALIB))
+    w_cal = max(dispatch_values(write_csv, "WRITE_SIZE", CALIB))
     fs, ws = calib_kib / f_cal, calib_kib / w_cal
     doc = {"workload": workload, "source_sha256": source_digest(), "command": command,
            "calibration": {"kernel": f"{CALIB}, 256 MiB device-to-device copy (bench.py --calib)",
@@ -155,6 +165,55 @@ def write_traffic(fetch_csv, write_csv, workload, command, calib_kib=262144.0, a
     return doc
 
 
+SQ = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM", "SQ_ACTIVE_INST_VALU",
+      "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT")
+
+
+def write_sq(csv_path, name, title, command, weights=None, kinds=None):
+    """profiles/sq_<name>.md: per-launch SQ counters of each kind (mean over the run's dispatches)
+    and what follows from them: instructions per wave, VALU lane-instructions per weight (weights:
+    kind -> weights per launch), SALU per VALU, the share of LDS cycles lost to bank conflicts."""
+    kinds = kinds or KINDS
+    per = {c: counter_per_dispatch(csv_path, c) for c in SQ}
+    rows = {}
+    for kind, prefix in kinds.items():
+        for c in SQ:
+            hits = {n: v for n, v in per[c].items() if n.startswith(prefix)}
+            if hits:
+                n = max(hits, key=lambda k: hits[k][1])
+                rows.setdefault(kind, {"kernel": n, "dispatches": hits[n][1]})[c] = hits[n][0]
+    lines = [f"# SQ counters: {title}", "", "Command (repo root, one MI355X):", "", f"    {command}", "",
+             "Mean per launch over the run's dispatches (whole-device sums):", "",
+             "| counter | " + " | ".join(rows) + " |", "|---" * (len(rows) + 1) + "|"]
+    for c in SQ:
+        lines.append(f"| {c} | " + " | ".join(f"{rows[k].get(c, 0):.0f}" for k in rows) + " |")
+    lines += ["", "| figure | " + " | ".join(rows) + " |", "|---" * (len(rows) + 1) + "|"]
+    def fig(label, f):
+        vals = []
+        for k in rows:
+            try:
+                vals.append(f(k, rows[k]))
+            except (KeyError, ZeroDivisionError, TypeError):
+                vals.append("-")
+        lines.append(f"| {label} | " + " | ".join(v if isinstance(v, str) else f"{v:.3f}" for v in vals) + " |")
+    fig("VALU instructions per wave", lambda k, r: r["SQ_INSTS_VALU"] / r["SQ_WAVES"])
+    fig("SALU instructions per wave", lambda k, r: r["SQ_INSTS_SALU"] / r["SQ_WAVES"])
+    fig("LDS instructions per wave", lambda k, r: r["SQ_INSTS_LDS"] / r["SQ_WAVES"])
+    fig("VMEM instructions per wave", lambda k, r: r["SQ_INSTS_VMEM"] / r["SQ_WAVES"])
+    if weights:
+        fig("VALU lane-instructions per weight (x 64)", lambda k, r: r["SQ_INSTS_VALU"] * 64 / weights[k])
+    fig("SALU per VALU instruction", lambda k, r: r["SQ_INSTS_SALU"] / r["SQ_INSTS_VALU"])
+    fig("LDS bank-conflict cycles / LDS active cycles",
+        lambda k, r: r["SQ_LDS_BANK_CONFLICT"] / r["SQ_LDS_IDX_ACTIVE"])
+    lines += [""] + [f"- {k}: `{r['kernel'][:100]}` ({r['dispatches']} dispatches)" for k, r in rows.items()]
+    if weights:
+        lines += [f"- weights per launch: " + ", ".join(f"{k} {w:,}" for k, w in weights.items())]
+    lines += ["", f"Kernel sources SHA-256: `{source_digest()}`", ""]
+    with open(os.path.join(PROFILES, f"sq_{name}.md"), "w") as f:
+        f.write("\n".join(lines))
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -169,7 +228,21 @@ def main():
     t.add_argument("--command", required=True)
     t.add_argument("--gate-up-bytes", type=int, default=0, help="algorithmic bytes per gate/up launch")
     t.add_argument("--down-bytes", type=int, default=0, help="algorithmic bytes per down launch")
+    q = sub.add_parser("sq")
+    q.add_argument("--csv", required=True)
+    q.add_argument("--name", required=True)
+    q.add_argument("--title", required=True)
+    q.add_argument("--command", required=True)
+    q.add_argument("--gate-up-weights", type=int, default=0)
+    q.add_argument("--down-weights", type=int, default=0)
+    q.add_argument("--prefill", action="store_true", help="the prompt path's GEMM launches")
     a = ap.parse_args()
+    if a.what == "sq":
+        w = {k: v for k, v in (("gate_up", a.gate_up_weights), ("down", a.down_weights)) if v}
+        rows = write_sq(a.csv, a.name, a.title, a.command, weights=w or None,
+                        kinds=PF_KIND if a.prefill else None)
+        print(json.dumps(rows, indent=1))
+        return
     if a.what == "kernels":
         doc = write_kernels(a.stats, a.workload, a.command)
     else:
