@@ -1315,7 +1315,10 @@ __host__ __device__ inline int ly_down_bytes(int cap_entries, int Ud, bool with_
 // arrays, T, E and n_embd: they come as the leading scalar arguments (copies of the struct's
 // fields), which the launch preloads into scalar registers, so those loads go out before any read
 // of the argument struct.
-template <int FMT, int MODE, int FD = FMT, bool RW = false>
+// ONE: the routed launch of a one-token window over at most 128 experts, compiled on its own: the
+// ranked routing alone and one-entry dot passes (the per-token routing and the passes over several
+// entries would only add code the launch never runs, and that code measurably slows it).
+template <int FMT, int MODE, int FD = FMT, bool RW = false, bool ONE = false>
 __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict__ logits0,
                                                         const int8_t* __restrict__ nl4_0,
                                                         const float* __restrict__ x0,
@@ -1336,7 +1339,8 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
   MOE_LDS uint32_t* rscr = (MOE_LDS uint32_t*)ring + wave * route_scr_words(E0);
   // routed: the routing waves rank every token's experts together when the window is small
   // enough (then all waves meet once the logits rows are in LDS); else one wave per token
-  const int rparts = MODE == GU_ROUTED ? route_parts(T0, E0, 64 * kRtWaves) : 0;
+  static_assert(!ONE || MODE == GU_ROUTED, "the one-token launch is a routed one");
+  const int rparts = ONE ? 4 : MODE == GU_ROUTED ? route_parts(T0, E0, 64 * kRtWaves) : 0;
   uint32_t t_nl4[4] = {0u, 0u, 0u, 0u};
   if constexpr (RT) {
     if (rw) {
@@ -1537,7 +1541,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
   int upc = 0, upre = 0, cpre = 0;
   int ng = 0, e0 = 0, n = 0;
   if constexpr (RT) {
-    if (a.T == 1) {   // one token: the union is its selection, each group holds one entry
+    if (ONE || a.T == 1) {   // one token: the union is its selection, each group holds one entry
       if (lane < nW) uw = selT[lane];
       upc = __popc(uw);
       upre = lane_prefix(upc, 6);
@@ -1829,8 +1833,11 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
           }
           MOE_LDS float* st = stage + c0 * 64 + prow;
           if (c0 == 0) wait_vm(G.upl);   // the scale planes (issued before this lane's code loads)
-          dot_pass_reg(rwt, (const MOE_LDS uint16_t*)myring, G.rp, G, tb, act, sidx, nc,
-                       [&](int i, int e, float v) { st[e * 64 + (i < half ? i : 32 + i - half)] = v; });
+          auto outr = [&](int i, int e, float v) { st[e * 64 + (i < half ? i : 32 + i - half)] = v; };
+          if constexpr (ONE)
+            dot_pass_reg_n<1>(rwt, (const MOE_LDS uint16_t*)myring, G.rp, G, tb, act, sidx, outr);
+          else
+            dot_pass_reg(rwt, (const MOE_LDS uint16_t*)myring, G.rp, G, tb, act, sidx, nc, outr);
         }
       } else if (wgv) {
         const int prow = (wave + q * a.sw) * half;   // first h row of the pass inside the block
@@ -1855,8 +1862,11 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
             }
           }
           MOE_LDS float* st = stage + c0 * 64 + prow;
-          dot_pass<FMT>((const MOE_LDS uint32_t*)ring, ra, rb0, half, G.rp, G, tb, act, sidx, nc,
-                        [&](int i, int e, float v) { st[e * 64 + (i < half ? i : 32 + i - half)] = v; });
+          auto outl = [&](int i, int e, float v) { st[e * 64 + (i < half ? i : 32 + i - half)] = v; };
+          if constexpr (ONE)
+            dot_pass_n<FMT, 1>((const MOE_LDS uint32_t*)ring, ra, rb0, half, G.rp, G, tb, act, sidx, outl);
+          else
+            dot_pass<FMT>((const MOE_LDS uint32_t*)ring, ra, rb0, half, G.rp, G, tb, act, sidx, nc, outl);
         }
       }
       if (!regw && kc + NS < nch) {
@@ -3274,7 +3284,8 @@ hipError_t allow_smem(K kern, int bytes) {
   return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-hipError_t launch_gu(int fmt, int fmt_down, int mode, const GuArgs& ga, int grid, int bytes, hipStream_t st) {
+hipError_t launch_gu(int fmt, int fmt_down, int mode, bool one, const GuArgs& ga, int grid, int bytes,
+                     hipStream_t st) {
   auto go = [&](auto kern) -> hipError_t {
     hipError_t e = allow_smem(kern, bytes);
     if (e != hipSuccess) return e;
@@ -3291,12 +3302,14 @@ hipError_t launch_gu(int fmt, int fmt_down, int mode, const GuArgs& ga, int grid
       switch (fmt_down) { MOE_LY(F, Q8_0) MOE_LY(F, NL4) MOE_LY(F, CB2) MOE_LY(F, CB3) MOE_LY(F, Q5_1) MOE_LY(F, NL4X) } \
       return hipErrorInvalidValue;                                           \
     }                                                                        \
+    if (mode == GU_ROUTED && one) return go(k_gate_up<F, GU_ROUTED, F, false, true>); \
     return mode == GU_COMPOSED ? go(k_gate_up<F, GU_COMPOSED>)               \
            : mode == GU_FUSED  ? go(k_gate_up<F, GU_FUSED>)                  \
                                : go(k_gate_up<F, GU_ROUTED>);
   if (ga.regw && fmt == NL4 && mode != GU_LAYER)
     return mode == GU_COMPOSED ? go(k_gate_up<NL4, GU_COMPOSED, NL4, true>)
            : mode == GU_FUSED  ? go(k_gate_up<NL4, GU_FUSED, NL4, true>)
+           : one               ? go(k_gate_up<NL4, GU_ROUTED, NL4, true, true>)
                                : go(k_gate_up<NL4, GU_ROUTED, NL4, true>);
   switch (fmt) {
     MOE_GU(Q8_0)
@@ -3487,11 +3500,14 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
     ga.ctr = (uint32_t*)(ws + kCtrOff);
     ga.spin_limit = 1 << 22;
   }
-  const hipError_t e = launch_gu(base_fmt(L->fmt_gate_up), base_fmt(L->fmt_down), mode, ga, grid, bytes, st);
+  // a routed one-token window over at most 128 experts takes the kernel compiled for it alone
+  const bool one = mode == GU_ROUTED && T == 1 && n_tokens == 1 && L->n_experts <= 128;
+  const hipError_t e = launch_gu(base_fmt(L->fmt_gate_up), base_fmt(L->fmt_down), mode, one, ga, grid, bytes, st);
   {
     static const char* mn[] = {"GU_COMPOSED", "GU_FUSED", "GU_ROUTED", "GU_LAYER"};
-    char ex[96];
-    snprintf(ex, sizeof ex, "%d streaming waves, %d-row passes, %d x %d KB ring slots", sw, G.rp, S.NS, S.M);
+    char ex[160];
+    snprintf(ex, sizeof ex, "%d streaming waves, %d-row passes, %s%s", sw, G.rp,
+             ga.regw ? "weights into registers" : "direct-to-LDS ring", one ? ", one-token instance" : "");
     note_choice("gate/up", L->fmt_gate_up, "k_gate_up", mn[mode & 3], grid, kGuThreads, bytes, ex);
   }
   return e == hipSuccess ? MOE_OK : hip_fail(e, "gate/up kernel");
