@@ -1315,9 +1315,10 @@ __host__ __device__ inline int ly_down_bytes(int cap_entries, int Ud, bool with_
 // arrays, T, E and n_embd: they come as the leading scalar arguments (copies of the struct's
 // fields), which the launch preloads into scalar registers, so those loads go out before any read
 // of the argument struct.
-// ONE: the routed launch of a one-token window over at most 128 experts, compiled on its own: the
-// ranked routing alone and one-entry dot passes (the per-token routing and the passes over several
-// entries would only add code the launch never runs, and that code measurably slows it).
+// ONE: the routed launch of a one-token window over at most 128 experts with n_embd <= 4096,
+// compiled on its own: the ranked routing alone, x in two register passes, one-entry dot passes
+// (the per-token routing, the other x stagings and the passes over several entries would only add
+// code the launch never runs, and that code measurably slows it).
 template <int FMT, int MODE, int FD = FMT, bool RW = false, bool ONE = false>
 __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict__ logits0,
                                                         const int8_t* __restrict__ nl4_0,
@@ -1356,7 +1357,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
   // routed, the other waves: x's rows (when they fit two register passes) and the gate and up
   // pointers of their experts, also from the preloaded arguments
   const int U0 = n_embd0 >> 5;
-  const bool early_x = RT && T0 * U0 * 8 <= 2 * kGuQThreads;
+  const bool early_x = RT && (ONE || T0 * U0 * 8 <= 2 * kGuQThreads);
   float4 xr0[2];
   uint64_t pg = 0, pu = 0, pd = 0;   // routed: expert q0's pointers (experts past kGuQThreads later)
   if constexpr (RT) {
@@ -2173,7 +2174,10 @@ __host__ __device__ inline int dn_smem_bytes(int lds_ring, int lds_act) {
 // the tile, dotted in wave passes of rp rows. Per-entry rows of o stay in LDS; at the end
 // every destination row is summed in ascending entry order: Y[d][r] = ((Y[d][r] + w_a o_a[r]) +
 // w_b o_b[r]) + ...
-template <int FMT, int MODE>
+// ONE: a one-token call (n_tokens == 1), compiled on its own with one-entry dot passes: a token's
+// groups hold one entry each (a larger group, from a caller's plan, takes one pass per entry: the
+// same sums), and the passes over several entries would only add code the launch never runs.
+template <int FMT, int MODE, bool ONE = false>
 __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const Geom& G = a.G;
@@ -2395,13 +2399,16 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
         for (int p0 = 0; p0 < c_nr; p0 += G.rp) {   // the chunk's rows in wave passes
           const int np = min(G.rp, c_nr - p0);
           const uint32_t rp0 = ra + (uint32_t)(p0 * G.rb);
-          for (int c0 = a0; c0 < a1; c0 += kSlots) {
-            const int ne = min(kSlots, a1 - c0);
+          for (int c0 = a0; c0 < a1; c0 += ONE ? 1 : kSlots) {
+            const int ne = ONE ? 1 : min(kSlots, a1 - c0);
             int sidx[kSlots];
 #pragma unroll
             for (int e = 0; e < kSlots; ++e) sidx[e] = e < ne ? c0 + e : 0;
-            dot_pass<FMT>((const MOE_LDS uint32_t*)ring, rp0, rp0, np, np, G, tb, act, sidx, ne,
-                          [&](int i, int e, float v) { ores[(c0 + e) * tr + o0 + p0 + i] = v; });
+            auto outd = [&](int i, int e, float v) { ores[(c0 + e) * tr + o0 + p0 + i] = v; };
+            if constexpr (ONE)
+              dot_pass_n<FMT, 1>((const MOE_LDS uint32_t*)ring, rp0, rp0, np, np, G, tb, act, sidx, outd);
+            else
+              dot_pass<FMT>((const MOE_LDS uint32_t*)ring, rp0, rp0, np, np, G, tb, act, sidx, ne, outd);
           }
         }
       }
@@ -3352,7 +3359,7 @@ int gu_layer_occupancy(int fmt, int fmt_down, int bytes) {
   return nb;
 }
 
-hipError_t launch_dn(int fmt, int mode, const DnArgs& da, int grid, int bytes, hipStream_t st) {
+hipError_t launch_dn(int fmt, int mode, bool one, const DnArgs& da, int grid, int bytes, hipStream_t st) {
   auto go = [&](auto kern) -> hipError_t {
     hipError_t e = allow_smem(kern, bytes);
     if (e != hipSuccess) return e;
@@ -3361,6 +3368,7 @@ hipError_t launch_dn(int fmt, int mode, const DnArgs& da, int grid, int bytes, h
   };
 #define MOE_DN(F) \
   case F:         \
+    if (one && mode == DN_DESC) return go(k_down<F, DN_DESC, true>); \
     return mode == DN_DESC ? go(k_down<F, DN_DESC>) : go(k_down<F, DN_PLAN>);
   switch (fmt) {
     MOE_DN(Q8_0)
@@ -3501,7 +3509,7 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
     ga.spin_limit = 1 << 22;
   }
   // a routed one-token window over at most 128 experts takes the kernel compiled for it alone
-  const bool one = mode == GU_ROUTED && T == 1 && n_tokens == 1 && L->n_experts <= 128;
+  const bool one = mode == GU_ROUTED && T == 1 && n_tokens == 1 && L->n_experts <= 128 && L->n_embd <= 4096;
   const hipError_t e = launch_gu(base_fmt(L->fmt_gate_up), base_fmt(L->fmt_down), mode, one, ga, grid, bytes, st);
   {
     static const char* mn[] = {"GU_COMPOSED", "GU_FUSED", "GU_ROUTED", "GU_LAYER"};
@@ -3514,7 +3522,7 @@ int run_gate_up(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode,
 }
 
 int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, const uint8_t* ws,
-             const uint8_t* hq, float* Y, int n_rows, int ldy, int grid_limit) {
+             const uint8_t* hq, float* Y, int n_rows, int ldy, int grid_limit, int n_tokens = 0) {
   const Geom G = down_geom(L);
   // one tile per CU: every CU streams the same share of the down rows
   int tr, rc;
@@ -3548,10 +3556,12 @@ int run_down(hipStream_t st, const moe_layer* L, const moe_plan* P, int mode, co
   da.ntiles = (L->n_embd + tr - 1) / tr;
   const int tiles = (L->n_embd + tr - 1) / tr;
   const int grid = grid_for(tiles, bytes, grid_limit);
-  const hipError_t e = launch_dn(base_fmt(L->fmt_down), mode, da, grid, bytes, st);
+  // a one-token call takes the kernel compiled for it alone
+  const bool one = mode == DN_DESC && n_tokens == 1;
+  const hipError_t e = launch_dn(base_fmt(L->fmt_down), mode, one, da, grid, bytes, st);
   {
     char ex[96];
-    snprintf(ex, sizeof ex, "%d-row tiles, %d-row chunks", tr, rc);
+    snprintf(ex, sizeof ex, "%d-row tiles, %d-row chunks%s", tr, rc, one ? ", one-token instance" : "");
     note_choice("down", L->fmt_down, "k_down", mode == DN_DESC ? "DN_DESC" : "DN_PLAN", grid, kDnThreads, bytes, ex);
   }
   return e == hipSuccess ? MOE_OK : hip_fail(e, "down kernel");
@@ -3833,7 +3843,7 @@ int moe_layer_down(void* stream, const moe_layer* L, const moe_plan* P, const vo
   const WsLayout wl = ws_layout(L, P);
   if (!ws || ws_bytes < wl.total || ((uintptr_t)ws & 255)) return MOE_E_WS;
   const uint8_t* b = (const uint8_t*)ws;
-  return run_down((hipStream_t)stream, L, P, DN_DESC, b, nullptr, Y, n_rows, ldy, grid_limit);
+  return run_down((hipStream_t)stream, L, P, DN_DESC, b, nullptr, Y, n_rows, ldy, grid_limit, n_tokens);
 }
 
 int moe_layer_decode(void* stream, const moe_layer* L, const moe_plan* P, const float* x, int n_tokens,
