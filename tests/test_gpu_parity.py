@@ -182,7 +182,8 @@ def test_layer_stages(name):
     assert np.array_equal(U.bits(r3["Y"]), U.bits(comp["Y"]))
 
 
-@pytest.mark.parametrize("E,T,k", [(128, 1, 8), (16, 2, 4), (8, 1, 2)])
+@pytest.mark.parametrize("E,T,k", [(128, 1, 8), (16, 2, 4), (8, 1, 2), (128, 2, 8), (128, 4, 8), (40, 3, 6),
+                                   (64, 8, 4), (256, 2, 8)])
 def test_routed_ties(E, T, k):
     """Exact ties in the logits through the routed step (the launch ranks the experts itself):
     at the k-th place (the lower id is chosen), inside the chosen set, and a -0 / +0 pair; the
@@ -200,7 +201,7 @@ def test_routed_ties(E, T, k):
     c = U.Case(f"ties_{E}_{T}", 256, 128, E, Q8_0, Q8_0, 9, need)
     c.logits, c.k, c.T = lg.astype(np.float32), k, T
     c.x = synth.activations(T, 256, 9)
-    n_rows = 8
+    n_rows = T + 4
     dst = np.arange(T, dtype=np.int32) + 2
     plan, ids, w = U.gpu_route_and_plan(c, T * k, T * k, entry_base=1, dst_of_token=dst)
     assert np.array_equal(ids.cpu().numpy(), oids)
