@@ -1,7 +1,7 @@
 // Device building blocks for the grouped routed-expert decode kernels (gfx950, wave64).
 //
 // * binary16 helpers and the q8_1 block quantizer (bit-exact IEEE float32: d = amax / 127,
-//   q = round half away from zero of x / d, clamped to +-127; s = fp16(f(d16) * sum q)). The
+//   q = x / d rounded half away from zero, clamped to +-127; s = fp16(f(d16) * sum q)). The
 //   36-byte q8_1 block is the activation format of "#2058 Verify window: the routed experts'
 //   gate/up with the group's q8_1 rows in shared memory", section "Why"; the rounding rule is the
 //   library's reading of a quantizer the pages leave unstated.
@@ -37,10 +37,59 @@ __device__ __forceinline__ uint32_t f2h(float f) {   // round to nearest even, s
 
 // ------------------------------------------------------------------ q8_1 ---------------------
 
-__device__ __forceinline__ float round_half_away(float v) {
-  float t = __builtin_truncf(v);
-  if (__builtin_fabsf(v - t) >= 0.5f) t += __builtin_copysignf(1.0f, v);  // v - t is exact
-  return t;
+// A block's scale d = amax / 127 and what quant_code needs besides it: rd = rcp(d), and whether
+// d is in the range where x rd is accurate (2^-100 <= d <= 2^100; false for 0, inf and NaN).
+struct QScale {
+  float d, rd;
+  bool ok;
+};
+__device__ __forceinline__ QScale q_scale(float amax) {
+  QScale s;
+  s.d = amax / 127.0f;
+  s.rd = __builtin_amdgcn_rcpf(s.d);
+  s.ok = s.d >= 0x1p-100f && s.d <= 0x1p100f;
+  return s;
+}
+
+// The code of a quotient y: rounded to the nearest integer, halves away from zero, clamped to +-127.
+__device__ __forceinline__ int code_of(float y) {
+  const float t = __builtin_truncf(y);
+  float r = __builtin_fabsf(y - t) >= 0.5f ? t + __builtin_copysignf(1.0f, y) : t;   // y - t is exact
+  r = r > 127.0f ? 127.0f : r;
+  r = r < -127.0f ? -127.0f : r;
+  return (int)r;
+}
+
+// The codes of x0..x3 in a block of scale s (|x| <= amax), packed little-endian: code_of(x / d)
+// with x / d the correctly rounded float32 quotient, as the definition has it, but without a
+// division in the common case. y = x rd is within 2^-15 of x / d (rcp is good to 1 ulp, the product
+// to half an ulp, and |x / d| < 128) and the rounded quotient within 2^-18 of x / d. While y is more
+// than 2^-14 from every half-integer, both lie strictly between the same two, so the code is
+// trunc(y + copysign(1/2, y)) (that sum is off by at most 2^-17, and no clamp is needed below
+// 127.5). A lane with some y + copysign(1/2, y) within 2^-13 of an integer (rare), and every lane
+// of a block whose scale is out of range, redoes its four with the division.
+__device__ __forceinline__ uint32_t quant_pack4(const float (&x)[4], const QScale& s) {
+  uint32_t packed = 0;
+  float gap = 1.0f;   // the least distance of a z from an integer (a NaN z gives code 0 either way)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float y = x[j] * s.rd;
+    const float z = y + __builtin_copysignf(0.5f, y);
+    gap = __builtin_fminf(gap, __builtin_fabsf(z - __builtin_rintf(z)));
+    packed |= ((uint32_t)(int)z & 0xFFu) << (8 * j);
+  }
+  if (!s.ok || gap <= 0x1p-13f) {
+    packed = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) packed |= ((uint32_t)code_of(x[j] / s.d) & 0xFFu) << (8 * j);
+  }
+  return packed;
+}
+// One code, as quant_pack4.
+__device__ __forceinline__ int quant_code(float x, const QScale& s) {
+  const float y = x * s.rd;
+  const float z = y + __builtin_copysignf(0.5f, y);
+  return (!s.ok || !(__builtin_fabsf(z - __builtin_rintf(z)) > 0x1p-13f)) ? code_of(x / s.d) : (int)z;
 }
 
 // s16 = fp16(f(d16) * isum). The product is exact in float32 (11 x 12 bits), so rounding it once
@@ -68,24 +117,16 @@ __device__ __forceinline__ QBlock quant_block(const float v[32]) {
     float a = __builtin_fabsf(v[i]);
     amax = a > amax ? a : amax;
   }
-  const float d = amax / 127.0f;
+  const QScale qs = q_scale(amax);
+  const float d = qs.d;
   QBlock b;
   int isum = 0;
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
-    uint32_t packed = 0;
+    const float x4[4] = {v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3]};
+    const uint32_t packed = amax != 0.0f ? quant_pack4(x4, qs) : 0u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int q = 0;
-      if (amax != 0.0f) {
-        float r = round_half_away(v[4 * w + j] / d);
-        r = r > 127.0f ? 127.0f : r;
-        r = r < -127.0f ? -127.0f : r;
-        q = (int)r;
-      }
-      isum += q;
-      packed |= ((uint32_t)q & 0xFFu) << (8 * j);
-    }
+    for (int j = 0; j < 4; ++j) isum += (int)(int8_t)(packed >> (8 * j));
     b.q[w] = packed;
   }
   b.d16 = f2h(d);

@@ -337,16 +337,16 @@ __host__ __device__ inline int act_bytes_kb(int rows, int U, bool with_s = false
 // Loads are branch-free (an index past the data reloads element 0, whose value is never used),
 // so they all issue back to back and the register arrays stay plain registers. `q` is the
 // thread's index among the NT threads (whole waves) that stage.
+// The rows are contiguous (row r, unit u is block r U + u at base + 32 (r U + u)), so float4 f of
+// the staged blocks sits at base + 4 f.
 template <int NT, int NP>
-__device__ __forceinline__ void act_issue_f(const float* base, long stride, int nblk, int U, int q,
-                                            float4 (&xr)[NP]) {
+__device__ __forceinline__ void act_issue_f(const float* base, int nblk, int q, float4 (&xr)[NP]) {
   if (nblk <= 0) return;
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     int f = q + p * NT;   // float4 f % 8 of block f / 8
     f = f < nblk * 8 ? f : 0;
-    const int b = f >> 3, r = b / U, u = b - r * U;
-    xr[p] = ((const float4*)(base + (long)r * stride + 32 * u))[f & 7];
+    xr[p] = ((const float4*)base)[f];
   }
 }
 
@@ -367,33 +367,26 @@ __device__ __forceinline__ void act_store_f(const float4 (&xr)[NP], int nblk, in
     m = fmaxf(m, dpp<0x141>(m));   // the other quad of the 8
     if (p * NT < nblk * 8 && f < nblk * 8) {
       const int b = f >> 3, part = f & 7;
-      const float d = m / 127.0f;
+      const QScale qs = q_scale(m);
       uint32_t packed = 0;
       if (m != 0.0f) {
         const float xs[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float r = round_half_away(xs[j] / d);
-          r = r > 127.0f ? 127.0f : r;
-          r = r < -127.0f ? -127.0f : r;
-          packed |= ((uint32_t)(int)r & 0xFFu) << (8 * j);
-        }
+        packed = quant_pack4(xs, qs);
       }
       if (part < 4)
         lo32[b * 4 + part] = packed;
       else
         hi32[b * 4 + part - 4] = packed;
-      if (part == 0) act.d[b] = h2f(f2h(d));
+      if (part == 0) act.d[b] = h2f(f2h(qs.d));
     }
   }
 }
 
 // The blocks past what the registers held: plain loads and the scalar quantizer.
 template <int NT>
-__device__ void act_rest_f(const float* base, long stride, int b0, int nblk, int U, int q, ActSplit act) {
+__device__ void act_rest_f(const float* base, int b0, int nblk, int q, ActSplit act) {
   for (int b = b0 + q; b < nblk; b += NT) {
-    const int r = b / U, u = b - r * U;
-    const float4* pp = (const float4*)(base + (long)r * stride + 32 * u);
+    const float4* pp = (const float4*)(base + 32 * (long)b);
     float v[32];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -456,39 +449,18 @@ __device__ void act_rest_q(const uint8_t* base, int b0, int nblk, ActSplit act) 
   }
 }
 
-// Stage nblk activation blocks into `act`: the register loads of the first blocks (up to
-// NT * NPMAX / 8 float rows, NT * NPMAX / 9 q8_1 rows) go out at once in a pass count rounded up to
-// a power of two (straight-line code, no register array merges), then mid() runs (work that must
-// not wait for those loads), then the blocks are quantized or split into LDS; blocks past the
-// register passes follow with plain loads.
+// Stage activation blocks into `act`: the register loads of the first blocks (float rows: nreg
+// blocks in NP passes; q8_1 rows: up to NT * NPMAX / 9 blocks in a pass count rounded up to a power
+// of two) go out at once (straight-line code, no register array merges), then mid() runs (work
+// that must not wait for those loads), then the blocks are quantized or split into LDS; blocks
+// past the register passes follow with plain loads.
 template <int NT, int NP, class Mid>
-__device__ __forceinline__ void act_stage_f_np(const float* base, long stride, int nreg, int U, int q,
-                                               const ActSplit& act, Mid& mid) {
+__device__ __forceinline__ void act_stage_f_np(const float* base, int nreg, int q, const ActSplit& act, Mid& mid) {
   float4 xr[NP];
-  act_issue_f<NT, NP>(base, stride, nreg, U, q, xr);
+  act_issue_f<NT, NP>(base, nreg, q, xr);
   mid(NP);
   act_store_f<NT, NP>(xr, nreg, q, act);
 }
-template <int NT, int NPMAX, class Mid>
-__device__ __forceinline__ void act_stage_f(const float* base, long stride, int nblk, int U, int q,
-                                            const ActSplit& act, Mid mid) {
-  const int nreg = min(nblk, NT * NPMAX / 8);
-  const int np = (nreg * 8 + NT - 1) / NT;
-  if (np == 0)
-    mid(0);
-  else if (np == 1)
-    act_stage_f_np<NT, 1>(base, stride, nreg, U, q, act, mid);
-  else if (np == 2)
-    act_stage_f_np<NT, 2>(base, stride, nreg, U, q, act, mid);
-  else if (np <= 4 || NPMAX < 8)
-    act_stage_f_np<NT, (NPMAX < 4 ? NPMAX : 4)>(base, stride, nreg, U, q, act, mid);
-  else if (np <= 8 || NPMAX < 16)
-    act_stage_f_np<NT, (NPMAX < 8 ? NPMAX : 8)>(base, stride, nreg, U, q, act, mid);
-  else
-    act_stage_f_np<NT, NPMAX>(base, stride, nreg, U, q, act, mid);
-  if (nblk > nreg) act_rest_f<NT>(base, stride, nreg, nblk, U, q, act);
-}
-
 template <int NT, int NP, class Mid>
 __device__ __forceinline__ void act_stage_q_np(const uint8_t* base, int nreg, const ActSplit& act, Mid& mid) {
   uint32_t qr[NP];
@@ -756,14 +728,9 @@ __device__ __forceinline__ void swiglu_q81_lanes(float gv, float uv, int l32, bo
   const float h = live ? swiglu(gv, uv) : 0.0f;
   if (live && hrow) hrow[l32] = h;
   const float amax = wave_max32(__builtin_fabsf(h));
-  const float d = amax / 127.0f;
-  int q = 0;
-  if (amax != 0.0f) {
-    float r = round_half_away(h / d);
-    r = r > 127.0f ? 127.0f : r;
-    r = r < -127.0f ? -127.0f : r;
-    q = (int)r;
-  }
+  const QScale qs = q_scale(amax);
+  const float d = qs.d;
+  const int q = amax != 0.0f ? quant_code(h, qs) : 0;
   const int isum = wave_sum32(q);
   if (live) {
     blk[4 + l32] = (uint8_t)(q & 0xFF);
@@ -786,14 +753,9 @@ __device__ __forceinline__ void swiglu_q81_split(float gv, float uv, int l32, bo
                                                  uint32_t* hi, float* dq, float* ds) {
   const float h = live ? swiglu(gv, uv) : 0.0f;
   const float amax = wave_max32(__builtin_fabsf(h));
-  const float d = amax / 127.0f;
-  int q = 0;
-  if (amax != 0.0f) {
-    float r = round_half_away(h / d);
-    r = r > 127.0f ? 127.0f : r;
-    r = r < -127.0f ? -127.0f : r;
-    q = (int)r;
-  }
+  const QScale qs = q_scale(amax);
+  const float d = qs.d;
+  const int q = amax != 0.0f ? quant_code(h, qs) : 0;
   const uint32_t b = (uint32_t)q & 0xFFu;
   const uint32_t w = b | (dppu<0x55>(b) << 8) | (dppu<0xAA>(b) << 16) | (dppu<0xFF>(b) << 24);   // quad lanes 1, 2, 3
   uint32_t sw = 0u;
@@ -1363,7 +1325,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
   if constexpr (RT) {
     if (!rw) {
       const int q = tid - 64 * kRtWaves;
-      if (early_x) act_issue_f<kGuQThreads, 2>(x0, n_embd0, T0 * U0, U0, q, xr0);
+      if (early_x) act_issue_f<kGuQThreads, 2>(x0, T0 * U0, q, xr0);
       if (q < E0) {
         pg = (uint64_t)(uintptr_t)gate0[q];
         pu = (uint64_t)(uintptr_t)up0[q];
@@ -1450,11 +1412,11 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
         none(2);
         act_store_f<kGuQThreads, 2>(xr0, nblk, q, act);
       } else if (nblk * 8 <= 2 * kGuQThreads) {
-        act_stage_f_np<kGuQThreads, 2>(a.x, a.A.n_embd, nblk, G.U, q, act, none);
+        act_stage_f_np<kGuQThreads, 2>(a.x, nblk, q, act, none);
       } else {
         const int nreg = min(nblk, kGuQThreads * kGuXPass / 8);
-        act_stage_f_np<kGuQThreads, kGuXPass>(a.x, a.A.n_embd, nreg, G.U, q, act, none);
-        if (nblk > nreg) act_rest_f<kGuQThreads>(a.x, a.A.n_embd, nreg, nblk, G.U, q, act);
+        act_stage_f_np<kGuQThreads, kGuXPass>(a.x, nreg, q, act, none);
+        if (nblk > nreg) act_rest_f<kGuQThreads>(a.x, nreg, nblk, q, act);
       }
     }
     if (q0 >= 0 && q0 < a.E) {
@@ -1501,22 +1463,17 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
         m = fmaxf(m, dpp<0x141>(m));   // the other quad of the 8 lanes of a block
         if (f < nf4) {
           const int bk = r0 * G.U + (f >> 3), part = f & 7;
-          const float d = m / 127.0f;
+          const QScale qs = q_scale(m);
           uint32_t packed = 0;
           if (m != 0.0f) {
             const float xs4[4] = {v.x, v.y, v.z, v.w};
-            for (int j = 0; j < 4; ++j) {
-              float r = round_half_away(xs4[j] / d);
-              r = r > 127.0f ? 127.0f : r;
-              r = r < -127.0f ? -127.0f : r;
-              packed |= ((uint32_t)(int)r & 0xFFu) << (8 * j);
-            }
+            packed = quant_pack4(xs4, qs);
           }
           if (part < 4)
             lo32[bk * 4 + part] = packed;
           else
             hi32[bk * 4 + part - 4] = packed;
-          if (part == 0) act.d[bk] = h2f(f2h(d));
+          if (part == 0) act.d[bk] = h2f(f2h(qs.d));
         }
       }
     }

@@ -43,6 +43,76 @@ def test_quantize_bitexact():
     U.assert_q81_equal(q.cpu().numpy(), oracle.quantize_q8_1(x), x)
 
 
+def near_tie_rows(n_rows, n, key):
+    """Rows of 32-value blocks whose quotients x / d sit on, or within a few ulp of, k + 1/2 for
+    every k in -127..126, under scales that are not powers of two (the division-free quantizer
+    must take the division there) and scales outside 2^-100..2^100 (every lane divides)."""
+    g = synth.rng(61, key)
+    amaxes = [np.float32(v) for v in (100.0, 3.7, 0.013, 1e-20, 1e-35, 1e36, 117.3)]
+    out = np.zeros((n_rows, n), np.float32)
+    for r in range(n_rows):
+        for b in range(n // 32):
+            amax = amaxes[(r * 7 + b) % len(amaxes)]
+            d = np.float32(amax / np.float32(127.0))
+            blk = np.empty(32, np.float32)
+            blk[0] = amax if b % 2 else -amax
+            ks = g.integers(-127, 127, 31)
+            steps = g.integers(-3, 4, 31)
+            for i in range(31):
+                x = np.float32(np.float32(ks[i] + 0.5) * d)
+                for _ in range(abs(int(steps[i]))):
+                    x = np.nextafter(x, np.float32(np.inf if steps[i] > 0 else -np.inf), dtype=np.float32)
+                blk[1 + i] = np.clip(x, -abs(amax), abs(amax))
+            out[r, 32 * b:32 * b + 32] = blk
+    return out
+
+
+def test_quantize_near_ties():
+    """Quotients on and next to every half-integer: the quantizer's bytes equal the oracle's (its
+    approximate quotient defers to the division there)."""
+    x = near_tie_rows(6, 2560, 1)
+    q = B.moe_quantize_q8_1(torch.from_numpy(x).to(U.dev()))
+    torch.cuda.synchronize()
+    U.assert_q81_equal(q.cpu().numpy(), oracle.quantize_q8_1(x), x)
+
+
+@pytest.mark.parametrize("name", ["nl4_t1", "q8_nl4_t3", "nl4_t4_shared"])
+def test_routed_near_tie_x(name):
+    """The same rows as x of the routed step: its in-kernel q8_1 of x gives the composed calls' bits
+    (whose quantizer the previous test pins to the oracle)."""
+    c = _routed(name)
+    c.x = near_tie_rows(c.T, c.n_embd, 2)
+    n_rows = 8
+    dst = np.arange(c.T, dtype=np.int32) + 1
+    plan, _, _ = U.gpu_route_and_plan(c, c.T * c.k, c.T * c.k, entry_base=0, dst_of_token=dst)
+    Y0 = U.y0_for(n_rows, c.n_embd, dst, 3)
+    comp = U.run_composed(c, plan, c.x, Y0, n_rows)
+    r = U.run_routed(c, c.x, Y0, entry_base=0, dst_of_token=dst)
+    f = U.run_fused(c, plan, c.x, Y0)
+    assert comp["err"] == 0 and r["err"] == 0 and f["err"] == 0
+    assert np.array_equal(U.bits(r["Y"]), U.bits(comp["Y"]))
+    assert np.array_equal(U.bits(f["Y"]), U.bits(comp["Y"]))
+
+
+def test_swiglu_near_ties():
+    """h = silu(30) u = 30 u (1 + e^-30 rounds to 1) placed on and next to half-integer quotients:
+    the q8_1 bytes of h equal the oracle's q8_1 of the same h."""
+    c = _routed("small_q8")
+    plan, _, _ = U.gpu_route_and_plan(c, c.T * c.k, c.T * c.k)
+    ecap = plan.ent_src.numel()
+    u_np = (near_tie_rows(ecap, c.n_ff, 3) / np.float32(30.0)).astype(np.float32)
+    g = torch.full((ecap, c.n_ff), 30.0, dtype=torch.float32, device=U.dev())
+    u = torch.from_numpy(u_np).to(U.dev())
+    h = torch.full((ecap, c.n_ff), float("nan"), dtype=torch.float32, device=U.dev())
+    hq = torch.full((ecap, c.n_ff // 32 * 36), 0xA5, dtype=torch.uint8, device=U.dev())
+    B.moe_swiglu_q8_1(plan, g, u, c.n_ff, hq, h=h)
+    torch.cuda.synchronize()
+    n = int(plan.get()["grp_start"][-1])
+    hh = h.cpu().numpy()[:n]
+    assert np.array_equal(U.bits(hh), U.bits(oracle.swiglu(g.cpu().numpy()[:n], u_np[:n])))
+    U.assert_q81_equal(hq.cpu().numpy()[:n], oracle.quantize_q8_1(hh), hh)
+
+
 def test_quantize_golden():
     import json
     import os
