@@ -572,10 +572,101 @@ __device__ __forceinline__ void dot_pass_n(const MOE_LDS uint32_t* W, uint32_t r
   }
 }
 
+// dot_pass_n for planar NL4 rows that start on a 16-byte boundary of LDS (ra, rb0 and the row
+// stride multiples of 16): a unit's codes are one aligned 16-byte read at row + 16 u, its scale a
+// 2-byte read at row + d_b + 2 u (no realignment of unaligned dwords). The same lane map, unit
+// order and sums as dot_pass_n, so the same bits.
+template <int NE, class Out>
+__device__ __forceinline__ void dot_pass_pa(const MOE_LDS uint8_t* W8, uint32_t ra, uint32_t rb0, int half,
+                                            int nrows, const Geom& G, const Tables& tb, const ActSplit& act,
+                                            const int (&sidx)[kSlots], Out& out) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane >> G.lgL, li = lane & (G.L - 1);
+  float acc[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = 0.0f;
+  if (i < nrows) {
+    const MOE_LDS uint8_t* row = W8 + (i < half ? ra + (uint32_t)(i * G.rb) : rb0 + (uint32_t)((i - half) * G.rb));
+    const MOE_LDS u32x4* cp = (const MOE_LDS u32x4*)row;
+    const MOE_LDS uint16_t* sp = (const MOE_LDS uint16_t*)(row + G.ly.d_b);
+    auto unit_at = [&](int k) {
+      const int u = li + (k << G.lgL);
+      return u < G.U ? u : 0;
+    };
+    auto step = [&](const u32x4& c4, uint32_t s16, int k) {
+      const bool valid = li + (k << G.lgL) < G.U;
+      const int u = unit_at(k);
+      uint32_t q[NE][8];
+      float dx[NE];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) act.get(sidx[e], u, q[e], dx[e]);
+      __builtin_amdgcn_sched_barrier(0);   // keep the reads above ahead of the decode
+      const float sc = h2f(s16);
+      uint32_t c[8];
+      c[0] = lut16(c4.x, tb);
+      c[1] = lut16(c4.y, tb);
+      c[2] = lut16(c4.z, tb);
+      c[3] = lut16(c4.w, tb);
+      c[4] = lut16(c4.x >> 4, tb);
+      c[5] = lut16(c4.y >> 4, tb);
+      c[6] = lut16(c4.z >> 4, tb);
+      c[7] = lut16(c4.w >> 4, tb);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        int s0 = __builtin_amdgcn_sdot4((int)c[0], (int)q[e][0], 0, false);
+        int s1 = __builtin_amdgcn_sdot4((int)c[1], (int)q[e][1], 0, false);
+        s0 = __builtin_amdgcn_sdot4((int)c[2], (int)q[e][2], s0, false);
+        s1 = __builtin_amdgcn_sdot4((int)c[3], (int)q[e][3], s1, false);
+        s0 = __builtin_amdgcn_sdot4((int)c[4], (int)q[e][4], s0, false);
+        s1 = __builtin_amdgcn_sdot4((int)c[5], (int)q[e][5], s1, false);
+        s0 = __builtin_amdgcn_sdot4((int)c[6], (int)q[e][6], s0, false);
+        s1 = __builtin_amdgcn_sdot4((int)c[7], (int)q[e][7], s1, false);
+        const float prod = (sc * dx[e]) * (float)(s0 + s1);
+        acc[e] = acc[e] + (valid ? prod : 0.0f);
+      }
+    };
+    u32x4 c0 = cp[unit_at(0)], c1;
+    uint32_t s0 = sp[unit_at(0)], s1;
+    MOE_WAIT_LGKM0;
+    for (int k = 0; k < G.upl; k += 2) {
+      c1 = cp[unit_at(k + 1)];
+      s1 = sp[unit_at(k + 1)];
+      __builtin_amdgcn_sched_barrier(0);
+      step(c0, s0, k);
+      if (k + 1 < G.upl) {
+        c0 = cp[unit_at(k + 2)];
+        s0 = sp[unit_at(k + 2)];
+        __builtin_amdgcn_sched_barrier(0);
+        step(c1, s1, k + 1);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = group_sum(acc[e], G.L);
+  if (i < nrows) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      if ((e & (G.L - 1)) == li) out(i, e, acc[e]);
+  }
+}
+
+// pa: planar NL4 rows at 16-byte boundaries (dot_pass_pa)
 template <int FMT, class Out>
 __device__ __forceinline__ void dot_pass(const MOE_LDS uint32_t* W, uint32_t ra, uint32_t rb0, int half,
                                          int nrows, const Geom& G, const Tables& tb, const ActSplit& act,
-                                         const int (&sidx)[kSlots], int ne, Out out) {
+                                         const int (&sidx)[kSlots], int ne, Out out, bool pa = false) {
+  if constexpr (FMT == NL4) {
+    if (pa) {
+      const MOE_LDS uint8_t* W8 = (const MOE_LDS uint8_t*)W;
+      switch (ne) {
+        case 1: dot_pass_pa<1>(W8, ra, rb0, half, nrows, G, tb, act, sidx, out); break;
+        case 2: dot_pass_pa<2>(W8, ra, rb0, half, nrows, G, tb, act, sidx, out); break;
+        case 3: dot_pass_pa<3>(W8, ra, rb0, half, nrows, G, tb, act, sidx, out); break;
+        default: dot_pass_pa<4>(W8, ra, rb0, half, nrows, G, tb, act, sidx, out); break;
+      }
+      return;
+    }
+  }
   switch (ne) {
     case 1: dot_pass_n<FMT, 1>(W, ra, rb0, half, nrows, G, tb, act, sidx, out); break;
     case 2: dot_pass_n<FMT, 2>(W, ra, rb0, half, nrows, G, tb, act, sidx, out); break;
@@ -1648,6 +1739,9 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
   };
   // register-direct (planar NL4): this lane's units of the chunk's rows straight into registers
   constexpr bool regw = RW;
+  // planar NL4 rows of a 16-byte multiple: a pass whose spans land 16-byte aligned takes the
+  // aligned reads
+  const bool pa_rows = FMT == NL4 && G.ly.c_a == 16u && G.ly.c_b == 0u && (G.rb & 15) == 0;
   RegW rwt;
   // the scale planes' lanes: lane j < rp U / 8 takes piece sj of the wave's row sri
   const int s16 = G.U >> 3, sri = lane / max(s16, 1), sj = lane - sri * s16;
@@ -1821,10 +1915,16 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
           }
           MOE_LDS float* st = stage + c0 * 64 + prow;
           auto outl = [&](int i, int e, float v) { st[e * 64 + (i < half ? i : 32 + i - half)] = v; };
-          if constexpr (ONE)
+          const bool pa = pa_rows && ((ra | rb0) & 15u) == 0;
+          if constexpr (ONE && FMT == NL4) {
+            if (pa)
+              dot_pass_pa<1>((const MOE_LDS uint8_t*)ring, ra, rb0, half, G.rp, G, tb, act, sidx, outl);
+            else
+              dot_pass_n<FMT, 1>((const MOE_LDS uint32_t*)ring, ra, rb0, half, G.rp, G, tb, act, sidx, outl);
+          } else if constexpr (ONE)
             dot_pass_n<FMT, 1>((const MOE_LDS uint32_t*)ring, ra, rb0, half, G.rp, G, tb, act, sidx, outl);
           else
-            dot_pass<FMT>((const MOE_LDS uint32_t*)ring, ra, rb0, half, G.rp, G, tb, act, sidx, nc, outl);
+            dot_pass<FMT>((const MOE_LDS uint32_t*)ring, ra, rb0, half, G.rp, G, tb, act, sidx, nc, outl, pa);
         }
       }
       if (!regw && kc + NS < nch) {
@@ -2338,6 +2438,9 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
   lds_barrier();
 
   // ---- 3. tiles
+  // planar NL4 rows of a 16-byte multiple: a chunk that lands 16-byte aligned takes the aligned
+  // reads (one-token launch)
+  const bool pa = FMT == NL4 && G.ly.c_a == 16u && G.ly.c_b == 0u && (G.rb & 15) == 0;
   int kc = 0;
   for (int kt = 0; kt < ntw; ++kt) {
     const int t = (int)blockIdx.x + kt * (int)gridDim.x;
@@ -2362,10 +2465,16 @@ __global__ __launch_bounds__(kDnThreads) void k_down(DnArgs a) {
 #pragma unroll
             for (int e = 0; e < kSlots; ++e) sidx[e] = e < ne ? c0 + e : 0;
             auto outd = [&](int i, int e, float v) { ores[(c0 + e) * tr + o0 + p0 + i] = v; };
-            if constexpr (ONE)
+            if constexpr (ONE && FMT == NL4) {
+              if (pa && (rp0 & 15u) == 0)
+                dot_pass_pa<1>(ring, rp0, rp0, np, np, G, tb, act, sidx, outd);
+              else
+                dot_pass_n<FMT, 1>((const MOE_LDS uint32_t*)ring, rp0, rp0, np, np, G, tb, act, sidx, outd);
+            } else if constexpr (ONE)
               dot_pass_n<FMT, 1>((const MOE_LDS uint32_t*)ring, rp0, rp0, np, np, G, tb, act, sidx, outd);
             else
-              dot_pass<FMT>((const MOE_LDS uint32_t*)ring, rp0, rp0, np, np, G, tb, act, sidx, ne, outd);
+              dot_pass<FMT>((const MOE_LDS uint32_t*)ring, rp0, rp0, np, np, G, tb, act, sidx, ne, outd,
+                            pa && (rp0 & 15u) == 0);
           }
         }
       }
