@@ -1865,7 +1865,14 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
         wait_vm((issued - 1 - kc) * M);
       }
       MOE_LDS uint8_t* slot = myring + slot_of(kc, NS) * M * 1024;
-      if (wgv && regw) {
+      if (wgv && regw && ONE) {   // a one-token window: the group's one entry (the token), one pass
+        const int prow = (wave + q * a.sw) * half;
+        const int sidx[kSlots] = {};
+        MOE_LDS float* st = stage + prow;
+        wait_vm(G.upl);   // the scale planes (issued before this lane's code loads)
+        auto outr = [&](int i, int e, float v) { st[e * 64 + (i < half ? i : 32 + i - half)] = v; };
+        dot_pass_reg_n<1>(rwt, (const MOE_LDS uint16_t*)myring, G.rp, G, tb, act, sidx, outr);
+      } else if (wgv && regw) {
         const int prow = (wave + q * a.sw) * half;
         uint64_t rest = tm;
         for (int c0 = 0; c0 < ne; c0 += kRegSlots) {
@@ -1886,10 +1893,7 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
           MOE_LDS float* st = stage + c0 * 64 + prow;
           if (c0 == 0) wait_vm(G.upl);   // the scale planes (issued before this lane's code loads)
           auto outr = [&](int i, int e, float v) { st[e * 64 + (i < half ? i : 32 + i - half)] = v; };
-          if constexpr (ONE)
-            dot_pass_reg_n<1>(rwt, (const MOE_LDS uint16_t*)myring, G.rp, G, tb, act, sidx, outr);
-          else
-            dot_pass_reg(rwt, (const MOE_LDS uint16_t*)myring, G.rp, G, tb, act, sidx, nc, outr);
+          dot_pass_reg(rwt, (const MOE_LDS uint16_t*)myring, G.rp, G, tb, act, sidx, nc, outr);
         }
       } else if (wgv) {
         const int prow = (wave + q * a.sw) * half;   // first h row of the pass inside the block
