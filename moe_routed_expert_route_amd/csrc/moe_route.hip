@@ -1947,6 +1947,9 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
           (r < 32 ? a.g : a.u)[(size_t)(e0 + a0 + e) * a.ld + blk * 32 + (r & 31)] = stage[idx];
         }
       } else {
+        // (register-direct instances read the destinations again here rather than hold them in
+        // scalar registers through the stream: measured faster there, slower in the others)
+        const GuArgs ah = RW ? args_after<GuArgs>(kGuArgsOff) : a;
         // 32 lanes per entry; every half-wave runs each round (the shuffles need all 32 lanes)
         for (int base = 0; base < ne; base += kGuThreads / 32) {
           const int e = base + (tid >> 5), l32 = tid & 31;
@@ -1955,8 +1958,8 @@ __global__ __launch_bounds__(kGuThreads) void k_gate_up(const float* __restrict_
           const float gv = live ? stage[e * 64 + l32] : 0.0f;
           const float uv = live ? stage[e * 64 + 32 + l32] : 0.0f;
           const size_t bk = (size_t)(a0 + (live ? e : 0)) * nb + blk;
-          swiglu_q81_split<MODE == GU_LAYER>(gv, uv, l32, live, a.hq_lo + 4 * bk, a.hq_hi + 4 * bk, a.hq_d + bk,
-                                              a.hq_s ? a.hq_s + bk : nullptr);
+          swiglu_q81_split<MODE == GU_LAYER>(gv, uv, l32, live, ah.hq_lo + 4 * bk, ah.hq_hi + 4 * bk, ah.hq_d + bk,
+                                              ah.hq_s ? ah.hq_s + bk : nullptr);
         }
       }
     }
