@@ -478,7 +478,7 @@ def main():
                     help="first copy 256 MiB device to device (a known-size kernel for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this build "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the library "
               "runs on a single GPU (the path would shard by expert ownership, one rank per GPU)",
               file=sys.stderr)
         sys.exit(2)
