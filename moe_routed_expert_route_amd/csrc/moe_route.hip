@@ -2980,8 +2980,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
       // (4) this wave's 16 x 16 tile, block after block
       const MOE_LDS uint8_t* pa = codes + (16 * mt + l16) * kPfCS + 8 * q;
       const MOE_LDS uint8_t* pb = quant + (16 * nt + l16) * kPfCS + 8 * q;
-#pragma unroll 4
-      for (int bl = 0; bl < nblk; ++bl) {
+      auto block_products = [&](int bl) {
         const long av = *(const MOE_LDS long*)(pa + 32 * bl);
         const long bv = *(const MOE_LDS long*)(pb + 32 * bl);
         typedef int v4i __attribute__((ext_vector_type(4)));
@@ -2999,11 +2998,19 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(PfArgs a) {
         const float dwv[4] = {dw.x, dw.y, dw.z, dw.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float prod = (dwv[i] * dx) * (float)d[i];
-          if constexpr (FMT == Q5_1) prod = prod + mw[i] * sx;
-          acc[i] = acc[i] + prod;
+          if constexpr (FMT == Q5_1) {
+            const float prod = (dwv[i] * dx) * (float)d[i] + mw[i] * sx;
+            acc[i] = acc[i] + prod;
+          } else {
+            // one fused multiply-add per block (the products are sums of float roundings either
+            // way; this path is held to a tolerance, not to the decode path's bits)
+            acc[i] = __builtin_fmaf(dwv[i] * dx, (float)d[i], acc[i]);
+          }
         }
-      }
+      };
+      // (a straight-line form of whole chunks took 12 more VGPRs, one workgroup less per CU, and
+      // was slower)
+      for (int bl = 0; bl < nblk; ++bl) block_products(bl);
       __syncthreads();   // the products' reads of codes and quants are done before they are rewritten
     }
     // outputs: lane holds rows 4 q + i of its row tile, entry l16 of its entry tile
