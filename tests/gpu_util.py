@@ -81,6 +81,36 @@ def planar_twin(c):
     return p
 
 
+def offset_twin(c, off):
+    """The same case with every expert matrix copied to `off` bytes past a 256-byte boundary (an
+    even offset: weight pointers need only 2-byte alignment), the layout kept."""
+    import copy
+    assert off % 2 == 0
+    p = copy.copy(c)
+    d = dev()
+
+    def moved(t):
+        buf = torch.zeros(t.numel() + 256, dtype=torch.uint8, device=d)
+        buf[off:off + t.numel()] = t.reshape(-1).view(torch.uint8)
+        return buf
+
+    p.dg = {e: moved(t) for e, t in c.dg.items()}
+    p.du = {e: moved(t) for e, t in c.du.items()}
+    p.dd = {e: moved(t) for e, t in c.dd.items()}
+    zg = torch.zeros(synth.row_bytes(c.fmt_gu & 0xFF, c.n_embd) * c.n_ff + 256, dtype=torch.uint8, device=d)
+    zd = torch.zeros(synth.row_bytes(c.fmt_dn & 0xFF, c.n_ff) * c.n_embd + 256, dtype=torch.uint8, device=d)
+    pg = [p.dg[e].data_ptr() + off if e in p.dg else zg.data_ptr() for e in range(c.E)]
+    pu = [p.du[e].data_ptr() + off if e in p.du else zg.data_ptr() for e in range(c.E)]
+    pd = [p.dd[e].data_ptr() + off if e in p.dd else zd.data_ptr() for e in range(c.E)]
+    t64 = dict(dtype=torch.int64, device=d)
+    L = c.layer
+    p.layer = B.Layer.from_pointers(
+        c.n_embd, c.n_ff, L.fmt_gate_up, L.fmt_down,
+        torch.tensor(pg, **t64), torch.tensor(pu, **t64), torch.tensor(pd, **t64),
+        nl4=L.nl4, cb2=L.cb2, cb3=L.cb3, keep=(zg, zd, p.dg, p.du, p.dd))
+    return p
+
+
 def routed_case(name, n_embd, n_ff, E, k, T, fmt_gu, fmt_dn, key, ids=None):
     """Logits routed on the host by the oracle only to know which experts to generate."""
     if ids is None:

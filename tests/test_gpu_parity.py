@@ -402,6 +402,31 @@ def test_planar_skipped_group_same_bits(name):
         assert np.array_equal(U.bits(got["Y"]), U.bits(ref["Y"]))
 
 
+@pytest.mark.parametrize("name,planar,off", [("nl4_t1", True, 2), ("nl4_t1", True, 6), ("nl4_t2_shared", True, 10),
+                                             ("nl4_t4_shared", True, 2), ("nl4_t1", False, 2)])
+def test_unaligned_experts_same_bits(name, planar, off):
+    """Expert matrices that start 2, 6 or 10 bytes past a 16-byte boundary (weight pointers need
+    only 2-byte alignment) give the aligned layer's bits on every path: the planar register loads
+    then read unaligned 16-byte pieces, and the LDS passes take the realigning reads."""
+    c = _routed(name, key=11)
+    ref_case = U.planar_twin(c) if planar else c
+    moved = U.offset_twin(ref_case, off)
+    T, k = c.T, c.k
+    base, n_rows = 1, 8
+    dst = synth.rng(43, T).choice(n_rows, T, replace=False).astype(np.int32)
+    plan, _, _ = U.gpu_route_and_plan(c, T * k, T * k, entry_base=base, dst_of_token=dst)
+    Y0 = U.y0_for(n_rows, c.n_embd, dst, 4)
+    ref = U.run_composed(ref_case, plan, c.x, Y0, n_rows)
+    got = U.run_composed(moved, plan, c.x, Y0, n_rows)
+    assert ref["err"] == 0 and got["err"] == 0
+    for key in ("g", "u", "h", "Y"):
+        assert np.array_equal(U.bits(got[key]), U.bits(ref[key])), key
+    f = U.run_fused(moved, plan, c.x, Y0)
+    assert f["err"] == 0 and np.array_equal(U.bits(f["Y"]), U.bits(ref["Y"]))
+    r = U.run_routed(moved, c.x, Y0, entry_base=base, dst_of_token=dst)
+    assert r["err"] == 0 and np.array_equal(U.bits(r["Y"]), U.bits(ref["Y"]))
+
+
 @pytest.mark.parametrize("name,planar", [("nl4_t1", False), ("cb2_nl4_t4_zipf", False), ("nl4_t1", True),
                                          ("nl4_t2_shared", True), ("nl4_t4_shared", True)])
 def test_grid_invariance(name, planar):
