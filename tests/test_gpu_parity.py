@@ -488,6 +488,29 @@ def test_edges_q8_4096(ng):
                               U.bits(comp["Y"])), gl
 
 
+@pytest.mark.parametrize("fmt,planar", [(Q8_0, False), (NL4, True)])
+def test_one_token_plan_with_repeated_entries(fmt, planar):
+    """A caller's plan for one token whose groups hold 1, 2 and 3 entries (the token chosen again,
+    to different rows): the one-token down launch takes one pass per entry; the fused call gives
+    the composed calls' bits, and the stages hold against the oracle."""
+    n_embd, n_ff = (2560, 768) if fmt == NL4 else (512, 256)
+    exps = np.array([3, 7, 11], np.int32)
+    c = U.Case(f"rep_{fmt}", n_embd, n_ff, 16, fmt, fmt, 12, exps)
+    c.x = synth.activations(1, n_embd, 12)
+    p = dict(n_groups=3, grp_expert=exps, grp_start=np.array([4, 5, 7, 10], np.int32), entry_base=4,
+             ent_src=np.zeros(6, np.int32), ent_dst=np.array([2, 2, 5, 2, 5, 7], np.int32),
+             ent_w=np.array([0.3, 0.7, 0.2, 0.9, 0.45, 0.6], np.float32), T=1)
+    plan = B.Plan(4, 8, entry_capacity=4 + 8, device=U.dev())
+    plan.set(p)
+    cc = U.planar_twin(c) if planar else c
+    Y0 = U.y0_for(8, n_embd, p["ent_dst"], 7)
+    comp = U.run_composed(cc, plan, c.x, Y0, 8)
+    assert comp["err"] == 0
+    U.check_stages(c, p, comp, Y0)
+    fused = U.run_fused(cc, plan, c.x, Y0)
+    assert fused["err"] == 0 and np.array_equal(U.bits(fused["Y"]), U.bits(comp["Y"]))
+
+
 # (matrix, byte offset in the expert's Q8_0 matrix, bits): Q8_0 block = fp16 d (bytes 0-1), 32 quants
 CORRUPT = {
     "gate_quant": ("gate", 34 * 3 + 2, 0x40),     # row 0, block 3, quant 0
