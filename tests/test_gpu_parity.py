@@ -185,6 +185,9 @@ ROUTED = {
     "nl4x_t1": dict(n_embd=2560, n_ff=768, E=128, k=8, T=1, fg=NL4X, fd=NL4X),
     "nl4x_q51_t4_zipf": dict(n_embd=512, n_ff=512, E=16, k=4, T=4, fg=NL4X, fd=Q5_1, ids="zipf"),
     "cb2_nl4x_t2": dict(n_embd=768, n_ff=256, E=12, k=3, T=2, fg=CB2, fd=NL4X),
+    # the widest one-token window: 4096 columns at 32 lanes a row (two register passes per wave),
+    # 64 experts (logits rows padded to the ranking's power of two)
+    "nl4_4096_t1": dict(n_embd=4096, n_ff=512, E=64, k=6, T=1, fg=NL4, fd=NL4),
 }
 
 
@@ -355,7 +358,7 @@ def test_repack_bytes(fmt, ncols):
 
 @pytest.mark.parametrize("name", ["small_q8", "nl4_t1", "nl4_t2_shared", "nl4_t4_shared", "cb2_nl4_t4_zipf", "cb3_q8_t2",
                                   "nl4_cb2_t2", "cb2_cb3_t4", "q8_q51_t3", "nl4x_q51_t4_zipf",
-                                  "nl4_t4_shared_tiny"])
+                                  "nl4_t4_shared_tiny", "nl4_4096_t1"])
 def test_planar_layer_same_bits(name):
     """Experts repacked into the planar layout give the row-major layer's bits on every path:
     composed (g, u, h, q8_1 of h, Y), fused, routed in two launches, and the one-launch step."""
